@@ -1,0 +1,162 @@
+/*
+ * dion3.h -- C ABI of libdion3.so, the Dion3 optimizer step on AMD gfx950.
+ *
+ * The step (source: "Dion3: Full-Stack Orthogonal Updates", agihunt.info
+ * summary, level-1 and level-3 paragraphs; the paper abstract on
+ * arxivlens.com / scholarbro.com):
+ *   1. score every row of the momentum matrix M (n x m) by its l1 norm;
+ *   2. select the k = ceil(f n) best rows (ties: lowest row index);
+ *   3. orthogonalize the selected k x m submatrix X with Gram Newton-Schulz:
+ *      the quintic iteration runs on the small symmetric Gram R = X X^T
+ *      (X^T X when k > m), restarting once (iteration 3 by default) from
+ *      X <- Q X, R <- X X^T, Q <- I, and only then is Q multiplied back
+ *      onto X; fp16 storage, fp32 accumulation;
+ *   4. W[S] <- W[S] - lr * O for the selected rows only, and
+ *      M[S] <- mu * M[S] (one fp32 multiply) for the selected rows only.
+ *
+ * Conventions for every entry point:
+ *   - Matrices are row-major.  "Rows" are dim 0 (output neurons).
+ *   - Every data pointer is a DEVICE pointer owned by the caller.  The
+ *     library never allocates or frees device memory: scratch lives in the
+ *     caller's workspace `ws` (at least dion3_workspace_size() bytes,
+ *     256-byte aligned).
+ *   - fp16 data is IEEE binary16 passed as uint16_t.
+ *   - `stream` is a hipStream_t (NULL: the null stream).  Calls only enqueue
+ *     work on `stream` and return without synchronizing.
+ *   - Errors are status codes; nothing aborts or throws across the ABI.  All
+ *     argument checks run before the first launch, so on any error W, M and
+ *     the outputs are untouched.
+ *   - NaN or Inf in M or X gives undefined results (no check is made).
+ *   - Concurrent calls are safe when their workspaces and outputs are
+ *     disjoint.  The library holds no mutable global state besides the
+ *     thread-local last HIP error.
+ */
+#ifndef DION3_H
+#define DION3_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define DION3_API __attribute__((visibility("default")))
+#else
+#define DION3_API
+#endif
+
+typedef enum {
+  DION3_OK = 0,
+  DION3_ERR_ARG = -1,          /* a null required pointer or an out-of-range size/parameter */
+  DION3_ERR_WORKSPACE = -2,    /* ws is NULL, misaligned or smaller than dion3_workspace_size() */
+  DION3_ERR_UNSUPPORTED = -3,  /* a shape beyond the library's limits (see DION3_MAX_DIM) */
+  DION3_ERR_HIP = -4           /* a HIP call or launch failed; see dion3_last_hip_error() */
+} dion3_status;
+
+#define DION3_MAX_ITERS 16
+#define DION3_MAX_RESTARTS 4
+#define DION3_MAX_DIM (1 << 20)   /* n, m, k each at most this */
+#define DION3_MAX_BATCH 65535
+
+/* Newton-Schulz schedule.  Iteration t (1-based) uses the quintic
+ * coefficients abc[t-1] = (a, b, c): Z = a I + b R + c R^2.  An iteration
+ * listed in restart_at[0..n_restart-1] first materializes X <- Q X,
+ * recomputes R <- X X^T and resets Q <- I ("Dion3: Full-Stack Orthogonal
+ * Updates", agihunt.info, level-1 paragraph: one restart at the 3rd
+ * iteration).  Valid: 1 <= iters <= 16, 0 <= n_restart <= 4, each restart
+ * index in [2, iters], strictly increasing.  eps >= 0 is added to ||X||_F in
+ * the normalization X / (||X||_F + eps). */
+typedef struct {
+  int32_t iters;
+  int32_t n_restart;
+  int32_t restart_at[DION3_MAX_RESTARTS];
+  float abc[DION3_MAX_ITERS][3];
+  float eps;
+} dion3_ns_cfg;
+
+/* Default schedule: 5 iterations of Muon's quintic (3.4445, -4.7750,
+ * 2.0315), one restart at iteration 3, eps = 1e-7. */
+DION3_API void dion3_ns_cfg_default(dion3_ns_cfg* cfg);
+
+/* k = ceil(f * n) (level-3 paragraph of the agihunt summary), computed in
+ * exact rationals: f is read as the nearest fraction with denominator
+ * <= 2^20 (so 0.07 * 100 gives 7, not 8).  The result is clamped to [1, n].
+ * Returns -1 if n < 1 or f is not finite and positive. */
+DION3_API int64_t dion3_k_from_fraction(double f, int64_t n);
+
+/* Workspace bytes needed by dion3_row_select, dion3_gram_ns, dion3_step
+ * and dion3_step_megabatch for `batch` matrices of n x m with k selected
+ * rows (for dion3_gram_ns pass n = k).  Host-only; no device work. */
+DION3_API dion3_status dion3_workspace_size(int32_t batch, int64_t n, int64_t m, int64_t k, size_t* bytes);
+
+/* Steps 1-2 on `batch` matrices stored back to back: M[b] starts at
+ * M + b * n * ld (fp32, row stride ld >= m).  Writes idx[b * k + j]
+ * (int32, the k selected rows of matrix b in ascending order) and, when
+ * scores is not NULL, scores[b * n + i] = sum_j |M[b][i][j]| (fp64). */
+DION3_API dion3_status dion3_row_select(const float* M, int32_t batch, int64_t n, int64_t m, int64_t ld,
+                              int64_t k, int32_t* idx, double* scores,
+                              void* ws, size_t ws_bytes, void* stream);
+
+/* Step 3 alone on `batch` fp16 matrices X[b] (k x m, contiguous, X + b*k*m):
+ * normalizes each by its Frobenius norm, runs Gram Newton-Schulz with `cfg`
+ * (NULL: the default) and writes O[b] (k x m fp16, contiguous). */
+DION3_API dion3_status dion3_gram_ns(const uint16_t* X, uint16_t* O, int32_t batch, int64_t k, int64_t m,
+                           const dion3_ns_cfg* cfg, void* ws, size_t ws_bytes, void* stream);
+
+/* The whole step on one matrix: W and M are fp32 n x m with row stride ld.
+ * lr is the final step size (the caller applies the 1/sqrt(f) scaling of
+ * the level-3 paragraph); mu is the momentum decay of the selected rows.
+ * Rows outside the selected set are never written.  Optional outputs (may
+ * be NULL): idx_out[k] (int32 ascending) and O_out (k x m fp16, the
+ * orthogonalized update before scaling by lr). */
+DION3_API dion3_status dion3_step(float* W, float* M, int64_t n, int64_t m, int64_t ld, int64_t k,
+                        float lr, float mu, const dion3_ns_cfg* cfg,
+                        int32_t* idx_out, uint16_t* O_out,
+                        void* ws, size_t ws_bytes, void* stream);
+
+/* The whole step on `batch` same-shape matrices in one call ("megabatching",
+ * level-4 paragraph of the agihunt summary, reduced to one GPU: one launch
+ * sequence per shape group).  W and M are DEVICE arrays of `batch` device
+ * pointers.  Optional outputs: idx_out[batch][k], O_out[batch][k][m].
+ * Results equal `batch` separate dion3_step calls bit for bit. */
+DION3_API dion3_status dion3_step_megabatch(float* const* W, float* const* M, int32_t batch,
+                                  int64_t n, int64_t m, int64_t ld, int64_t k,
+                                  float lr, float mu, const dion3_ns_cfg* cfg,
+                                  int32_t* idx_out, uint16_t* O_out,
+                                  void* ws, size_t ws_bytes, void* stream);
+
+/* The symmetric products of the level-2 paragraph, usable on their own.
+ *
+ * dion3_syrk_f16: R[b] = A[b] A[b]^T for `batch` fp16 matrices A[b]
+ * (rows x cols, row stride lda, batch stride rows*lda).  R[b] is rows x rows
+ * fp16 with row stride ldr (batch stride rows*ldr); only lower-triangle
+ * tiles are computed and each is mirrored, so R is exactly symmetric.
+ * rows and cols must be multiples of 128 and lda, ldr multiples of 8. */
+DION3_API dion3_status dion3_syrk_f16(const uint16_t* A, uint16_t* R, int32_t batch, int64_t rows,
+                            int64_t cols, int64_t lda, int64_t ldr, void* stream);
+
+/* dion3_symm_f16 ("A^2 + B"): C[b] = alpha A[b] B[b] + beta D[b] + gamma I
+ * for symmetric, commuting s x s fp16 matrices A[b], B[b] (so the product is
+ * symmetric); D may be NULL when beta == 0.  All four share row stride ld and
+ * batch stride s*ld; s must be a multiple of 128, ld a multiple of 8.  Only
+ * lower-triangle tiles are computed, then mirrored.  C must not alias A, B
+ * or D. */
+DION3_API dion3_status dion3_symm_f16(const uint16_t* A, const uint16_t* B, const uint16_t* D, uint16_t* C,
+                            int32_t batch, int64_t s, int64_t ld, float alpha, float beta,
+                            float gamma, void* stream);
+
+DION3_API const char* dion3_status_string(dion3_status status);
+
+/* hipError_t of the last DION3_ERR_HIP returned on the calling thread (0 if none). */
+DION3_API int dion3_last_hip_error(void);
+
+/* Library version, for the binding's load check. */
+DION3_API int dion3_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DION3_H */

@@ -1,0 +1,299 @@
+"""ctypes binding of libdion3.so: argument marshalling only.
+
+Every step of the optimizer runs in the library's HIP kernels; this module
+turns torch tensors into device pointers, picks torch's current stream and
+keeps a workspace tensor.  If the library is missing it raises: there is no
+fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Tuple
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libdion3.so")
+
+DION3_OK = 0
+MAX_ITERS = 16
+MAX_RESTARTS = 4
+STATUS = {0: "ok", -1: "invalid argument", -2: "workspace missing, misaligned or too small",
+          -3: "shape beyond the library's limits", -4: "HIP call or kernel launch failed"}
+
+MUON_ABC = (3.4445, -4.7750, 2.0315)
+
+
+class Dion3Error(RuntimeError):
+    def __init__(self, status: int, where: str, hip_error: int = 0):
+        msg = f"{where}: {STATUS.get(status, 'unknown status')} (status {status}"
+        if status == -4:
+            msg += f", hipError {hip_error}"
+        super().__init__(msg + ")")
+        self.status = status
+        self.hip_error = hip_error
+
+
+class NsCfg(ctypes.Structure):
+    """Mirror of dion3_ns_cfg."""
+    _fields_ = [("iters", ctypes.c_int32), ("n_restart", ctypes.c_int32),
+                ("restart_at", ctypes.c_int32 * MAX_RESTARTS),
+                ("abc", (ctypes.c_float * 3) * MAX_ITERS), ("eps", ctypes.c_float)]
+
+
+_lib = None
+
+
+def _declare(lib):
+    c = ctypes
+    vp, i32, i64, f32, f64, sz = c.c_void_p, c.c_int32, c.c_int64, c.c_float, c.c_double, c.c_size_t
+    sig = {
+        "dion3_version": (c.c_int, []),
+        "dion3_ns_cfg_default": (None, [c.POINTER(NsCfg)]),
+        "dion3_k_from_fraction": (i64, [f64, i64]),
+        "dion3_workspace_size": (c.c_int, [i32, i64, i64, i64, c.POINTER(sz)]),
+        "dion3_row_select": (c.c_int, [vp, i32, i64, i64, i64, i64, vp, vp, vp, sz, vp]),
+        "dion3_gram_ns": (c.c_int, [vp, vp, i32, i64, i64, c.POINTER(NsCfg), vp, sz, vp]),
+        "dion3_step": (c.c_int, [vp, vp, i64, i64, i64, i64, f32, f32, c.POINTER(NsCfg), vp, vp,
+                                 vp, sz, vp]),
+        "dion3_step_megabatch": (c.c_int, [vp, vp, i32, i64, i64, i64, i64, f32, f32,
+                                           c.POINTER(NsCfg), vp, vp, vp, sz, vp]),
+        "dion3_syrk_f16": (c.c_int, [vp, vp, i32, i64, i64, i64, i64, vp]),
+        "dion3_symm_f16": (c.c_int, [vp, vp, vp, vp, i32, i64, i64, f32, f32, f32, vp]),
+        "dion3_status_string": (c.c_char_p, [c.c_int]),
+        "dion3_last_hip_error": (c.c_int, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+EXPORTED = ("dion3_version", "dion3_ns_cfg_default", "dion3_k_from_fraction",
+            "dion3_workspace_size", "dion3_row_select", "dion3_gram_ns", "dion3_step",
+            "dion3_step_megabatch", "dion3_syrk_f16", "dion3_symm_f16", "dion3_status_string",
+            "dion3_last_hip_error")
+
+
+def lib():
+    """Load libdion3.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m orthogonalizing_optimizer_amd.build`")
+        _lib = _declare(ctypes.CDLL(LIB_PATH))
+    return _lib
+
+
+def _check(status: int, where: str):
+    if status != DION3_OK:
+        raise Dion3Error(status, where, lib().dion3_last_hip_error() if status == -4 else 0)
+
+
+# ------------------------------------------------------------- host-only API
+
+def ns_cfg(iters: int = 5, restart_at: Sequence[int] = (3,),
+           coeffs: Optional[Sequence[Tuple[float, float, float]]] = None,
+           eps: float = 1e-7) -> NsCfg:
+    """Build a dion3_ns_cfg (validated by the library at call time)."""
+    cfg = NsCfg()
+    lib().dion3_ns_cfg_default(ctypes.byref(cfg))
+    if len(restart_at) > MAX_RESTARTS or iters > MAX_ITERS:
+        raise ValueError("too many restarts or iterations")
+    cfg.iters = iters
+    cfg.n_restart = len(restart_at)
+    for i, r in enumerate(restart_at):
+        cfg.restart_at[i] = int(r)
+    if coeffs is not None:
+        if len(coeffs) != iters:
+            raise ValueError("need one (a, b, c) per iteration")
+        for t, (a, b, c) in enumerate(coeffs):
+            cfg.abc[t][0], cfg.abc[t][1], cfg.abc[t][2] = a, b, c
+    cfg.eps = eps
+    return cfg
+
+
+def default_cfg() -> NsCfg:
+    cfg = NsCfg()
+    lib().dion3_ns_cfg_default(ctypes.byref(cfg))
+    return cfg
+
+
+def k_from_fraction(f: float, n: int) -> int:
+    k = lib().dion3_k_from_fraction(float(f), int(n))
+    if k < 0:
+        raise ValueError("invalid fraction or n")
+    return int(k)
+
+
+def workspace_size(batch: int, n: int, m: int, k: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib().dion3_workspace_size(batch, n, m, k, ctypes.byref(out)), "dion3_workspace_size")
+    return int(out.value)
+
+
+def status_string(status: int) -> str:
+    return lib().dion3_status_string(status).decode()
+
+
+# ------------------------------------------------------------- device API
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(device) -> int:
+    torch = _torch()
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+class Workspace:
+    """A reusable device workspace (a uint8 torch tensor, 256-byte aligned)."""
+
+    def __init__(self):
+        self.buf = None
+
+    def get(self, nbytes: int, device):
+        torch = _torch()
+        if self.buf is None or self.buf.numel() < nbytes or self.buf.device != torch.device(device):
+            self.buf = torch.empty(max(nbytes, 256) + 256, dtype=torch.uint8, device=device)
+        base = self.buf.data_ptr()
+        off = (-base) % 256
+        return base + off, self.buf.numel() - off
+
+
+_default_ws = Workspace()
+
+
+def _req(t, dtype, name):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}")
+
+
+def row_select(M, k: int, return_scores: bool = False, ws: Optional[Workspace] = None):
+    """Top-k l1 rows of M ([n, m] or [batch, n, m] fp32, rows contiguous)."""
+    torch = _torch()
+    _req(M, torch.float32, "M")
+    Mb = M.unsqueeze(0) if M.dim() == 2 else M
+    if Mb.dim() != 3 or Mb.stride(2) != 1 or Mb.stride(0) != Mb.shape[1] * Mb.stride(1):
+        raise ValueError("M must be [n, m] or [batch, n, m] with contiguous rows")
+    B, n, m = Mb.shape
+    ld = Mb.stride(1)
+    idx = torch.empty((B, k), dtype=torch.int32, device=M.device)
+    scores = torch.empty((B, n), dtype=torch.float64, device=M.device) if return_scores else None
+    p, nb = (ws or _default_ws).get(workspace_size(B, n, m, k), M.device)
+    _check(lib().dion3_row_select(Mb.data_ptr(), B, n, m, ld, k, idx.data_ptr(), _ptr(scores), p,
+                                  nb, _stream(M.device)), "dion3_row_select")
+    if M.dim() == 2:
+        idx = idx[0]
+        scores = scores[0] if scores is not None else None
+    return (idx, scores) if return_scores else idx
+
+
+def gram_ns(X, cfg: Optional[NsCfg] = None, ws: Optional[Workspace] = None):
+    """Gram Newton-Schulz of X ([k, m] or [batch, k, m] fp16, contiguous)."""
+    torch = _torch()
+    _req(X, torch.float16, "X")
+    if not X.is_contiguous():
+        raise ValueError("X must be contiguous")
+    Xb = X.unsqueeze(0) if X.dim() == 2 else X
+    B, k, m = Xb.shape
+    O = torch.empty_like(Xb)
+    p, nb = (ws or _default_ws).get(workspace_size(B, k, m, k), X.device)
+    _check(lib().dion3_gram_ns(Xb.data_ptr(), O.data_ptr(), B, k, m,
+                               ctypes.byref(cfg) if cfg is not None else None, p, nb,
+                               _stream(X.device)), "dion3_gram_ns")
+    return O[0] if X.dim() == 2 else O
+
+
+def step(W, M, k: int, lr: float, mu: float, cfg: Optional[NsCfg] = None,
+         return_idx: bool = False, return_O: bool = False, ws: Optional[Workspace] = None):
+    """One Dion3 step on one matrix, in place on W and M (fp32, [n, m])."""
+    torch = _torch()
+    _req(W, torch.float32, "W")
+    _req(M, torch.float32, "M")
+    if W.shape != M.shape or W.dim() != 2 or W.stride() != M.stride() or W.stride(1) != 1:
+        raise ValueError("W and M must be [n, m] with equal strides and contiguous rows")
+    n, m = M.shape
+    idx = torch.empty(k, dtype=torch.int32, device=M.device) if return_idx else None
+    O = torch.empty((k, m), dtype=torch.float16, device=M.device) if return_O else None
+    p, nb = (ws or _default_ws).get(workspace_size(1, n, m, k), M.device)
+    _check(lib().dion3_step(W.data_ptr(), M.data_ptr(), n, m, M.stride(0), k, lr, mu,
+                            ctypes.byref(cfg) if cfg is not None else None, _ptr(idx), _ptr(O), p,
+                            nb, _stream(M.device)), "dion3_step")
+    return idx, O
+
+
+def pointer_array(tensors, device):
+    """Device array of the tensors' data pointers (int64)."""
+    torch = _torch()
+    return torch.tensor([t.data_ptr() for t in tensors], dtype=torch.int64).to(device)
+
+
+def step_megabatch(Ws, Ms, k: int, lr: float, mu: float, cfg: Optional[NsCfg] = None,
+                   return_idx: bool = False, return_O: bool = False,
+                   ws: Optional[Workspace] = None, ptrs=None):
+    """One Dion3 step on a group of same-shape matrices in one call.
+    ``ptrs`` may carry cached (W pointer array, M pointer array)."""
+    torch = _torch()
+    if len(Ws) != len(Ms) or not Ws:
+        raise ValueError("need equally many W and M matrices")
+    shape, stride = Ms[0].shape, Ms[0].stride()
+    for t in list(Ws) + list(Ms):
+        _req(t, torch.float32, "W/M")
+        if t.shape != shape or t.stride() != stride or t.dim() != 2 or t.stride(1) != 1:
+            raise ValueError("all matrices must share shape and strides with contiguous rows")
+    dev = Ms[0].device
+    B = len(Ms)
+    n, m = shape
+    if ptrs is None:
+        ptrs = (pointer_array(Ws, dev), pointer_array(Ms, dev))
+    idx = torch.empty((B, k), dtype=torch.int32, device=dev) if return_idx else None
+    O = torch.empty((B, k, m), dtype=torch.float16, device=dev) if return_O else None
+    p, nb = (ws or _default_ws).get(workspace_size(B, n, m, k), dev)
+    _check(lib().dion3_step_megabatch(ptrs[0].data_ptr(), ptrs[1].data_ptr(), B, n, m, stride[0], k,
+                                      lr, mu, ctypes.byref(cfg) if cfg is not None else None,
+                                      _ptr(idx), _ptr(O), p, nb, _stream(dev)),
+           "dion3_step_megabatch")
+    return idx, O
+
+
+def syrk_f16(A):
+    """R = A A^T for fp16 A ([rows, cols] or [batch, rows, cols], both multiples of 128)."""
+    torch = _torch()
+    _req(A, torch.float16, "A")
+    Ab = A.unsqueeze(0) if A.dim() == 2 else A
+    if not Ab.is_contiguous():
+        raise ValueError("A must be contiguous")
+    B, r, c = Ab.shape
+    R = torch.empty((B, r, r), dtype=torch.float16, device=A.device)
+    _check(lib().dion3_syrk_f16(Ab.data_ptr(), R.data_ptr(), B, r, c, c, r, _stream(A.device)),
+           "dion3_syrk_f16")
+    return R[0] if A.dim() == 2 else R
+
+
+def symm_f16(A, B, D=None, alpha: float = 1.0, beta: float = 0.0, gamma: float = 0.0):
+    """C = alpha A B + beta D + gamma I for symmetric commuting fp16 A, B."""
+    torch = _torch()
+    for t, nm in ((A, "A"), (B, "B")):
+        _req(t, torch.float16, nm)
+    Ab = A.unsqueeze(0) if A.dim() == 2 else A
+    Bb = B.unsqueeze(0) if B.dim() == 2 else B
+    Db = None if D is None else (D.unsqueeze(0) if D.dim() == 2 else D)
+    for t in (Ab, Bb) + ((Db,) if Db is not None else ()):
+        if not t.is_contiguous() or t.shape != Ab.shape:
+            raise ValueError("A, B, D must be contiguous and of one shape")
+    nb, s, _ = Ab.shape
+    C = torch.empty_like(Ab)
+    _check(lib().dion3_symm_f16(Ab.data_ptr(), Bb.data_ptr(), _ptr(Db), C.data_ptr(), nb, s, s,
+                                alpha, beta, gamma, _stream(A.device)), "dion3_symm_f16")
+    return C[0] if A.dim() == 2 else C

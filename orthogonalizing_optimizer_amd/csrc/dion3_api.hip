@@ -1,0 +1,457 @@
+// C ABI of libdion3.so: argument checks, workspace layout and the launch
+// schedule of the Dion3 step on one stream.  The contract of every entry
+// point is stated in include/dion3.h.
+#include <math.h>
+#include <string.h>
+
+#include "../../include/dion3.h"
+#include "dion3_internal.h"
+
+using namespace dion3;
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+dion3_status hip_fail(hipError_t e) {
+  g_last_hip_error = (int)e;
+  return DION3_ERR_HIP;
+}
+
+#define HIP_TRY(expr)                              \
+  do {                                             \
+    hipError_t _e = (expr);                        \
+    if (_e != hipSuccess) return hip_fail(_e);     \
+  } while (0)
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Workspace layout for `B` matrices of n x m with k selected rows.  The
+// selected rows X live in a zero-padded [kp][mp] fp16 block per matrix (the
+// "rows" layout, used for both orientations); the s x s Gram-side matrices
+// are zero-padded to sp x sp.  Zero padding is exact for Gram Newton-Schulz:
+// the padded block stays decoupled from the real one and its output rows
+// and columns are zero.
+struct Plan {
+  int B;
+  long long n, m, k;
+  bool tr;                 // k > m: the Gram is X^T X (s = m)
+  long long kp, mp, sp, Lp;
+  size_t o_l1, o_sq, o_idx, o_scale, o_Xa, o_Xb, o_R, o_Z, o_T, o_Q0, o_Q1, total;
+};
+
+Plan make_plan(int B, long long n, long long m, long long k) {
+  Plan P;
+  P.B = B; P.n = n; P.m = m; P.k = k;
+  P.tr = k > m;
+  P.kp = pad_to(k, kTile);
+  P.mp = pad_to(m, kTile);
+  P.sp = P.tr ? P.mp : P.kp;
+  P.Lp = P.tr ? P.kp : P.mp;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
+  P.o_l1 = take((size_t)B * n * 8);
+  P.o_sq = take((size_t)B * n * 8);
+  P.o_idx = take((size_t)B * k * 4);
+  P.o_scale = take((size_t)B * 8);
+  const size_t xb = (size_t)B * P.kp * P.mp * 2, sb = (size_t)B * P.sp * P.sp * 2;
+  P.o_Xa = take(xb);
+  P.o_Xb = take(xb);
+  P.o_R = take(sb);
+  P.o_Z = take(sb);
+  P.o_T = take(sb);
+  P.o_Q0 = take(sb);
+  P.o_Q1 = take(sb);
+  P.total = off;
+  return P;
+}
+
+bool dims_ok(long long v) { return v >= 1 && v <= DION3_MAX_DIM; }
+
+dion3_status check_cfg(const dion3_ns_cfg* c) {
+  if (c->iters < 1 || c->iters > DION3_MAX_ITERS) return DION3_ERR_ARG;
+  if (c->n_restart < 0 || c->n_restart > DION3_MAX_RESTARTS) return DION3_ERR_ARG;
+  int prev = 1;
+  for (int i = 0; i < c->n_restart; ++i) {
+    const int r = c->restart_at[i];
+    if (r < 2 || r > c->iters || r <= prev) return DION3_ERR_ARG;
+    prev = r;
+  }
+  if (!(c->eps >= 0.0f) || !isfinite(c->eps)) return DION3_ERR_ARG;
+  for (int t = 0; t < c->iters; ++t)
+    for (int j = 0; j < 3; ++j)
+      if (!isfinite(c->abc[t][j])) return DION3_ERR_ARG;
+  return DION3_OK;
+}
+
+dion3_status check_ws(const Plan& P, void* ws, size_t ws_bytes, size_t need) {
+  (void)P;
+  if (!ws || ((uintptr_t)ws & 255) != 0) return DION3_ERR_WORKSPACE;
+  if (ws_bytes < need) return DION3_ERR_WORKSPACE;
+  return DION3_OK;
+}
+
+bool restart_at(const dion3_ns_cfg& c, int t) {
+  for (int i = 0; i < c.n_restart; ++i)
+    if (c.restart_at[i] == t) return true;
+  return false;
+}
+
+// --------------------------------------------------------------- Gram NS
+
+struct Bufs {
+  f16 *Xa, *Xb, *R, *Z, *T, *Q0, *Q1;
+};
+
+Bufs carve(const Plan& P, void* ws) {
+  char* w = (char*)ws;
+  Bufs b;
+  b.Xa = (f16*)(w + P.o_Xa);
+  b.Xb = (f16*)(w + P.o_Xb);
+  b.R = (f16*)(w + P.o_R);
+  b.Z = (f16*)(w + P.o_Z);
+  b.T = (f16*)(w + P.o_T);
+  b.Q0 = (f16*)(w + P.o_Q0);
+  b.Q1 = (f16*)(w + P.o_Q1);
+  return b;
+}
+
+// R = X X^T on the Gram side (X^T X in rows layout when transposed).
+hipError_t gram(const Plan& P, const f16* X, f16* R, hipStream_t s) {
+  GemmDesc d = {};
+  d.A = X; d.sA = P.kp * P.mp; d.lda = (int)P.mp; d.a_col = P.tr;
+  d.B = X; d.sB = P.kp * P.mp; d.ldb = (int)P.mp; d.b_col = P.tr;
+  d.C = R; d.sC = P.sp * P.sp; d.ldc = (int)P.sp; d.c_t = false;
+  d.M = d.N = (int)P.sp; d.K = (int)P.Lp; d.batch = P.B;
+  d.lower = true; d.epilogue = false;
+  d.alpha = 1.0f;
+  return launch_gemm(d, s);
+}
+
+// C = alpha A B + beta D + gamma I for symmetric commuting s x s matrices.
+hipError_t symm(const Plan& P, const f16* A, const f16* B, const f16* D, f16* C, float alpha,
+                float beta, float gamma, bool epi, hipStream_t s) {
+  GemmDesc d = {};
+  const long long ss = P.sp * P.sp;
+  d.A = A; d.sA = ss; d.lda = (int)P.sp;
+  d.B = B; d.sB = ss; d.ldb = (int)P.sp;
+  d.C = C; d.sC = ss; d.ldc = (int)P.sp;
+  d.D = D; d.sD = ss; d.ldd = (int)P.sp;
+  d.M = d.N = d.K = (int)P.sp; d.batch = P.B;
+  d.lower = true; d.epilogue = epi;
+  d.alpha = alpha; d.beta = beta; d.gamma = gamma;
+  return launch_gemm(d, s);
+}
+
+// Y = Q X on the Gram side, written in rows layout.
+hipError_t rect(const Plan& P, const f16* Q, const f16* X, f16* Y, hipStream_t s) {
+  GemmDesc d = {};
+  d.A = Q; d.sA = P.sp * P.sp; d.lda = (int)P.sp; d.a_col = false;
+  d.B = X; d.sB = P.kp * P.mp; d.ldb = (int)P.mp; d.b_col = !P.tr;
+  d.C = Y; d.sC = P.kp * P.mp; d.ldc = (int)P.mp; d.c_t = P.tr;
+  d.M = (int)P.sp; d.N = (int)P.Lp; d.K = (int)P.sp; d.batch = P.B;
+  d.lower = false; d.epilogue = false;
+  d.alpha = 1.0f;
+  return launch_gemm(d, s);
+}
+
+// Gram Newton-Schulz on the normalized, padded X held in bufs.Xa ("Dion3:
+// Full-Stack Orthogonal Updates", agihunt.info, level-1 paragraph).  Every
+// matrix here is a polynomial in the first Gram, so all products commute,
+// are symmetric, and only their lower triangles are computed.  Returns the
+// buffer holding O (rows layout).
+dion3_status gram_ns(const Plan& P, const dion3_ns_cfg& cfg, const Bufs& bf, f16** out,
+                     hipStream_t s) {
+  f16 *X = bf.Xa, *Xalt = bf.Xb;
+  f16 *R = bf.R, *Z = bf.Z, *Tm = bf.T, *Q = bf.Q0, *Qn = bf.Q1;
+  HIP_TRY(gram(P, X, R, s));
+  bool q_identity = true;
+  const int T = cfg.iters;
+  for (int t = 1; t <= T; ++t) {
+    if (restart_at(cfg, t)) {
+      if (!q_identity) {
+        HIP_TRY(rect(P, Q, X, Xalt, s));
+        f16* tmp = X; X = Xalt; Xalt = tmp;
+      }
+      HIP_TRY(gram(P, X, R, s));
+      q_identity = true;
+    }
+    const float a = cfg.abc[t - 1][0], b = cfg.abc[t - 1][1], c = cfg.abc[t - 1][2];
+    // Z = a I + b R + c R^2  (the "A^2 + B" product)
+    HIP_TRY(symm(P, R, R, R, Z, c, b, a, true, s));
+    f16* Zv;
+    if (q_identity) {           // Q <- Z Q with Q = I: just adopt Z
+      f16* tmp = Q; Q = Z; Z = tmp;
+      Zv = Q;
+      q_identity = false;
+    } else {
+      HIP_TRY(symm(P, Z, Q, nullptr, Qn, 1.0f, 0.0f, 0.0f, false, s));
+      f16* tmp = Q; Q = Qn; Qn = tmp;
+      Zv = Z;
+    }
+    if (t < T && !restart_at(cfg, t + 1)) {   // R <- Z R Z
+      HIP_TRY(symm(P, Zv, R, nullptr, Tm, 1.0f, 0.0f, 0.0f, false, s));
+      HIP_TRY(symm(P, Tm, Zv, nullptr, R, 1.0f, 0.0f, 0.0f, false, s));
+    }
+  }
+  HIP_TRY(rect(P, Q, X, Xalt, s));
+  *out = Xalt;
+  return DION3_OK;
+}
+
+dion3_status step_impl(BatchPtr<float> W, BatchPtr<float> M, int batch, long long n, long long m,
+                       long long ld, long long k, float lr, float mu, const dion3_ns_cfg* cfg_in,
+                       int32_t* idx_out, uint16_t* O_out, void* ws, size_t ws_bytes,
+                       void* stream) {
+  if (batch < 1 || batch > DION3_MAX_BATCH) return DION3_ERR_ARG;
+  if (!dims_ok(n) || !dims_ok(m) || !dims_ok(k)) return DION3_ERR_UNSUPPORTED;
+  if (k > n || ld < m) return DION3_ERR_ARG;
+  if (!isfinite(lr) || !isfinite(mu)) return DION3_ERR_ARG;
+  dion3_ns_cfg cfg;
+  if (cfg_in) cfg = *cfg_in; else dion3_ns_cfg_default(&cfg);
+  dion3_status st = check_cfg(&cfg);
+  if (st != DION3_OK) return st;
+  const Plan P = make_plan(batch, n, m, k);
+  st = check_ws(P, ws, ws_bytes, P.total);
+  if (st != DION3_OK) return st;
+
+  hipStream_t s = (hipStream_t)stream;
+  char* w = (char*)ws;
+  double* l1 = (double*)(w + P.o_l1);
+  double* sq = (double*)(w + P.o_sq);
+  int* idx = (int*)(w + P.o_idx);
+  double* scale = (double*)(w + P.o_scale);
+  const Bufs bf = carve(P, ws);
+  const bool all = (k == n);
+
+  BatchPtr<const float> Mc = {M.base, M.stride, (const float* const*)M.ptrs};
+  HIP_TRY(launch_row_score_f32(Mc, batch, (int)n, (int)m, ld, all ? nullptr : l1, sq, s));
+  HIP_TRY(launch_topk(l1, sq, batch, (int)n, (int)k, idx, scale, (double)cfg.eps, s));
+  HIP_TRY(launch_gather_f32(M, batch, (int)n, (int)m, ld, idx, (int)k, scale, mu, true, bf.Xa,
+                            P.kp * P.mp, (int)P.kp, (int)P.mp, s));
+  f16* O = nullptr;
+  st = gram_ns(P, cfg, bf, &O, s);
+  if (st != DION3_OK) return st;
+  HIP_TRY(launch_update(W, batch, (int)n, (int)m, ld, idx, (int)k, O, P.kp * P.mp, (int)P.mp, lr,
+                        (f16*)O_out, s));
+  if (idx_out)
+    HIP_TRY(hipMemcpyAsync(idx_out, idx, (size_t)batch * k * sizeof(int32_t),
+                           hipMemcpyDeviceToDevice, s));
+  return DION3_OK;
+}
+
+// Best rational approximation p/q of x = mant / 2^e with q <= qmax
+// (continued-fraction convergents and the last semiconvergent).
+void best_rational(unsigned long long mant, int e, unsigned long long qmax,
+                   unsigned long long* pp, unsigned long long* qq) {
+  typedef unsigned __int128 u128;
+  const u128 num0 = mant, den0 = (u128)1 << e;
+  if (den0 <= qmax) {
+    u128 g = num0, h = den0;
+    while (h) { u128 t = g % h; g = h; h = t; }
+    *pp = (unsigned long long)(num0 / g);
+    *qq = (unsigned long long)(den0 / g);
+    return;
+  }
+  u128 p0 = 0, q0 = 1, p1 = 1, q1 = 0, nn = num0, dd = den0;
+  for (;;) {
+    const u128 a = nn / dd;
+    const u128 q2 = q0 + a * q1;
+    if (q2 > qmax) break;
+    const u128 p2 = p0 + a * p1;
+    p0 = p1; q0 = q1; p1 = p2; q1 = q2;
+    const u128 r = nn - a * dd;
+    nn = dd; dd = r;
+    if (dd == 0) break;
+  }
+  const u128 j = (qmax - q0) / q1;
+  const u128 pb = p0 + j * p1, qb = q0 + j * q1;
+  // |p/q - x| = |p 2^e - mant q| / (q 2^e); compare the two candidates.
+  auto dist = [&](u128 p, u128 q) {
+    const u128 lhs = p * den0, rhs = num0 * q;
+    return lhs > rhs ? lhs - rhs : rhs - lhs;
+  };
+  const u128 d1 = dist(p1, q1), db = dist(pb, qb);
+  if (d1 * qb <= db * q1) { *pp = (unsigned long long)p1; *qq = (unsigned long long)q1; }
+  else { *pp = (unsigned long long)pb; *qq = (unsigned long long)qb; }
+}
+
+}  // namespace
+
+extern "C" {
+
+int dion3_version(void) { return 1; }
+
+void dion3_ns_cfg_default(dion3_ns_cfg* cfg) {
+  if (!cfg) return;
+  memset(cfg, 0, sizeof(*cfg));
+  cfg->iters = 5;
+  cfg->n_restart = 1;
+  cfg->restart_at[0] = 3;
+  for (int t = 0; t < DION3_MAX_ITERS; ++t) {
+    cfg->abc[t][0] = 3.4445f;
+    cfg->abc[t][1] = -4.7750f;
+    cfg->abc[t][2] = 2.0315f;
+  }
+  cfg->eps = 1e-7f;
+}
+
+int64_t dion3_k_from_fraction(double f, int64_t n) {
+  if (n < 1 || !(f > 0.0) || !isfinite(f)) return -1;
+  if (f >= 1.0) return n;
+  const unsigned long long qmax = 1ull << 20;
+  unsigned long long p, q;
+  if (f < ldexp(1.0, -21)) {          // nearer to 0/1 than to 1/2^20
+    p = 0; q = 1;
+  } else {
+    int ex;
+    const double fr = frexp(f, &ex);  // f = fr * 2^ex, fr in [0.5, 1)
+    unsigned long long mant = (unsigned long long)ldexp(fr, 53);
+    int e = 53 - ex;                  // f = mant / 2^e, e <= 74
+    while (e > 0 && (mant & 1ull) == 0) { mant >>= 1; --e; }
+    best_rational(mant, e, qmax, &p, &q);
+  }
+  const unsigned __int128 num = (unsigned __int128)p * (unsigned long long)n;
+  unsigned __int128 k = (num + q - 1) / q;
+  if (k < 1) k = 1;
+  if (k > (unsigned __int128)n) k = n;
+  return (int64_t)k;
+}
+
+dion3_status dion3_workspace_size(int32_t batch, int64_t n, int64_t m, int64_t k, size_t* bytes) {
+  if (!bytes) return DION3_ERR_ARG;
+  if (batch < 1 || batch > DION3_MAX_BATCH) return DION3_ERR_ARG;
+  if (!dims_ok(n) || !dims_ok(m) || !dims_ok(k)) return DION3_ERR_UNSUPPORTED;
+  if (k > n) return DION3_ERR_ARG;
+  *bytes = make_plan(batch, n, m, k).total;
+  return DION3_OK;
+}
+
+dion3_status dion3_row_select(const float* M, int32_t batch, int64_t n, int64_t m, int64_t ld,
+                              int64_t k, int32_t* idx, double* scores, void* ws, size_t ws_bytes,
+                              void* stream) {
+  if (!M || !idx) return DION3_ERR_ARG;
+  if (batch < 1 || batch > DION3_MAX_BATCH) return DION3_ERR_ARG;
+  if (!dims_ok(n) || !dims_ok(m) || !dims_ok(k)) return DION3_ERR_UNSUPPORTED;
+  if (k > n || ld < m) return DION3_ERR_ARG;
+  const Plan P = make_plan(batch, n, m, k);
+  dion3_status st = check_ws(P, ws, ws_bytes, P.o_Xa);
+  if (st != DION3_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  char* w = (char*)ws;
+  double* l1 = (double*)(w + P.o_l1);
+  double* sq = (double*)(w + P.o_sq);
+  double* scale = (double*)(w + P.o_scale);
+  BatchPtr<const float> Mb = {M, n * ld, nullptr};
+  HIP_TRY(launch_row_score_f32(Mb, batch, (int)n, (int)m, ld, l1, sq, s));
+  HIP_TRY(launch_topk(l1, sq, batch, (int)n, (int)k, idx, scale, 0.0, s));
+  if (scores)
+    HIP_TRY(hipMemcpyAsync(scores, l1, (size_t)batch * n * sizeof(double), hipMemcpyDeviceToDevice,
+                           s));
+  return DION3_OK;
+}
+
+dion3_status dion3_gram_ns(const uint16_t* X, uint16_t* O, int32_t batch, int64_t k, int64_t m,
+                           const dion3_ns_cfg* cfg_in, void* ws, size_t ws_bytes, void* stream) {
+  if (!X || !O) return DION3_ERR_ARG;
+  if (batch < 1 || batch > DION3_MAX_BATCH) return DION3_ERR_ARG;
+  if (!dims_ok(k) || !dims_ok(m)) return DION3_ERR_UNSUPPORTED;
+  dion3_ns_cfg cfg;
+  if (cfg_in) cfg = *cfg_in; else dion3_ns_cfg_default(&cfg);
+  dion3_status st = check_cfg(&cfg);
+  if (st != DION3_OK) return st;
+  const Plan P = make_plan(batch, k, m, k);
+  st = check_ws(P, ws, ws_bytes, P.total);
+  if (st != DION3_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  char* w = (char*)ws;
+  double* sq = (double*)(w + P.o_sq);
+  int* idx = (int*)(w + P.o_idx);
+  double* scale = (double*)(w + P.o_scale);
+  const Bufs bf = carve(P, ws);
+  BatchPtr<const f16> Xb = {(const f16*)X, k * m, nullptr};
+  HIP_TRY(launch_row_score_f16(Xb, batch, (int)k, (int)m, m, sq, s));
+  HIP_TRY(launch_topk(nullptr, sq, batch, (int)k, (int)k, idx, scale, (double)cfg.eps, s));
+  HIP_TRY(launch_gather_f16(Xb, batch, (int)m, m, (int)k, scale, bf.Xa, P.kp * P.mp, (int)P.kp,
+                            (int)P.mp, s));
+  f16* Ob = nullptr;
+  st = gram_ns(P, cfg, bf, &Ob, s);
+  if (st != DION3_OK) return st;
+  BatchPtr<float> none = {nullptr, 0, nullptr};
+  HIP_TRY(launch_update(none, batch, (int)k, (int)m, m, nullptr, (int)k, Ob, P.kp * P.mp, (int)P.mp, 0.0f,
+                        (f16*)O, s));
+  return DION3_OK;
+}
+
+dion3_status dion3_step(float* W, float* M, int64_t n, int64_t m, int64_t ld, int64_t k, float lr,
+                        float mu, const dion3_ns_cfg* cfg, int32_t* idx_out, uint16_t* O_out,
+                        void* ws, size_t ws_bytes, void* stream) {
+  if (!W || !M) return DION3_ERR_ARG;
+  BatchPtr<float> Wb = {W, 0, nullptr}, Mb = {M, 0, nullptr};
+  return step_impl(Wb, Mb, 1, n, m, ld, k, lr, mu, cfg, idx_out, O_out, ws, ws_bytes, stream);
+}
+
+dion3_status dion3_step_megabatch(float* const* W, float* const* M, int32_t batch, int64_t n,
+                                  int64_t m, int64_t ld, int64_t k, float lr, float mu,
+                                  const dion3_ns_cfg* cfg, int32_t* idx_out, uint16_t* O_out,
+                                  void* ws, size_t ws_bytes, void* stream) {
+  if (!W || !M) return DION3_ERR_ARG;
+  BatchPtr<float> Wb = {nullptr, 0, W}, Mb = {nullptr, 0, M};
+  return step_impl(Wb, Mb, batch, n, m, ld, k, lr, mu, cfg, idx_out, O_out, ws, ws_bytes, stream);
+}
+
+dion3_status dion3_syrk_f16(const uint16_t* A, uint16_t* R, int32_t batch, int64_t rows,
+                            int64_t cols, int64_t lda, int64_t ldr, void* stream) {
+  if (!A || !R) return DION3_ERR_ARG;
+  if (batch < 1 || batch > DION3_MAX_BATCH) return DION3_ERR_ARG;
+  if (!dims_ok(rows) || !dims_ok(cols)) return DION3_ERR_UNSUPPORTED;
+  if (rows % kTile || cols % kTile || lda < cols || ldr < rows || lda % 8 || ldr % 8)
+    return DION3_ERR_ARG;
+  if (((uintptr_t)A | (uintptr_t)R) & 15) return DION3_ERR_ARG;
+  GemmDesc d = {};
+  d.A = (const f16*)A; d.sA = rows * lda; d.lda = (int)lda;
+  d.B = (const f16*)A; d.sB = rows * lda; d.ldb = (int)lda;
+  d.C = (f16*)R; d.sC = rows * ldr; d.ldc = (int)ldr;
+  d.M = d.N = (int)rows; d.K = (int)cols; d.batch = batch;
+  d.lower = true; d.alpha = 1.0f;
+  HIP_TRY(launch_gemm(d, (hipStream_t)stream));
+  return DION3_OK;
+}
+
+dion3_status dion3_symm_f16(const uint16_t* A, const uint16_t* B, const uint16_t* D, uint16_t* C,
+                            int32_t batch, int64_t s, int64_t ld, float alpha, float beta,
+                            float gamma, void* stream) {
+  if (!A || !B || !C || (beta != 0.0f && !D)) return DION3_ERR_ARG;
+  if (batch < 1 || batch > DION3_MAX_BATCH) return DION3_ERR_ARG;
+  if (!dims_ok(s)) return DION3_ERR_UNSUPPORTED;
+  if (s % kTile || ld < s || ld % 8) return DION3_ERR_ARG;
+  if (!isfinite(alpha) || !isfinite(beta) || !isfinite(gamma)) return DION3_ERR_ARG;
+  if (C == A || C == B || (D && C == D)) return DION3_ERR_ARG;
+  if (((uintptr_t)A | (uintptr_t)B | (uintptr_t)C | (uintptr_t)D) & 15) return DION3_ERR_ARG;
+  GemmDesc d = {};
+  const long long ss = s * ld;
+  d.A = (const f16*)A; d.sA = ss; d.lda = (int)ld;
+  d.B = (const f16*)B; d.sB = ss; d.ldb = (int)ld;
+  d.C = (f16*)C; d.sC = ss; d.ldc = (int)ld;
+  d.D = beta != 0.0f ? (const f16*)D : nullptr; d.sD = ss; d.ldd = (int)ld;
+  d.M = d.N = d.K = (int)s; d.batch = batch;
+  d.lower = true; d.epilogue = true;
+  d.alpha = alpha; d.beta = beta; d.gamma = gamma;
+  HIP_TRY(launch_gemm(d, (hipStream_t)stream));
+  return DION3_OK;
+}
+
+const char* dion3_status_string(dion3_status st) {
+  switch (st) {
+    case DION3_OK: return "ok";
+    case DION3_ERR_ARG: return "invalid argument";
+    case DION3_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case DION3_ERR_UNSUPPORTED: return "shape beyond the library's limits";
+    case DION3_ERR_HIP: return "HIP call or kernel launch failed";
+  }
+  return "unknown status";
+}
+
+int dion3_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

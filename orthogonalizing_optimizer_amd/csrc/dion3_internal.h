@@ -1,0 +1,72 @@
+// Internal interfaces between the C-ABI layer and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dion3 {
+
+typedef _Float16 f16;
+
+// A batch of same-shape matrices: either `ptrs[b]` (a device array of
+// pointers, the megabatch form) or `base + b * stride`.
+template <typename T>
+struct BatchPtr {
+  T* base;
+  long long stride;
+  T* const* ptrs;
+  __device__ __forceinline__ T* get(int b) const { return ptrs ? ptrs[b] : base + (long long)b * stride; }
+};
+
+// Tile edge of every GEMM output tile; workspace dimensions are padded to it.
+constexpr int kTile = 128;
+
+inline long long pad_to(long long x, long long p) { return (x + p - 1) / p * p; }
+
+// C = alpha * A * B^T (+ beta * D + gamma * I when `epilogue`), batched.
+//  A is logically M x K: row form A[m * lda + k], col form A[k * lda + m].
+//  B is logically N x K: row form B[n * ldb + k], col form B[k * ldb + n].
+//  C is M x N written C[m * ldc + n], or C[n * ldc + m] when c_t.
+//  lower: M == N, only tiles on or below the diagonal are computed and
+//  every element (r >= c) is written to both C[r][c] and C[c][r].
+// M, N must be multiples of 128, K a multiple of 64, ld* multiples of 8.
+struct GemmDesc {
+  const f16* A; long long sA; int lda; bool a_col;
+  const f16* B; long long sB; int ldb; bool b_col;
+  f16* C; long long sC; int ldc; bool c_t;
+  const f16* D; long long sD; int ldd;
+  int M, N, K, batch;
+  bool lower, epilogue;
+  float alpha, beta, gamma;
+};
+hipError_t launch_gemm(const GemmDesc& d, hipStream_t s);
+
+// Per-row l1 (optional) and sum of squares in fp64, one wave per row.
+hipError_t launch_row_score_f32(BatchPtr<const float> M, int batch, int n, int m, long long ld,
+                                double* l1, double* sq, hipStream_t s);
+hipError_t launch_row_score_f16(BatchPtr<const f16> X, int batch, int n, int m, long long ld,
+                                double* sq, hipStream_t s);
+
+// Top-k on l1 (ties to lowest index), ascending idx[b][k]; scale[b] =
+// 1 / (sqrt(sum_{i in S} sq[i]) + eps).  k == n selects every row.
+hipError_t launch_topk(const double* l1, const double* sq, int batch, int n, int k, int* idx,
+                       double* scale, double eps, hipStream_t s);
+
+// X[b][r][:] = fp16(M[b][idx[r]][:] * scale[b]) for r < k, zero padding up to
+// kp x mp; when decay, M[b][idx[r]][:] *= mu (one fp32 multiply).
+// idx == nullptr means the identity.
+hipError_t launch_gather_f32(BatchPtr<float> M, int batch, int n, int m, long long ld,
+                             const int* idx, int k, const double* scale, float mu, bool decay,
+                             f16* X, long long sX, int kp, int mp, hipStream_t s);
+hipError_t launch_gather_f16(BatchPtr<const f16> Xin, int batch, int m, long long ld, int k,
+                             const double* scale, f16* X, long long sX, int kp, int mp,
+                             hipStream_t s);
+
+// W[b][idx[r]][:] -= lr * O[b][r][:] (skipped when W has no pointers), and
+// O_out[b][r][:] = O[b][r][:m] when O_out is not null.  Row indices outside
+// [0, n) are skipped.
+hipError_t launch_update(BatchPtr<float> W, int batch, int n, int m, long long ld, const int* idx,
+                         int k, const f16* O, long long sO, int mp, float lr, f16* O_out,
+                         hipStream_t s);
+
+}  // namespace dion3

@@ -1,0 +1,356 @@
+// Row kernels of the Dion3 step on gfx950: l1 scoring, top-k selection,
+// gather + normalize + momentum decay, and the row-sparse weight update
+// ("Dion3: Full-Stack Orthogonal Updates", agihunt.info, level-3 paragraph:
+// k = ceil(f n) rows picked by l1 norm, only those weight rows updated, only
+// those momentum rows decayed by mu, the rest left untouched).
+//
+// Scoring, gather and update stream HBM: one 64-lane wave per row, 16-byte
+// loads when the row is 16-byte aligned.  Every reduction runs in a fixed
+// order in fp64, so results are deterministic run to run.
+#include "dion3_internal.h"
+
+namespace dion3 {
+namespace {
+
+typedef f16 half4 __attribute__((ext_vector_type(4)));
+typedef f16 half8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+// ------------------------------------------------------------- scoring
+
+__global__ __launch_bounds__(256) void k_row_score_f32(BatchPtr<const float> M, int n, int m,
+                                                       long long ld, double* __restrict__ l1,
+                                                       double* __restrict__ sq) {
+  const int b = blockIdx.y;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= n) return;
+  const float* __restrict__ src = M.get(b) + (long long)row * ld;
+  double a0 = 0.0, a1 = 0.0, q0 = 0.0, q1 = 0.0;
+  if (((uintptr_t)src & 15) == 0 && (m & 3) == 0) {
+    const float4* s4 = (const float4*)src;
+    const int m4 = m >> 2;
+    int j = lane;
+    for (; j + 64 < m4; j += 128) {
+      const float4 x = s4[j], y = s4[j + 64];
+      a0 += (double)fabsf(x.x) + (double)fabsf(x.y) + (double)fabsf(x.z) + (double)fabsf(x.w);
+      a1 += (double)fabsf(y.x) + (double)fabsf(y.y) + (double)fabsf(y.z) + (double)fabsf(y.w);
+      q0 += (double)x.x * x.x + (double)x.y * x.y + (double)x.z * x.z + (double)x.w * x.w;
+      q1 += (double)y.x * y.x + (double)y.y * y.y + (double)y.z * y.z + (double)y.w * y.w;
+    }
+    if (j < m4) {
+      const float4 x = s4[j];
+      a0 += (double)fabsf(x.x) + (double)fabsf(x.y) + (double)fabsf(x.z) + (double)fabsf(x.w);
+      q0 += (double)x.x * x.x + (double)x.y * x.y + (double)x.z * x.z + (double)x.w * x.w;
+    }
+  } else {
+    for (int j = lane; j < m; j += 64) {
+      const double x = (double)src[j];
+      a0 += fabs(x);
+      q0 += x * x;
+    }
+  }
+  const double a = wave_sum(a0 + a1), q = wave_sum(q0 + q1);
+  if (lane == 0) {
+    if (l1) l1[(long long)b * n + row] = a;
+    sq[(long long)b * n + row] = q;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_row_score_f16(BatchPtr<const f16> X, int n, int m,
+                                                       long long ld, double* __restrict__ sq) {
+  const int b = blockIdx.y;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= n) return;
+  const f16* __restrict__ src = X.get(b) + (long long)row * ld;
+  double q = 0.0;
+  if (((uintptr_t)src & 15) == 0 && (m & 7) == 0) {
+    const half8* s8 = (const half8*)src;
+    for (int j = lane; j < (m >> 3); j += 64) {
+      const half8 x = s8[j];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) q += (double)x[e] * (double)x[e];
+    }
+  } else {
+    for (int j = lane; j < m; j += 64) {
+      const double x = (double)src[j];
+      q += x * x;
+    }
+  }
+  q = wave_sum(q);
+  if (lane == 0) sq[(long long)b * n + row] = q;
+}
+
+// ------------------------------------------------------------- top-k
+
+constexpr int TK_THREADS = 1024;
+
+// Exclusive prefix sum over the block (one value per thread); returns the
+// block total through `total`.
+__device__ int block_exclusive_scan(int v, int* sh, int& total) {
+  const int tid = threadIdx.x;
+  sh[tid] = v;
+  __syncthreads();
+  for (int off = 1; off < TK_THREADS; off <<= 1) {
+    const int add = tid >= off ? sh[tid - off] : 0;
+    __syncthreads();
+    sh[tid] += add;
+    __syncthreads();
+  }
+  const int incl = sh[tid];
+  total = sh[TK_THREADS - 1];
+  __syncthreads();
+  return incl - v;
+}
+
+// One workgroup per matrix.  Scores are non-negative doubles, so their bit
+// patterns order like the values; an MSB-first 8-bit radix select finds the
+// k-th largest key T exactly, then rows with key > T and the lowest-index
+// rows with key == T are taken, compacted in index order.
+__global__ __launch_bounds__(TK_THREADS) void k_topk(const double* __restrict__ l1,
+                                                     const double* __restrict__ sq, int n, int k,
+                                                     int* __restrict__ idx,
+                                                     double* __restrict__ scale, double eps) {
+  __shared__ unsigned hist[256];
+  __shared__ int scan_sh[TK_THREADS];
+  __shared__ double red_sh[TK_THREADS];
+  __shared__ unsigned long long prefix_sh;
+  __shared__ int rem_sh;
+
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const double* __restrict__ sc = l1 + (long long)b * n;
+  const double* __restrict__ q = sq + (long long)b * n;
+  int* __restrict__ out = idx + (long long)b * k;
+
+  unsigned long long T = 0;
+  int need_eq = 0;
+  const bool all = (k >= n);
+  if (!all) {
+    unsigned long long prefix = 0, mask = 0;
+    int rem = k;
+    for (int shift = 56; shift >= 0; shift -= 8) {
+      for (int i = tid; i < 256; i += TK_THREADS) hist[i] = 0;
+      __syncthreads();
+      for (int i = tid; i < n; i += TK_THREADS) {
+        const unsigned long long key = (unsigned long long)__double_as_longlong(sc[i]);
+        if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+      }
+      __syncthreads();
+      if (tid == 0) {
+        int cum = 0, d = 255;
+        for (; d > 0; --d) {
+          if (cum + (int)hist[d] >= rem) break;
+          cum += (int)hist[d];
+        }
+        prefix_sh = prefix | ((unsigned long long)d << shift);
+        rem_sh = rem - cum;
+      }
+      __syncthreads();
+      prefix = prefix_sh;
+      rem = rem_sh;
+      mask |= 255ull << shift;
+      __syncthreads();
+    }
+    T = prefix;
+    need_eq = rem;
+  }
+
+  // Contiguous chunk per thread, so prefix sums follow index order.
+  const int per = (n + TK_THREADS - 1) / TK_THREADS;
+  const int c0 = min(n, tid * per), c1 = min(n, c0 + per);
+  int n_eq = 0;
+  if (!all)
+    for (int i = c0; i < c1; ++i)
+      n_eq += ((unsigned long long)__double_as_longlong(sc[i]) == T);
+  int tot;
+  const int eq_start = all ? 0 : block_exclusive_scan(n_eq, scan_sh, tot);
+  int n_sel = 0;
+  int eqb = eq_start;
+  for (int i = c0; i < c1; ++i) {
+    bool take = all;
+    if (!all) {
+      const unsigned long long key = (unsigned long long)__double_as_longlong(sc[i]);
+      take = key > T || (key == T && eqb < need_eq);
+      eqb += (key == T);
+    }
+    n_sel += take;
+  }
+  int pos = block_exclusive_scan(n_sel, scan_sh, tot);
+  // Second pass over the chunk: write the taken indices in index order and
+  // sum their squares (fixed order, then a fixed tree over the block).
+  double part = 0.0;
+  eqb = eq_start;
+  for (int i = c0; i < c1; ++i) {
+    bool take = all;
+    if (!all) {
+      const unsigned long long key = (unsigned long long)__double_as_longlong(sc[i]);
+      take = key > T || (key == T && eqb < need_eq);
+      eqb += (key == T);
+    }
+    if (take && pos < k) {
+      out[pos++] = i;
+      part += q[i];
+    }
+  }
+  red_sh[tid] = part;
+  __syncthreads();
+  for (int off = TK_THREADS / 2; off >= 1; off >>= 1) {
+    if (tid < off) red_sh[tid] += red_sh[tid + off];
+    __syncthreads();
+  }
+  if (tid == 0) scale[b] = 1.0 / (sqrt(red_sh[0]) + eps);
+}
+
+// ------------------------------------------------------------- gather
+
+__global__ __launch_bounds__(256) void k_gather_f32(BatchPtr<float> M, int n, int m, long long ld,
+                                                    const int* __restrict__ idx, int k,
+                                                    const double* __restrict__ scale, float mu,
+                                                    int decay, f16* __restrict__ X, long long sX,
+                                                    int kp, int mp) {
+  const int b = blockIdx.y;
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (r >= kp) return;
+  f16* __restrict__ dst = X + (long long)b * sX + (long long)r * mp;
+  int j0 = 0;
+  const int row = r < k ? (idx ? idx[(long long)b * k + r] : r) : -1;
+  if (row >= 0 && row < n) {
+    float* __restrict__ src = M.get(b) + (long long)row * ld;
+    const float s = (float)scale[b];
+    if (((uintptr_t)src & 15) == 0 && (m & 3) == 0) {
+      float4* s4 = (float4*)src;
+      half4* d4 = (half4*)dst;
+      for (int j = lane; j < (m >> 2); j += 64) {
+        const float4 x = s4[j];
+        half4 h;
+        h[0] = (f16)(x.x * s); h[1] = (f16)(x.y * s); h[2] = (f16)(x.z * s); h[3] = (f16)(x.w * s);
+        d4[j] = h;
+        if (decay) s4[j] = make_float4(mu * x.x, mu * x.y, mu * x.z, mu * x.w);
+      }
+    } else {
+      for (int j = lane; j < m; j += 64) {
+        const float x = src[j];
+        dst[j] = (f16)(x * s);
+        if (decay) src[j] = mu * x;
+      }
+    }
+    j0 = m;
+  }
+  for (int j = j0 + lane; j < mp; j += 64) dst[j] = (f16)0.0f;
+}
+
+__global__ __launch_bounds__(256) void k_gather_f16(BatchPtr<const f16> Xin, int m, long long ld,
+                                                    int k, const double* __restrict__ scale,
+                                                    f16* __restrict__ X, long long sX, int kp,
+                                                    int mp) {
+  const int b = blockIdx.y;
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (r >= kp) return;
+  f16* __restrict__ dst = X + (long long)b * sX + (long long)r * mp;
+  int j0 = 0;
+  if (r < k) {
+    const f16* __restrict__ src = Xin.get(b) + (long long)r * ld;
+    const float s = (float)scale[b];
+    for (int j = lane; j < m; j += 64) dst[j] = (f16)((float)src[j] * s);
+    j0 = m;
+  }
+  for (int j = j0 + lane; j < mp; j += 64) dst[j] = (f16)0.0f;
+}
+
+// ------------------------------------------------------------- update
+
+__global__ __launch_bounds__(256) void k_update(BatchPtr<float> W, int n, int m, long long ld,
+                                                const int* __restrict__ idx, int k,
+                                                const f16* __restrict__ O, long long sO, int mp,
+                                                float lr, f16* __restrict__ O_out) {
+  const int b = blockIdx.y;
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (r >= k) return;
+  const f16* __restrict__ o = O + (long long)b * sO + (long long)r * mp;
+  f16* __restrict__ oo = O_out ? O_out + ((long long)b * k + r) * m : nullptr;
+  float* __restrict__ dst = nullptr;
+  if (W.ptrs || W.base) {
+    const int row = idx ? idx[(long long)b * k + r] : r;
+    if (row >= 0 && row < n) dst = W.get(b) + (long long)row * ld;
+  }
+  if (dst && ((uintptr_t)dst & 15) == 0 && (m & 3) == 0) {
+    float4* d4 = (float4*)dst;
+    const half4* o4 = (const half4*)o;
+    for (int j = lane; j < (m >> 2); j += 64) {
+      const half4 h = o4[j];
+      float4 w = d4[j];
+      w.x = __builtin_fmaf(-lr, (float)h[0], w.x);
+      w.y = __builtin_fmaf(-lr, (float)h[1], w.y);
+      w.z = __builtin_fmaf(-lr, (float)h[2], w.z);
+      w.w = __builtin_fmaf(-lr, (float)h[3], w.w);
+      d4[j] = w;
+      if (oo) {
+        oo[4 * j] = h[0]; oo[4 * j + 1] = h[1]; oo[4 * j + 2] = h[2]; oo[4 * j + 3] = h[3];
+      }
+    }
+  } else {
+    for (int j = lane; j < m; j += 64) {
+      const f16 h = o[j];
+      if (dst) dst[j] = __builtin_fmaf(-lr, (float)h, dst[j]);
+      if (oo) oo[j] = h;
+    }
+  }
+}
+
+inline unsigned blocks_for(long long rows) { return (unsigned)((rows + 3) / 4); }
+
+}  // namespace
+
+hipError_t launch_row_score_f32(BatchPtr<const float> M, int batch, int n, int m, long long ld,
+                                double* l1, double* sq, hipStream_t s) {
+  hipLaunchKernelGGL(k_row_score_f32, dim3(blocks_for(n), batch), dim3(256), 0, s, M, n, m, ld, l1,
+                     sq);
+  return hipGetLastError();
+}
+
+hipError_t launch_row_score_f16(BatchPtr<const f16> X, int batch, int n, int m, long long ld,
+                                double* sq, hipStream_t s) {
+  hipLaunchKernelGGL(k_row_score_f16, dim3(blocks_for(n), batch), dim3(256), 0, s, X, n, m, ld, sq);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk(const double* l1, const double* sq, int batch, int n, int k, int* idx,
+                       double* scale, double eps, hipStream_t s) {
+  hipLaunchKernelGGL(k_topk, dim3(batch), dim3(TK_THREADS), 0, s, l1, sq, n, k, idx, scale, eps);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_f32(BatchPtr<float> M, int batch, int n, int m, long long ld,
+                             const int* idx, int k, const double* scale, float mu, bool decay,
+                             f16* X, long long sX, int kp, int mp, hipStream_t s) {
+  hipLaunchKernelGGL(k_gather_f32, dim3(blocks_for(kp), batch), dim3(256), 0, s, M, n, m, ld, idx, k,
+                     scale, mu, decay ? 1 : 0, X, sX, kp, mp);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_f16(BatchPtr<const f16> Xin, int batch, int m, long long ld, int k,
+                             const double* scale, f16* X, long long sX, int kp, int mp,
+                             hipStream_t s) {
+  hipLaunchKernelGGL(k_gather_f16, dim3(blocks_for(kp), batch), dim3(256), 0, s, Xin, m, ld, k,
+                     scale, X, sX, kp, mp);
+  return hipGetLastError();
+}
+
+hipError_t launch_update(BatchPtr<float> W, int batch, int n, int m, long long ld, const int* idx,
+                         int k, const f16* O, long long sO, int mp, float lr, f16* O_out,
+                         hipStream_t s) {
+  hipLaunchKernelGGL(k_update, dim3(blocks_for(k), batch), dim3(256), 0, s, W, n, m, ld, idx, k, O, sO,
+                     mp, lr, O_out);
+  return hipGetLastError();
+}
+
+}  // namespace dion3

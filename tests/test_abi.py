@@ -1,0 +1,159 @@
+"""Host-side checks of the C ABI: the library loads, exports every symbol the
+header declares, and its host logic (k from f, workspace sizes, argument and
+workspace validation) behaves as documented.  No kernel is launched: every
+call here fails its checks before the first launch.  CPU only."""
+import ctypes
+import json
+import os
+import re
+from fractions import Fraction
+
+import pytest
+
+import orthogonalizing_optimizer_amd as d3
+from orthogonalizing_optimizer_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dion3.h")
+GOLDEN = os.path.join(ROOT, "tests", "golden")
+
+ERR_ARG, ERR_WS, ERR_UNSUP = -1, -2, -3
+FAKE = 1 << 20           # a non-null, 256-aligned address that is never dereferenced
+
+
+def declared_symbols():
+    txt = open(HEADER).read()
+    return sorted(set(re.findall(r"DION3_API\s+[\w\s\*]+?\b(dion3_\w+)\s*\(", txt)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = d3.lib()
+    names = declared_symbols()
+    assert len(names) >= 12
+    for name in names:
+        assert hasattr(lib, name), name
+    assert set(names) == set(_lib.EXPORTED)
+    assert lib.dion3_version() >= 1
+
+
+def test_k_from_fraction_golden():
+    d = json.load(open(os.path.join(GOLDEN, "k_examples.json")))
+    for case in d["cases"]:
+        f = float(Fraction(case["f"]))
+        assert d3.k_from_fraction(f, case["n"]) == case["k"], case
+
+
+def test_k_from_fraction_edges():
+    lib = d3.lib()
+    assert lib.dion3_k_from_fraction(0.25, 0) == -1
+    assert lib.dion3_k_from_fraction(0.0, 10) == -1
+    assert lib.dion3_k_from_fraction(float("nan"), 10) == -1
+    assert lib.dion3_k_from_fraction(1e-30, 10) == 1
+    assert lib.dion3_k_from_fraction(2.5, 10) == 10
+    assert lib.dion3_k_from_fraction(1 / 3, 3) == 1
+    assert lib.dion3_k_from_fraction(1 / 3, 4) == 2
+    for n in (1, 7, 100, 13824, 1 << 20):
+        for num, den in ((1, 8), (1, 4), (1, 2), (3, 7), (5, 16)):
+            want = max(1, min(n, -((-num * n) // den)))
+            assert lib.dion3_k_from_fraction(num / den, n) == want
+
+
+def test_default_cfg():
+    cfg = d3.default_cfg()
+    assert cfg.iters == 5 and cfg.n_restart == 1 and cfg.restart_at[0] == 3
+    assert abs(cfg.abc[0][0] - 3.4445) < 1e-6 and abs(cfg.abc[4][2] - 2.0315) < 1e-6
+    assert abs(cfg.eps - 1e-7) < 1e-12
+
+
+def test_workspace_size_layout():
+    # padded: kp = mp = 128 and sp = 128; 2 X blocks + 5 Gram-side blocks
+    b = d3.workspace_size(1, 128, 100, 32)
+    assert b >= 7 * 128 * 128 * 2
+    assert d3.workspace_size(4, 128, 100, 32) > 3 * b
+    # transposed side (k > m) pads the Gram to m
+    assert d3.workspace_size(1, 1000, 64, 900) < d3.workspace_size(1, 1000, 1000, 900)
+    with pytest.raises(d3.Dion3Error):
+        d3.workspace_size(1, 10, 10, 11)
+    with pytest.raises(d3.Dion3Error):
+        d3.workspace_size(0, 10, 10, 1)
+    out = ctypes.c_size_t()
+    assert d3.lib().dion3_workspace_size(1, (1 << 20) + 1, 4, 1, ctypes.byref(out)) == ERR_UNSUP
+
+
+def _cfg(**kw):
+    cfg = d3.default_cfg()
+    for k, v in kw.items():
+        setattr(cfg, k, v)
+    return cfg
+
+
+def _step(lib, W=FAKE, M=FAKE, n=64, m=32, ld=32, k=16, lr=0.04, mu=0.95, cfg=None, ws=FAKE,
+          nbytes=None):
+    if nbytes is None:
+        nbytes = d3.workspace_size(1, n, m, min(k, n)) if 1 <= k <= n else 1 << 30
+    return lib.dion3_step(W, M, n, m, ld, k, lr, mu, ctypes.byref(cfg) if cfg else None, None,
+                          None, ws, nbytes, None)
+
+
+def test_step_rejects_bad_arguments_before_launch():
+    lib = d3.lib()
+    assert _step(lib, W=None) == ERR_ARG
+    assert _step(lib, M=None) == ERR_ARG
+    assert _step(lib, k=0) == ERR_UNSUP
+    assert _step(lib, k=65) == ERR_ARG
+    assert _step(lib, ld=31) == ERR_ARG
+    assert _step(lib, lr=float("inf")) == ERR_ARG
+    assert _step(lib, cfg=_cfg(iters=0)) == ERR_ARG
+    assert _step(lib, cfg=_cfg(iters=17)) == ERR_ARG
+    bad = _cfg()
+    bad.restart_at[0] = 1
+    assert _step(lib, cfg=bad) == ERR_ARG
+    bad = _cfg()
+    bad.restart_at[0] = 6
+    assert _step(lib, cfg=bad) == ERR_ARG
+    bad = _cfg(n_restart=2)
+    bad.restart_at[0], bad.restart_at[1] = 3, 3
+    assert _step(lib, cfg=bad) == ERR_ARG
+    assert _step(lib, cfg=_cfg(eps=-1.0)) == ERR_ARG
+
+
+def test_step_rejects_bad_workspace_before_launch():
+    lib = d3.lib()
+    need = d3.workspace_size(1, 64, 32, 16)
+    assert _step(lib, ws=None) == ERR_WS
+    assert _step(lib, ws=FAKE + 16) == ERR_WS
+    assert _step(lib, nbytes=need - 1) == ERR_WS
+
+
+def test_other_entry_points_validate():
+    lib = d3.lib()
+    cfg = None
+    assert lib.dion3_step_megabatch(None, FAKE, 2, 8, 8, 8, 2, 0.1, 0.9, cfg, None, None, FAKE,
+                                    1 << 30, None) == ERR_ARG
+    assert lib.dion3_step_megabatch(FAKE, FAKE, 0, 8, 8, 8, 2, 0.1, 0.9, cfg, None, None, FAKE,
+                                    1 << 30, None) == ERR_ARG
+    assert lib.dion3_row_select(None, 1, 8, 8, 8, 2, FAKE, None, FAKE, 1 << 30, None) == ERR_ARG
+    assert lib.dion3_row_select(FAKE, 1, 8, 8, 8, 9, FAKE, None, FAKE, 1 << 30, None) == ERR_ARG
+    assert lib.dion3_row_select(FAKE, 1, 8, 8, 8, 2, FAKE, None, FAKE, 0, None) == ERR_WS
+    assert lib.dion3_gram_ns(None, FAKE, 1, 8, 8, cfg, FAKE, 1 << 30, None) == ERR_ARG
+    assert lib.dion3_gram_ns(FAKE, FAKE, 1, 8, 8, cfg, FAKE, 16, None) == ERR_WS
+    assert lib.dion3_syrk_f16(FAKE, FAKE, 1, 100, 128, 128, 128, None) == ERR_ARG
+    assert lib.dion3_syrk_f16(FAKE, FAKE, 1, 128, 128, 120, 128, None) == ERR_ARG
+    assert lib.dion3_symm_f16(FAKE, FAKE, None, FAKE + 256, 1, 128, 128, 1.0, 0.5, 0.0,
+                              None) == ERR_ARG          # beta != 0 needs D
+    assert lib.dion3_symm_f16(FAKE, FAKE + 256, None, FAKE, 1, 128, 128, 1.0, 0.0, 0.0,
+                              None) == ERR_ARG          # C aliases A
+
+
+def test_status_strings():
+    for st in (0, -1, -2, -3, -4):
+        assert d3.status_string(st)
+    assert d3.status_string(7) == "unknown status"
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    with pytest.raises(TypeError):
+        d3.step(torch.zeros(4, 4), torch.zeros(4, 4), 2, 0.1, 0.9)
+    with pytest.raises(TypeError):
+        d3.gram_ns(torch.zeros(4, 4, dtype=torch.float16))

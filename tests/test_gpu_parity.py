@@ -1,0 +1,258 @@
+"""GPU parity of the HIP path (called through the C ABI) against the fp64
+oracle, on seeded inputs spanning several tiles, ragged tails and the
+degenerate cases of the method."""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+from oracle import dion3_oracle as orc
+from tests.parity import O_TOL, check_selection, check_step, rel
+from workloads import c1_inputs, c2_inputs, host_gaussian, host_lowrank, host_tied
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+import orthogonalizing_optimizer_amd as d3  # noqa: E402
+
+DEV = "cuda:0"
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def run_step(W, M, k, lr, mu, cfg=None):
+    Wd, Md = dev(W), dev(M)
+    idx, O = d3.step(Wd, Md, k, lr, mu, cfg, return_idx=True, return_O=True)
+    torch.cuda.synchronize()
+    return Wd.cpu().numpy(), Md.cpu().numpy(), idx.cpu().numpy(), O.cpu().numpy()
+
+
+# ------------------------------------------------------------ selection
+
+SELECT_CASES = [
+    ("gauss", 128, 512, 32), ("gauss", 1000, 77, 250), ("gauss", 1, 5, 1), ("gauss", 300, 300, 300),
+    ("gauss", 13824, 8, 1728), ("tied", 37, 11, 5), ("tied", 4096, 64, 1024), ("tied", 999, 3, 998),
+    ("gauss", 2049, 130, 2048),
+]
+
+
+@pytest.mark.parametrize("kind,n,m,k", SELECT_CASES)
+def test_row_select_exact(kind, n, m, k):
+    say("row_select", kind, n, m, k)
+    M = host_gaussian((n, m), [1, n, m]) if kind == "gauss" else host_tied(n, m, n, n_distinct=7)
+    idx, scores = d3.row_select(dev(M), k, return_scores=True)
+    torch.cuda.synchronize()
+    l1, _ = orc.row_scores(M)
+    assert rel(scores.cpu().numpy(), l1) <= 1e-12
+    S = idx.cpu().numpy()
+    if kind == "tied":        # exact ties: the lowest-index rule decides, no band
+        assert np.array_equal(S, orc.select_rows(l1, k))
+    else:
+        check_selection(S, M, k)
+
+
+def test_row_select_batched():
+    say("row_select batched")
+    M = np.stack([host_tied(500, 40, b, 9) for b in range(3)])
+    idx = d3.row_select(dev(M), 123).cpu().numpy()
+    for b in range(3):
+        l1, _ = orc.row_scores(M[b])
+        assert np.array_equal(idx[b], orc.select_rows(l1, 123))
+
+
+# ------------------------------------------------------------ symmetric kernels
+
+@pytest.mark.parametrize("B,rows,cols", [(1, 128, 128), (3, 256, 384), (2, 384, 1024)])
+def test_syrk_f16(B, rows, cols):
+    say("syrk", B, rows, cols)
+    A = (host_gaussian((B, rows, cols), [2, rows, cols]) * 0.05).astype(np.float16)
+    R = d3.syrk_f16(dev(A)).cpu().numpy()
+    for b in range(B):
+        ref = A[b].astype(np.float64) @ A[b].astype(np.float64).T
+        assert rel(R[b], ref) <= 2e-3
+        assert np.array_equal(R[b], R[b].T)
+
+
+@pytest.mark.parametrize("s", [128, 384])
+def test_symm_f16_poly(s):
+    say("symm poly", s)
+    G = host_gaussian((s, s), [3, s]).astype(np.float64)
+    A64 = G @ G.T
+    A64 /= np.linalg.norm(A64, 2)                      # symmetric, spectrum in [0, 1]
+    A = A64.astype(np.float16)
+    a, b, c = 3.4445, -4.7750, 2.0315
+    C = d3.symm_f16(dev(A), dev(A), dev(A), alpha=c, beta=b, gamma=a).cpu().numpy()
+    Af = A.astype(np.float64)
+    ref = c * Af @ Af + b * Af + a * np.eye(s)
+    assert rel(C, ref) <= 2e-3
+    assert np.array_equal(C, C.T)
+    # plain product of two commuting symmetric matrices
+    B2 = (Af @ Af).astype(np.float16)
+    P = d3.symm_f16(dev(A), dev(B2)).cpu().numpy()
+    assert rel(P, Af @ B2.astype(np.float64)) <= 2e-3
+    assert np.array_equal(P, P.T)
+
+
+# ------------------------------------------------------------ Gram Newton-Schulz
+
+GRAM_CASES = [(1, 32, 512), (2, 100, 300), (1, 300, 100), (1, 1, 1), (1, 1, 7), (1, 7, 1),
+              (2, 128, 128), (1, 257, 1000), (1, 1000, 257), (4, 64, 4096)]
+
+
+@pytest.mark.parametrize("B,k,m", GRAM_CASES)
+def test_gram_ns(B, k, m):
+    say("gram_ns", B, k, m)
+    X = host_gaussian((B, k, m), [4, k, m]).astype(np.float16)
+    O = d3.gram_ns(dev(X)).cpu().numpy()
+    co = orc.default_coeffs()
+    for b in range(B):
+        ref = orc.ns_gram(X[b].astype(np.float64), co, (3,))
+        assert rel(O[b], ref) <= O_TOL, (b, rel(O[b], ref))
+
+
+@pytest.mark.parametrize("iters,restarts", [(5, ()), (5, (2, 4)), (3, (2,)), (7, (3, 6)), (1, ())])
+def test_gram_ns_schedules(iters, restarts):
+    say("gram_ns schedule", iters, restarts)
+    X = host_gaussian((2, 96, 333), [5, iters]).astype(np.float16)
+    co = [orc.MUON_COEFFS] * iters
+    cfg = d3.ns_cfg(iters=iters, restart_at=restarts, coeffs=co)
+    O = d3.gram_ns(dev(X), cfg).cpu().numpy()
+    for b in range(2):
+        ref = orc.ns_gram(X[b].astype(np.float64), co, restarts)
+        assert rel(O[b], ref) <= O_TOL
+
+
+def test_gram_ns_deterministic():
+    say("gram_ns twice")
+    X = dev(host_gaussian((3, 200, 700), 6).astype(np.float16))
+    a = d3.gram_ns(X).cpu().numpy()
+    b = d3.gram_ns(X).cpu().numpy()
+    assert a.tobytes() == b.tobytes()
+
+
+def test_restart_diagnostic_lowrank():
+    """Ill-conditioned input (rank 64, singular values i^-1.5, 1e-3 noise):
+    without the restart the fp16 Gram iteration drifts (spurious negative
+    eigenvalues grow); with it the error against the oracle on the same fp16
+    bytes must meet the tolerance."""
+    say("restart diagnostic")
+    M = host_lowrank(640, 2048, 11)
+    Xn = (M.astype(np.float64) / np.linalg.norm(M.astype(np.float64))).astype(np.float16)
+    co = orc.default_coeffs()
+    ref = orc.ns_gram(Xn.astype(np.float64), co, (3,))
+    ref_exact = orc.ns_gram(M.astype(np.float64), co, (3,))
+    with_r = d3.gram_ns(dev(Xn)).cpu().numpy()
+    no_r = d3.gram_ns(dev(Xn), d3.ns_cfg(iters=5, restart_at=())).cpu().numpy()
+    e1, e0 = rel(with_r, ref), rel(no_r, ref)
+    print(f"lowrank 640x2048: kernel rel err with restart {e1:.3e}, without {e0:.3e}; "
+          f"fp16 input rounding alone {rel(ref, ref_exact):.3e}", flush=True)
+    assert e1 <= O_TOL
+    assert e0 > 5 * e1
+
+
+# ------------------------------------------------------------ the step
+
+def test_step_single_128x512():
+    say("step 128x512 k=32")
+    W, M = c1_inputs()
+    k, lr, mu = 32, 0.02 / math.sqrt(0.25), 0.95
+    assert d3.k_from_fraction(0.25, 128) == k
+    W1, M1, S, O = run_step(W, M, k, lr, mu)
+    err = check_step(W, M, W1, M1, S, O, k, lr, mu)
+    print(f"128x512 k=32: O rel err {err:.3e}", flush=True)
+
+
+STEP_CASES = [(256, 64, 100), (300, 200, 75), (64, 64, 64), (1, 16, 1), (17, 1, 5), (2048, 512, 1),
+              (130, 130, 129), (700, 1300, 350), (1500, 260, 1100)]
+
+
+@pytest.mark.parametrize("n,m,k", STEP_CASES)
+def test_step_shapes(n, m, k):
+    say("step", n, m, k)
+    W = host_gaussian((n, m), [7, n, m], std=0.02)
+    M = host_gaussian((n, m), [8, n, m])
+    W1, M1, S, O = run_step(W, M, k, 0.04, 0.95)
+    check_step(W, M, W1, M1, S, O, k, 0.04, 0.95)
+
+
+def test_step_ties_take_lowest_index():
+    say("step ties")
+    M = host_tied(200, 48, 3, n_distinct=4)
+    W = host_gaussian((200, 48), 9, std=0.02)
+    W1, M1, S, O = run_step(W, M, 50, 0.04, 0.95)
+    l1, _ = orc.row_scores(M)
+    assert np.array_equal(S, orc.select_rows(l1, 50))
+    check_step(W, M, W1, M1, S, O, 50, 0.04, 0.95)
+
+
+def test_step_strided_rows():
+    """Row stride larger than m (a column slice of a wider buffer)."""
+    say("step strided")
+    n, m, ldm, k = 96, 40, 64, 24
+    Wb = dev(host_gaussian((n, ldm), 10, std=0.02))
+    Mb = dev(host_gaussian((n, ldm), 11))
+    W0, M0 = Wb.cpu().numpy().copy(), Mb.cpu().numpy().copy()
+    idx, O = d3.step(Wb[:, :m], Mb[:, :m], k, 0.04, 0.95, return_idx=True, return_O=True)
+    W1, M1 = Wb.cpu().numpy(), Mb.cpu().numpy()
+    assert W1[:, m:].tobytes() == W0[:, m:].tobytes() and M1[:, m:].tobytes() == M0[:, m:].tobytes()
+    check_step(np.ascontiguousarray(W0[:, :m]), np.ascontiguousarray(M0[:, :m]),
+               np.ascontiguousarray(W1[:, :m]), np.ascontiguousarray(M1[:, :m]),
+               idx.cpu().numpy(), O.cpu().numpy(), k, 0.04, 0.95)
+
+
+def test_megabatch_equals_single_calls_bitwise():
+    say("megabatch vs single")
+    B, n, m, k = 5, 200, 300, 50
+    Ws = [host_gaussian((n, m), [12, b], std=0.02) for b in range(B)]
+    Ms = [host_gaussian((n, m), [13, b]) for b in range(B)]
+    Wd, Md = [dev(w) for w in Ws], [dev(x) for x in Ms]
+    idx, O = d3.step_megabatch(Wd, Md, k, 0.04, 0.95, return_idx=True, return_O=True)
+    torch.cuda.synchronize()
+    for b in range(B):
+        W1, M1, S, Ob = run_step(Ws[b], Ms[b], k, 0.04, 0.95)
+        assert np.array_equal(idx[b].cpu().numpy(), S)
+        assert O[b].cpu().numpy().tobytes() == Ob.tobytes()
+        assert Wd[b].cpu().numpy().tobytes() == W1.tobytes()
+        assert Md[b].cpu().numpy().tobytes() == M1.tobytes()
+
+
+def test_megabatch_16x1024x4096_f1():
+    """16 matrices of 1024x4096, f = 1 (every row, the Muon-equivalent path), one call."""
+    say("megabatch 16x1024x4096 f=1")
+    Ws, Ms = c2_inputs()
+    Wd, Md = [dev(w) for w in Ws], [dev(x) for x in Ms]
+    k = d3.k_from_fraction(1.0, 1024)
+    idx, O = d3.step_megabatch(Wd, Md, k, 0.02, 0.95, return_idx=True, return_O=True)
+    torch.cuda.synchronize()
+    for b in (0, 7, 15):
+        S = idx[b].cpu().numpy()
+        assert np.array_equal(S, np.arange(1024))
+        err = check_step(Ws[b], Ms[b], Wd[b].cpu().numpy(), Md[b].cpu().numpy(), S,
+                         O[b].cpu().numpy(), k, 0.02, 0.95)
+        print(f"16x1024x4096 f=1 matrix {b}: O rel err {err:.3e}", flush=True)
+
+
+def test_dion3step_groups_by_shape():
+    say("Dion3Step grouping")
+    shapes = [(64, 96), (96, 64), (64, 96), (64, 96), (96, 64)]
+    Ws = [dev(host_gaussian(s, [14, i], std=0.02)) for i, s in enumerate(shapes)]
+    Ms = [dev(host_gaussian(s, [15, i])) for i, s in enumerate(shapes)]
+    W0 = [w.cpu().numpy() for w in Ws]
+    M0 = [x.cpu().numpy() for x in Ms]
+    opt = d3.Dion3Step(Ws, Ms, lr=0.02, fraction=0.25, mu=0.9)
+    assert len(opt.groups) == 2
+    opt.step()
+    torch.cuda.synchronize()
+    for i, s in enumerate(shapes):
+        k = orc.k_from_fraction(0.25, s[0])
+        ref = orc.dion3_step(W0[i], M0[i], k, 0.04, 0.9)
+        assert rel(Ws[i].cpu().numpy() - W0[i], ref["W"] - W0[i]) <= O_TOL
+        assert Ms[i].cpu().numpy().tobytes() == ref["M"].tobytes()

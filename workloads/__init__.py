@@ -126,14 +126,16 @@ def host_lowrank(n: int, m: int, seed: int, rank: int = 64, decay: float = 1.5,
 
 
 def host_tied(n: int, m: int, seed: int, n_distinct: int) -> np.ndarray:
-    """Matrix whose rows repeat ``n_distinct`` base rows (as permuted copies),
-    so many rows share exactly the same l1 score: a tie-stress input."""
+    """Matrix whose rows are sign-flipped, permuted copies of ``n_distinct``
+    base rows with entries in {-2, -1.75, ..., 2}: every sum of their absolute
+    values is exact in any order, so rows from one base row tie exactly in
+    l1 (a tie-stress input)."""
     rng = np.random.default_rng(seed)
-    base = rng.standard_normal((n_distinct, m)).astype(np.float32)
+    base = (rng.integers(-8, 9, size=(n_distinct, m)) / 4.0).astype(np.float32)
     pick = rng.integers(0, n_distinct, size=n)
     out = np.empty((n, m), np.float32)
     for i in range(n):
-        out[i] = rng.permutation(base[pick[i]])
+        out[i] = rng.permutation(base[pick[i]]) * rng.choice(np.array([-1.0, 1.0], np.float32), size=m)
     return out
 
 
@@ -151,11 +153,15 @@ def device_matrix(kind: str, n: int, m: int, seed: int, device: str = "cuda"):
         scale = 0.1 + 9.9 * torch.rand((), generator=g, device=device, dtype=torch.float64).item()
         return x.mul_(scale)
     if kind == "lowrank":
+        # orthonormal factors from a host QR (seeded PCG64), product on the device
+        rng = np.random.default_rng(seed)
         r = min(64, n, m)
-        u, _ = torch.linalg.qr(torch.randn((n, r), generator=g, device=device, dtype=torch.float32))
-        v, _ = torch.linalg.qr(torch.randn((m, r), generator=g, device=device, dtype=torch.float32))
-        sv = torch.arange(1, r + 1, device=device, dtype=torch.float32).pow(-1.5)
-        low = (u * sv) @ v.T
+        u, _ = np.linalg.qr(rng.standard_normal((n, r)))
+        v, _ = np.linalg.qr(rng.standard_normal((m, r)))
+        sv = np.arange(1, r + 1, dtype=np.float64) ** (-1.5)
+        ud = torch.from_numpy((u * sv).astype(np.float32)).to(device)
+        vd = torch.from_numpy(v.astype(np.float32)).to(device)
+        low = ud @ vd.T
         noise = torch.randn((n, m), generator=g, device=device, dtype=torch.float32)
         noise.mul_(1e-3 * low.norm() / noise.norm())
         return low.add_(noise)
