@@ -1,0 +1,269 @@
+"""Benchmark of the Dion3 optimizer step on one MI355X.
+
+One step = one Dion3 optimizer step over a whole model's weight set: for
+every shape group, l1 row scoring, top-k selection, Gram Newton-Schulz on
+the selected rows and the row-sparse update with momentum decay, all in the
+library's kernels, inputs resident in HBM.  Prints one JSON line.
+
+Default workload: the 7B-like dense transformer weight set (hidden 4096, 32
+layers: 128 x 4096x4096, 64 x 11008x4096, 32 x 4096x11008; fp32 W and M) at
+f = 1/4, the setting of the pages' largest measured step speedup.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+FP16_PEAK_TFLOPS = 2500.0      # MI355X dense fp16 MFMA
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+METRIC = "Dion3 optimizer-step ms per model + Gram-NS TFLOP/s (% fp16 MFMA peak)"
+
+GEMM_SYMBOLS = {
+    "gemm_gram": "k_gemm<0,...> (Gram X X^T, lower tiles mirrored)",
+    "gemm_poly": "k_gemm<1,...> (Z = aI + bR + cR^2, lower tiles mirrored)",
+    "gemm_symm": "k_gemm<2,...> (symmetric product, lower tiles mirrored)",
+    "gemm_rect": "k_gemm<3,...> (rectangular multiply-back Q X)",
+    "row_score": "k_row_score_f32",
+    "topk": "k_topk",
+    "gather": "k_gather_f32",
+    "update": "k_update",
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default="c4", help="c1, c2, c3, c4 (7B f=1/4), c4h (7B f=1/2), c5")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-trace", action="store_true")
+    p.add_argument("--cpu-sample", type=int, default=1, help="oracle matrices per shape group")
+    return p.parse_args()
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("gemm_f16.hip", "rows.hip", "dion3_internal.h"):
+        with open(os.path.join(ROOT, "orthogonalizing_optimizer_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary,
+    or None when absent or taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        d = json.load(open(path))
+        ent = d.get(workload, {}).get(kernel)
+        if not ent or ent.get("source_hash") != kernel_source_hash():
+            return None
+        return float(ent["bytes_per_launch"])
+    except (ValueError, KeyError, TypeError):
+        return None
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: every matrix of a Dion3 step is independent, and this "
+              "build runs the step on a single MI355X (multi-GPU sharding is a design note only). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import orthogonalizing_optimizer_amd as d3
+    from workloads import WORKLOADS, device_workload
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    dev = "cuda:0"
+    wl = WORKLOADS[args.workload]
+    cfg = d3.default_cfg()
+    mu = 0.95
+    lr = wl.lr
+
+    t_gen = time.time()
+    data = device_workload(wl, dev)
+    torch.cuda.synchronize()
+    log(f"generated {wl.name}: {wl.n_matrices} matrices, {wl.n_params / 1e9:.2f} B params "
+        f"in {time.time() - t_gen:.1f}s")
+
+    # host copies of the CPU-baseline sample (initial state)
+    samples = []
+    if not args.no_cpu_baseline:
+        for g, Ws, Ms in data:
+            for j in range(min(args.cpu_sample, g.count)):
+                samples.append((g, Ws[j].cpu().numpy(), Ms[j].cpu().numpy()))
+
+    groups = []
+    max_ws = 0
+    for g, Ws, Ms in data:
+        k = d3.k_from_fraction(float(wl.fraction), g.n)
+        ptrs = (d3.pointer_array(Ws, dev), d3.pointer_array(Ms, dev))
+        groups.append((g, Ws, Ms, k, ptrs))
+        max_ws = max(max_ws, d3.workspace_size(len(Ms), g.n, g.m, k))
+    ws = d3.Workspace()
+    ws.get(max_ws, dev)
+
+    def one_step():
+        for g, Ws, Ms, k, ptrs in groups:
+            d3.step_megabatch(Ws, Ms, k, lr, mu, cfg, ws=ws, ptrs=ptrs)
+
+    for _ in range(args.warmup):
+        one_step()
+    torch.cuda.synchronize()
+
+    launches_per_step = sum(3 + 1 + 2 * (1 + cfg.n_restart) + 4 * cfg.iters for _ in groups)
+    if not args.no_trace:
+        d3.trace_enable(launches_per_step * args.steps + 64)
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        one_step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_total = e0.elapsed_time(e1)
+    ms_per_step = ms_total / args.steps
+
+    # per-kernel statistics over the timed region
+    kernels = {}
+    if not args.no_trace:
+        for name, ms, fl, by in d3.trace_records():
+            st = kernels.setdefault(name, {"launches": 0, "ms": 0.0, "flops": 0.0, "bytes": 0.0})
+            st["launches"] += 1
+            st["ms"] += ms
+            st["flops"] += fl
+            st["bytes"] += by
+        d3.trace_disable()
+    for name, st in kernels.items():
+        st["avg_us"] = 1e3 * st["ms"] / st["launches"]
+        if st["flops"] > 0:
+            st["tflops"] = st["flops"] / (st["ms"] * 1e-3) / 1e12
+            st["frac_fp16_peak"] = st["tflops"] / FP16_PEAK_TFLOPS
+        else:
+            st["gbs"] = st["bytes"] / (st["ms"] * 1e-3) / 1e9
+            st["frac_hbm"] = st["gbs"] / HBM_PEAK_GBS
+        st["ms_per_step"] = st["ms"] / args.steps
+        log(f"  {name:10s} launches/step {st['launches'] / args.steps:5.1f}  "
+            f"avg {st['avg_us']:9.1f} us  ms/step {st['ms_per_step']:8.3f}  " +
+            (f"{st['tflops']:7.1f} TFLOP/s ({100 * st['frac_fp16_peak']:.1f}% fp16 peak)"
+             if st["flops"] > 0 else f"{st['gbs']:7.1f} GB/s ({100 * st['frac_hbm']:.1f}% HBM)"))
+
+    gemm = [st for nm, st in kernels.items() if nm.startswith("gemm_")]
+    gemm_flops = sum(st["flops"] for st in gemm) / max(1, args.steps)
+    gemm_ms = sum(st["ms"] for st in gemm) / max(1, args.steps)
+    gram_tflops = gemm_flops / (gemm_ms * 1e-3) / 1e12 if gemm_ms > 0 else None
+
+    # standard-NS dense-equivalent work (a labelled "effective" number only)
+    eff_flops = 0.0
+    for g, Ws, Ms, k, ptrs in groups:
+        s, L = min(k, g.m), max(k, g.m)
+        eff_flops += g.count * cfg.iters * (4.0 * s * s * L + 2.0 * s ** 3)
+
+    roofline = None
+    if kernels:
+        dom = max(kernels, key=lambda nm: kernels[nm]["ms"])
+        st = kernels[dom]
+        per_launch_work = (st["flops"] if st["flops"] > 0 else st["bytes"]) / st["launches"]
+        if st["flops"] > 0:
+            roofline = {"bound": "mfma", "achieved": round(st["tflops"], 2),
+                        "peak": FP16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                        "frac": round(st["tflops"] / FP16_PEAK_TFLOPS, 4)}
+        else:
+            roofline = {"bound": "hbm", "achieved": round(st["gbs"], 1), "peak": HBM_PEAK_GBS,
+                        "unit": "GB/s", "frac": round(st["gbs"] / HBM_PEAK_GBS, 4)}
+        roofline["traffic"] = load_traffic(dom, args.workload)
+        roofline["kernel"] = GEMM_SYMBOLS.get(dom, dom)
+        roofline["avg_launch_us"] = round(st["avg_us"], 2)
+        roofline["work_per_launch"] = per_launch_work
+
+    # CPU baseline: the fp64 oracle on a bounded sample, scaled to the model
+    cpu_baseline = None
+    if samples:
+        from oracle import dion3_oracle as orc
+        try:
+            from threadpoolctl import threadpool_info
+            threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                           if i.get("user_api") == "blas"] or [1])
+        except Exception:
+            threads = os.cpu_count() or 1
+        per_group = {}
+        t_cpu = 0.0
+        for g, W0, M0 in samples:
+            k = orc.k_from_fraction(wl.fraction, g.n)
+            t = time.perf_counter()
+            orc.dion3_step(W0, M0, k, lr, mu)
+            dt = time.perf_counter() - t
+            t_cpu += dt
+            per_group.setdefault((g.n, g.m, g.count), []).append(dt)
+        cpu_ms = 1e3 * sum(g[2] * (sum(v) / len(v)) for g, v in per_group.items())
+        cpu_baseline = {"value": round(cpu_ms, 1), "unit": "ms per model step",
+                        "cores": threads, "kind": "oracle",
+                        "sample": f"{len(samples)} matrices ({args.cpu_sample} per shape group: "
+                                  + ", ".join(f"{n}x{m}" for (n, m, c) in per_group) +
+                                  f"), fp64 NumPy, {t_cpu:.1f}s of CPU work, scaled by each "
+                                  "group's matrix count to the whole model"}
+        log(f"cpu oracle: {t_cpu:.1f}s for {len(samples)} matrices -> {cpu_ms:.0f} ms/model step "
+            f"({threads} BLAS threads, os.cpu_count()={os.cpu_count()})")
+
+    out = {
+        "metric": METRIC,
+        "value": round(ms_per_step, 3),
+        "unit": "ms",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16",
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name,
+            "matrices": wl.n_matrices,
+            "params": wl.n_params,
+            "shape_groups": [f"{g.count}x{g.n}x{g.m}" for g in wl.groups],
+            "fraction": str(wl.fraction),
+            "k": [k for (_, _, _, k, _) in groups],
+            "lr": lr, "mu": mu, "ns_iters": cfg.iters,
+            "restart_at": [cfg.restart_at[i] for i in range(cfg.n_restart)],
+            "state_dtype": "fp32 W and M; fp16 X, Gram, polynomials and O with fp32 accumulation",
+            "parallelism": "single GPU, one megabatched call per shape group",
+        },
+        "matrices_per_s": round(wl.n_matrices / (ms_per_step * 1e-3), 1),
+        "gram_ns_tflops": round(gram_tflops, 2) if gram_tflops else None,
+        "gram_ns_frac_fp16_peak": round(gram_tflops / FP16_PEAK_TFLOPS, 4) if gram_tflops else None,
+        "effective_standard_ns_tflops": round(eff_flops / (ms_per_step * 1e-3) / 1e12, 2),
+        "roofline": roofline,
+        "cpu_baseline": cpu_baseline,
+        "kernels": {nm: {kk: (round(v, 4) if isinstance(v, float) else v) for kk, v in st.items()}
+                    for nm, st in kernels.items()},
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

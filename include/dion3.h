@@ -28,8 +28,8 @@
  *     the outputs are untouched.
  *   - NaN or Inf in M or X gives undefined results (no check is made).
  *   - Concurrent calls are safe when their workspaces and outputs are
- *     disjoint.  The library holds no mutable global state besides the
- *     thread-local last HIP error.
+ *     disjoint.  The library's only mutable global state is the thread-local
+ *     last HIP error and the optional timing trace (dion3_trace_*).
  */
 #ifndef DION3_H
 #define DION3_H
@@ -146,6 +146,21 @@ DION3_API dion3_status dion3_syrk_f16(const uint16_t* A, uint16_t* R, int32_t ba
 DION3_API dion3_status dion3_symm_f16(const uint16_t* A, const uint16_t* B, const uint16_t* D, uint16_t* C,
                             int32_t batch, int64_t s, int64_t ld, float alpha, float beta,
                             float gamma, void* stream);
+
+/* Kernel timing trace, for benchmarks.  dion3_trace_enable(capacity > 0)
+ * creates 2 * capacity HIP events (no device memory) and starts recording:
+ * each kernel the library then launches is bracketed by an event pair on the
+ * caller's stream and noted with its name and the algorithmic work it does
+ * on unpadded sizes (flops for the MFMA products, HBM bytes for the row
+ * kernels).  Records past the capacity are dropped.  capacity <= 0 stops and
+ * frees the trace.  dion3_trace_record(i, ...) waits for record i's second
+ * event and returns its kernel name (a static string), elapsed ms, flops and
+ * bytes.  The trace is process-wide; it is meant for one benchmarking thread. */
+DION3_API dion3_status dion3_trace_enable(int32_t capacity);
+DION3_API int32_t dion3_trace_count(void);
+DION3_API void dion3_trace_reset(void);
+DION3_API dion3_status dion3_trace_record(int32_t i, const char** name, double* ms, double* flops,
+                                          double* bytes);
 
 DION3_API const char* dion3_status_string(dion3_status status);
 

@@ -59,6 +59,11 @@ def _declare(lib):
                                            c.POINTER(NsCfg), vp, vp, vp, sz, vp]),
         "dion3_syrk_f16": (c.c_int, [vp, vp, i32, i64, i64, i64, i64, vp]),
         "dion3_symm_f16": (c.c_int, [vp, vp, vp, vp, i32, i64, i64, f32, f32, f32, vp]),
+        "dion3_trace_enable": (c.c_int, [i32]),
+        "dion3_trace_count": (i32, []),
+        "dion3_trace_reset": (None, []),
+        "dion3_trace_record": (c.c_int, [i32, c.POINTER(c.c_char_p), c.POINTER(f64),
+                                         c.POINTER(f64), c.POINTER(f64)]),
         "dion3_status_string": (c.c_char_p, [c.c_int]),
         "dion3_last_hip_error": (c.c_int, []),
     }
@@ -71,7 +76,8 @@ def _declare(lib):
 
 EXPORTED = ("dion3_version", "dion3_ns_cfg_default", "dion3_k_from_fraction",
             "dion3_workspace_size", "dion3_row_select", "dion3_gram_ns", "dion3_step",
-            "dion3_step_megabatch", "dion3_syrk_f16", "dion3_symm_f16", "dion3_status_string",
+            "dion3_step_megabatch", "dion3_syrk_f16", "dion3_symm_f16", "dion3_trace_enable",
+            "dion3_trace_count", "dion3_trace_reset", "dion3_trace_record", "dion3_status_string",
             "dion3_last_hip_error")
 
 
@@ -297,3 +303,31 @@ def symm_f16(A, B, D=None, alpha: float = 1.0, beta: float = 0.0, gamma: float =
     _check(lib().dion3_symm_f16(Ab.data_ptr(), Bb.data_ptr(), _ptr(Db), C.data_ptr(), nb, s, s,
                                 alpha, beta, gamma, _stream(A.device)), "dion3_symm_f16")
     return C[0] if A.dim() == 2 else C
+
+
+# ------------------------------------------------------------- timing trace
+
+def trace_enable(capacity: int):
+    """Start recording an event pair around every kernel the library launches."""
+    _check(lib().dion3_trace_enable(int(capacity)), "dion3_trace_enable")
+
+
+def trace_disable():
+    _check(lib().dion3_trace_enable(0), "dion3_trace_enable")
+
+
+def trace_reset():
+    lib().dion3_trace_reset()
+
+
+def trace_records():
+    """[(kernel name, ms, algorithmic flops, algorithmic bytes)] in launch order
+    (waits for the recorded kernels to finish)."""
+    out = []
+    name = ctypes.c_char_p()
+    ms, fl, by = ctypes.c_double(), ctypes.c_double(), ctypes.c_double()
+    for i in range(lib().dion3_trace_count()):
+        _check(lib().dion3_trace_record(i, ctypes.byref(name), ctypes.byref(ms), ctypes.byref(fl),
+                                        ctypes.byref(by)), "dion3_trace_record")
+        out.append((name.value.decode(), ms.value, fl.value, by.value))
+    return out

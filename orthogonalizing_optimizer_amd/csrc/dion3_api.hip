@@ -117,8 +117,17 @@ Bufs carve(const Plan& P, void* ws) {
 }
 
 // R = X X^T on the Gram side (X^T X in rows layout when transposed).
+double dbl(long long v) { return (double)v; }
+
+// Unpadded Gram-side sizes: s = min(k, m), L = max(k, m).
+double s_of(const Plan& P) { return dbl(P.tr ? P.m : P.k); }
+double L_of(const Plan& P) { return dbl(P.tr ? P.k : P.m); }
+
 hipError_t gram(const Plan& P, const f16* X, f16* R, hipStream_t s) {
+  const double sv = s_of(P);
+  TraceScope ts("gemm_gram", P.B * sv * sv * L_of(P), 0.0, s);
   GemmDesc d = {};
+  d.role = kRoleGram;
   d.A = X; d.sA = P.kp * P.mp; d.lda = (int)P.mp; d.a_col = P.tr;
   d.B = X; d.sB = P.kp * P.mp; d.ldb = (int)P.mp; d.b_col = P.tr;
   d.C = R; d.sC = P.sp * P.sp; d.ldc = (int)P.sp; d.c_t = false;
@@ -131,7 +140,10 @@ hipError_t gram(const Plan& P, const f16* X, f16* R, hipStream_t s) {
 // C = alpha A B + beta D + gamma I for symmetric commuting s x s matrices.
 hipError_t symm(const Plan& P, const f16* A, const f16* B, const f16* D, f16* C, float alpha,
                 float beta, float gamma, bool epi, hipStream_t s) {
+  const double sv = s_of(P);
+  TraceScope ts(epi ? "gemm_poly" : "gemm_symm", P.B * sv * sv * sv, 0.0, s);
   GemmDesc d = {};
+  d.role = epi ? kRolePoly : kRoleSymm;
   const long long ss = P.sp * P.sp;
   d.A = A; d.sA = ss; d.lda = (int)P.sp;
   d.B = B; d.sB = ss; d.ldb = (int)P.sp;
@@ -145,7 +157,10 @@ hipError_t symm(const Plan& P, const f16* A, const f16* B, const f16* D, f16* C,
 
 // Y = Q X on the Gram side, written in rows layout.
 hipError_t rect(const Plan& P, const f16* Q, const f16* X, f16* Y, hipStream_t s) {
+  const double sv = s_of(P);
+  TraceScope ts("gemm_rect", 2.0 * P.B * sv * sv * L_of(P), 0.0, s);
   GemmDesc d = {};
+  d.role = kRoleRect;
   d.A = Q; d.sA = P.sp * P.sp; d.lda = (int)P.sp; d.a_col = false;
   d.B = X; d.sB = P.kp * P.mp; d.ldb = (int)P.mp; d.b_col = !P.tr;
   d.C = Y; d.sC = P.kp * P.mp; d.ldc = (int)P.mp; d.c_t = P.tr;
@@ -225,15 +240,28 @@ dion3_status step_impl(BatchPtr<float> W, BatchPtr<float> M, int batch, long lon
   const bool all = (k == n);
 
   BatchPtr<const float> Mc = {M.base, M.stride, (const float* const*)M.ptrs};
-  HIP_TRY(launch_row_score_f32(Mc, batch, (int)n, (int)m, ld, all ? nullptr : l1, sq, s));
-  HIP_TRY(launch_topk(l1, sq, batch, (int)n, (int)k, idx, scale, (double)cfg.eps, s));
-  HIP_TRY(launch_gather_f32(M, batch, (int)n, (int)m, ld, idx, (int)k, scale, mu, true, bf.Xa,
-                            P.kp * P.mp, (int)P.kp, (int)P.mp, s));
+  const double Bd = batch, nm = dbl(n) * dbl(m), km = dbl(k) * dbl(m);
+  {
+    TraceScope ts("row_score", 0.0, Bd * nm * 4.0, s);
+    HIP_TRY(launch_row_score_f32(Mc, batch, (int)n, (int)m, ld, all ? nullptr : l1, sq, s));
+  }
+  {
+    TraceScope ts("topk", 0.0, Bd * dbl(n) * 16.0, s);
+    HIP_TRY(launch_topk(l1, sq, batch, (int)n, (int)k, idx, scale, (double)cfg.eps, s));
+  }
+  {
+    TraceScope ts("gather", 0.0, Bd * km * 10.0, s);
+    HIP_TRY(launch_gather_f32(M, batch, (int)n, (int)m, ld, idx, (int)k, scale, mu, true, bf.Xa,
+                              P.kp * P.mp, (int)P.kp, (int)P.mp, s));
+  }
   f16* O = nullptr;
   st = gram_ns(P, cfg, bf, &O, s);
   if (st != DION3_OK) return st;
-  HIP_TRY(launch_update(W, batch, (int)n, (int)m, ld, idx, (int)k, O, P.kp * P.mp, (int)P.mp, lr,
-                        (f16*)O_out, s));
+  {
+    TraceScope ts("update", 0.0, Bd * km * (O_out ? 12.0 : 10.0), s);
+    HIP_TRY(launch_update(W, batch, (int)n, (int)m, ld, idx, (int)k, O, P.kp * P.mp, (int)P.mp,
+                          lr, (f16*)O_out, s));
+  }
   if (idx_out)
     HIP_TRY(hipMemcpyAsync(idx_out, idx, (size_t)batch * k * sizeof(int32_t),
                            hipMemcpyDeviceToDevice, s));
@@ -409,6 +437,7 @@ dion3_status dion3_syrk_f16(const uint16_t* A, uint16_t* R, int32_t batch, int64
     return DION3_ERR_ARG;
   if (((uintptr_t)A | (uintptr_t)R) & 15) return DION3_ERR_ARG;
   GemmDesc d = {};
+  d.role = kRoleGram;
   d.A = (const f16*)A; d.sA = rows * lda; d.lda = (int)lda;
   d.B = (const f16*)A; d.sB = rows * lda; d.ldb = (int)lda;
   d.C = (f16*)R; d.sC = rows * ldr; d.ldc = (int)ldr;
@@ -429,6 +458,7 @@ dion3_status dion3_symm_f16(const uint16_t* A, const uint16_t* B, const uint16_t
   if (C == A || C == B || (D && C == D)) return DION3_ERR_ARG;
   if (((uintptr_t)A | (uintptr_t)B | (uintptr_t)C | (uintptr_t)D) & 15) return DION3_ERR_ARG;
   GemmDesc d = {};
+  d.role = kRolePoly;
   const long long ss = s * ld;
   d.A = (const f16*)A; d.sA = ss; d.lda = (int)ld;
   d.B = (const f16*)B; d.sB = ss; d.ldb = (int)ld;

@@ -30,7 +30,10 @@ inline long long pad_to(long long x, long long p) { return (x + p - 1) / p * p; 
 //  lower: M == N, only tiles on or below the diagonal are computed and
 //  every element (r >= c) is written to both C[r][c] and C[c][r].
 // M, N must be multiples of 128, K a multiple of 64, ld* multiples of 8.
+enum GemmRole { kRoleGram = 0, kRolePoly = 1, kRoleSymm = 2, kRoleRect = 3 };
+
 struct GemmDesc {
+  int role;
   const f16* A; long long sA; int lda; bool a_col;
   const f16* B; long long sB; int ldb; bool b_col;
   f16* C; long long sC; int ldc; bool c_t;
@@ -40,6 +43,15 @@ struct GemmDesc {
   float alpha, beta, gamma;
 };
 hipError_t launch_gemm(const GemmDesc& d, hipStream_t s);
+
+// Optional kernel timing trace (benchmarks): while enabled, each launch is
+// bracketed by two HIP events on its stream and its algorithmic work noted.
+struct TraceScope {
+  TraceScope(const char* name, double flops, double bytes, hipStream_t s);
+  ~TraceScope();
+  int slot;
+  hipStream_t stream;
+};
 
 // Per-row l1 (optional) and sum of squares in fp64, one wave per row.
 hipError_t launch_row_score_f32(BatchPtr<const float> M, int batch, int n, int m, long long ld,

@@ -70,7 +70,9 @@ __device__ __forceinline__ void store_tile(f16* __restrict__ s, int tid, const h
   }
 }
 
-template <bool A_COL, bool B_COL, bool C_T, bool LOWER, bool EPI>
+// ROLE only names the instance (0 Gram, 1 polynomial, 2 symmetric product,
+// 3 rectangular) so that profilers report each role as its own kernel.
+template <int ROLE, bool A_COL, bool B_COL, bool C_T, bool LOWER, bool EPI>
 __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs p) {
   __shared__ __attribute__((aligned(16))) f16 sA[2][BM * LDSK];
   __shared__ __attribute__((aligned(16))) f16 sB[2][BN * LDSK];
@@ -176,7 +178,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs p) {
       }
 }
 
-template <bool A_COL, bool B_COL, bool C_T, bool LOWER, bool EPI>
+template <int ROLE, bool A_COL, bool B_COL, bool C_T, bool LOWER, bool EPI>
 hipError_t launch(const GemmDesc& d, hipStream_t s) {
   GemmArgs p;
   p.A = d.A; p.B = d.B; p.C = d.C; p.D = d.D;
@@ -190,7 +192,7 @@ hipError_t launch(const GemmDesc& d, hipStream_t s) {
   if (total <= 0 || total > 0x7fffffffLL) return hipErrorInvalidValue;
   p.total = (int)total;
   p.alpha = d.alpha; p.beta = d.beta; p.gamma = d.gamma;
-  hipLaunchKernelGGL((k_gemm<A_COL, B_COL, C_T, LOWER, EPI>), dim3(p.total), dim3(256), 0, s, p);
+  hipLaunchKernelGGL((k_gemm<ROLE, A_COL, B_COL, C_T, LOWER, EPI>), dim3(p.total), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
@@ -199,18 +201,24 @@ hipError_t launch(const GemmDesc& d, hipStream_t s) {
 hipError_t launch_gemm(const GemmDesc& d, hipStream_t s) {
   if (d.M % BM || d.N % BN || d.K % BK || d.K <= 0 || d.batch <= 0) return hipErrorInvalidValue;
   if (d.lower && d.M != d.N) return hipErrorInvalidValue;
-  if (d.lower) {
-    if (d.c_t) return hipErrorInvalidValue;
-    if (!d.a_col && !d.b_col)
-      return d.epilogue ? launch<false, false, false, true, true>(d, s)
-                        : launch<false, false, false, true, false>(d, s);
-    if (d.a_col && d.b_col && !d.epilogue) return launch<true, true, false, true, false>(d, s);
-    return hipErrorInvalidValue;
+  switch (d.role) {
+    case kRoleGram:
+      if (!d.lower || d.c_t || d.epilogue || d.a_col != d.b_col) break;
+      return d.a_col ? launch<kRoleGram, true, true, false, true, false>(d, s)
+                     : launch<kRoleGram, false, false, false, true, false>(d, s);
+    case kRolePoly:
+      if (!d.lower || d.c_t || !d.epilogue || d.a_col || d.b_col) break;
+      return launch<kRolePoly, false, false, false, true, true>(d, s);
+    case kRoleSymm:
+      if (!d.lower || d.c_t || d.epilogue || d.a_col || d.b_col) break;
+      return launch<kRoleSymm, false, false, false, true, false>(d, s);
+    case kRoleRect:
+      if (d.lower || d.epilogue || d.a_col) break;
+      if (d.b_col && !d.c_t) return launch<kRoleRect, false, true, false, false, false>(d, s);
+      if (!d.b_col && d.c_t) return launch<kRoleRect, false, false, true, false, false>(d, s);
+      if (!d.b_col && !d.c_t) return launch<kRoleRect, false, false, false, false, false>(d, s);
+      break;
   }
-  if (d.epilogue || d.a_col) return hipErrorInvalidValue;
-  if (d.b_col && !d.c_t) return launch<false, true, false, false, false>(d, s);
-  if (!d.b_col && d.c_t) return launch<false, false, true, false, false>(d, s);
-  if (!d.b_col && !d.c_t) return launch<false, false, false, false, false>(d, s);
   return hipErrorInvalidValue;
 }
 

@@ -1,0 +1,99 @@
+// Kernel timing trace for benchmarks.  While enabled, each kernel the
+// library launches is bracketed by two HIP events on the caller's stream and
+// its algorithmic work (flops or bytes the method needs, on unpadded sizes)
+// is recorded, so a benchmark can time every kernel of the step live.
+#include <mutex>
+#include <vector>
+
+#include "../../include/dion3.h"
+#include "dion3_internal.h"
+
+namespace dion3 {
+namespace {
+
+struct TraceRec {
+  const char* name;
+  double flops, bytes;
+  hipEvent_t e0, e1;
+};
+
+std::mutex g_mu;
+std::vector<TraceRec> g_recs;
+int g_count = 0;
+bool g_on = false;
+
+}  // namespace
+
+TraceScope::TraceScope(const char* name, double flops, double bytes, hipStream_t s)
+    : slot(-1), stream(s) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  if (!g_on || g_count >= (int)g_recs.size()) return;
+  slot = g_count++;
+  TraceRec& r = g_recs[slot];
+  r.name = name;
+  r.flops = flops;
+  r.bytes = bytes;
+  hipEventRecord(r.e0, s);
+}
+
+TraceScope::~TraceScope() {
+  if (slot < 0) return;
+  std::lock_guard<std::mutex> lk(g_mu);
+  hipEventRecord(g_recs[slot].e1, stream);
+}
+
+}  // namespace dion3
+
+using namespace dion3;
+
+extern "C" {
+
+dion3_status dion3_trace_enable(int32_t capacity) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  for (TraceRec& r : g_recs) {
+    hipEventDestroy(r.e0);
+    hipEventDestroy(r.e1);
+  }
+  g_recs.clear();
+  g_count = 0;
+  g_on = false;
+  if (capacity <= 0) return DION3_OK;
+  if (capacity > (1 << 20)) return DION3_ERR_ARG;
+  g_recs.resize(capacity);
+  for (int i = 0; i < capacity; ++i) {
+    TraceRec& r = g_recs[i];
+    if (hipEventCreate(&r.e0) != hipSuccess || hipEventCreate(&r.e1) != hipSuccess) {
+      g_recs.resize(i);
+      return DION3_ERR_HIP;
+    }
+  }
+  g_on = true;
+  return DION3_OK;
+}
+
+int32_t dion3_trace_count(void) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  return g_count;
+}
+
+void dion3_trace_reset(void) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  g_count = 0;
+}
+
+dion3_status dion3_trace_record(int32_t i, const char** name, double* ms, double* flops,
+                                double* bytes) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  if (i < 0 || i >= g_count || !name || !ms || !flops || !bytes) return DION3_ERR_ARG;
+  TraceRec& r = g_recs[i];
+  if (hipEventSynchronize(r.e1) != hipSuccess) return DION3_ERR_HIP;
+  float t = 0.0f;
+  if (hipEventElapsedTime(&t, r.e0, r.e1) != hipSuccess) return DION3_ERR_HIP;
+  *name = r.name;
+  *ms = t;
+  *flops = r.flops;
+  *bytes = r.bytes;
+  return DION3_OK;
+}
+
+}  // extern "C"
