@@ -50,8 +50,35 @@ def parse():
     p.add_argument("--workload", default="c4", help="c1, c2, c3, c4 (7B f=1/4), c4h (7B f=1/2), c5")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-trace", action="store_true")
-    p.add_argument("--cpu-sample", type=int, default=1, help="oracle matrices per shape group")
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="CPU-baseline budget: oracle matrices are taken round-robin over the "
+                        "shape groups until this much CPU time is spent (at least one per group)")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run a plain 2 GiB device-to-device copy (a known-size kernel for "
+                        "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE) and print its GB/s")
     return p.parse_args()
+
+
+def copy_calibration():
+    """A plain device copy of known size: its FETCH_SIZE / WRITE_SIZE counters
+    give the factor between counter units and bytes, and its rate is the
+    practical HBM ceiling."""
+    import torch
+    n = 1 << 29                      # 512 Mi fp32 = 2 GiB read + 2 GiB written
+    a = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 5
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n,
+                      "ms": round(ms, 4), "gbs": round(8 * n / (ms * 1e-3) / 1e9, 1)}), flush=True)
 
 
 def kernel_source_hash() -> str:
@@ -80,6 +107,9 @@ def load_traffic(kernel: str, workload: str):
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: every matrix of a Dion3 step is independent, and this "
               "build runs the step on a single MI355X (multi-GPU sharding is a design note only). "
@@ -108,12 +138,14 @@ def main():
     log(f"generated {wl.name}: {wl.n_matrices} matrices, {wl.n_params / 1e9:.2f} B params "
         f"in {time.time() - t_gen:.1f}s")
 
-    # host copies of the CPU-baseline sample (initial state)
+    # host copies of the CPU-baseline sample candidates (initial state); at
+    # most 8 per group, used round-robin until the CPU budget is spent
     samples = []
     if not args.no_cpu_baseline:
-        for g, Ws, Ms in data:
-            for j in range(min(args.cpu_sample, g.count)):
-                samples.append((g, Ws[j].cpu().numpy(), Ms[j].cpu().numpy()))
+        for j in range(8):
+            for g, Ws, Ms in data:
+                if j < g.count:
+                    samples.append((g, Ws[j].cpu().numpy(), Ms[j].cpu().numpy()))
 
     groups = []
     max_ws = 0
@@ -211,21 +243,28 @@ def main():
             threads = os.cpu_count() or 1
         per_group = {}
         t_cpu = 0.0
+        used = 0
         for g, W0, M0 in samples:
+            key = (g.n, g.m, g.count)
+            if t_cpu >= args.cpu_seconds and key in per_group:
+                continue
             k = orc.k_from_fraction(wl.fraction, g.n)
             t = time.perf_counter()
             orc.dion3_step(W0, M0, k, lr, mu)
             dt = time.perf_counter() - t
             t_cpu += dt
-            per_group.setdefault((g.n, g.m, g.count), []).append(dt)
+            used += 1
+            per_group.setdefault(key, []).append(dt)
         cpu_ms = 1e3 * sum(g[2] * (sum(v) / len(v)) for g, v in per_group.items())
         cpu_baseline = {"value": round(cpu_ms, 1), "unit": "ms per model step",
                         "cores": threads, "kind": "oracle",
-                        "sample": f"{len(samples)} matrices ({args.cpu_sample} per shape group: "
-                                  + ", ".join(f"{n}x{m}" for (n, m, c) in per_group) +
-                                  f"), fp64 NumPy, {t_cpu:.1f}s of CPU work, scaled by each "
-                                  "group's matrix count to the whole model"}
-        log(f"cpu oracle: {t_cpu:.1f}s for {len(samples)} matrices -> {cpu_ms:.0f} ms/model step "
+                        "sample": f"{used} matrices of the set ("
+                                  + ", ".join(f"{len(v)} x {n}x{m}" for (n, m, c), v in
+                                              per_group.items()) +
+                                  f"), fp64 NumPy oracle, {t_cpu:.1f}s of CPU work; the mean time "
+                                  "per matrix of each shape group is scaled by the group's "
+                                  "matrix count to one whole-model step"}
+        log(f"cpu oracle: {t_cpu:.1f}s for {used} matrices -> {cpu_ms:.0f} ms/model step "
             f"({threads} BLAS threads, os.cpu_count()={os.cpu_count()})")
 
     out = {

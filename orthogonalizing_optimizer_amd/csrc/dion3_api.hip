@@ -27,17 +27,17 @@ dion3_status hip_fail(hipError_t e) {
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Workspace layout for `B` matrices of n x m with k selected rows.  The
-// selected rows X live in a zero-padded [kp][mp] fp16 block per matrix (the
-// "rows" layout, used for both orientations); the s x s Gram-side matrices
-// are zero-padded to sp x sp.  Zero padding is exact for Gram Newton-Schulz:
-// the padded block stays decoupled from the real one and its output rows
-// and columns are zero.
+// selected rows X live in zero-padded fp16 blocks per matrix, both in rows
+// layout [kp][mp] and transposed [mp][kp], so that every product reads
+// K-contiguous operands; the s x s Gram-side matrices are zero-padded to
+// sp x sp.  Zero padding is exact for Gram Newton-Schulz: the padded block
+// stays decoupled from the real one and its output rows and columns are zero.
 struct Plan {
   int B;
   long long n, m, k;
   bool tr;                 // k > m: the Gram is X^T X (s = m)
   long long kp, mp, sp, Lp;
-  size_t o_l1, o_sq, o_idx, o_scale, o_Xa, o_Xb, o_R, o_Z, o_T, o_Q0, o_Q1, total;
+  size_t o_l1, o_sq, o_idx, o_scale, o_Xa, o_XaT, o_Xb, o_XbT, o_R, o_Z, o_T, o_Q0, o_Q1, total;
 };
 
 Plan make_plan(int B, long long n, long long m, long long k) {
@@ -56,7 +56,9 @@ Plan make_plan(int B, long long n, long long m, long long k) {
   P.o_scale = take((size_t)B * 8);
   const size_t xb = (size_t)B * P.kp * P.mp * 2, sb = (size_t)B * P.sp * P.sp * 2;
   P.o_Xa = take(xb);
+  P.o_XaT = take(xb);
   P.o_Xb = take(xb);
+  P.o_XbT = take(xb);
   P.o_R = take(sb);
   P.o_Z = take(sb);
   P.o_T = take(sb);
@@ -99,15 +101,23 @@ bool restart_at(const dion3_ns_cfg& c, int t) {
 
 // --------------------------------------------------------------- Gram NS
 
+// A selected-row block in both layouts: X [kp][mp] and XT [mp][kp].
+struct XPair {
+  f16 *X, *XT;
+};
+
 struct Bufs {
-  f16 *Xa, *Xb, *R, *Z, *T, *Q0, *Q1;
+  XPair a, b;
+  f16 *R, *Z, *T, *Q0, *Q1;
 };
 
 Bufs carve(const Plan& P, void* ws) {
   char* w = (char*)ws;
   Bufs b;
-  b.Xa = (f16*)(w + P.o_Xa);
-  b.Xb = (f16*)(w + P.o_Xb);
+  b.a.X = (f16*)(w + P.o_Xa);
+  b.a.XT = (f16*)(w + P.o_XaT);
+  b.b.X = (f16*)(w + P.o_Xb);
+  b.b.XT = (f16*)(w + P.o_XbT);
   b.R = (f16*)(w + P.o_R);
   b.Z = (f16*)(w + P.o_Z);
   b.T = (f16*)(w + P.o_T);
@@ -116,21 +126,26 @@ Bufs carve(const Plan& P, void* ws) {
   return b;
 }
 
-// R = X X^T on the Gram side (X^T X in rows layout when transposed).
 double dbl(long long v) { return (double)v; }
 
 // Unpadded Gram-side sizes: s = min(k, m), L = max(k, m).
 double s_of(const Plan& P) { return dbl(P.tr ? P.m : P.k); }
 double L_of(const Plan& P) { return dbl(P.tr ? P.k : P.m); }
 
-hipError_t gram(const Plan& P, const f16* X, f16* R, hipStream_t s) {
+// The Gram side works on X_math (sp x Lp): the selected rows when k <= m,
+// their transpose when k > m.  Its row-form copy has row stride Lp and its
+// transpose (Lp x sp) row stride sp.
+const f16* xmath(const Plan& P, const XPair& x) { return P.tr ? x.XT : x.X; }
+const f16* xmathT(const Plan& P, const XPair& x) { return P.tr ? x.X : x.XT; }
+
+// R = X_math X_math^T.
+hipError_t gram(const Plan& P, const XPair& x, f16* R, hipStream_t s) {
   const double sv = s_of(P);
   TraceScope ts("gemm_gram", P.B * sv * sv * L_of(P), 0.0, s);
   GemmDesc d = {};
   d.role = kRoleGram;
-  d.A = X; d.sA = P.kp * P.mp; d.lda = (int)P.mp; d.a_col = P.tr;
-  d.B = X; d.sB = P.kp * P.mp; d.ldb = (int)P.mp; d.b_col = P.tr;
-  d.C = R; d.sC = P.sp * P.sp; d.ldc = (int)P.sp; d.c_t = false;
+  d.A = d.B = xmath(P, x); d.sA = d.sB = P.kp * P.mp; d.lda = d.ldb = (int)P.Lp;
+  d.C = R; d.sC = P.sp * P.sp; d.ldc = (int)P.sp;
   d.M = d.N = (int)P.sp; d.K = (int)P.Lp; d.batch = P.B;
   d.lower = true; d.epilogue = false;
   d.alpha = 1.0f;
@@ -155,40 +170,44 @@ hipError_t symm(const Plan& P, const f16* A, const f16* B, const f16* D, f16* C,
   return launch_gemm(d, s);
 }
 
-// Y = Q X on the Gram side, written in rows layout.
-hipError_t rect(const Plan& P, const f16* Q, const f16* X, f16* Y, hipStream_t s) {
+// Y_math = Q X_math.  The restart needs Y in both layouts; the final
+// product only in rows layout (what the update reads).
+hipError_t rect(const Plan& P, const f16* Q, const XPair& x, const XPair& y, bool both,
+                hipStream_t s) {
   const double sv = s_of(P);
   TraceScope ts("gemm_rect", 2.0 * P.B * sv * sv * L_of(P), 0.0, s);
   GemmDesc d = {};
   d.role = kRoleRect;
-  d.A = Q; d.sA = P.sp * P.sp; d.lda = (int)P.sp; d.a_col = false;
-  d.B = X; d.sB = P.kp * P.mp; d.ldb = (int)P.mp; d.b_col = !P.tr;
-  d.C = Y; d.sC = P.kp * P.mp; d.ldc = (int)P.mp; d.c_t = P.tr;
+  d.A = Q; d.sA = P.sp * P.sp; d.lda = (int)P.sp;
+  d.B = xmathT(P, x); d.sB = P.kp * P.mp; d.ldb = (int)P.sp;
+  const bool want_math = both || !P.tr, want_mathT = both || P.tr;
+  d.C = want_math ? (f16*)xmath(P, y) : nullptr; d.sC = P.kp * P.mp; d.ldc = (int)P.Lp;
+  d.CT = want_mathT ? (f16*)xmathT(P, y) : nullptr; d.sCT = P.kp * P.mp; d.ldct = (int)P.sp;
   d.M = (int)P.sp; d.N = (int)P.Lp; d.K = (int)P.sp; d.batch = P.B;
   d.lower = false; d.epilogue = false;
   d.alpha = 1.0f;
   return launch_gemm(d, s);
 }
 
-// Gram Newton-Schulz on the normalized, padded X held in bufs.Xa ("Dion3:
+// Gram Newton-Schulz on the normalized, padded X held in bufs.a ("Dion3:
 // Full-Stack Orthogonal Updates", agihunt.info, level-1 paragraph).  Every
 // matrix here is a polynomial in the first Gram, so all products commute,
 // are symmetric, and only their lower triangles are computed.  Returns the
-// buffer holding O (rows layout).
+// buffer holding O in rows layout.
 dion3_status gram_ns(const Plan& P, const dion3_ns_cfg& cfg, const Bufs& bf, f16** out,
                      hipStream_t s) {
-  f16 *X = bf.Xa, *Xalt = bf.Xb;
+  XPair x = bf.a, xalt = bf.b;
   f16 *R = bf.R, *Z = bf.Z, *Tm = bf.T, *Q = bf.Q0, *Qn = bf.Q1;
-  HIP_TRY(gram(P, X, R, s));
+  HIP_TRY(gram(P, x, R, s));
   bool q_identity = true;
   const int T = cfg.iters;
   for (int t = 1; t <= T; ++t) {
-    if (restart_at(cfg, t)) {
+    if (restart_at(cfg, t)) {      // X <- Q X, R <- X X^T, Q <- I
       if (!q_identity) {
-        HIP_TRY(rect(P, Q, X, Xalt, s));
-        f16* tmp = X; X = Xalt; Xalt = tmp;
+        HIP_TRY(rect(P, Q, x, xalt, true, s));
+        XPair tmp = x; x = xalt; xalt = tmp;
       }
-      HIP_TRY(gram(P, X, R, s));
+      HIP_TRY(gram(P, x, R, s));
       q_identity = true;
     }
     const float a = cfg.abc[t - 1][0], b = cfg.abc[t - 1][1], c = cfg.abc[t - 1][2];
@@ -209,8 +228,8 @@ dion3_status gram_ns(const Plan& P, const dion3_ns_cfg& cfg, const Bufs& bf, f16
       HIP_TRY(symm(P, Tm, Zv, nullptr, R, 1.0f, 0.0f, 0.0f, false, s));
     }
   }
-  HIP_TRY(rect(P, Q, X, Xalt, s));
-  *out = Xalt;
+  HIP_TRY(rect(P, Q, x, xalt, false, s));
+  *out = xalt.X;
   return DION3_OK;
 }
 
@@ -251,8 +270,8 @@ dion3_status step_impl(BatchPtr<float> W, BatchPtr<float> M, int batch, long lon
   }
   {
     TraceScope ts("gather", 0.0, Bd * km * 10.0, s);
-    HIP_TRY(launch_gather_f32(M, batch, (int)n, (int)m, ld, idx, (int)k, scale, mu, true, bf.Xa,
-                              P.kp * P.mp, (int)P.kp, (int)P.mp, s));
+    HIP_TRY(launch_gather_f32(M, batch, (int)n, (int)m, ld, idx, (int)k, scale, mu, true, bf.a.X,
+                              bf.a.XT, P.kp * P.mp, (int)P.kp, (int)P.mp, s));
   }
   f16* O = nullptr;
   st = gram_ns(P, cfg, bf, &O, s);
@@ -400,8 +419,8 @@ dion3_status dion3_gram_ns(const uint16_t* X, uint16_t* O, int32_t batch, int64_
   BatchPtr<const f16> Xb = {(const f16*)X, k * m, nullptr};
   HIP_TRY(launch_row_score_f16(Xb, batch, (int)k, (int)m, m, sq, s));
   HIP_TRY(launch_topk(nullptr, sq, batch, (int)k, (int)k, idx, scale, (double)cfg.eps, s));
-  HIP_TRY(launch_gather_f16(Xb, batch, (int)m, m, (int)k, scale, bf.Xa, P.kp * P.mp, (int)P.kp,
-                            (int)P.mp, s));
+  HIP_TRY(launch_gather_f16(Xb, batch, (int)m, m, (int)k, scale, bf.a.X, bf.a.XT, P.kp * P.mp,
+                            (int)P.kp, (int)P.mp, s));
   f16* Ob = nullptr;
   st = gram_ns(P, cfg, bf, &Ob, s);
   if (st != DION3_OK) return st;

@@ -24,19 +24,20 @@ constexpr int kTile = 128;
 inline long long pad_to(long long x, long long p) { return (x + p - 1) / p * p; }
 
 // C = alpha * A * B^T (+ beta * D + gamma * I when `epilogue`), batched.
-//  A is logically M x K: row form A[m * lda + k], col form A[k * lda + m].
-//  B is logically N x K: row form B[n * ldb + k], col form B[k * ldb + n].
-//  C is M x N written C[m * ldc + n], or C[n * ldc + m] when c_t.
-//  lower: M == N, only tiles on or below the diagonal are computed and
-//  every element (r >= c) is written to both C[r][c] and C[c][r].
+//  A is M x K stored A[m * lda + k]; B is N x K stored B[n * ldb + k].
+//  Rows outside M (or N) read as zero; outputs outside M x N are not written.
+//  lower: M == N, only tiles on or below the diagonal are computed and each
+//  element (r >= c) is written to both C[r][c] and C[c][r].
+//  Otherwise C[m][n] is written when C is set and CT[n][m] when CT is set.
 // M, N must be multiples of 128, K a multiple of 64, ld* multiples of 8.
 enum GemmRole { kRoleGram = 0, kRolePoly = 1, kRoleSymm = 2, kRoleRect = 3 };
 
 struct GemmDesc {
   int role;
-  const f16* A; long long sA; int lda; bool a_col;
-  const f16* B; long long sB; int ldb; bool b_col;
-  f16* C; long long sC; int ldc; bool c_t;
+  const f16* A; long long sA; int lda;
+  const f16* B; long long sB; int ldb;
+  f16* C; long long sC; int ldc;
+  f16* CT; long long sCT; int ldct;
   const f16* D; long long sD; int ldd;
   int M, N, K, batch;
   bool lower, epilogue;
@@ -64,14 +65,15 @@ hipError_t launch_row_score_f16(BatchPtr<const f16> X, int batch, int n, int m, 
 hipError_t launch_topk(const double* l1, const double* sq, int batch, int n, int k, int* idx,
                        double* scale, double eps, hipStream_t s);
 
-// X[b][r][:] = fp16(M[b][idx[r]][:] * scale[b]) for r < k, zero padding up to
-// kp x mp; when decay, M[b][idx[r]][:] *= mu (one fp32 multiply).
-// idx == nullptr means the identity.
+// Gather of the selected rows into both layouts: X[b][r][j] and
+// XT[b][j][r] = fp16(M[b][idx[r]][j] * scale[b]) for r < k, j < m, zero in
+// the padding up to kp x mp (X) and mp x kp (XT).  With decay,
+// M[b][idx[r]][j] *= mu (one fp32 multiply).  idx == nullptr: identity.
 hipError_t launch_gather_f32(BatchPtr<float> M, int batch, int n, int m, long long ld,
                              const int* idx, int k, const double* scale, float mu, bool decay,
-                             f16* X, long long sX, int kp, int mp, hipStream_t s);
+                             f16* X, f16* XT, long long sX, int kp, int mp, hipStream_t s);
 hipError_t launch_gather_f16(BatchPtr<const f16> Xin, int batch, int m, long long ld, int k,
-                             const double* scale, f16* X, long long sX, int kp, int mp,
+                             const double* scale, f16* X, f16* XT, long long sX, int kp, int mp,
                              hipStream_t s);
 
 // W[b][idx[r]][:] -= lr * O[b][r][:] (skipped when W has no pointers), and

@@ -4,31 +4,54 @@
 // level-1 and level-2 paragraphs: symmetric products need only the lower
 // triangle, which is then copied to the upper one).
 //
-// Block tile 128 x 128, K step 64, 256 threads = 4 waves in a 2 x 2 grid,
-// each wave owning a 64 x 64 sub-tile as 2 x 2 v_mfma_f32_32x32x16_f16.
-// Operand tiles are staged through LDS in K-contiguous rows (padded by 8
-// halves) with a register prefetch of the next K step and two LDS buffers,
-// so one barrier per K step.  Operands stored with M/N contiguous ("col"
-// form) are transposed while being written to LDS.
+// C = alpha * A * B^T (+ beta * D + gamma * I), with both operands stored
+// K-contiguous (the step keeps X in both layouts so that every product has
+// this form).  Two tile configurations:
+//   * 256 x 256 block, 8 waves in 2 x 4, each wave 128 x 64 = 4 x 2
+//     v_mfma_f32_32x32x16_f16 tiles (one block per CU, 147 KB of LDS);
+//   * 128 x 128 block, 4 waves in 2 x 2, each wave 64 x 64 (two blocks per CU),
+//     for grids too small to fill 256 CUs with the large tile.
+// K advances 64 at a time through two LDS buffers (rows padded by 8 halves:
+// conflict-free 16-byte fragment reads) fed by a two-deep register prefetch,
+// so each global load has two K steps of MFMA work to land.  The epilogue
+// stages the fp16 tile in LDS and writes it with 16-byte stores as rows, and
+// for the mirrored (symmetric) or transposed outputs as columns.
 #include "dion3_internal.h"
 
 namespace dion3 {
 namespace {
 
-constexpr int BM = 128, BN = 128, BK = 64;
-constexpr int LDSK = BK + 8;   // halves per LDS row (144 bytes: 16-byte aligned, bank-skewed)
+constexpr int BK = 64;
+constexpr int LDSK = BK + 8;   // halves per LDS operand row
 
 typedef f16 half8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
 struct GemmArgs {
-  const f16* A; const f16* B; f16* C; const f16* D;
-  long long sA, sB, sC, sD;
-  int lda, ldb, ldc, ldd;
-  int K;
-  int tilesN, tilesPerMat, total;
+  const f16* A; const f16* B; f16* C; f16* CT; const f16* D;
+  long long sA, sB, sC, sCT, sD;
+  int lda, ldb, ldc, ldct, ldd;
+  int M, N, K;
+  int tilesM, tilesN, tilesPerMat, total;
   float alpha, beta, gamma;
 };
+
+template <int BM_, int WAVES_M, int WAVES_N, int PF_>
+struct Cfg {
+  static constexpr int BM = BM_, BN = BM_;
+  static constexpr int PF = PF_;                         // K steps of register prefetch
+  static constexpr int NT = 64 * WAVES_M * WAVES_N;
+  static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
+  static constexpr int FM = WTM / 32, FN = WTN / 32;
+  static constexpr int CH = BM * (BK / 8) / NT;          // 16-byte chunks per thread per operand
+  static constexpr int STAGE = (BM + BN) * LDSK;         // halves per LDS stage
+  static constexpr int EP = BN + 8;                      // epilogue staging row stride
+  static constexpr int LDS = (2 * STAGE > BM * EP) ? 2 * STAGE : BM * EP;
+  static_assert(CH * NT == BM * (BK / 8), "chunk split");
+};
+
+typedef Cfg<256, 2, 4, 1> CfgL;   // large tile (128 accumulators per lane: one prefetch set)
+typedef Cfg<128, 2, 2, 2> CfgS;   // small tile
 
 __device__ __forceinline__ void tri_index(int t, int& bi, int& bj) {
   int i = (int)((sqrtf(8.0f * (float)t + 1.0f) - 1.0f) * 0.5f);
@@ -38,47 +61,59 @@ __device__ __forceinline__ void tri_index(int t, int& bi, int& bj) {
   bj = t - i * (i + 1) / 2;
 }
 
-template <bool COL>
-__device__ __forceinline__ void load_tile(const f16* __restrict__ g, int ld, int r0, int k0, int tid,
-                                          half8 (&reg)[4]) {
+template <class C>
+__device__ __forceinline__ void gload(const f16* __restrict__ g, int ld, int r0, int rows, int k0,
+                                      int tid, half8 (&reg)[C::CH]) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    int c = tid + 256 * i;
-    if (!COL) {
-      int row = c >> 3, kc = c & 7;
+  for (int i = 0; i < C::CH; ++i) {
+    const int c = tid + C::NT * i;
+    const int row = c >> 3, kc = c & 7;
+    if (r0 + row < rows) {
       reg[i] = *(const half8*)(g + (long long)(r0 + row) * ld + k0 + kc * 8);
     } else {
-      int kr = c >> 4, rc = c & 15;
-      reg[i] = *(const half8*)(g + (long long)(k0 + kr) * ld + r0 + rc * 8);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) reg[i][e] = (f16)0.0f;
     }
   }
 }
 
-template <bool COL>
-__device__ __forceinline__ void store_tile(f16* __restrict__ s, int tid, const half8 (&reg)[4]) {
+template <class C>
+__device__ __forceinline__ void lstore(f16* __restrict__ s, int tid, const half8 (&reg)[C::CH]) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    int c = tid + 256 * i;
-    if (!COL) {
-      int row = c >> 3, kc = c & 7;
-      *(half8*)(s + row * LDSK + kc * 8) = reg[i];
-    } else {
-      int kr = c >> 4, rc = c & 15;
+  for (int i = 0; i < C::CH; ++i) {
+    const int c = tid + C::NT * i;
+    *(half8*)(s + (c >> 3) * LDSK + (c & 7) * 8) = reg[i];
+  }
+}
+
+template <class C>
+__device__ __forceinline__ void mma_stage(const f16* __restrict__ st, int wm, int wn, int lane,
+                                          floatx16 (&acc)[C::FM][C::FN]) {
+  const f16* a_s = st + (wm * C::WTM + (lane & 31)) * LDSK + (lane >> 5) * 8;
+  const f16* b_s = st + (C::BM + wn * C::WTN + (lane & 31)) * LDSK + (lane >> 5) * 8;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) s[(rc * 8 + e) * LDSK + kr] = reg[i][e];
-    }
+  for (int kk = 0; kk < BK / 16; ++kk) {
+    half8 af[C::FM], bf[C::FN];
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i) af[i] = *(const half8*)(a_s + i * 32 * LDSK + kk * 16);
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) bf[j] = *(const half8*)(b_s + j * 32 * LDSK + kk * 16);
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
   }
 }
 
 // ROLE only names the instance (0 Gram, 1 polynomial, 2 symmetric product,
 // 3 rectangular) so that profilers report each role as its own kernel.
-template <int ROLE, bool A_COL, bool B_COL, bool C_T, bool LOWER, bool EPI>
-__global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs p) {
-  __shared__ __attribute__((aligned(16))) f16 sA[2][BM * LDSK];
-  __shared__ __attribute__((aligned(16))) f16 sB[2][BN * LDSK];
+template <class C, int ROLE, bool LOWER, bool EPI>
+__global__ __launch_bounds__(C::NT, (C::BM == 256 ? 1 : 2)) void k_gemm(GemmArgs p) {
+  __shared__ __attribute__((aligned(16))) f16 lds[C::LDS];
 
   // Workgroups are dispatched round-robin over the 8 XCDs; renumber them so
-  // that each XCD works on a contiguous run of tiles (mostly the same
+  // that each XCD works on a contiguous run of tiles (mostly of the same
   // matrices), which keeps their operand panels in that XCD's L2.
   const int w = blockIdx.x, G = p.total;
   const int q = G >> 3, rem = G & 7, xcd = w & 7, slot = w >> 3;
@@ -89,135 +124,219 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs p) {
   if (LOWER) {
     tri_index(t, bi, bj);
   } else {
-    bi = t / p.tilesN;
-    bj = t - bi * p.tilesN;
+    // groups of 8 tile rows, column-major inside a group: consecutive tiles
+    // share the B panel and cycle through 8 A panels
+    const int GR = 8;
+    const int per_group = GR * p.tilesN;
+    const int g0 = (t / per_group) * GR;
+    const int gsz = min(p.tilesM - g0, GR);
+    const int r = t - (t / per_group) * per_group;
+    bi = g0 + r % gsz;
+    bj = r / gsz;
   }
-  const int m0 = bi * BM, n0 = bj * BN;
+  const int m0 = bi * C::BM, n0 = bj * C::BN;
 
   const f16* __restrict__ Ab = p.A + (long long)b * p.sA;
   const f16* __restrict__ Bb = p.B + (long long)b * p.sB;
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int wm = wid >> 1, wn = wid & 1;
+  const int wm = wid / (C::BN / C::WTN), wn = wid % (C::BN / C::WTN);
 
-  floatx16 acc[2][2];
+  floatx16 acc[C::FM][C::FN];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < C::FM; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < C::FN; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-  half8 ra[4], rb[4];
   const int nk = p.K / BK;
-  load_tile<A_COL>(Ab, p.lda, m0, 0, tid, ra);
-  load_tile<B_COL>(Bb, p.ldb, n0, 0, tid, rb);
-  store_tile<A_COL>(sA[0], tid, ra);
-  store_tile<B_COL>(sB[0], tid, rb);
-  __syncthreads();
+  if constexpr (C::PF == 2) {
+    // Two register sets; set s holds the tile of K step t with t % 2 == s.
+    // Step t multiplies LDS stage t%2 and stores tile t+1 into the other
+    // stage; after the barrier its register set is refilled with tile t+3.
+    half8 ra0[C::CH], rb0[C::CH], ra1[C::CH], rb1[C::CH];
+    gload<C>(Ab, p.lda, m0, p.M, 0, tid, ra0);
+    gload<C>(Bb, p.ldb, n0, p.N, 0, tid, rb0);
+    lstore<C>(lds, tid, ra0);
+    lstore<C>(lds + C::BM * LDSK, tid, rb0);
+    if (nk > 1) {
+      gload<C>(Ab, p.lda, m0, p.M, BK, tid, ra1);
+      gload<C>(Bb, p.ldb, n0, p.N, BK, tid, rb1);
+    }
+    if (nk > 2) {
+      gload<C>(Ab, p.lda, m0, p.M, 2 * BK, tid, ra0);
+      gload<C>(Bb, p.ldb, n0, p.N, 2 * BK, tid, rb0);
+    }
+    __syncthreads();
+    for (int kt = 0; kt < nk; kt += 2) {
+      mma_stage<C>(lds, wm, wn, lane, acc);
+      if (kt + 1 < nk) {
+        lstore<C>(lds + C::STAGE, tid, ra1);
+        lstore<C>(lds + C::STAGE + C::BM * LDSK, tid, rb1);
+      }
+      __syncthreads();
+      if (kt + 3 < nk) {
+        gload<C>(Ab, p.lda, m0, p.M, (kt + 3) * BK, tid, ra1);
+        gload<C>(Bb, p.ldb, n0, p.N, (kt + 3) * BK, tid, rb1);
+      }
+      if (kt + 1 >= nk) break;
+      mma_stage<C>(lds + C::STAGE, wm, wn, lane, acc);
+      if (kt + 2 < nk) {
+        lstore<C>(lds, tid, ra0);
+        lstore<C>(lds + C::BM * LDSK, tid, rb0);
+      }
+      __syncthreads();
+      if (kt + 4 < nk) {
+        gload<C>(Ab, p.lda, m0, p.M, (kt + 4) * BK, tid, ra0);
+        gload<C>(Bb, p.ldb, n0, p.N, (kt + 4) * BK, tid, rb0);
+      }
+    }
+  } else {
+    // One register set: step t multiplies stage t%2 while tile t+1 waits in
+    // registers; it is stored into the other stage and, after the barrier,
+    // the registers are refilled with tile t+2.
+    half8 ra[C::CH], rb[C::CH];
+    gload<C>(Ab, p.lda, m0, p.M, 0, tid, ra);
+    gload<C>(Bb, p.ldb, n0, p.N, 0, tid, rb);
+    lstore<C>(lds, tid, ra);
+    lstore<C>(lds + C::BM * LDSK, tid, rb);
+    if (nk > 1) {
+      gload<C>(Ab, p.lda, m0, p.M, BK, tid, ra);
+      gload<C>(Bb, p.ldb, n0, p.N, BK, tid, rb);
+    }
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+      f16* cur = lds + (kt & 1) * C::STAGE;
+      f16* nxt = lds + ((kt + 1) & 1) * C::STAGE;
+      mma_stage<C>(cur, wm, wn, lane, acc);
+      if (kt + 1 < nk) {
+        lstore<C>(nxt, tid, ra);
+        lstore<C>(nxt + C::BM * LDSK, tid, rb);
+      }
+      __syncthreads();
+      if (kt + 2 < nk) {
+        gload<C>(Ab, p.lda, m0, p.M, (kt + 2) * BK, tid, ra);
+        gload<C>(Bb, p.ldb, n0, p.N, (kt + 2) * BK, tid, rb);
+      }
+    }
+  }
 
-  const int frag_row = lane & 31, frag_k = (lane >> 5) * 8;
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    const bool more = kt + 1 < nk;
-    if (more) {
-      load_tile<A_COL>(Ab, p.lda, m0, (kt + 1) * BK, tid, ra);
-      load_tile<B_COL>(Bb, p.ldb, n0, (kt + 1) * BK, tid, rb);
-    }
-    const f16* a_s = sA[cur] + (wm * 64 + frag_row) * LDSK + frag_k;
-    const f16* b_s = sB[cur] + (wn * 64 + frag_row) * LDSK + frag_k;
+  // Epilogue: final fp32 value (alpha, D, gamma I) -> fp16 tile in LDS.
+  // Accumulator layout of the 32x32 MFMA: lane l, value v holds row
+  // 8*(v/4) + 4*(l/32) + v%4, column l%32 of its 32x32 block.
+  const f16* __restrict__ Db = EPI && p.D ? p.D + (long long)b * p.sD : nullptr;
+  f16* S = lds;
 #pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      half8 af[2], bf[2];
+  for (int i = 0; i < C::FM; ++i)
 #pragma unroll
-      for (int i = 0; i < 2; ++i) af[i] = *(const half8*)(a_s + i * 32 * LDSK + kk * 16);
+    for (int j = 0; j < C::FN; ++j)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) bf[j] = *(const half8*)(b_s + j * 32 * LDSK + kk * 16);
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
-    }
-    if (more) {
-      store_tile<A_COL>(sA[cur ^ 1], tid, ra);
-      store_tile<B_COL>(sB[cur ^ 1], tid, rb);
+      for (int v = 0; v < 16; ++v) {
+        const int r = wm * C::WTM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        const int c = wn * C::WTN + j * 32 + (lane & 31);
+        float val = acc[i][j][v];
+        if (EPI) {
+          val *= p.alpha;
+          const int gr = m0 + r, gc = n0 + c;
+          if (Db && gr < p.M && gc < p.N) val += p.beta * (float)Db[(long long)gr * p.ldd + gc];
+          if (gr == gc) val += p.gamma;
+        }
+        S[r * C::EP + c] = (f16)val;
+      }
+  __syncthreads();
+  if (LOWER && bi == bj) {
+    // diagonal tile: the upper half takes the mirror of the lower half
+    for (int e = tid; e < C::BM * C::BM; e += C::NT) {
+      const int r = e / C::BM, c = e - r * C::BM;
+      if (r < c) S[r * C::EP + c] = S[c * C::EP + r];
     }
     __syncthreads();
   }
 
-  // Epilogue.  Accumulator layout of the 32x32 MFMA: lane l, value v holds
-  // row 8*(v/4) + 4*(l/32) + v%4, column l%32 of the 32x32 block.
-  f16* __restrict__ Cb = p.C + (long long)b * p.sC;
-  const f16* __restrict__ Db = EPI && p.D ? p.D + (long long)b * p.sD : nullptr;
+  f16* __restrict__ Cb = p.C ? p.C + (long long)b * p.sC : nullptr;
+  if (Cb) {   // rows: C[m0 + r][n0 + c]
+    for (int e = tid; e < C::BM * (C::BN / 8); e += C::NT) {
+      const int r = e / (C::BN / 8), c8 = e - r * (C::BN / 8);
+      const int gr = m0 + r, gc = n0 + c8 * 8;
+      if (gr < p.M && gc < p.N)
+        *(half8*)(Cb + (long long)gr * p.ldc + gc) = *(const half8*)(S + r * C::EP + c8 * 8);
+    }
+  }
+  // columns: the mirror of an off-diagonal lower tile into C, or the
+  // transposed output CT[n0 + c][m0 + r]
+  f16* __restrict__ Tb = nullptr;
+  int ldt = 0;
+  if (LOWER) {
+    if (bi != bj) { Tb = Cb; ldt = p.ldc; }
+  } else if (p.CT) {
+    Tb = p.CT + (long long)b * p.sCT;
+    ldt = p.ldct;
+  }
+  if (Tb) {
+    for (int e = tid; e < C::BN * (C::BM / 8); e += C::NT) {
+      const int r8 = e / C::BN, c = e - r8 * C::BN;
+      const int gr = n0 + c, gc = m0 + r8 * 8;
+      if (gr < p.N && gc < p.M) {
+        half8 v;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int rr = m0 + wm * 64 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        const int cc = n0 + wn * 64 + j * 32 + (lane & 31);
-        float val = acc[i][j][v];
-        if (EPI) {
-          val *= p.alpha;
-          if (Db) val += p.beta * (float)Db[(long long)rr * p.ldd + cc];
-          if (rr == cc) val += p.gamma;
-        }
-        const f16 h = (f16)val;
-        if (LOWER) {
-          if (rr >= cc) {
-            Cb[(long long)rr * p.ldc + cc] = h;
-            Cb[(long long)cc * p.ldc + rr] = h;
-          }
-        } else if (C_T) {
-          Cb[(long long)cc * p.ldc + rr] = h;
-        } else {
-          Cb[(long long)rr * p.ldc + cc] = h;
-        }
+        for (int k = 0; k < 8; ++k) v[k] = S[(r8 * 8 + k) * C::EP + c];
+        *(half8*)(Tb + (long long)gr * ldt + gc) = v;
       }
+    }
+  }
 }
 
-template <int ROLE, bool A_COL, bool B_COL, bool C_T, bool LOWER, bool EPI>
+template <class C, int ROLE, bool LOWER, bool EPI>
 hipError_t launch(const GemmDesc& d, hipStream_t s) {
   GemmArgs p;
-  p.A = d.A; p.B = d.B; p.C = d.C; p.D = d.D;
-  p.sA = d.sA; p.sB = d.sB; p.sC = d.sC; p.sD = d.sD;
-  p.lda = d.lda; p.ldb = d.ldb; p.ldc = d.ldc; p.ldd = d.ldd;
-  p.K = d.K;
-  const int tm = d.M / BM, tn = d.N / BN;
-  p.tilesN = tn;
-  p.tilesPerMat = LOWER ? tm * (tm + 1) / 2 : tm * tn;
+  p.A = d.A; p.B = d.B; p.C = d.C; p.CT = d.CT; p.D = d.D;
+  p.sA = d.sA; p.sB = d.sB; p.sC = d.sC; p.sCT = d.sCT; p.sD = d.sD;
+  p.lda = d.lda; p.ldb = d.ldb; p.ldc = d.ldc; p.ldct = d.ldct; p.ldd = d.ldd;
+  p.M = d.M; p.N = d.N; p.K = d.K;
+  p.tilesM = (d.M + C::BM - 1) / C::BM;
+  p.tilesN = (d.N + C::BN - 1) / C::BN;
+  p.tilesPerMat = LOWER ? p.tilesM * (p.tilesM + 1) / 2 : p.tilesM * p.tilesN;
   const long long total = (long long)p.tilesPerMat * d.batch;
   if (total <= 0 || total > 0x7fffffffLL) return hipErrorInvalidValue;
   p.total = (int)total;
   p.alpha = d.alpha; p.beta = d.beta; p.gamma = d.gamma;
-  hipLaunchKernelGGL((k_gemm<ROLE, A_COL, B_COL, C_T, LOWER, EPI>), dim3(p.total), dim3(256), 0, s, p);
+  hipLaunchKernelGGL((k_gemm<C, ROLE, LOWER, EPI>), dim3(p.total), dim3(C::NT), 0, s, p);
   return hipGetLastError();
+}
+
+// The large tile needs about two full waves of blocks over the 256 CUs to
+// beat the small one (two blocks per CU).
+bool use_large(const GemmDesc& d) {
+  const long long tm = (d.M + 255) / 256, tn = (d.N + 255) / 256;
+  const long long tiles = d.lower ? tm * (tm + 1) / 2 : tm * tn;
+  return tiles * d.batch >= 512;
+}
+
+template <int ROLE, bool LOWER, bool EPI>
+hipError_t launch_cfg(const GemmDesc& d, hipStream_t s) {
+  return use_large(d) ? launch<CfgL, ROLE, LOWER, EPI>(d, s) : launch<CfgS, ROLE, LOWER, EPI>(d, s);
 }
 
 }  // namespace
 
 hipError_t launch_gemm(const GemmDesc& d, hipStream_t s) {
-  if (d.M % BM || d.N % BN || d.K % BK || d.K <= 0 || d.batch <= 0) return hipErrorInvalidValue;
-  if (d.lower && d.M != d.N) return hipErrorInvalidValue;
+  if (d.M % 128 || d.N % 128 || d.K % BK || d.K <= 0 || d.batch <= 0) return hipErrorInvalidValue;
+  if (d.lower && (d.M != d.N || d.CT || !d.C)) return hipErrorInvalidValue;
+  if (!d.lower && !d.C && !d.CT) return hipErrorInvalidValue;
   switch (d.role) {
     case kRoleGram:
-      if (!d.lower || d.c_t || d.epilogue || d.a_col != d.b_col) break;
-      return d.a_col ? launch<kRoleGram, true, true, false, true, false>(d, s)
-                     : launch<kRoleGram, false, false, false, true, false>(d, s);
+      if (!d.lower || d.epilogue) break;
+      return launch_cfg<kRoleGram, true, false>(d, s);
     case kRolePoly:
-      if (!d.lower || d.c_t || !d.epilogue || d.a_col || d.b_col) break;
-      return launch<kRolePoly, false, false, false, true, true>(d, s);
+      if (!d.lower || !d.epilogue) break;
+      return launch_cfg<kRolePoly, true, true>(d, s);
     case kRoleSymm:
-      if (!d.lower || d.c_t || d.epilogue || d.a_col || d.b_col) break;
-      return launch<kRoleSymm, false, false, false, true, false>(d, s);
+      if (!d.lower || d.epilogue) break;
+      return launch_cfg<kRoleSymm, true, false>(d, s);
     case kRoleRect:
-      if (d.lower || d.epilogue || d.a_col) break;
-      if (d.b_col && !d.c_t) return launch<kRoleRect, false, true, false, false, false>(d, s);
-      if (!d.b_col && d.c_t) return launch<kRoleRect, false, false, true, false, false>(d, s);
-      if (!d.b_col && !d.c_t) return launch<kRoleRect, false, false, false, false, false>(d, s);
-      break;
+      if (d.lower || d.epilogue) break;
+      return launch_cfg<kRoleRect, false, false>(d, s);
   }
   return hipErrorInvalidValue;
 }

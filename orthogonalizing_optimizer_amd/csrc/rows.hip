@@ -209,60 +209,83 @@ __global__ __launch_bounds__(TK_THREADS) void k_topk(const double* __restrict__ 
 
 // ------------------------------------------------------------- gather
 
-__global__ __launch_bounds__(256) void k_gather_f32(BatchPtr<float> M, int n, int m, long long ld,
-                                                    const int* __restrict__ idx, int k,
-                                                    const double* __restrict__ scale, float mu,
-                                                    int decay, f16* __restrict__ X, long long sX,
-                                                    int kp, int mp) {
-  const int b = blockIdx.y;
-  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (r >= kp) return;
-  f16* __restrict__ dst = X + (long long)b * sX + (long long)r * mp;
-  int j0 = 0;
-  const int row = r < k ? (idx ? idx[(long long)b * k + r] : r) : -1;
-  if (row >= 0 && row < n) {
-    float* __restrict__ src = M.get(b) + (long long)row * ld;
-    const float s = (float)scale[b];
-    if (((uintptr_t)src & 15) == 0 && (m & 3) == 0) {
-      float4* s4 = (float4*)src;
-      half4* d4 = (half4*)dst;
-      for (int j = lane; j < (m >> 2); j += 64) {
-        const float4 x = s4[j];
-        half4 h;
-        h[0] = (f16)(x.x * s); h[1] = (f16)(x.y * s); h[2] = (f16)(x.z * s); h[3] = (f16)(x.w * s);
-        d4[j] = h;
-        if (decay) s4[j] = make_float4(mu * x.x, mu * x.y, mu * x.z, mu * x.w);
-      }
-    } else {
-      for (int j = lane; j < m; j += 64) {
-        const float x = src[j];
-        dst[j] = (f16)(x * s);
-        if (decay) src[j] = mu * x;
-      }
-    }
-    j0 = m;
+// One block per 64 selected rows x 64 columns: reads the rows of M once
+// (256-byte row segments), writes X in rows layout directly and, through an
+// LDS tile, its transpose XT, so that every product of the Gram iteration
+// reads K-contiguous operands; with DECAY also writes M back times mu.
+constexpr int GT = 64;
+
+template <typename T>
+__device__ __forceinline__ void load4(const T* __restrict__ src, int c, int m, float (&v)[4]) {
+  if (sizeof(T) == 4 && c + 3 < m && ((uintptr_t)src & 15) == 0) {
+    const float4 x = *(const float4*)src;
+    v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+  } else if (sizeof(T) == 2 && c + 3 < m && ((uintptr_t)src & 7) == 0) {
+    const half4 x = *(const half4*)src;
+    v[0] = (float)x[0]; v[1] = (float)x[1]; v[2] = (float)x[2]; v[3] = (float)x[3];
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = c + e < m ? (float)src[e] : 0.0f;
   }
-  for (int j = j0 + lane; j < mp; j += 64) dst[j] = (f16)0.0f;
 }
 
-__global__ __launch_bounds__(256) void k_gather_f16(BatchPtr<const f16> Xin, int m, long long ld,
-                                                    int k, const double* __restrict__ scale,
-                                                    f16* __restrict__ X, long long sX, int kp,
-                                                    int mp) {
-  const int b = blockIdx.y;
-  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (r >= kp) return;
-  f16* __restrict__ dst = X + (long long)b * sX + (long long)r * mp;
-  int j0 = 0;
-  if (r < k) {
-    const f16* __restrict__ src = Xin.get(b) + (long long)r * ld;
-    const float s = (float)scale[b];
-    for (int j = lane; j < m; j += 64) dst[j] = (f16)((float)src[j] * s);
-    j0 = m;
+__device__ __forceinline__ void decay4(float* __restrict__ src, int c, int m, float mu,
+                                       const float (&v)[4]) {
+  if (c + 3 < m && ((uintptr_t)src & 15) == 0) {
+    *(float4*)src = make_float4(mu * v[0], mu * v[1], mu * v[2], mu * v[3]);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (c + e < m) src[e] = mu * v[e];
   }
-  for (int j = j0 + lane; j < mp; j += 64) dst[j] = (f16)0.0f;
+}
+
+template <typename T, bool DECAY>
+__global__ __launch_bounds__(256) void k_gather(BatchPtr<T> M, int n, int m, long long ld,
+                                                const int* __restrict__ idx, int k,
+                                                const double* __restrict__ scale, float mu,
+                                                f16* __restrict__ X, f16* __restrict__ XT,
+                                                long long sX, int kp, int mp) {
+  __shared__ f16 tile[GT][GT + 2];
+  const int b = blockIdx.z;
+  const int c0 = blockIdx.x * GT, r0 = blockIdx.y * GT;
+  const int tid = threadIdx.x;
+  const int cl = 4 * (tid & 15);
+  const float sc = (float)scale[b];
+  f16* __restrict__ Xb = X + (long long)b * sX;
+  f16* __restrict__ XTb = XT + (long long)b * sX;
+  T* base = M.get(b);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int rl = (tid >> 4) + 16 * i;
+    const int r = r0 + rl, c = c0 + cl;
+    int row = -1;
+    if (r < k) {
+      row = idx ? idx[(long long)b * k + r] : r;
+      if (row >= n) row = -1;
+    }
+    float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (row >= 0 && c < m) {
+      T* src = base + (long long)row * ld + c;
+      load4<T>(src, c, m, v);
+      if constexpr (DECAY) decay4((float*)src, c, m, mu, v);
+    }
+    half4 h;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      h[e] = (f16)(v[e] * sc);
+      tile[rl][cl + e] = h[e];
+    }
+    *(half4*)(Xb + (long long)r * mp + c) = h;
+  }
+  __syncthreads();
+  for (int e = tid; e < GT * (GT / 8); e += 256) {
+    const int col = e >> 3, r8 = e & 7;
+    half8 v;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v[q] = tile[r8 * 8 + q][col];
+    *(half8*)(XTb + (long long)(c0 + col) * kp + r0 + r8 * 8) = v;
+  }
 }
 
 // ------------------------------------------------------------- update
@@ -331,17 +354,23 @@ hipError_t launch_topk(const double* l1, const double* sq, int batch, int n, int
 
 hipError_t launch_gather_f32(BatchPtr<float> M, int batch, int n, int m, long long ld,
                              const int* idx, int k, const double* scale, float mu, bool decay,
-                             f16* X, long long sX, int kp, int mp, hipStream_t s) {
-  hipLaunchKernelGGL(k_gather_f32, dim3(blocks_for(kp), batch), dim3(256), 0, s, M, n, m, ld, idx, k,
-                     scale, mu, decay ? 1 : 0, X, sX, kp, mp);
+                             f16* X, f16* XT, long long sX, int kp, int mp, hipStream_t s) {
+  const dim3 grid(mp / GT, kp / GT, batch);
+  if (decay)
+    hipLaunchKernelGGL((k_gather<float, true>), grid, dim3(256), 0, s, M, n, m, ld, idx, k, scale,
+                       mu, X, XT, sX, kp, mp);
+  else
+    hipLaunchKernelGGL((k_gather<float, false>), grid, dim3(256), 0, s, M, n, m, ld, idx, k, scale,
+                       mu, X, XT, sX, kp, mp);
   return hipGetLastError();
 }
 
 hipError_t launch_gather_f16(BatchPtr<const f16> Xin, int batch, int m, long long ld, int k,
-                             const double* scale, f16* X, long long sX, int kp, int mp,
+                             const double* scale, f16* X, f16* XT, long long sX, int kp, int mp,
                              hipStream_t s) {
-  hipLaunchKernelGGL(k_gather_f16, dim3(blocks_for(kp), batch), dim3(256), 0, s, Xin, m, ld, k,
-                     scale, X, sX, kp, mp);
+  const dim3 grid(mp / GT, kp / GT, batch);
+  hipLaunchKernelGGL((k_gather<const f16, false>), grid, dim3(256), 0, s, Xin, k, m, ld, nullptr, k,
+                     scale, 1.0f, X, XT, sX, kp, mp);
   return hipGetLastError();
 }
 
