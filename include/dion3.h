@@ -139,7 +139,7 @@ DION3_API dion3_status dion3_syrk_f16(const uint16_t* A, uint16_t* R, int32_t ba
 
 /* dion3_symm_f16 ("A^2 + B"): C[b] = alpha A[b] B[b] + beta D[b] + gamma I
  * for symmetric, commuting s x s fp16 matrices A[b], B[b] (so the product is
- * symmetric); D may be NULL when beta == 0.  All four share row stride ld and
+ * symmetric) and a symmetric D[b]; D may be NULL when beta == 0.  All four share row stride ld and
  * batch stride s*ld; s must be a multiple of 128, ld a multiple of 8.  Only
  * lower-triangle tiles are computed, then mirrored.  C must not alias A, B
  * or D. */

@@ -50,7 +50,7 @@ struct Cfg {
   static_assert(CH * NT == BM * (BK / 8), "chunk split");
 };
 
-typedef Cfg<256, 2, 4, 1> CfgL;   // large tile (128 accumulators per lane: one prefetch set)
+typedef Cfg<256, 2, 4, 1> CfgL;   // large tile (2 waves per SIMD: one prefetch set fits)
 typedef Cfg<128, 2, 2, 2> CfgS;   // small tile
 
 __device__ __forceinline__ void tri_index(int t, int& bi, int& bj) {
@@ -61,19 +61,25 @@ __device__ __forceinline__ void tri_index(int t, int& bi, int& bj) {
   bj = t - i * (i + 1) / 2;
 }
 
+typedef int int4v __attribute__((ext_vector_type(4)));
+
+// Buffer resource over one operand matrix: `rows` rows of `ld` halves.  Raw
+// buffer loads past num_records return zero, which zero-fills the rows of a
+// tile that lie beyond the matrix without any branch.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t operand_rsrc(const f16* base, int rows, int ld) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, rows * ld * 2, 0x00020000);
+}
+
 template <class C>
-__device__ __forceinline__ void gload(const f16* __restrict__ g, int ld, int r0, int rows, int k0,
-                                      int tid, half8 (&reg)[C::CH]) {
+__device__ __forceinline__ void gload(__amdgpu_buffer_rsrc_t rs, int ld, int r0, int k0, int tid,
+                                      half8 (&reg)[C::CH]) {
+  const int row = tid >> 3, kc = tid & 7;
+  const int voff = ((r0 + row) * ld + kc * 8) * 2;
+  constexpr int ROWS_PER = C::NT / 8;
 #pragma unroll
   for (int i = 0; i < C::CH; ++i) {
-    const int c = tid + C::NT * i;
-    const int row = c >> 3, kc = c & 7;
-    if (r0 + row < rows) {
-      reg[i] = *(const half8*)(g + (long long)(r0 + row) * ld + k0 + kc * 8);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) reg[i][e] = (f16)0.0f;
-    }
+    const int4v v = __builtin_amdgcn_raw_buffer_load_b128(rs, voff + i * ROWS_PER * ld * 2, k0 * 2, 0);
+    reg[i] = __builtin_bit_cast(half8, v);
   }
 }
 
@@ -98,6 +104,45 @@ __device__ __forceinline__ void mma_stage(const f16* __restrict__ st, int wm, in
     for (int i = 0; i < C::FM; ++i) af[i] = *(const half8*)(a_s + i * 32 * LDSK + kk * 16);
 #pragma unroll
     for (int j = 0; j < C::FN; ++j) bf[j] = *(const half8*)(b_s + j * 32 * LDSK + kk * 16);
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+  }
+}
+
+// One K step of MFMAs on LDS stage `st`; right after the first fragment
+// reads it writes the next tile (held in registers) into stage `nxt` and
+// refills the registers with the tile after that, so that the LDS writes
+// and the global loads overlap the MFMAs of this step.
+template <class C>
+__device__ __forceinline__ void mma_stage_fused(const f16* __restrict__ st, f16* __restrict__ nxt,
+                                                bool store_next, bool load_next,
+                                                __amdgpu_buffer_rsrc_t Ab, __amdgpu_buffer_rsrc_t Bb,
+                                                int lda, int ldb, int m0, int n0, int k0_next,
+                                                int tid, half8 (&ra)[C::CH], half8 (&rb)[C::CH],
+                                                int wm, int wn, int lane,
+                                                floatx16 (&acc)[C::FM][C::FN]) {
+  const f16* a_s = st + (wm * C::WTM + (lane & 31)) * LDSK + (lane >> 5) * 8;
+  const f16* b_s = st + (C::BM + wn * C::WTN + (lane & 31)) * LDSK + (lane >> 5) * 8;
+#pragma unroll
+  for (int kk = 0; kk < BK / 16; ++kk) {
+    half8 af[C::FM], bf[C::FN];
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i) af[i] = *(const half8*)(a_s + i * 32 * LDSK + kk * 16);
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) bf[j] = *(const half8*)(b_s + j * 32 * LDSK + kk * 16);
+    if (kk == 0) {
+      if (store_next) {
+        lstore<C>(nxt, tid, ra);
+        lstore<C>(nxt + C::BM * LDSK, tid, rb);
+      }
+      if (load_next) {
+        gload<C>(Ab, lda, m0, k0_next, tid, ra);
+        gload<C>(Bb, ldb, n0, k0_next, tid, rb);
+      }
+    }
 #pragma unroll
     for (int i = 0; i < C::FM; ++i)
 #pragma unroll
@@ -136,8 +181,8 @@ __global__ __launch_bounds__(C::NT, (C::BM == 256 ? 1 : 2)) void k_gemm(GemmArgs
   }
   const int m0 = bi * C::BM, n0 = bj * C::BN;
 
-  const f16* __restrict__ Ab = p.A + (long long)b * p.sA;
-  const f16* __restrict__ Bb = p.B + (long long)b * p.sB;
+  const __amdgpu_buffer_rsrc_t Ab = operand_rsrc(p.A + (long long)b * p.sA, p.M, p.lda);
+  const __amdgpu_buffer_rsrc_t Bb = operand_rsrc(p.B + (long long)b * p.sB, p.N, p.ldb);
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wm = wid / (C::BN / C::WTN), wn = wid % (C::BN / C::WTN);
@@ -156,17 +201,17 @@ __global__ __launch_bounds__(C::NT, (C::BM == 256 ? 1 : 2)) void k_gemm(GemmArgs
     // Step t multiplies LDS stage t%2 and stores tile t+1 into the other
     // stage; after the barrier its register set is refilled with tile t+3.
     half8 ra0[C::CH], rb0[C::CH], ra1[C::CH], rb1[C::CH];
-    gload<C>(Ab, p.lda, m0, p.M, 0, tid, ra0);
-    gload<C>(Bb, p.ldb, n0, p.N, 0, tid, rb0);
+    gload<C>(Ab, p.lda, m0, 0, tid, ra0);
+    gload<C>(Bb, p.ldb, n0, 0, tid, rb0);
     lstore<C>(lds, tid, ra0);
     lstore<C>(lds + C::BM * LDSK, tid, rb0);
     if (nk > 1) {
-      gload<C>(Ab, p.lda, m0, p.M, BK, tid, ra1);
-      gload<C>(Bb, p.ldb, n0, p.N, BK, tid, rb1);
+      gload<C>(Ab, p.lda, m0, BK, tid, ra1);
+      gload<C>(Bb, p.ldb, n0, BK, tid, rb1);
     }
     if (nk > 2) {
-      gload<C>(Ab, p.lda, m0, p.M, 2 * BK, tid, ra0);
-      gload<C>(Bb, p.ldb, n0, p.N, 2 * BK, tid, rb0);
+      gload<C>(Ab, p.lda, m0, 2 * BK, tid, ra0);
+      gload<C>(Bb, p.ldb, n0, 2 * BK, tid, rb0);
     }
     __syncthreads();
     for (int kt = 0; kt < nk; kt += 2) {
@@ -177,8 +222,8 @@ __global__ __launch_bounds__(C::NT, (C::BM == 256 ? 1 : 2)) void k_gemm(GemmArgs
       }
       __syncthreads();
       if (kt + 3 < nk) {
-        gload<C>(Ab, p.lda, m0, p.M, (kt + 3) * BK, tid, ra1);
-        gload<C>(Bb, p.ldb, n0, p.N, (kt + 3) * BK, tid, rb1);
+        gload<C>(Ab, p.lda, m0, (kt + 3) * BK, tid, ra1);
+        gload<C>(Bb, p.ldb, n0, (kt + 3) * BK, tid, rb1);
       }
       if (kt + 1 >= nk) break;
       mma_stage<C>(lds + C::STAGE, wm, wn, lane, acc);
@@ -188,43 +233,39 @@ __global__ __launch_bounds__(C::NT, (C::BM == 256 ? 1 : 2)) void k_gemm(GemmArgs
       }
       __syncthreads();
       if (kt + 4 < nk) {
-        gload<C>(Ab, p.lda, m0, p.M, (kt + 4) * BK, tid, ra0);
-        gload<C>(Bb, p.ldb, n0, p.N, (kt + 4) * BK, tid, rb0);
+        gload<C>(Ab, p.lda, m0, (kt + 4) * BK, tid, ra0);
+        gload<C>(Bb, p.ldb, n0, (kt + 4) * BK, tid, rb0);
       }
     }
   } else {
-    // One register set: step t multiplies stage t%2 while tile t+1 waits in
-    // registers; it is stored into the other stage and, after the barrier,
-    // the registers are refilled with tile t+2.
+    // One register set.  Step t multiplies stage t%2; at its start tile t+1
+    // goes from the registers into the other stage (free since the barrier
+    // that ended step t-1) and tile t+2 is requested into the registers.
     half8 ra[C::CH], rb[C::CH];
-    gload<C>(Ab, p.lda, m0, p.M, 0, tid, ra);
-    gload<C>(Bb, p.ldb, n0, p.N, 0, tid, rb);
+    gload<C>(Ab, p.lda, m0, 0, tid, ra);
+    gload<C>(Bb, p.ldb, n0, 0, tid, rb);
     lstore<C>(lds, tid, ra);
     lstore<C>(lds + C::BM * LDSK, tid, rb);
     if (nk > 1) {
-      gload<C>(Ab, p.lda, m0, p.M, BK, tid, ra);
-      gload<C>(Bb, p.ldb, n0, p.N, BK, tid, rb);
+      gload<C>(Ab, p.lda, m0, BK, tid, ra);
+      gload<C>(Bb, p.ldb, n0, BK, tid, rb);
     }
     __syncthreads();
     for (int kt = 0; kt < nk; ++kt) {
       f16* cur = lds + (kt & 1) * C::STAGE;
       f16* nxt = lds + ((kt + 1) & 1) * C::STAGE;
-      mma_stage<C>(cur, wm, wn, lane, acc);
-      if (kt + 1 < nk) {
-        lstore<C>(nxt, tid, ra);
-        lstore<C>(nxt + C::BM * LDSK, tid, rb);
-      }
+      mma_stage_fused<C>(cur, nxt, kt + 1 < nk, kt + 2 < nk, Ab, Bb, p.lda, p.ldb, m0, n0,
+                         (kt + 2) * BK, tid, ra, rb, wm, wn, lane, acc);
       __syncthreads();
-      if (kt + 2 < nk) {
-        gload<C>(Ab, p.lda, m0, p.M, (kt + 2) * BK, tid, ra);
-        gload<C>(Bb, p.ldb, n0, p.N, (kt + 2) * BK, tid, rb);
-      }
     }
   }
 
   // Epilogue: final fp32 value (alpha, D, gamma I) -> fp16 tile in LDS.
   // Accumulator layout of the 32x32 MFMA: lane l, value v holds row
-  // 8*(v/4) + 4*(l/32) + v%4, column l%32 of its 32x32 block.
+  // 8*(v/4) + 4*(l/32) + v%4, column l%32 of its 32x32 block, so each lane
+  // owns runs of 4 consecutive rows of one column.  D is symmetric, so the
+  // 4 values D[r..r+3][c] are read as the contiguous D[c][r..r+3].
+  typedef f16 half4 __attribute__((ext_vector_type(4)));
   const f16* __restrict__ Db = EPI && p.D ? p.D + (long long)b * p.sD : nullptr;
   f16* S = lds;
 #pragma unroll
@@ -232,17 +273,24 @@ __global__ __launch_bounds__(C::NT, (C::BM == 256 ? 1 : 2)) void k_gemm(GemmArgs
 #pragma unroll
     for (int j = 0; j < C::FN; ++j)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int r = wm * C::WTM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+      for (int v4 = 0; v4 < 4; ++v4) {
+        const int r = wm * C::WTM + i * 32 + 8 * v4 + 4 * (lane >> 5);
         const int c = wn * C::WTN + j * 32 + (lane & 31);
-        float val = acc[i][j][v];
+        float val[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) val[e] = acc[i][j][4 * v4 + e];
         if (EPI) {
-          val *= p.alpha;
           const int gr = m0 + r, gc = n0 + c;
-          if (Db && gr < p.M && gc < p.N) val += p.beta * (float)Db[(long long)gr * p.ldd + gc];
-          if (gr == gc) val += p.gamma;
+          half4 dv = {};
+          if (Db && gr < p.M && gc < p.N) dv = *(const half4*)(Db + (long long)gc * p.ldd + gr);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            val[e] = val[e] * p.alpha + p.beta * (float)dv[e];
+            if (gr + e == gc) val[e] += p.gamma;
+          }
         }
-        S[r * C::EP + c] = (f16)val;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) S[(r + e) * C::EP + c] = (f16)val[e];
       }
   __syncthreads();
   if (LOWER && bi == bj) {
