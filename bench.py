@@ -26,14 +26,19 @@ FP16_PEAK_TFLOPS = 2500.0      # MI355X dense fp16 MFMA
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 METRIC = "Dion3 optimizer-step ms per model + Gram-NS TFLOP/s (% fp16 MFMA peak)"
 
-GEMM_SYMBOLS = {
-    "gemm_gram": "k_gemm<0,...> (Gram X X^T, lower tiles mirrored)",
-    "gemm_poly": "k_gemm<1,...> (Z = aI + bR + cR^2, lower tiles mirrored)",
-    "gemm_symm": "k_gemm<2,...> (symmetric product, lower tiles mirrored)",
-    "gemm_rect": "k_gemm<3,...> (rectangular multiply-back Q X)",
+# trace name -> the kernel symbol rocprofv3 reports for it
+KERNEL_SYMBOLS = {
+    "gemm_gram_256": "k_gemm<Cfg<256, 2, 4, 1>, 0, true, false>",
+    "gemm_poly_256": "k_gemm<Cfg<256, 2, 4, 1>, 1, true, true>",
+    "gemm_symm_256": "k_gemm<Cfg<256, 2, 4, 1>, 2, true, false>",
+    "gemm_rect_256": "k_gemm<Cfg<256, 2, 4, 1>, 3, false, false>",
+    "gemm_gram_128": "k_gemm<Cfg<128, 2, 2, 2>, 0, true, false>",
+    "gemm_poly_128": "k_gemm<Cfg<128, 2, 2, 2>, 1, true, true>",
+    "gemm_symm_128": "k_gemm<Cfg<128, 2, 2, 2>, 2, true, false>",
+    "gemm_rect_128": "k_gemm<Cfg<128, 2, 2, 2>, 3, false, false>",
     "row_score": "k_row_score_f32",
     "topk": "k_topk",
-    "gather": "k_gather_f32",
+    "gather": "k_gather<float, true>",
     "update": "k_update",
 }
 
@@ -181,14 +186,25 @@ def main():
 
     # per-kernel statistics over the timed region
     kernels = {}
+    by_group = {}
     if not args.no_trace:
+        gi = -1
         for name, ms, fl, by in d3.trace_records():
-            st = kernels.setdefault(name, {"launches": 0, "ms": 0.0, "flops": 0.0, "bytes": 0.0})
-            st["launches"] += 1
-            st["ms"] += ms
-            st["flops"] += fl
-            st["bytes"] += by
+            if name == "row_score":          # every group's launch sequence starts with it
+                gi = (gi + 1) % len(groups)
+            for table, key in ((kernels, name), (by_group, (gi, name))):
+                st = table.setdefault(key, {"launches": 0, "ms": 0.0, "flops": 0.0, "bytes": 0.0})
+                st["launches"] += 1
+                st["ms"] += ms
+                st["flops"] += fl
+                st["bytes"] += by
         d3.trace_disable()
+    for (gi, name), st in sorted(by_group.items()):
+        g = groups[gi][0]
+        rate = (f"{st['flops'] / (st['ms'] * 1e-3) / 1e12:7.1f} TFLOP/s" if st["flops"] > 0 else
+                f"{st['bytes'] / (st['ms'] * 1e-3) / 1e9:7.1f} GB/s")
+        log(f"  group {gi} ({g.count}x{g.n}x{g.m}, k={groups[gi][3]}) {name:10s} "
+            f"avg {1e3 * st['ms'] / st['launches']:9.1f} us  ms/step {st['ms'] / args.steps:7.3f}  {rate}")
     for name, st in kernels.items():
         st["avg_us"] = 1e3 * st["ms"] / st["launches"]
         if st["flops"] > 0:
@@ -227,7 +243,7 @@ def main():
             roofline = {"bound": "hbm", "achieved": round(st["gbs"], 1), "peak": HBM_PEAK_GBS,
                         "unit": "GB/s", "frac": round(st["gbs"] / HBM_PEAK_GBS, 4)}
         roofline["traffic"] = load_traffic(dom, args.workload)
-        roofline["kernel"] = GEMM_SYMBOLS.get(dom, dom)
+        roofline["kernel"] = KERNEL_SYMBOLS.get(dom, dom)
         roofline["avg_launch_us"] = round(st["avg_us"], 2)
         roofline["work_per_launch"] = per_launch_work
 

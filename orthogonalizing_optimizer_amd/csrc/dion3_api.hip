@@ -141,8 +141,8 @@ const f16* xmathT(const Plan& P, const XPair& x) { return P.tr ? x.X : x.XT; }
 // R = X_math X_math^T.
 hipError_t gram(const Plan& P, const XPair& x, f16* R, hipStream_t s) {
   const double sv = s_of(P);
-  TraceScope ts("gemm_gram", P.B * sv * sv * L_of(P), 0.0, s);
   GemmDesc d = {};
+  d.trace_flops = P.B * sv * sv * L_of(P);
   d.role = kRoleGram;
   d.A = d.B = xmath(P, x); d.sA = d.sB = P.kp * P.mp; d.lda = d.ldb = (int)P.Lp;
   d.C = R; d.sC = P.sp * P.sp; d.ldc = (int)P.sp;
@@ -156,8 +156,8 @@ hipError_t gram(const Plan& P, const XPair& x, f16* R, hipStream_t s) {
 hipError_t symm(const Plan& P, const f16* A, const f16* B, const f16* D, f16* C, float alpha,
                 float beta, float gamma, bool epi, hipStream_t s) {
   const double sv = s_of(P);
-  TraceScope ts(epi ? "gemm_poly" : "gemm_symm", P.B * sv * sv * sv, 0.0, s);
   GemmDesc d = {};
+  d.trace_flops = P.B * sv * sv * sv;
   d.role = epi ? kRolePoly : kRoleSymm;
   const long long ss = P.sp * P.sp;
   d.A = A; d.sA = ss; d.lda = (int)P.sp;
@@ -175,8 +175,8 @@ hipError_t symm(const Plan& P, const f16* A, const f16* B, const f16* D, f16* C,
 hipError_t rect(const Plan& P, const f16* Q, const XPair& x, const XPair& y, bool both,
                 hipStream_t s) {
   const double sv = s_of(P);
-  TraceScope ts("gemm_rect", 2.0 * P.B * sv * sv * L_of(P), 0.0, s);
   GemmDesc d = {};
+  d.trace_flops = 2.0 * P.B * sv * sv * L_of(P);
   d.role = kRoleRect;
   d.A = Q; d.sA = P.sp * P.sp; d.lda = (int)P.sp;
   d.B = xmathT(P, x); d.sB = P.kp * P.mp; d.ldb = (int)P.sp;
@@ -457,6 +457,7 @@ dion3_status dion3_syrk_f16(const uint16_t* A, uint16_t* R, int32_t batch, int64
   if (((uintptr_t)A | (uintptr_t)R) & 15) return DION3_ERR_ARG;
   GemmDesc d = {};
   d.role = kRoleGram;
+  d.trace_flops = (double)batch * rows * rows * cols;
   d.A = (const f16*)A; d.sA = rows * lda; d.lda = (int)lda;
   d.B = (const f16*)A; d.sB = rows * lda; d.ldb = (int)lda;
   d.C = (f16*)R; d.sC = rows * ldr; d.ldc = (int)ldr;
@@ -478,6 +479,7 @@ dion3_status dion3_symm_f16(const uint16_t* A, const uint16_t* B, const uint16_t
   if (((uintptr_t)A | (uintptr_t)B | (uintptr_t)C | (uintptr_t)D) & 15) return DION3_ERR_ARG;
   GemmDesc d = {};
   d.role = kRolePoly;
+  d.trace_flops = (double)batch * s * s * s;
   const long long ss = s * ld;
   d.A = (const f16*)A; d.sA = ss; d.lda = (int)ld;
   d.B = (const f16*)B; d.sB = ss; d.ldb = (int)ld;

@@ -42,7 +42,10 @@ struct GemmDesc {
   int M, N, K, batch;
   bool lower, epilogue;
   float alpha, beta, gamma;
+  double trace_flops;   // algorithmic flops of this launch, for the timing trace
 };
+// Launches the product; records it in the timing trace (when enabled) under
+// "<role>_<tile edge>", e.g. "gemm_symm_256".
 hipError_t launch_gemm(const GemmDesc& d, hipStream_t s);
 
 // Optional kernel timing trace (benchmarks): while enabled, each launch is

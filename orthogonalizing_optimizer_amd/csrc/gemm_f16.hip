@@ -12,8 +12,11 @@
 //   * 128 x 128 block, 4 waves in 2 x 2, each wave 64 x 64 (two blocks per CU),
 //     for grids too small to fill 256 CUs with the large tile.
 // K advances 64 at a time through two LDS buffers (rows padded by 8 halves:
-// conflict-free 16-byte fragment reads) fed by a two-deep register prefetch,
-// so each global load has two K steps of MFMA work to land.  The epilogue
+// conflict-free 16-byte fragment reads).  Operands arrive through raw buffer
+// loads (rows past the matrix read as zero) into a register prefetch of one
+// K step (large tile; its 128 accumulators leave no room for more at two
+// waves per SIMD) or two K steps (small tile); the next tile's LDS stores
+// and global loads are issued at the start of each step's MFMAs.  The epilogue
 // stages the fp16 tile in LDS and writes it with 16-byte stores as rows, and
 // for the mirrored (symmetric) or transposed outputs as columns.
 #include "dion3_internal.h"
@@ -50,7 +53,7 @@ struct Cfg {
   static_assert(CH * NT == BM * (BK / 8), "chunk split");
 };
 
-typedef Cfg<256, 2, 4, 1> CfgL;   // large tile (2 waves per SIMD: one prefetch set fits)
+typedef Cfg<256, 2, 4, 1> CfgL;   // large tile, 8 waves of 128 x 64 (2 waves per SIMD)
 typedef Cfg<128, 2, 2, 2> CfgS;   // small tile
 
 __device__ __forceinline__ void tri_index(int t, int& bi, int& bj) {
@@ -126,13 +129,24 @@ __device__ __forceinline__ void mma_stage_fused(const f16* __restrict__ st, f16*
                                                 floatx16 (&acc)[C::FM][C::FN]) {
   const f16* a_s = st + (wm * C::WTM + (lane & 31)) * LDSK + (lane >> 5) * 8;
   const f16* b_s = st + (C::BM + wn * C::WTN + (lane & 31)) * LDSK + (lane >> 5) * 8;
+  // fragments double-buffered: those of k-slice kk+1 are read before the
+  // MFMAs of slice kk, so LDS latency hides behind them
+  half8 af[2][C::FM], bf[2][C::FN];
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i) af[0][i] = *(const half8*)(a_s + i * 32 * LDSK);
+#pragma unroll
+  for (int j = 0; j < C::FN; ++j) bf[0][j] = *(const half8*)(b_s + j * 32 * LDSK);
 #pragma unroll
   for (int kk = 0; kk < BK / 16; ++kk) {
-    half8 af[C::FM], bf[C::FN];
+    const int cb = kk & 1;
+    if (kk + 1 < BK / 16) {
 #pragma unroll
-    for (int i = 0; i < C::FM; ++i) af[i] = *(const half8*)(a_s + i * 32 * LDSK + kk * 16);
+      for (int i = 0; i < C::FM; ++i)
+        af[cb ^ 1][i] = *(const half8*)(a_s + i * 32 * LDSK + (kk + 1) * 16);
 #pragma unroll
-    for (int j = 0; j < C::FN; ++j) bf[j] = *(const half8*)(b_s + j * 32 * LDSK + kk * 16);
+      for (int j = 0; j < C::FN; ++j)
+        bf[cb ^ 1][j] = *(const half8*)(b_s + j * 32 * LDSK + (kk + 1) * 16);
+    }
     if (kk == 0) {
       if (store_next) {
         lstore<C>(nxt, tid, ra);
@@ -147,7 +161,7 @@ __device__ __forceinline__ void mma_stage_fused(const f16* __restrict__ st, f16*
     for (int i = 0; i < C::FM; ++i)
 #pragma unroll
       for (int j = 0; j < C::FN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[cb][i], bf[cb][j], acc[i][j], 0, 0, 0);
   }
 }
 
@@ -361,9 +375,19 @@ bool use_large(const GemmDesc& d) {
   return tiles * d.batch >= 512;
 }
 
+const char* trace_name(int role, bool large) {
+  static const char* names[4][2] = {{"gemm_gram_128", "gemm_gram_256"},
+                                    {"gemm_poly_128", "gemm_poly_256"},
+                                    {"gemm_symm_128", "gemm_symm_256"},
+                                    {"gemm_rect_128", "gemm_rect_256"}};
+  return names[role][large ? 1 : 0];
+}
+
 template <int ROLE, bool LOWER, bool EPI>
 hipError_t launch_cfg(const GemmDesc& d, hipStream_t s) {
-  return use_large(d) ? launch<CfgL, ROLE, LOWER, EPI>(d, s) : launch<CfgS, ROLE, LOWER, EPI>(d, s);
+  const bool large = use_large(d);
+  TraceScope ts(trace_name(ROLE, large), d.trace_flops, 0.0, s);
+  return large ? launch<CfgL, ROLE, LOWER, EPI>(d, s) : launch<CfgS, ROLE, LOWER, EPI>(d, s);
 }
 
 }  // namespace
