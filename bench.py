@@ -39,7 +39,6 @@ KERNEL_SYMBOLS = {
     "row_score": "k_row_score_f32",
     "topk": "k_topk",
     "gather": "k_gather<float, true>",
-    "update": "k_update",
 }
 
 

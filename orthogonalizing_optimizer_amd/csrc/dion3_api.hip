@@ -170,10 +170,21 @@ hipError_t symm(const Plan& P, const f16* A, const f16* B, const f16* D, f16* C,
   return launch_gemm(d, s);
 }
 
-// Y_math = Q X_math.  The restart needs Y in both layouts; the final
-// product only in rows layout (what the update reads).
+// Row-sparse update fused into the final product: W[idx[r]] -= lr * O[r]
+// and, when requested, O_out = O (rows layout, unpadded).
+struct UpdateSink {
+  BatchPtr<float> W;
+  long long ldw;
+  const int* idx;
+  float lr;
+  f16* Oout;
+};
+
+// Y_math = Q X_math.  The restart needs Y in both layouts.  The final
+// product (sink set) stores nothing: its rows-layout output goes straight
+// into the update of W (and O_out).
 hipError_t rect(const Plan& P, const f16* Q, const XPair& x, const XPair& y, bool both,
-                hipStream_t s) {
+                hipStream_t s, const UpdateSink* sink = nullptr) {
   const double sv = s_of(P);
   GemmDesc d = {};
   d.trace_flops = 2.0 * P.B * sv * sv * L_of(P);
@@ -183,6 +194,15 @@ hipError_t rect(const Plan& P, const f16* Q, const XPair& x, const XPair& y, boo
   const bool want_math = both || !P.tr, want_mathT = both || P.tr;
   d.C = want_math ? (f16*)xmath(P, y) : nullptr; d.sC = P.kp * P.mp; d.ldc = (int)P.Lp;
   d.CT = want_mathT ? (f16*)xmathT(P, y) : nullptr; d.sCT = P.kp * P.mp; d.ldct = (int)P.sp;
+  if (sink) {
+    // rows layout is the math layout when k <= m (the C pass) and its
+    // transpose when k > m (the CT pass)
+    d.sink = P.tr ? 2 : 1;
+    d.C = nullptr;
+    d.CT = nullptr;
+    d.W = sink->W; d.ldw = sink->ldw; d.idx = sink->idx; d.lr = sink->lr; d.Oout = sink->Oout;
+    d.kval = (int)P.k; d.mval = (int)P.m; d.nrows = (int)P.n;
+  }
   d.M = (int)P.sp; d.N = (int)P.Lp; d.K = (int)P.sp; d.batch = P.B;
   d.lower = false; d.epilogue = false;
   d.alpha = 1.0f;
@@ -192,10 +212,10 @@ hipError_t rect(const Plan& P, const f16* Q, const XPair& x, const XPair& y, boo
 // Gram Newton-Schulz on the normalized, padded X held in bufs.a ("Dion3:
 // Full-Stack Orthogonal Updates", agihunt.info, level-1 paragraph).  Every
 // matrix here is a polynomial in the first Gram, so all products commute,
-// are symmetric, and only their lower triangles are computed.  Returns the
-// buffer holding O in rows layout.
-dion3_status gram_ns(const Plan& P, const dion3_ns_cfg& cfg, const Bufs& bf, f16** out,
-                     hipStream_t s) {
+// are symmetric, and only their lower triangles are computed.  The final
+// product hands O to `sink` (the row-sparse update and/or O_out).
+dion3_status gram_ns(const Plan& P, const dion3_ns_cfg& cfg, const Bufs& bf,
+                     const UpdateSink& sink, hipStream_t s) {
   XPair x = bf.a, xalt = bf.b;
   f16 *R = bf.R, *Z = bf.Z, *Tm = bf.T, *Q = bf.Q0, *Qn = bf.Q1;
   HIP_TRY(gram(P, x, R, s));
@@ -228,8 +248,7 @@ dion3_status gram_ns(const Plan& P, const dion3_ns_cfg& cfg, const Bufs& bf, f16
       HIP_TRY(symm(P, Tm, Zv, nullptr, R, 1.0f, 0.0f, 0.0f, false, s));
     }
   }
-  HIP_TRY(rect(P, Q, x, xalt, false, s));
-  *out = xalt.X;
+  HIP_TRY(rect(P, Q, x, xalt, false, s, &sink));
   return DION3_OK;
 }
 
@@ -273,14 +292,9 @@ dion3_status step_impl(BatchPtr<float> W, BatchPtr<float> M, int batch, long lon
     HIP_TRY(launch_gather_f32(M, batch, (int)n, (int)m, ld, idx, (int)k, scale, mu, true, bf.a.X,
                               bf.a.XT, P.kp * P.mp, (int)P.kp, (int)P.mp, s));
   }
-  f16* O = nullptr;
-  st = gram_ns(P, cfg, bf, &O, s);
+  const UpdateSink sink = {W, ld, idx, lr, (f16*)O_out};
+  st = gram_ns(P, cfg, bf, sink, s);
   if (st != DION3_OK) return st;
-  {
-    TraceScope ts("update", 0.0, Bd * km * (O_out ? 12.0 : 10.0), s);
-    HIP_TRY(launch_update(W, batch, (int)n, (int)m, ld, idx, (int)k, O, P.kp * P.mp, (int)P.mp,
-                          lr, (f16*)O_out, s));
-  }
   if (idx_out)
     HIP_TRY(hipMemcpyAsync(idx_out, idx, (size_t)batch * k * sizeof(int32_t),
                            hipMemcpyDeviceToDevice, s));
@@ -421,12 +435,9 @@ dion3_status dion3_gram_ns(const uint16_t* X, uint16_t* O, int32_t batch, int64_
   HIP_TRY(launch_topk(nullptr, sq, batch, (int)k, (int)k, idx, scale, (double)cfg.eps, s));
   HIP_TRY(launch_gather_f16(Xb, batch, (int)m, m, (int)k, scale, bf.a.X, bf.a.XT, P.kp * P.mp,
                             (int)P.kp, (int)P.mp, s));
-  f16* Ob = nullptr;
-  st = gram_ns(P, cfg, bf, &Ob, s);
+  const UpdateSink sink = {{nullptr, 0, nullptr}, 0, idx, 0.0f, (f16*)O};
+  st = gram_ns(P, cfg, bf, sink, s);
   if (st != DION3_OK) return st;
-  BatchPtr<float> none = {nullptr, 0, nullptr};
-  HIP_TRY(launch_update(none, batch, (int)k, (int)m, m, nullptr, (int)k, Ob, P.kp * P.mp, (int)P.mp, 0.0f,
-                        (f16*)O, s));
   return DION3_OK;
 }
 

@@ -43,6 +43,18 @@ struct GemmDesc {
   bool lower, epilogue;
   float alpha, beta, gamma;
   double trace_flops;   // algorithmic flops of this launch, for the timing trace
+  // Fused row-sparse update (rectangular products only): the output in rows
+  // layout (the C pass when sink == 1, the CT pass when sink == 2) is not
+  // stored; instead, for output row r < kval and column c < mval,
+  //   W[b][idx[b][r]][c] = fma(-lr, O[r][c], W[...])   (when W has pointers)
+  //   Oout[b][r][c] = O[r][c]                         (when Oout is set).
+  int sink;
+  BatchPtr<float> W;
+  long long ldw;
+  const int* idx;
+  float lr;
+  f16* Oout;
+  int kval, mval, nrows;   // nrows: rows of W (row indices outside are skipped)
 };
 // Launches the product; records it in the timing trace (when enabled) under
 // "<role>_<tile edge>", e.g. "gemm_symm_256".
@@ -78,12 +90,5 @@ hipError_t launch_gather_f32(BatchPtr<float> M, int batch, int n, int m, long lo
 hipError_t launch_gather_f16(BatchPtr<const f16> Xin, int batch, int m, long long ld, int k,
                              const double* scale, f16* X, f16* XT, long long sX, int kp, int mp,
                              hipStream_t s);
-
-// W[b][idx[r]][:] -= lr * O[b][r][:] (skipped when W has no pointers), and
-// O_out[b][r][:] = O[b][r][:m] when O_out is not null.  Row indices outside
-// [0, n) are skipped.
-hipError_t launch_update(BatchPtr<float> W, int batch, int n, int m, long long ld, const int* idx,
-                         int k, const f16* O, long long sO, int mp, float lr, f16* O_out,
-                         hipStream_t s);
 
 }  // namespace dion3

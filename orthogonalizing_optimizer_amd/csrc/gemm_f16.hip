@@ -37,7 +37,54 @@ struct GemmArgs {
   int M, N, K;
   int tilesM, tilesN, tilesPerMat, total;
   float alpha, beta, gamma;
+  int sink;
+  BatchPtr<float> W;
+  long long ldw;
+  const int* idx;
+  float lr;
+  f16* Oout;
+  int kval, mval, nrows;
 };
+
+// One 8-wide chunk of the output in rows layout (row r, columns c..c+7)
+// goes to the fused update instead of memory: W[idx[r]][c..] -= lr * O and
+// optionally O_out[r][c..] = O.
+__device__ __forceinline__ void sink_chunk(const GemmArgs& p, int b, int r, int c, const half8& v) {
+  if (r >= p.kval || c >= p.mval) return;
+  const bool full = c + 8 <= p.mval;
+  if (p.Oout) {
+    f16* o = p.Oout + ((long long)b * p.kval + r) * p.mval + c;
+    if (full && ((uintptr_t)o & 15) == 0) {
+      *(half8*)o = v;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (c + e < p.mval) o[e] = v[e];
+    }
+  }
+  if (p.W.ptrs || p.W.base) {
+    const int row = p.idx[(long long)b * p.kval + r];
+    if (row < 0 || row >= p.nrows) return;
+    float* w = p.W.get(b) + (long long)row * p.ldw + c;
+    if (full && ((uintptr_t)w & 15) == 0) {
+      float4 w0 = ((float4*)w)[0], w1 = ((float4*)w)[1];
+      w0.x = __builtin_fmaf(-p.lr, (float)v[0], w0.x);
+      w0.y = __builtin_fmaf(-p.lr, (float)v[1], w0.y);
+      w0.z = __builtin_fmaf(-p.lr, (float)v[2], w0.z);
+      w0.w = __builtin_fmaf(-p.lr, (float)v[3], w0.w);
+      w1.x = __builtin_fmaf(-p.lr, (float)v[4], w1.x);
+      w1.y = __builtin_fmaf(-p.lr, (float)v[5], w1.y);
+      w1.z = __builtin_fmaf(-p.lr, (float)v[6], w1.z);
+      w1.w = __builtin_fmaf(-p.lr, (float)v[7], w1.w);
+      ((float4*)w)[0] = w0;
+      ((float4*)w)[1] = w1;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (c + e < p.mval) w[e] = __builtin_fmaf(-p.lr, (float)v[e], w[e]);
+    }
+  }
+}
 
 template <int BM_, int WAVES_M, int WAVES_N, int PF_>
 struct Cfg {
@@ -317,12 +364,15 @@ __global__ __launch_bounds__(C::NT, (C::BM == 256 ? 1 : 2)) void k_gemm(GemmArgs
   }
 
   f16* __restrict__ Cb = p.C ? p.C + (long long)b * p.sC : nullptr;
-  if (Cb) {   // rows: C[m0 + r][n0 + c]
+  if (Cb || (!LOWER && p.sink == 1)) {   // rows: C[m0 + r][n0 + c]
     for (int e = tid; e < C::BM * (C::BN / 8); e += C::NT) {
       const int r = e / (C::BN / 8), c8 = e - r * (C::BN / 8);
       const int gr = m0 + r, gc = n0 + c8 * 8;
-      if (gr < p.M && gc < p.N)
-        *(half8*)(Cb + (long long)gr * p.ldc + gc) = *(const half8*)(S + r * C::EP + c8 * 8);
+      if (gr < p.M && gc < p.N) {
+        const half8 v = *(const half8*)(S + r * C::EP + c8 * 8);
+        if (!LOWER && p.sink == 1) sink_chunk(p, b, gr, gc, v);
+        else *(half8*)(Cb + (long long)gr * p.ldc + gc) = v;
+      }
     }
   }
   // columns: the mirror of an off-diagonal lower tile into C, or the
@@ -335,7 +385,7 @@ __global__ __launch_bounds__(C::NT, (C::BM == 256 ? 1 : 2)) void k_gemm(GemmArgs
     Tb = p.CT + (long long)b * p.sCT;
     ldt = p.ldct;
   }
-  if (Tb) {
+  if (Tb || (!LOWER && p.sink == 2)) {
     for (int e = tid; e < C::BN * (C::BM / 8); e += C::NT) {
       const int r8 = e / C::BN, c = e - r8 * C::BN;
       const int gr = n0 + c, gc = m0 + r8 * 8;
@@ -343,7 +393,8 @@ __global__ __launch_bounds__(C::NT, (C::BM == 256 ? 1 : 2)) void k_gemm(GemmArgs
         half8 v;
 #pragma unroll
         for (int k = 0; k < 8; ++k) v[k] = S[(r8 * 8 + k) * C::EP + c];
-        *(half8*)(Tb + (long long)gr * ldt + gc) = v;
+        if (!LOWER && p.sink == 2) sink_chunk(p, b, gr, gc, v);
+        else *(half8*)(Tb + (long long)gr * ldt + gc) = v;
       }
     }
   }
@@ -363,6 +414,8 @@ hipError_t launch(const GemmDesc& d, hipStream_t s) {
   if (total <= 0 || total > 0x7fffffffLL) return hipErrorInvalidValue;
   p.total = (int)total;
   p.alpha = d.alpha; p.beta = d.beta; p.gamma = d.gamma;
+  p.sink = d.sink; p.W = d.W; p.ldw = d.ldw; p.idx = d.idx; p.lr = d.lr; p.Oout = d.Oout;
+  p.kval = d.kval; p.mval = d.mval; p.nrows = d.nrows;
   hipLaunchKernelGGL((k_gemm<C, ROLE, LOWER, EPI>), dim3(p.total), dim3(C::NT), 0, s, p);
   return hipGetLastError();
 }
@@ -395,7 +448,8 @@ hipError_t launch_cfg(const GemmDesc& d, hipStream_t s) {
 hipError_t launch_gemm(const GemmDesc& d, hipStream_t s) {
   if (d.M % 128 || d.N % 128 || d.K % BK || d.K <= 0 || d.batch <= 0) return hipErrorInvalidValue;
   if (d.lower && (d.M != d.N || d.CT || !d.C)) return hipErrorInvalidValue;
-  if (!d.lower && !d.C && !d.CT) return hipErrorInvalidValue;
+  if (!d.lower && !d.C && !d.CT && !d.sink) return hipErrorInvalidValue;
+  if (d.sink && (d.lower || (d.sink == 1 && d.C) || (d.sink == 2 && d.CT))) return hipErrorInvalidValue;
   switch (d.role) {
     case kRoleGram:
       if (!d.lower || d.epilogue) break;

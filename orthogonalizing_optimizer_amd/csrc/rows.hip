@@ -1,10 +1,11 @@
-// Row kernels of the Dion3 step on gfx950: l1 scoring, top-k selection,
-// gather + normalize + momentum decay, and the row-sparse weight update
+// Row kernels of the Dion3 step on gfx950: l1 scoring, top-k selection and
+// gather + normalize + momentum decay (the row-sparse weight update is fused
+// into the epilogue of the final multiply-back product)
 // ("Dion3: Full-Stack Orthogonal Updates", agihunt.info, level-3 paragraph:
 // k = ceil(f n) rows picked by l1 norm, only those weight rows updated, only
 // those momentum rows decayed by mu, the rest left untouched).
 //
-// Scoring, gather and update stream HBM: one 64-lane wave per row, 16-byte
+// Scoring and gather stream HBM: scoring runs one 64-lane wave per row, 16-byte
 // loads when the row is 16-byte aligned.  Every reduction runs in a fixed
 // order in fp64, so results are deterministic run to run.
 #include "dion3_internal.h"
@@ -288,47 +289,6 @@ __global__ __launch_bounds__(256) void k_gather(BatchPtr<T> M, int n, int m, lon
   }
 }
 
-// ------------------------------------------------------------- update
-
-__global__ __launch_bounds__(256) void k_update(BatchPtr<float> W, int n, int m, long long ld,
-                                                const int* __restrict__ idx, int k,
-                                                const f16* __restrict__ O, long long sO, int mp,
-                                                float lr, f16* __restrict__ O_out) {
-  const int b = blockIdx.y;
-  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (r >= k) return;
-  const f16* __restrict__ o = O + (long long)b * sO + (long long)r * mp;
-  f16* __restrict__ oo = O_out ? O_out + ((long long)b * k + r) * m : nullptr;
-  float* __restrict__ dst = nullptr;
-  if (W.ptrs || W.base) {
-    const int row = idx ? idx[(long long)b * k + r] : r;
-    if (row >= 0 && row < n) dst = W.get(b) + (long long)row * ld;
-  }
-  if (dst && ((uintptr_t)dst & 15) == 0 && (m & 3) == 0) {
-    float4* d4 = (float4*)dst;
-    const half4* o4 = (const half4*)o;
-    for (int j = lane; j < (m >> 2); j += 64) {
-      const half4 h = o4[j];
-      float4 w = d4[j];
-      w.x = __builtin_fmaf(-lr, (float)h[0], w.x);
-      w.y = __builtin_fmaf(-lr, (float)h[1], w.y);
-      w.z = __builtin_fmaf(-lr, (float)h[2], w.z);
-      w.w = __builtin_fmaf(-lr, (float)h[3], w.w);
-      d4[j] = w;
-      if (oo) {
-        oo[4 * j] = h[0]; oo[4 * j + 1] = h[1]; oo[4 * j + 2] = h[2]; oo[4 * j + 3] = h[3];
-      }
-    }
-  } else {
-    for (int j = lane; j < m; j += 64) {
-      const f16 h = o[j];
-      if (dst) dst[j] = __builtin_fmaf(-lr, (float)h, dst[j]);
-      if (oo) oo[j] = h;
-    }
-  }
-}
-
 inline unsigned blocks_for(long long rows) { return (unsigned)((rows + 3) / 4); }
 
 }  // namespace
@@ -374,12 +334,5 @@ hipError_t launch_gather_f16(BatchPtr<const f16> Xin, int batch, int m, long lon
   return hipGetLastError();
 }
 
-hipError_t launch_update(BatchPtr<float> W, int batch, int n, int m, long long ld, const int* idx,
-                         int k, const f16* O, long long sO, int mp, float lr, f16* O_out,
-                         hipStream_t s) {
-  hipLaunchKernelGGL(k_update, dim3(blocks_for(k), batch), dim3(256), 0, s, W, n, m, ld, idx, k, O, sO,
-                     mp, lr, O_out);
-  return hipGetLastError();
-}
 
 }  // namespace dion3
