@@ -210,11 +210,12 @@ __global__ __launch_bounds__(TK_THREADS) void k_topk(const double* __restrict__ 
 
 // ------------------------------------------------------------- gather
 
-// One block per 64 selected rows x 64 columns: reads the rows of M once
-// (256-byte row segments), writes X in rows layout directly and, through an
-// LDS tile, its transpose XT, so that every product of the Gram iteration
-// reads K-contiguous operands; with DECAY also writes M back times mu.
-constexpr int GT = 64;
+// One block per 64 selected rows x 256 columns: reads 1 KB of each selected
+// row of M, writes X in rows layout directly and, through an LDS tile, its
+// transpose XT (each thread writes one whole 128-byte run of an XT row), so
+// that every product of the Gram iteration reads K-contiguous operands; with
+// DECAY it also writes the rows of M back times mu.
+constexpr int GR = 64, GC = 256, GPAD = 8;
 
 template <typename T>
 __device__ __forceinline__ void load4(const T* __restrict__ src, int c, int m, float (&v)[4]) {
@@ -247,45 +248,59 @@ __global__ __launch_bounds__(256) void k_gather(BatchPtr<T> M, int n, int m, lon
                                                 const double* __restrict__ scale, float mu,
                                                 f16* __restrict__ X, f16* __restrict__ XT,
                                                 long long sX, int kp, int mp) {
-  __shared__ f16 tile[GT][GT + 2];
+  __shared__ __attribute__((aligned(16))) f16 tile[GR][GC + GPAD];
   const int b = blockIdx.z;
-  const int c0 = blockIdx.x * GT, r0 = blockIdx.y * GT;
+  const int c0 = blockIdx.x * GC, r0 = blockIdx.y * GR;
   const int tid = threadIdx.x;
-  const int cl = 4 * (tid & 15);
+  const int cl = 4 * (tid & 63);          // 4 columns per thread
+  const int rq = tid >> 6;                // rows rq, rq + 4, ..., rq + 60
   const float sc = (float)scale[b];
   f16* __restrict__ Xb = X + (long long)b * sX;
   f16* __restrict__ XTb = XT + (long long)b * sX;
   T* base = M.get(b);
+  const int c = c0 + cl;
+  if (c < mp) {
+    float v[16][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int rl = (tid >> 4) + 16 * i;
-    const int r = r0 + rl, c = c0 + cl;
-    int row = -1;
-    if (r < k) {
-      row = idx ? idx[(long long)b * k + r] : r;
-      if (row >= n) row = -1;
-    }
-    float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    if (row >= 0 && c < m) {
-      T* src = base + (long long)row * ld + c;
-      load4<T>(src, c, m, v);
-      if constexpr (DECAY) decay4((float*)src, c, m, mu, v);
-    }
-    half4 h;
+    for (int i = 0; i < 16; ++i) {
+      const int r = r0 + rq + 4 * i;
+      int row = -1;
+      if (r < k) {
+        row = idx ? idx[(long long)b * k + r] : r;
+        if (row >= n) row = -1;
+      }
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      h[e] = (f16)(v[e] * sc);
-      tile[rl][cl + e] = h[e];
+      for (int e = 0; e < 4; ++e) v[i][e] = 0.0f;
+      if (row >= 0 && c < m) load4<T>(base + (long long)row * ld + c, c, m, v[i]);
     }
-    *(half4*)(Xb + (long long)r * mp + c) = h;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int rl = rq + 4 * i, r = r0 + rl;
+      if constexpr (DECAY) {
+        if (r < k && c < m) {
+          const int row = idx ? idx[(long long)b * k + r] : r;
+          if (row < n) decay4((float*)(base + (long long)row * ld + c), c, m, mu, v[i]);
+        }
+      }
+      half4 h;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) h[e] = (f16)(v[i][e] * sc);
+      *(half4*)&tile[rl][cl] = h;
+      *(half4*)(Xb + (long long)r * mp + c) = h;
+    }
   }
   __syncthreads();
-  for (int e = tid; e < GT * (GT / 8); e += 256) {
-    const int col = e >> 3, r8 = e & 7;
-    half8 v;
+  // transposed: XT[c0 + col][r0 .. r0 + 63], one 128-byte run per thread
+  const int col = tid;
+  if (c0 + col < mp) {
+    f16* dst = XTb + (long long)(c0 + col) * kp + r0;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) v[q] = tile[r8 * 8 + q][col];
-    *(half8*)(XTb + (long long)(c0 + col) * kp + r0 + r8 * 8) = v;
+    for (int r8 = 0; r8 < GR / 8; ++r8) {
+      half8 v;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[q] = tile[r8 * 8 + q][col];
+      *(half8*)(dst + r8 * 8) = v;
+    }
   }
 }
 
@@ -315,7 +330,7 @@ hipError_t launch_topk(const double* l1, const double* sq, int batch, int n, int
 hipError_t launch_gather_f32(BatchPtr<float> M, int batch, int n, int m, long long ld,
                              const int* idx, int k, const double* scale, float mu, bool decay,
                              f16* X, f16* XT, long long sX, int kp, int mp, hipStream_t s) {
-  const dim3 grid(mp / GT, kp / GT, batch);
+  const dim3 grid((mp + GC - 1) / GC, kp / GR, batch);
   if (decay)
     hipLaunchKernelGGL((k_gather<float, true>), grid, dim3(256), 0, s, M, n, m, ld, idx, k, scale,
                        mu, X, XT, sX, kp, mp);
@@ -328,7 +343,7 @@ hipError_t launch_gather_f32(BatchPtr<float> M, int batch, int n, int m, long lo
 hipError_t launch_gather_f16(BatchPtr<const f16> Xin, int batch, int m, long long ld, int k,
                              const double* scale, f16* X, f16* XT, long long sX, int kp, int mp,
                              hipStream_t s) {
-  const dim3 grid(mp / GT, kp / GT, batch);
+  const dim3 grid((mp + GC - 1) / GC, kp / GR, batch);
   hipLaunchKernelGGL((k_gather<const f16, false>), grid, dim3(256), 0, s, Xin, k, m, ld, nullptr, k,
                      scale, 1.0f, X, XT, sX, kp, mp);
   return hipGetLastError();
