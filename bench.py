@@ -37,6 +37,7 @@ KERNEL_SYMBOLS = {
     "gemm_symm_128": "k_gemm<Cfg<128, 2, 2, 2>, 2, true, false>",
     "gemm_rect_128": "k_gemm<Cfg<128, 2, 2, 2>, 3, false, false>",
     "row_score": "k_row_score_f32",
+    "accum_score": "k_accum_score_f32",
     "topk": "k_topk",
     "gather": "k_gather<float, true>",
 }
@@ -54,6 +55,9 @@ def parse():
     p.add_argument("--workload", default="c4", help="c1, c2, c3, c4 (7B f=1/4), c4h (7B f=1/2), c5")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-trace", action="store_true")
+    p.add_argument("--accumulate", action="store_true",
+                   help="each step first accumulates a gradient into the momentum (M <- M + G, "
+                        "fused into the row scoring); gradients are fixed seeded N(0, 0.1^2)")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="CPU-baseline budget: oracle matrices are taken round-robin over the "
                         "shape groups until this much CPU time is spent (at least one per group)")
@@ -152,18 +156,25 @@ def main():
                     samples.append((g, Ws[j].cpu().numpy(), Ms[j].cpu().numpy()))
 
     groups = []
+    grads = {}
     max_ws = 0
-    for g, Ws, Ms in data:
+    for gi, (g, Ws, Ms) in enumerate(data):
         k = d3.k_from_fraction(float(wl.fraction), g.n)
         ptrs = (d3.pointer_array(Ws, dev), d3.pointer_array(Ms, dev))
         groups.append((g, Ws, Ms, k, ptrs))
         max_ws = max(max_ws, d3.workspace_size(len(Ms), g.n, g.m, k))
+        if args.accumulate:
+            gen = torch.Generator(device=dev)
+            gen.manual_seed(7000 + gi)
+            Gs = [torch.randn(M.shape, generator=gen, device=dev).mul_(0.1) for M in Ms]
+            grads[gi] = (Gs, d3.pointer_array(Gs, dev))
     ws = d3.Workspace()
     ws.get(max_ws, dev)
 
     def one_step():
-        for g, Ws, Ms, k, ptrs in groups:
-            d3.step_megabatch(Ws, Ms, k, lr, mu, cfg, ws=ws, ptrs=ptrs)
+        for gi, (g, Ws, Ms, k, ptrs) in enumerate(groups):
+            gp = grads[gi][1] if gi in grads else None
+            d3.step_megabatch(Ws, Ms, k, lr, mu, cfg, ws=ws, ptrs=ptrs, gptrs=gp)
 
     for _ in range(args.warmup):
         one_step()
@@ -189,7 +200,7 @@ def main():
     if not args.no_trace:
         gi = -1
         for name, ms, fl, by in d3.trace_records():
-            if name == "row_score":          # every group's launch sequence starts with it
+            if name in ("row_score", "accum_score"):   # every group's launch sequence starts so
                 gi = (gi + 1) % len(groups)
             for table, key in ((kernels, name), (by_group, (gi, name))):
                 st = table.setdefault(key, {"launches": 0, "ms": 0.0, "flops": 0.0, "bytes": 0.0})
@@ -306,6 +317,7 @@ def main():
             "restart_at": [cfg.restart_at[i] for i in range(cfg.n_restart)],
             "state_dtype": "fp32 W and M; fp16 X, Gram, polynomials and O with fp32 accumulation",
             "parallelism": "single GPU, one megabatched call per shape group",
+            "gradient_accumulation": bool(args.accumulate),
         },
         "matrices_per_s": round(wl.n_matrices / (ms_per_step * 1e-3), 1),
         "gram_ns_tflops": round(gram_tflops, 2) if gram_tflops else None,

@@ -127,6 +127,27 @@ DION3_API dion3_status dion3_step_megabatch(float* const* W, float* const* M, in
                                   int32_t* idx_out, uint16_t* O_out,
                                   void* ws, size_t ws_bytes, void* stream);
 
+/* The step with the gradient accumulated into the momentum buffer first:
+ * M <- M + G (one fp32 add per element, every row of M), then the step as in
+ * dion3_step / dion3_step_megabatch on the updated M.  Error feedback keeps
+ * the unselected rows of the buffer for later steps and decays only the
+ * selected ones ("Dion3: Full-Stack Orthogonal Updates", agihunt.info,
+ * level-3 paragraph), so the buffer is a running sum of gradients.  The
+ * addition is fused into the row scoring, which reads M and G once.  G has
+ * the shape and row stride of M and is not written; for the megabatch form
+ * it is a DEVICE array of `batch` device pointers.  Results equal adding G
+ * to M in fp32 and then calling dion3_step, bit for bit. */
+DION3_API dion3_status dion3_step_accum(float* W, float* M, const float* G, int64_t n, int64_t m,
+                                        int64_t ld, int64_t k, float lr, float mu,
+                                        const dion3_ns_cfg* cfg, int32_t* idx_out,
+                                        uint16_t* O_out, void* ws, size_t ws_bytes, void* stream);
+DION3_API dion3_status dion3_step_megabatch_accum(float* const* W, float* const* M,
+                                                  const float* const* G, int32_t batch, int64_t n,
+                                                  int64_t m, int64_t ld, int64_t k, float lr,
+                                                  float mu, const dion3_ns_cfg* cfg,
+                                                  int32_t* idx_out, uint16_t* O_out, void* ws,
+                                                  size_t ws_bytes, void* stream);
+
 /* The symmetric products of the level-2 paragraph, usable on their own.
  *
  * dion3_syrk_f16: R[b] = A[b] A[b]^T for `batch` fp16 matrices A[b]

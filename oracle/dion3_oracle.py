@@ -38,7 +38,11 @@ Readings where the pages are silent (each is also a row of the design notes):
 * "rows" are dim 0 of the row-major n x m matrix;
 * k = ceil(f n) is computed in exact rationals and clamped to [1, n];
 * ties in the l1 score go to the lowest row index;
-* X is built from the undecayed momentum rows, then those rows are decayed.
+* X is built from the undecayed momentum rows, then those rows are decayed;
+* when a gradient G is given, it is first accumulated into the buffer,
+  M <- M + G (one fp32 addition): error feedback keeps every row of the
+  buffer and only the selected ones are decayed after use ([AGI] level-3
+  paragraph), so the buffer is a running sum.
 
 Parity pins for every function live in tests/test_oracle.py (SVD polar
 factor, the scalar Newton-Schulz map on singular values, Gram NS against
@@ -226,7 +230,8 @@ def ns_gram(X, coeffs: Sequence[Tuple[float, float, float]],
 def dion3_step(W: np.ndarray, M: np.ndarray, k: int, lr: float, mu: float,
                coeffs: Optional[Sequence[Tuple[float, float, float]]] = None,
                restart_at: Iterable[int] = DEFAULT_RESTART_AT, eps: float = DEFAULT_EPS,
-               S_override: Optional[np.ndarray] = None, method: str = "gram") -> dict:
+               S_override: Optional[np.ndarray] = None, method: str = "gram",
+               G: Optional[np.ndarray] = None) -> dict:
     """One Dion3 step on one matrix ([AGI] level-3 paragraph, [ABS]).
 
     1. score rows by l1 and keep the k best (ties: lowest index);
@@ -236,11 +241,19 @@ def dion3_step(W: np.ndarray, M: np.ndarray, k: int, lr: float, mu: float,
     4. M[S] <- mu * M[S] as one correctly rounded fp32 product, other momentum
        rows untouched (error feedback keeps them for later steps).
 
+    With a gradient G, the buffer first accumulates it: M <- fl32(M + G).
+
     Returns W' (fp64 on S, the input bytes elsewhere), M' (fp32), S, O and
     the normalized fp64 submatrix that entered the iteration.
     """
     W = np.asarray(W)
     M = np.asarray(M)
+    if G is not None:
+        G = np.asarray(G)
+        if G.dtype != np.float32 or G.shape != M.shape:
+            raise TypeError("G must be float32 with the shape of M")
+        # exact sum in fp64, one rounding to fp32: the correctly rounded fp32 add
+        M = (M.astype(np.float64) + G.astype(np.float64)).astype(np.float32)
     if M.dtype != np.float32 or W.dtype != np.float32:
         raise TypeError("W and M must be float32")
     n, m = M.shape

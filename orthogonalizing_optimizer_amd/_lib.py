@@ -57,6 +57,10 @@ def _declare(lib):
                                  vp, sz, vp]),
         "dion3_step_megabatch": (c.c_int, [vp, vp, i32, i64, i64, i64, i64, f32, f32,
                                            c.POINTER(NsCfg), vp, vp, vp, sz, vp]),
+        "dion3_step_accum": (c.c_int, [vp, vp, vp, i64, i64, i64, i64, f32, f32,
+                                       c.POINTER(NsCfg), vp, vp, vp, sz, vp]),
+        "dion3_step_megabatch_accum": (c.c_int, [vp, vp, vp, i32, i64, i64, i64, i64, f32, f32,
+                                                 c.POINTER(NsCfg), vp, vp, vp, sz, vp]),
         "dion3_syrk_f16": (c.c_int, [vp, vp, i32, i64, i64, i64, i64, vp]),
         "dion3_symm_f16": (c.c_int, [vp, vp, vp, vp, i32, i64, i64, f32, f32, f32, vp]),
         "dion3_trace_enable": (c.c_int, [i32]),
@@ -76,7 +80,8 @@ def _declare(lib):
 
 EXPORTED = ("dion3_version", "dion3_ns_cfg_default", "dion3_k_from_fraction",
             "dion3_workspace_size", "dion3_row_select", "dion3_gram_ns", "dion3_step",
-            "dion3_step_megabatch", "dion3_syrk_f16", "dion3_symm_f16", "dion3_trace_enable",
+            "dion3_step_megabatch", "dion3_step_accum", "dion3_step_megabatch_accum",
+            "dion3_syrk_f16", "dion3_symm_f16", "dion3_trace_enable",
             "dion3_trace_count", "dion3_trace_reset", "dion3_trace_record", "dion3_status_string",
             "dion3_last_hip_error")
 
@@ -222,20 +227,32 @@ def gram_ns(X, cfg: Optional[NsCfg] = None, ws: Optional[Workspace] = None):
 
 
 def step(W, M, k: int, lr: float, mu: float, cfg: Optional[NsCfg] = None,
-         return_idx: bool = False, return_O: bool = False, ws: Optional[Workspace] = None):
-    """One Dion3 step on one matrix, in place on W and M (fp32, [n, m])."""
+         return_idx: bool = False, return_O: bool = False, ws: Optional[Workspace] = None,
+         G=None):
+    """One Dion3 step on one matrix, in place on W and M (fp32, [n, m]).
+    With G (same shape and strides as M), M <- M + G first, fused into the
+    row scoring."""
     torch = _torch()
     _req(W, torch.float32, "W")
     _req(M, torch.float32, "M")
     if W.shape != M.shape or W.dim() != 2 or W.stride() != M.stride() or W.stride(1) != 1:
         raise ValueError("W and M must be [n, m] with equal strides and contiguous rows")
+    if G is not None:
+        _req(G, torch.float32, "G")
+        if G.shape != M.shape or G.stride() != M.stride():
+            raise ValueError("G must have the shape and strides of M")
     n, m = M.shape
     idx = torch.empty(k, dtype=torch.int32, device=M.device) if return_idx else None
     O = torch.empty((k, m), dtype=torch.float16, device=M.device) if return_O else None
     p, nb = (ws or _default_ws).get(workspace_size(1, n, m, k), M.device)
-    _check(lib().dion3_step(W.data_ptr(), M.data_ptr(), n, m, M.stride(0), k, lr, mu,
-                            ctypes.byref(cfg) if cfg is not None else None, _ptr(idx), _ptr(O), p,
-                            nb, _stream(M.device)), "dion3_step")
+    c = ctypes.byref(cfg) if cfg is not None else None
+    if G is None:
+        _check(lib().dion3_step(W.data_ptr(), M.data_ptr(), n, m, M.stride(0), k, lr, mu, c,
+                                _ptr(idx), _ptr(O), p, nb, _stream(M.device)), "dion3_step")
+    else:
+        _check(lib().dion3_step_accum(W.data_ptr(), M.data_ptr(), G.data_ptr(), n, m, M.stride(0),
+                                      k, lr, mu, c, _ptr(idx), _ptr(O), p, nb,
+                                      _stream(M.device)), "dion3_step_accum")
     return idx, O
 
 
@@ -247,14 +264,18 @@ def pointer_array(tensors, device):
 
 def step_megabatch(Ws, Ms, k: int, lr: float, mu: float, cfg: Optional[NsCfg] = None,
                    return_idx: bool = False, return_O: bool = False,
-                   ws: Optional[Workspace] = None, ptrs=None):
+                   ws: Optional[Workspace] = None, ptrs=None, Gs=None, gptrs=None):
     """One Dion3 step on a group of same-shape matrices in one call.
-    ``ptrs`` may carry cached (W pointer array, M pointer array)."""
+    ``ptrs`` may carry cached (W pointer array, M pointer array).  With
+    gradients ``Gs`` (or their cached pointer array ``gptrs``), each M <- M + G
+    first, fused into the row scoring."""
     torch = _torch()
     if len(Ws) != len(Ms) or not Ws:
         raise ValueError("need equally many W and M matrices")
+    if Gs is not None and len(Gs) != len(Ms):
+        raise ValueError("need one gradient per matrix")
     shape, stride = Ms[0].shape, Ms[0].stride()
-    for t in list(Ws) + list(Ms):
+    for t in list(Ws) + list(Ms) + list(Gs or []):
         _req(t, torch.float32, "W/M")
         if t.shape != shape or t.stride() != stride or t.dim() != 2 or t.stride(1) != 1:
             raise ValueError("all matrices must share shape and strides with contiguous rows")
@@ -266,10 +287,18 @@ def step_megabatch(Ws, Ms, k: int, lr: float, mu: float, cfg: Optional[NsCfg] = 
     idx = torch.empty((B, k), dtype=torch.int32, device=dev) if return_idx else None
     O = torch.empty((B, k, m), dtype=torch.float16, device=dev) if return_O else None
     p, nb = (ws or _default_ws).get(workspace_size(B, n, m, k), dev)
-    _check(lib().dion3_step_megabatch(ptrs[0].data_ptr(), ptrs[1].data_ptr(), B, n, m, stride[0], k,
-                                      lr, mu, ctypes.byref(cfg) if cfg is not None else None,
-                                      _ptr(idx), _ptr(O), p, nb, _stream(dev)),
-           "dion3_step_megabatch")
+    c = ctypes.byref(cfg) if cfg is not None else None
+    if Gs is None and gptrs is None:
+        _check(lib().dion3_step_megabatch(ptrs[0].data_ptr(), ptrs[1].data_ptr(), B, n, m, stride[0],
+                                          k, lr, mu, c, _ptr(idx), _ptr(O), p, nb, _stream(dev)),
+               "dion3_step_megabatch")
+    else:
+        if gptrs is None:
+            gptrs = pointer_array(Gs, dev)
+        _check(lib().dion3_step_megabatch_accum(ptrs[0].data_ptr(), ptrs[1].data_ptr(),
+                                                gptrs.data_ptr(), B, n, m, stride[0], k, lr, mu, c,
+                                                _ptr(idx), _ptr(O), p, nb, _stream(dev)),
+               "dion3_step_megabatch_accum")
     return idx, O
 
 

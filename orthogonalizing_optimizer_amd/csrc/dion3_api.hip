@@ -252,7 +252,8 @@ dion3_status gram_ns(const Plan& P, const dion3_ns_cfg& cfg, const Bufs& bf,
   return DION3_OK;
 }
 
-dion3_status step_impl(BatchPtr<float> W, BatchPtr<float> M, int batch, long long n, long long m,
+dion3_status step_impl(BatchPtr<float> W, BatchPtr<float> M, BatchPtr<const float> G, int batch,
+                       long long n, long long m,
                        long long ld, long long k, float lr, float mu, const dion3_ns_cfg* cfg_in,
                        int32_t* idx_out, uint16_t* O_out, void* ws, size_t ws_bytes,
                        void* stream) {
@@ -279,7 +280,10 @@ dion3_status step_impl(BatchPtr<float> W, BatchPtr<float> M, int batch, long lon
 
   BatchPtr<const float> Mc = {M.base, M.stride, (const float* const*)M.ptrs};
   const double Bd = batch, nm = dbl(n) * dbl(m), km = dbl(k) * dbl(m);
-  {
+  if (G.base || G.ptrs) {   // accumulate the gradient into the buffer while scoring
+    TraceScope ts("accum_score", 0.0, Bd * nm * 12.0, s);
+    HIP_TRY(launch_accum_score_f32(M, G, batch, (int)n, (int)m, ld, all ? nullptr : l1, sq, s));
+  } else {
     TraceScope ts("row_score", 0.0, Bd * nm * 4.0, s);
     HIP_TRY(launch_row_score_f32(Mc, batch, (int)n, (int)m, ld, all ? nullptr : l1, sq, s));
   }
@@ -446,7 +450,18 @@ dion3_status dion3_step(float* W, float* M, int64_t n, int64_t m, int64_t ld, in
                         void* ws, size_t ws_bytes, void* stream) {
   if (!W || !M) return DION3_ERR_ARG;
   BatchPtr<float> Wb = {W, 0, nullptr}, Mb = {M, 0, nullptr};
-  return step_impl(Wb, Mb, 1, n, m, ld, k, lr, mu, cfg, idx_out, O_out, ws, ws_bytes, stream);
+  BatchPtr<const float> Gb = {nullptr, 0, nullptr};
+  return step_impl(Wb, Mb, Gb, 1, n, m, ld, k, lr, mu, cfg, idx_out, O_out, ws, ws_bytes, stream);
+}
+
+dion3_status dion3_step_accum(float* W, float* M, const float* G, int64_t n, int64_t m, int64_t ld,
+                              int64_t k, float lr, float mu, const dion3_ns_cfg* cfg,
+                              int32_t* idx_out, uint16_t* O_out, void* ws, size_t ws_bytes,
+                              void* stream) {
+  if (!W || !M || !G) return DION3_ERR_ARG;
+  BatchPtr<float> Wb = {W, 0, nullptr}, Mb = {M, 0, nullptr};
+  BatchPtr<const float> Gb = {G, 0, nullptr};
+  return step_impl(Wb, Mb, Gb, 1, n, m, ld, k, lr, mu, cfg, idx_out, O_out, ws, ws_bytes, stream);
 }
 
 dion3_status dion3_step_megabatch(float* const* W, float* const* M, int32_t batch, int64_t n,
@@ -455,7 +470,21 @@ dion3_status dion3_step_megabatch(float* const* W, float* const* M, int32_t batc
                                   void* ws, size_t ws_bytes, void* stream) {
   if (!W || !M) return DION3_ERR_ARG;
   BatchPtr<float> Wb = {nullptr, 0, W}, Mb = {nullptr, 0, M};
-  return step_impl(Wb, Mb, batch, n, m, ld, k, lr, mu, cfg, idx_out, O_out, ws, ws_bytes, stream);
+  BatchPtr<const float> Gb = {nullptr, 0, nullptr};
+  return step_impl(Wb, Mb, Gb, batch, n, m, ld, k, lr, mu, cfg, idx_out, O_out, ws, ws_bytes,
+                   stream);
+}
+
+dion3_status dion3_step_megabatch_accum(float* const* W, float* const* M, const float* const* G,
+                                        int32_t batch, int64_t n, int64_t m, int64_t ld, int64_t k,
+                                        float lr, float mu, const dion3_ns_cfg* cfg,
+                                        int32_t* idx_out, uint16_t* O_out, void* ws,
+                                        size_t ws_bytes, void* stream) {
+  if (!W || !M || !G) return DION3_ERR_ARG;
+  BatchPtr<float> Wb = {nullptr, 0, W}, Mb = {nullptr, 0, M};
+  BatchPtr<const float> Gb = {nullptr, 0, G};
+  return step_impl(Wb, Mb, Gb, batch, n, m, ld, k, lr, mu, cfg, idx_out, O_out, ws, ws_bytes,
+                   stream);
 }
 
 dion3_status dion3_syrk_f16(const uint16_t* A, uint16_t* R, int32_t batch, int64_t rows,

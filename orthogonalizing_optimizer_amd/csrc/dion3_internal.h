@@ -72,6 +72,9 @@ struct TraceScope {
 // Per-row l1 (optional) and sum of squares in fp64, one wave per row.
 hipError_t launch_row_score_f32(BatchPtr<const float> M, int batch, int n, int m, long long ld,
                                 double* l1, double* sq, hipStream_t s);
+// M <- M + G (fp32) fused with the scoring of the updated rows.
+hipError_t launch_accum_score_f32(BatchPtr<float> M, BatchPtr<const float> G, int batch, int n, int m,
+                                  long long ld, double* l1, double* sq, hipStream_t s);
 hipError_t launch_row_score_f16(BatchPtr<const f16> X, int batch, int n, int m, long long ld,
                                 double* sq, hipStream_t s);
 

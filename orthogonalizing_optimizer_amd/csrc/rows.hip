@@ -63,6 +63,45 @@ __global__ __launch_bounds__(256) void k_row_score_f32(BatchPtr<const float> M, 
   }
 }
 
+// Gradient accumulation fused into scoring: M <- M + G (one fp32 add per
+// element, written back) and the l1 / sum of squares of the updated row.
+__global__ __launch_bounds__(256) void k_accum_score_f32(BatchPtr<float> M, BatchPtr<const float> G,
+                                                         int n, int m, long long ld,
+                                                         double* __restrict__ l1,
+                                                         double* __restrict__ sq) {
+  const int b = blockIdx.y;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= n) return;
+  float* __restrict__ dst = M.get(b) + (long long)row * ld;
+  const float* __restrict__ g = G.get(b) + (long long)row * ld;
+  double a = 0.0, q = 0.0;
+  if (((uintptr_t)dst & 15) == 0 && ((uintptr_t)g & 15) == 0 && (m & 3) == 0) {
+    float4* d4 = (float4*)dst;
+    const float4* g4 = (const float4*)g;
+    for (int j = lane; j < (m >> 2); j += 64) {
+      const float4 x = d4[j], y = g4[j];
+      const float4 z = make_float4(x.x + y.x, x.y + y.y, x.z + y.z, x.w + y.w);
+      d4[j] = z;
+      a += (double)fabsf(z.x) + (double)fabsf(z.y) + (double)fabsf(z.z) + (double)fabsf(z.w);
+      q += (double)z.x * z.x + (double)z.y * z.y + (double)z.z * z.z + (double)z.w * z.w;
+    }
+  } else {
+    for (int j = lane; j < m; j += 64) {
+      const float z = dst[j] + g[j];
+      dst[j] = z;
+      a += fabs((double)z);
+      q += (double)z * z;
+    }
+  }
+  a = wave_sum(a);
+  q = wave_sum(q);
+  if (lane == 0) {
+    if (l1) l1[(long long)b * n + row] = a;
+    sq[(long long)b * n + row] = q;
+  }
+}
+
 __global__ __launch_bounds__(256) void k_row_score_f16(BatchPtr<const f16> X, int n, int m,
                                                        long long ld, double* __restrict__ sq) {
   const int b = blockIdx.y;
@@ -312,6 +351,13 @@ hipError_t launch_row_score_f32(BatchPtr<const float> M, int batch, int n, int m
                                 double* l1, double* sq, hipStream_t s) {
   hipLaunchKernelGGL(k_row_score_f32, dim3(blocks_for(n), batch), dim3(256), 0, s, M, n, m, ld, l1,
                      sq);
+  return hipGetLastError();
+}
+
+hipError_t launch_accum_score_f32(BatchPtr<float> M, BatchPtr<const float> G, int batch, int n, int m,
+                                  long long ld, double* l1, double* sq, hipStream_t s) {
+  hipLaunchKernelGGL(k_accum_score_f32, dim3(blocks_for(n), batch), dim3(256), 0, s, M, G, n, m, ld,
+                     l1, sq);
   return hipGetLastError();
 }
 

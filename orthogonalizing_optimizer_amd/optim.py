@@ -35,6 +35,7 @@ class Dion3Step:
         self.mu = float(mu)
         self.cfg = cfg
         self.groups: "OrderedDict[Tuple, Dict]" = OrderedDict()
+        self._order = list(weights)
         for w, m in zip(weights, momenta):
             if w.dim() != 2 or w.shape != m.shape:
                 raise ValueError("Dion3 steps 2-D matrices with same-shape momentum")
@@ -52,7 +53,16 @@ class Dion3Step:
     def lr_eff(self) -> float:
         return self.lr / math.sqrt(float(self.fraction))
 
-    def step(self):
+    def step(self, grads: Optional[Sequence] = None):
+        """One step over every group.  With ``grads`` (one per weight, in the
+        order the weights were given), each momentum first accumulates its
+        gradient, M <- M + G, fused into the row scoring."""
+        gmap = None
+        if grads is not None:
+            if len(grads) != sum(len(g["W"]) for g in self.groups.values()):
+                raise ValueError("need one gradient per weight")
+            gmap = {id(w): gr for w, gr in zip(self._order, grads)}
         for key, g in self.groups.items():
+            Gs = [gmap[id(w)] for w in g["W"]] if gmap is not None else None
             _lib.step_megabatch(g["W"], g["M"], g["k"], self.lr_eff, self.mu, self.cfg,
-                                ws=self.ws, ptrs=g["ptrs"])
+                                ws=self.ws, ptrs=g["ptrs"], Gs=Gs)

@@ -42,8 +42,11 @@ def oracle_for(W, M, k, lr, mu, S_gpu, coeffs=None, restart_at=(3,)):
                           S_override=override)
 
 
-def check_step(W0, M0, W1, M1, S_gpu, O_gpu, k, lr, mu, coeffs=None, restart_at=(3,)):
-    """Full acceptance of one matrix's step.  Returns the O error."""
+def check_step(W0, M0, W1, M1, S_gpu, O_gpu, k, lr, mu, coeffs=None, restart_at=(3,), G=None):
+    """Full acceptance of one matrix's step.  Returns the O error.  With a
+    gradient G, the buffer the step starts from is fl32(M0 + G)."""
+    if G is not None:
+        M0 = M0 + G          # numpy float32 add: the correctly rounded sum
     ref = oracle_for(W0, M0, k, lr, mu, S_gpu, coeffs, restart_at)
     S = ref["S"]
     n = M0.shape[0]

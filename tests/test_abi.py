@@ -132,6 +132,10 @@ def test_other_entry_points_validate():
                                     1 << 30, None) == ERR_ARG
     assert lib.dion3_step_megabatch(FAKE, FAKE, 0, 8, 8, 8, 2, 0.1, 0.9, cfg, None, None, FAKE,
                                     1 << 30, None) == ERR_ARG
+    assert lib.dion3_step_accum(FAKE, FAKE, None, 8, 8, 8, 2, 0.1, 0.9, cfg, None, None, FAKE,
+                                1 << 30, None) == ERR_ARG
+    assert lib.dion3_step_megabatch_accum(FAKE, FAKE, None, 2, 8, 8, 8, 2, 0.1, 0.9, cfg, None,
+                                          None, FAKE, 1 << 30, None) == ERR_ARG
     assert lib.dion3_row_select(None, 1, 8, 8, 8, 2, FAKE, None, FAKE, 1 << 30, None) == ERR_ARG
     assert lib.dion3_row_select(FAKE, 1, 8, 8, 8, 9, FAKE, None, FAKE, 1 << 30, None) == ERR_ARG
     assert lib.dion3_row_select(FAKE, 1, 8, 8, 8, 2, FAKE, None, FAKE, 0, None) == ERR_WS

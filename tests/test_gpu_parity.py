@@ -240,6 +240,39 @@ def test_megabatch_16x1024x4096_f1():
         print(f"16x1024x4096 f=1 matrix {b}: O rel err {err:.3e}", flush=True)
 
 
+@pytest.mark.parametrize("n,m,k", [(300, 200, 75), (128, 512, 32), (250, 40, 200)])
+def test_step_accumulates_gradient(n, m, k):
+    """M <- M + G fused into the scoring, then the step on the updated M."""
+    say("step accum", n, m, k)
+    W = host_gaussian((n, m), [16, n], std=0.02)
+    M = host_gaussian((n, m), [17, n])
+    G = host_gaussian((n, m), [18, n], std=0.3)
+    Wd, Md, Gd = dev(W), dev(M), dev(G)
+    idx, O = d3.step(Wd, Md, k, 0.04, 0.95, return_idx=True, return_O=True, G=Gd)
+    torch.cuda.synchronize()
+    check_step(W, M, Wd.cpu().numpy(), Md.cpu().numpy(), idx.cpu().numpy(), O.cpu().numpy(),
+               k, 0.04, 0.95, G=G)
+    assert Gd.cpu().numpy().tobytes() == G.tobytes()          # G is read only
+
+
+def test_megabatch_accum_equals_add_then_step_bitwise():
+    say("megabatch accum vs add + step")
+    B, n, m, k = 4, 180, 260, 45
+    Ws = [host_gaussian((n, m), [19, b], std=0.02) for b in range(B)]
+    Ms = [host_gaussian((n, m), [20, b]) for b in range(B)]
+    Gs = [host_gaussian((n, m), [21, b], std=0.5) for b in range(B)]
+    Wa, Ma, Ga = [dev(w) for w in Ws], [dev(x) for x in Ms], [dev(g) for g in Gs]
+    ia, Oa = d3.step_megabatch(Wa, Ma, k, 0.04, 0.95, return_idx=True, return_O=True, Gs=Ga)
+    Wb, Mb = [dev(w) for w in Ws], [dev(x + g) for x, g in zip(Ms, Gs)]
+    ib, Ob = d3.step_megabatch(Wb, Mb, k, 0.04, 0.95, return_idx=True, return_O=True)
+    torch.cuda.synchronize()
+    assert ia.cpu().numpy().tobytes() == ib.cpu().numpy().tobytes()
+    assert Oa.cpu().numpy().tobytes() == Ob.cpu().numpy().tobytes()
+    for b in range(B):
+        assert Wa[b].cpu().numpy().tobytes() == Wb[b].cpu().numpy().tobytes()
+        assert Ma[b].cpu().numpy().tobytes() == Mb[b].cpu().numpy().tobytes()
+
+
 def test_dion3step_groups_by_shape():
     say("Dion3Step grouping")
     shapes = [(64, 96), (96, 64), (64, 96), (64, 96), (96, 64)]

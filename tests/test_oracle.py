@@ -259,6 +259,23 @@ def test_step_rejects_bad_input():
         orc.dion3_step(W, M2, 2, 0.1, 0.9)
 
 
+def test_step_accumulates_gradient_exactly():
+    """M <- M + G is one correctly rounded fp32 add (numpy's own fp32 add is
+    that), every row of the buffer keeps it, and the selection and update
+    follow the accumulated buffer."""
+    W = host_gaussian((50, 30), 71, std=0.02)
+    M = host_gaussian((50, 30), 72)
+    G = host_gaussian((50, 30), 73, std=0.1)
+    r = orc.dion3_step(W, M, 12, 0.04, 0.95, G=G)
+    acc = M + G                                  # numpy float32 add
+    mask = np.zeros(50, bool)
+    mask[r["S"]] = True
+    assert r["M"][~mask].tobytes() == acc[~mask].tobytes()
+    assert r["M"][mask].tobytes() == (np.float32(0.95) * acc[mask]).tobytes()
+    ref = orc.dion3_step(W, acc, 12, 0.04, 0.95)
+    assert np.array_equal(r["S"], ref["S"]) and rel(r["W"], ref["W"]) == 0.0
+
+
 def test_step_standard_and_gram_agree():
     W = host_gaussian((30, 50), 61, std=0.02)
     M = host_gaussian((30, 50), 62)
