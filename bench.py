@@ -32,6 +32,8 @@ KERNEL_SYMBOLS = {
     "gemm_poly_256": "k_gemm<Cfg<256, 2, 4, 1>, 1, true, true>",
     "gemm_symm_256": "k_gemm<Cfg<256, 2, 4, 1>, 2, true, false>",
     "gemm_rect_256": "k_gemm<Cfg<256, 2, 4, 1>, 3, false, false>",
+    "gemm_nsx_256": "k_gemm<Cfg<256, 2, 4, 1>, 4, false, true>",
+    "gemm_nsx_128": "k_gemm<Cfg<128, 2, 2, 2>, 4, false, true>",
     "gemm_gram_128": "k_gemm<Cfg<128, 2, 2, 2>, 0, true, false>",
     "gemm_poly_128": "k_gemm<Cfg<128, 2, 2, 2>, 1, true, true>",
     "gemm_symm_128": "k_gemm<Cfg<128, 2, 2, 2>, 2, true, false>",
@@ -52,8 +54,12 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=10)
     p.add_argument("--warmup", type=int, default=3)
-    p.add_argument("--workload", default="c4", help="c1, c2, c3, c4 (7B f=1/4), c4h (7B f=1/2), c5")
+    p.add_argument("--workload", default="c4",
+                   help="c1, c2, c3, c4 (7B f=1/4), c4h (7B f=1/2), c4f (7B f=1), c5")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--method", default="gram", choices=["gram", "standard"],
+                   help="gram: Gram Newton-Schulz (the step); standard: the iteration on X itself "
+                        "(the Muon baseline, on the same kernels)")
     p.add_argument("--no-trace", action="store_true")
     p.add_argument("--accumulate", action="store_true",
                    help="each step first accumulates a gradient into the momentum (M <- M + G, "
@@ -137,6 +143,8 @@ def main():
     dev = "cuda:0"
     wl = WORKLOADS[args.workload]
     cfg = d3.default_cfg()
+    if args.method == "standard":
+        cfg.method = d3.NS_STANDARD
     mu = 0.95
     lr = wl.lr
 
@@ -276,7 +284,7 @@ def main():
                 continue
             k = orc.k_from_fraction(wl.fraction, g.n)
             t = time.perf_counter()
-            orc.dion3_step(W0, M0, k, lr, mu)
+            orc.dion3_step(W0, M0, k, lr, mu, method=args.method)
             dt = time.perf_counter() - t
             t_cpu += dt
             used += 1

@@ -74,10 +74,18 @@ typedef struct {
   int32_t restart_at[DION3_MAX_RESTARTS];
   float abc[DION3_MAX_ITERS][3];
   float eps;
+  int32_t method;   /* DION3_NS_GRAM (default) or DION3_NS_STANDARD */
 } dion3_ns_cfg;
 
-/* Default schedule: 5 iterations of Muon's quintic (3.4445, -4.7750,
- * 2.0315), one restart at iteration 3, eps = 1e-7. */
+/* method: DION3_NS_GRAM iterates on the Gram matrix (the level-1 paragraph);
+ * DION3_NS_STANDARD runs the standard quintic iteration on X itself,
+ * X <- a X + (b A + c A^2) X with A = X X^T, on the same fp16 MFMA kernels
+ * (the Muon baseline the pages compare against; restarts do not apply). */
+#define DION3_NS_GRAM 0
+#define DION3_NS_STANDARD 1
+
+/* Default schedule: Gram Newton-Schulz, 5 iterations of Muon's quintic
+ * (3.4445, -4.7750, 2.0315), one restart at iteration 3, eps = 1e-7. */
 DION3_API void dion3_ns_cfg_default(dion3_ns_cfg* cfg);
 
 /* k = ceil(f * n) (level-3 paragraph of the agihunt summary), computed in

@@ -37,7 +37,12 @@ class NsCfg(ctypes.Structure):
     """Mirror of dion3_ns_cfg."""
     _fields_ = [("iters", ctypes.c_int32), ("n_restart", ctypes.c_int32),
                 ("restart_at", ctypes.c_int32 * MAX_RESTARTS),
-                ("abc", (ctypes.c_float * 3) * MAX_ITERS), ("eps", ctypes.c_float)]
+                ("abc", (ctypes.c_float * 3) * MAX_ITERS), ("eps", ctypes.c_float),
+                ("method", ctypes.c_int32)]
+
+
+NS_GRAM = 0
+NS_STANDARD = 1
 
 
 _lib = None
@@ -106,10 +111,12 @@ def _check(status: int, where: str):
 
 def ns_cfg(iters: int = 5, restart_at: Sequence[int] = (3,),
            coeffs: Optional[Sequence[Tuple[float, float, float]]] = None,
-           eps: float = 1e-7) -> NsCfg:
-    """Build a dion3_ns_cfg (validated by the library at call time)."""
+           eps: float = 1e-7, method: int = NS_GRAM) -> NsCfg:
+    """Build a dion3_ns_cfg (validated by the library at call time).
+    method: NS_GRAM (Gram Newton-Schulz) or NS_STANDARD (iteration on X)."""
     cfg = NsCfg()
     lib().dion3_ns_cfg_default(ctypes.byref(cfg))
+    cfg.method = method
     if len(restart_at) > MAX_RESTARTS or iters > MAX_ITERS:
         raise ValueError("too many restarts or iterations")
     cfg.iters = iters

@@ -80,6 +80,7 @@ dion3_status check_cfg(const dion3_ns_cfg* c) {
     prev = r;
   }
   if (!(c->eps >= 0.0f) || !isfinite(c->eps)) return DION3_ERR_ARG;
+  if (c->method != DION3_NS_GRAM && c->method != DION3_NS_STANDARD) return DION3_ERR_ARG;
   for (int t = 0; t < c->iters; ++t)
     for (int j = 0; j < 3; ++j)
       if (!isfinite(c->abc[t][j])) return DION3_ERR_ARG;
@@ -252,6 +253,56 @@ dion3_status gram_ns(const Plan& P, const dion3_ns_cfg& cfg, const Bufs& bf,
   return DION3_OK;
 }
 
+// Standard quintic Newton-Schulz on X itself (the iteration the Gram form
+// replaces, level-1 paragraph): A = X X^T, B = b A + c A^2, X <- a X + B X.
+// The last update goes to `sink`.
+hipError_t ns_update(const Plan& P, const f16* B, const XPair& x, const XPair& y, float a,
+                     bool both, hipStream_t s, const UpdateSink* sink) {
+  const double sv = s_of(P);
+  GemmDesc d = {};
+  d.trace_flops = 2.0 * P.B * sv * sv * L_of(P);
+  d.role = kRoleNsX;
+  d.A = B; d.sA = P.sp * P.sp; d.lda = (int)P.sp;
+  d.B = xmathT(P, x); d.sB = P.kp * P.mp; d.ldb = (int)P.sp;
+  d.D = xmathT(P, x); d.sD = P.kp * P.mp; d.ldd = (int)P.sp;   // a X, read transposed
+  d.epilogue = true; d.alpha = 1.0f; d.beta = a; d.gamma = 0.0f;
+  const bool want_math = both || !P.tr, want_mathT = both || P.tr;
+  d.C = want_math ? (f16*)xmath(P, y) : nullptr; d.sC = P.kp * P.mp; d.ldc = (int)P.Lp;
+  d.CT = want_mathT ? (f16*)xmathT(P, y) : nullptr; d.sCT = P.kp * P.mp; d.ldct = (int)P.sp;
+  if (sink) {
+    d.sink = P.tr ? 2 : 1;
+    d.C = nullptr;
+    d.CT = nullptr;
+    d.W = sink->W; d.ldw = sink->ldw; d.idx = sink->idx; d.lr = sink->lr; d.Oout = sink->Oout;
+    d.kval = (int)P.k; d.mval = (int)P.m; d.nrows = (int)P.n;
+  }
+  d.M = (int)P.sp; d.N = (int)P.Lp; d.K = (int)P.sp; d.batch = P.B;
+  return launch_gemm(d, s);
+}
+
+dion3_status standard_ns(const Plan& P, const dion3_ns_cfg& cfg, const Bufs& bf,
+                         const UpdateSink& sink, hipStream_t s) {
+  XPair x = bf.a, xalt = bf.b;
+  for (int t = 1; t <= cfg.iters; ++t) {
+    const float a = cfg.abc[t - 1][0], b = cfg.abc[t - 1][1], c = cfg.abc[t - 1][2];
+    HIP_TRY(gram(P, x, bf.R, s));                                  // A = X X^T
+    HIP_TRY(symm(P, bf.R, bf.R, bf.R, bf.Z, c, b, 0.0f, true, s));  // B = b A + c A^2
+    if (t < cfg.iters) {
+      HIP_TRY(ns_update(P, bf.Z, x, xalt, a, true, s, nullptr));
+      XPair tmp = x; x = xalt; xalt = tmp;
+    } else {
+      HIP_TRY(ns_update(P, bf.Z, x, xalt, a, false, s, &sink));
+    }
+  }
+  return DION3_OK;
+}
+
+dion3_status orthogonalize(const Plan& P, const dion3_ns_cfg& cfg, const Bufs& bf,
+                           const UpdateSink& sink, hipStream_t s) {
+  return cfg.method == DION3_NS_STANDARD ? standard_ns(P, cfg, bf, sink, s)
+                                         : gram_ns(P, cfg, bf, sink, s);
+}
+
 dion3_status step_impl(BatchPtr<float> W, BatchPtr<float> M, BatchPtr<const float> G, int batch,
                        long long n, long long m,
                        long long ld, long long k, float lr, float mu, const dion3_ns_cfg* cfg_in,
@@ -297,7 +348,7 @@ dion3_status step_impl(BatchPtr<float> W, BatchPtr<float> M, BatchPtr<const floa
                               bf.a.XT, P.kp * P.mp, (int)P.kp, (int)P.mp, s));
   }
   const UpdateSink sink = {W, ld, idx, lr, (f16*)O_out};
-  st = gram_ns(P, cfg, bf, sink, s);
+  st = orthogonalize(P, cfg, bf, sink, s);
   if (st != DION3_OK) return st;
   if (idx_out)
     HIP_TRY(hipMemcpyAsync(idx_out, idx, (size_t)batch * k * sizeof(int32_t),
@@ -440,7 +491,7 @@ dion3_status dion3_gram_ns(const uint16_t* X, uint16_t* O, int32_t batch, int64_
   HIP_TRY(launch_gather_f16(Xb, batch, (int)m, m, (int)k, scale, bf.a.X, bf.a.XT, P.kp * P.mp,
                             (int)P.kp, (int)P.mp, s));
   const UpdateSink sink = {{nullptr, 0, nullptr}, 0, idx, 0.0f, (f16*)O};
-  st = gram_ns(P, cfg, bf, sink, s);
+  st = orthogonalize(P, cfg, bf, sink, s);
   if (st != DION3_OK) return st;
   return DION3_OK;
 }

@@ -30,7 +30,9 @@ inline long long pad_to(long long x, long long p) { return (x + p - 1) / p * p; 
 //  element (r >= c) is written to both C[r][c] and C[c][r].
 //  Otherwise C[m][n] is written when C is set and CT[n][m] when CT is set.
 // M, N must be multiples of 128, K a multiple of 64, ld* multiples of 8.
-enum GemmRole { kRoleGram = 0, kRolePoly = 1, kRoleSymm = 2, kRoleRect = 3 };
+// kRoleNsX: the standard-iteration update X' = B X + beta X (rectangular,
+// epilogue reading D = X^T as contiguous runs).
+enum GemmRole { kRoleGram = 0, kRolePoly = 1, kRoleSymm = 2, kRoleRect = 3, kRoleNsX = 4 };
 
 struct GemmDesc {
   int role;

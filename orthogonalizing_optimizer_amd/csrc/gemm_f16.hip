@@ -213,7 +213,8 @@ __device__ __forceinline__ void mma_stage_fused(const f16* __restrict__ st, f16*
 }
 
 // ROLE only names the instance (0 Gram, 1 polynomial, 2 symmetric product,
-// 3 rectangular) so that profilers report each role as its own kernel.
+// 3 rectangular, 4 standard-iteration update) so that profilers report each
+// role as its own kernel.
 template <class C, int ROLE, bool LOWER, bool EPI>
 __global__ __launch_bounds__(C::NT, (C::BM == 256 ? 1 : 2)) void k_gemm(GemmArgs p) {
   __shared__ __attribute__((aligned(16))) f16 lds[C::LDS];
@@ -324,8 +325,10 @@ __global__ __launch_bounds__(C::NT, (C::BM == 256 ? 1 : 2)) void k_gemm(GemmArgs
   // Epilogue: final fp32 value (alpha, D, gamma I) -> fp16 tile in LDS.
   // Accumulator layout of the 32x32 MFMA: lane l, value v holds row
   // 8*(v/4) + 4*(l/32) + v%4, column l%32 of its 32x32 block, so each lane
-  // owns runs of 4 consecutive rows of one column.  D is symmetric, so the
-  // 4 values D[r..r+3][c] are read as the contiguous D[c][r..r+3].
+  // owns runs of 4 consecutive rows of one column.  The 4 values
+  // D[r..r+3][c] are read as the contiguous run Dt[c][r..r+3] of the
+  // transposed addend: D itself when it is symmetric (the polynomial), the
+  // transposed copy of X for the standard-iteration update.
   typedef f16 half4 __attribute__((ext_vector_type(4)));
   const f16* __restrict__ Db = EPI && p.D ? p.D + (long long)b * p.sD : nullptr;
   f16* S = lds;
@@ -429,10 +432,11 @@ bool use_large(const GemmDesc& d) {
 }
 
 const char* trace_name(int role, bool large) {
-  static const char* names[4][2] = {{"gemm_gram_128", "gemm_gram_256"},
+  static const char* names[5][2] = {{"gemm_gram_128", "gemm_gram_256"},
                                     {"gemm_poly_128", "gemm_poly_256"},
                                     {"gemm_symm_128", "gemm_symm_256"},
-                                    {"gemm_rect_128", "gemm_rect_256"}};
+                                    {"gemm_rect_128", "gemm_rect_256"},
+                                    {"gemm_nsx_128", "gemm_nsx_256"}};
   return names[role][large ? 1 : 0];
 }
 
@@ -463,6 +467,9 @@ hipError_t launch_gemm(const GemmDesc& d, hipStream_t s) {
     case kRoleRect:
       if (d.lower || d.epilogue) break;
       return launch_cfg<kRoleRect, false, false>(d, s);
+    case kRoleNsX:
+      if (d.lower || !d.epilogue || !d.D) break;
+      return launch_cfg<kRoleNsX, false, true>(d, s);
   }
   return hipErrorInvalidValue;
 }

@@ -61,6 +61,7 @@ def test_k_from_fraction_edges():
 def test_default_cfg():
     cfg = d3.default_cfg()
     assert cfg.iters == 5 and cfg.n_restart == 1 and cfg.restart_at[0] == 3
+    assert cfg.method == d3.NS_GRAM
     assert abs(cfg.abc[0][0] - 3.4445) < 1e-6 and abs(cfg.abc[4][2] - 2.0315) < 1e-6
     assert abs(cfg.eps - 1e-7) < 1e-12
 
@@ -115,6 +116,7 @@ def test_step_rejects_bad_arguments_before_launch():
     bad.restart_at[0], bad.restart_at[1] = 3, 3
     assert _step(lib, cfg=bad) == ERR_ARG
     assert _step(lib, cfg=_cfg(eps=-1.0)) == ERR_ARG
+    assert _step(lib, cfg=_cfg(method=2)) == ERR_ARG
 
 
 def test_step_rejects_bad_workspace_before_launch():

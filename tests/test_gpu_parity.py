@@ -130,6 +130,33 @@ def test_gram_ns_schedules(iters, restarts):
         assert rel(O[b], ref) <= O_TOL
 
 
+@pytest.mark.parametrize("B,k,m", [(2, 100, 300), (1, 300, 100), (1, 257, 1000), (3, 64, 64)])
+def test_standard_ns(B, k, m):
+    """The standard iteration on X (the Muon baseline) on the same kernels."""
+    say("standard ns", B, k, m)
+    X = host_gaussian((B, k, m), [22, k, m]).astype(np.float16)
+    O = d3.gram_ns(dev(X), d3.ns_cfg(method=d3.NS_STANDARD)).cpu().numpy()
+    co = orc.default_coeffs()
+    for b in range(B):
+        ref = orc.ns_standard(X[b].astype(np.float64), co)
+        assert rel(O[b], ref) <= O_TOL, (b, rel(O[b], ref))
+
+
+@pytest.mark.parametrize("n,m,k", [(256, 512, 256), (400, 160, 400), (300, 200, 75)])
+def test_step_standard_method(n, m, k):
+    say("step standard", n, m, k)
+    W = host_gaussian((n, m), [23, n], std=0.02)
+    M = host_gaussian((n, m), [24, n])
+    W1, M1, S, O = run_step(W, M, k, 0.02, 0.95, d3.ns_cfg(method=d3.NS_STANDARD))
+    ref = orc.dion3_step(W, M, k, 0.02, 0.95, method="standard")
+    assert np.array_equal(S, ref["S"])
+    assert rel(O, ref["O"]) <= O_TOL
+    mask = np.zeros(n, bool)
+    mask[S] = True
+    assert W1[~mask].tobytes() == W[~mask].tobytes() and M1[~mask].tobytes() == M[~mask].tobytes()
+    assert M1[mask].tobytes() == ref["M"][mask].tobytes()
+
+
 def test_gram_ns_deterministic():
     say("gram_ns twice")
     X = dev(host_gaussian((3, 200, 700), 6).astype(np.float16))

@@ -80,6 +80,7 @@ WORKLOADS: Dict[str, Workload] = {
     "c3": Workload("c3-1B-f1/4", _model_groups(2048, 5504, 24), Fraction(1, 4), "scaled", 3000),
     "c4h": Workload("c4-7B-f1/2", _model_groups(4096, 11008, 32), Fraction(1, 2), "gaussian", 4000),
     "c4": Workload("c4-7B-f1/4", _model_groups(4096, 11008, 32), Fraction(1, 4), "gaussian", 4000),
+    "c4f": Workload("c4-7B-f1", _model_groups(4096, 11008, 32), Fraction(1, 1), "gaussian", 4000),
     "c5": Workload("c5-14B-f1/8", _model_groups(5120, 13824, 40), Fraction(1, 8), "lowrank", 5000),
 }
 
