@@ -67,6 +67,9 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="CPU-baseline budget: oracle matrices are taken round-robin over the "
                         "shape groups until this much CPU time is spent (at least one per group)")
+    p.add_argument("--graph", action="store_true",
+                   help="capture one whole step (every group's launches) in a HIP graph and time "
+                        "its replays (the per-kernel trace is then off)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 2 GiB device-to-device copy (a known-size kernel for "
                         "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE) and print its GB/s")
@@ -188,6 +191,15 @@ def main():
         one_step()
     torch.cuda.synchronize()
 
+    graph = None
+    if args.graph:
+        args.no_trace = True
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            one_step()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
     launches_per_step = sum(3 + 1 + 2 * (1 + cfg.n_restart) + 4 * cfg.iters for _ in groups)
     if not args.no_trace:
         d3.trace_enable(launches_per_step * args.steps + 64)
@@ -196,7 +208,10 @@ def main():
     torch.cuda.synchronize()
     e0.record(stream)
     for _ in range(args.steps):
-        one_step()
+        if graph is not None:
+            graph.replay()
+        else:
+            one_step()
     e1.record(stream)
     torch.cuda.synchronize()
     ms_total = e0.elapsed_time(e1)
@@ -326,6 +341,7 @@ def main():
             "state_dtype": "fp32 W and M; fp16 X, Gram, polynomials and O with fp32 accumulation",
             "parallelism": "single GPU, one megabatched call per shape group",
             "gradient_accumulation": bool(args.accumulate),
+            "hip_graph": bool(args.graph),
         },
         "matrices_per_s": round(wl.n_matrices / (ms_per_step * 1e-3), 1),
         "gram_ns_tflops": round(gram_tflops, 2) if gram_tflops else None,

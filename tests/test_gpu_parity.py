@@ -300,6 +300,41 @@ def test_megabatch_accum_equals_add_then_step_bitwise():
         assert Ma[b].cpu().numpy().tobytes() == Mb[b].cpu().numpy().tobytes()
 
 
+def test_graph_capture_replays_match_eager():
+    """The step's launch sequence (no allocation, no memset) captured in a HIP
+    graph: every replay, with eager work and synchronizations in between,
+    equals the same number of eager steps bit for bit."""
+    say("graph capture")
+    B, n, m, k = 3, 160, 288, 40
+    Ws = [host_gaussian((n, m), [25, b], std=0.02) for b in range(B)]
+    Ms = [host_gaussian((n, m), [26, b]) for b in range(B)]
+    We, Me = [dev(w) for w in Ws], [dev(x) for x in Ms]
+    Wg, Mg = [dev(w) for w in Ws], [dev(x) for x in Ms]
+    ws_e, ws_g = d3.Workspace(), d3.Workspace()
+    pg = (d3.pointer_array(Wg, DEV), d3.pointer_array(Mg, DEV))
+    ws_g.get(d3.workspace_size(B, n, m, k), DEV)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):          # warm the path outside the capture
+        d3.step_megabatch(Wg, Mg, k, 0.04, 0.95, ws=ws_g, ptrs=pg)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    d3.step_megabatch(We, Me, k, 0.04, 0.95, ws=ws_e)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        d3.step_megabatch(Wg, Mg, k, 0.04, 0.95, ws=ws_g, ptrs=pg)
+    for rep in range(3):
+        graph.replay()
+        d3.step_megabatch(We, Me, k, 0.04, 0.95, ws=ws_e)
+        junk = torch.randn(1000, device=DEV).sum()        # eager work between replays
+        torch.cuda.synchronize()
+        assert float(junk) == float(junk)
+        for b in range(B):
+            assert Wg[b].cpu().numpy().tobytes() == We[b].cpu().numpy().tobytes(), (rep, b)
+            assert Mg[b].cpu().numpy().tobytes() == Me[b].cpu().numpy().tobytes(), (rep, b)
+
+
 def test_dion3step_groups_by_shape():
     say("Dion3Step grouping")
     shapes = [(64, 96), (96, 64), (64, 96), (64, 96), (96, 64)]
