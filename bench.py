@@ -67,6 +67,11 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="CPU-baseline budget: oracle matrices are taken round-robin over the "
                         "shape groups until this much CPU time is spent (at least one per group)")
+    p.add_argument("--streams", type=int, default=1,
+                   help="run the shape groups on this many HIP streams (forked from and joined "
+                        "back into the current stream each step), each group with its own "
+                        "workspace, so that one group's memory-bound kernels overlap another's "
+                        "products")
     p.add_argument("--graph", action="store_true",
                    help="capture one whole step (every group's launches) in a HIP graph and time "
                         "its replays (the per-kernel trace is then off)")
@@ -179,13 +184,34 @@ def main():
             gen.manual_seed(7000 + gi)
             Gs = [torch.randn(M.shape, generator=gen, device=dev).mul_(0.1) for M in Ms]
             grads[gi] = (Gs, d3.pointer_array(Gs, dev))
-    ws = d3.Workspace()
-    ws.get(max_ws, dev)
+    nstreams = max(1, min(args.streams, len(groups)))
+    if nstreams == 1:
+        ws = d3.Workspace()
+        ws.get(max_ws, dev)
+        wss = [ws] * len(groups)
+    else:
+        wss = []
+        for g, Ws, Ms, k, ptrs in groups:
+            w_ = d3.Workspace()
+            w_.get(d3.workspace_size(len(Ms), g.n, g.m, k), dev)
+            wss.append(w_)
+    side = [torch.cuda.Stream() for _ in range(nstreams)] if nstreams > 1 else []
 
     def one_step():
+        if nstreams == 1:
+            for gi, (g, Ws, Ms, k, ptrs) in enumerate(groups):
+                gp = grads[gi][1] if gi in grads else None
+                d3.step_megabatch(Ws, Ms, k, lr, mu, cfg, ws=wss[gi], ptrs=ptrs, gptrs=gp)
+            return
+        main = torch.cuda.current_stream()
+        for st in side:
+            st.wait_stream(main)
         for gi, (g, Ws, Ms, k, ptrs) in enumerate(groups):
             gp = grads[gi][1] if gi in grads else None
-            d3.step_megabatch(Ws, Ms, k, lr, mu, cfg, ws=ws, ptrs=ptrs, gptrs=gp)
+            with torch.cuda.stream(side[gi % nstreams]):
+                d3.step_megabatch(Ws, Ms, k, lr, mu, cfg, ws=wss[gi], ptrs=ptrs, gptrs=gp)
+        for st in side:
+            main.wait_stream(st)
 
     for _ in range(args.warmup):
         one_step()
@@ -339,7 +365,8 @@ def main():
             "lr": lr, "mu": mu, "ns_iters": cfg.iters,
             "restart_at": [cfg.restart_at[i] for i in range(cfg.n_restart)],
             "state_dtype": "fp32 W and M; fp16 X, Gram, polynomials and O with fp32 accumulation",
-            "parallelism": "single GPU, one megabatched call per shape group",
+            "parallelism": "single GPU, one megabatched call per shape group" +
+                           (f", groups on {nstreams} streams" if nstreams > 1 else ""),
             "gradient_accumulation": bool(args.accumulate),
             "hip_graph": bool(args.graph),
         },
