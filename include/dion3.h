@@ -51,7 +51,10 @@ typedef enum {
   DION3_OK = 0,
   DION3_ERR_ARG = -1,          /* a null required pointer or an out-of-range size/parameter */
   DION3_ERR_WORKSPACE = -2,    /* ws is NULL, misaligned or smaller than dion3_workspace_size() */
-  DION3_ERR_UNSUPPORTED = -3,  /* a shape beyond the library's limits (see DION3_MAX_DIM) */
+  DION3_ERR_UNSUPPORTED = -3,  /* a shape beyond the library's limits: a dimension above
+                                  DION3_MAX_DIM, or a zero-padded per-matrix block (the selected
+                                  rows, padded to multiples of 128, or the Gram side) of 2^31
+                                  bytes or more */
   DION3_ERR_HIP = -4           /* a HIP call or launch failed; see dion3_last_hip_error() */
 } dion3_status;
 

@@ -70,6 +70,13 @@ Plan make_plan(int B, long long n, long long m, long long k) {
 
 bool dims_ok(long long v) { return v >= 1 && v <= DION3_MAX_DIM; }
 
+// The products address each matrix through a buffer resource with 32-bit
+// byte offsets, so every padded per-matrix operand must stay below 2^31 bytes.
+constexpr long long kMaxOperandBytes = 1LL << 31;
+bool plan_fits(const Plan& P) {
+  return P.kp * P.mp * 2 < kMaxOperandBytes && P.sp * P.sp * 2 < kMaxOperandBytes;
+}
+
 dion3_status check_cfg(const dion3_ns_cfg* c) {
   if (c->iters < 1 || c->iters > DION3_MAX_ITERS) return DION3_ERR_ARG;
   if (c->n_restart < 0 || c->n_restart > DION3_MAX_RESTARTS) return DION3_ERR_ARG;
@@ -317,6 +324,7 @@ dion3_status step_impl(BatchPtr<float> W, BatchPtr<float> M, BatchPtr<const floa
   dion3_status st = check_cfg(&cfg);
   if (st != DION3_OK) return st;
   const Plan P = make_plan(batch, n, m, k);
+  if (!plan_fits(P)) return DION3_ERR_UNSUPPORTED;
   st = check_ws(P, ws, ws_bytes, P.total);
   if (st != DION3_OK) return st;
 
@@ -439,7 +447,9 @@ dion3_status dion3_workspace_size(int32_t batch, int64_t n, int64_t m, int64_t k
   if (batch < 1 || batch > DION3_MAX_BATCH) return DION3_ERR_ARG;
   if (!dims_ok(n) || !dims_ok(m) || !dims_ok(k)) return DION3_ERR_UNSUPPORTED;
   if (k > n) return DION3_ERR_ARG;
-  *bytes = make_plan(batch, n, m, k).total;
+  const Plan P = make_plan(batch, n, m, k);
+  if (!plan_fits(P)) return DION3_ERR_UNSUPPORTED;
+  *bytes = P.total;
   return DION3_OK;
 }
 
@@ -477,6 +487,7 @@ dion3_status dion3_gram_ns(const uint16_t* X, uint16_t* O, int32_t batch, int64_
   dion3_status st = check_cfg(&cfg);
   if (st != DION3_OK) return st;
   const Plan P = make_plan(batch, k, m, k);
+  if (!plan_fits(P)) return DION3_ERR_UNSUPPORTED;
   st = check_ws(P, ws, ws_bytes, P.total);
   if (st != DION3_OK) return st;
   hipStream_t s = (hipStream_t)stream;
@@ -545,6 +556,8 @@ dion3_status dion3_syrk_f16(const uint16_t* A, uint16_t* R, int32_t batch, int64
   if (!dims_ok(rows) || !dims_ok(cols)) return DION3_ERR_UNSUPPORTED;
   if (rows % kTile || cols % kTile || lda < cols || ldr < rows || lda % 8 || ldr % 8)
     return DION3_ERR_ARG;
+  if (rows * lda * 2 >= kMaxOperandBytes || rows * ldr * 2 >= kMaxOperandBytes)
+    return DION3_ERR_UNSUPPORTED;
   if (((uintptr_t)A | (uintptr_t)R) & 15) return DION3_ERR_ARG;
   GemmDesc d = {};
   d.role = kRoleGram;
@@ -565,6 +578,7 @@ dion3_status dion3_symm_f16(const uint16_t* A, const uint16_t* B, const uint16_t
   if (batch < 1 || batch > DION3_MAX_BATCH) return DION3_ERR_ARG;
   if (!dims_ok(s)) return DION3_ERR_UNSUPPORTED;
   if (s % kTile || ld < s || ld % 8) return DION3_ERR_ARG;
+  if (s * ld * 2 >= kMaxOperandBytes) return DION3_ERR_UNSUPPORTED;
   if (!isfinite(alpha) || !isfinite(beta) || !isfinite(gamma)) return DION3_ERR_ARG;
   if (C == A || C == B || (D && C == D)) return DION3_ERR_ARG;
   if (((uintptr_t)A | (uintptr_t)B | (uintptr_t)C | (uintptr_t)D) & 15) return DION3_ERR_ARG;

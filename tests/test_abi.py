@@ -79,6 +79,9 @@ def test_workspace_size_layout():
         d3.workspace_size(0, 10, 10, 1)
     out = ctypes.c_size_t()
     assert d3.lib().dion3_workspace_size(1, (1 << 20) + 1, 4, 1, ctypes.byref(out)) == ERR_UNSUP
+    # padded selected block of 2^31 bytes or more: rejected (32-bit buffer offsets)
+    assert d3.lib().dion3_workspace_size(1, 1 << 16, 1 << 15, 1 << 15, ctypes.byref(out)) == ERR_UNSUP
+    assert d3.lib().dion3_workspace_size(1, 1 << 16, 1 << 14, 1 << 15, ctypes.byref(out)) == 0
 
 
 def _cfg(**kw):

@@ -335,6 +335,34 @@ def test_graph_capture_replays_match_eager():
             assert Mg[b].cpu().numpy().tobytes() == Me[b].cpu().numpy().tobytes(), (rep, b)
 
 
+def test_timing_trace_records_every_kernel():
+    say("trace")
+    W = dev(host_gaussian((300, 500), 27, std=0.02))
+    M = dev(host_gaussian((300, 500), 28))
+    d3.step(W, M, 75, 0.04, 0.95)          # warm
+    torch.cuda.synchronize()
+    d3.trace_enable(256)
+    try:
+        d3.step(W, M, 75, 0.04, 0.95)
+        recs = d3.trace_records()
+    finally:
+        d3.trace_disable()
+    names = [r[0] for r in recs]
+    assert names[:3] == ["row_score", "topk", "gather"]
+    gemms = [r for r in recs if r[0].startswith("gemm_")]
+    # 5 iterations with a restart at 3: 2 Grams, 5 polynomials, 2 multiply-backs
+    # and 9 symmetric products (iterations 1-2: R <- Z R Z, Q <- Z Q; iterations
+    # 3-5: R <- Z R Z twice, Q <- Z Q twice)
+    assert sum(1 for r in gemms if r[0].startswith("gemm_gram")) == 2
+    assert sum(1 for r in gemms if r[0].startswith("gemm_poly")) == 5
+    assert sum(1 for r in gemms if r[0].startswith("gemm_symm")) == 9
+    assert sum(1 for r in gemms if r[0].startswith("gemm_rect")) == 2
+    assert all(r[1] > 0 for r in recs)
+    s_, L_ = 75.0, 500.0
+    flops = sum(r[2] for r in gemms)
+    assert flops == pytest.approx(6 * s_ * s_ * L_ + 14 * s_ ** 3)
+
+
 def test_dion3step_groups_by_shape():
     say("Dion3Step grouping")
     shapes = [(64, 96), (96, 64), (64, 96), (64, 96), (96, 64)]
