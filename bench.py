@@ -103,12 +103,11 @@ def copy_calibration():
                       "ms": round(ms, 4), "gbs": round(8 * n / (ms * 1e-3) / 1e9, 1)}), flush=True)
 
 
-def kernel_source_hash() -> str:
-    h = hashlib.sha256()
-    for f in ("gemm_f16.hip", "rows.hip", "dion3_internal.h"):
-        with open(os.path.join(ROOT, "orthogonalizing_optimizer_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:16]
+def kernel_source_hash(kernel: str) -> str:
+    """Hash of the source file that holds this kernel's device code."""
+    f = "gemm_f16.hip" if kernel.startswith("gemm_") else "rows.hip"
+    with open(os.path.join(ROOT, "orthogonalizing_optimizer_amd", "csrc", f), "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()[:16]
 
 
 def load_traffic(kernel: str, workload: str):
@@ -120,7 +119,7 @@ def load_traffic(kernel: str, workload: str):
     try:
         d = json.load(open(path))
         ent = d.get(workload, {}).get(kernel)
-        if not ent or ent.get("source_hash") != kernel_source_hash():
+        if not ent or ent.get("source_hash") != kernel_source_hash(kernel):
             return None
         return float(ent["bytes_per_launch"])
     except (ValueError, KeyError, TypeError):
