@@ -42,7 +42,13 @@ KERNEL_SYMBOLS = {
     "accum_score": "k_accum_score_f32",
     "topk": "k_topk",
     "gather": "k_gather<float, true>",
+    "gram_ns_fused_128": "k_gram_ns_small",
 }
+
+
+def is_ns_kernel(name: str) -> bool:
+    """The orthogonalization's products: tiled GEMMs or the fused small-Gram kernel."""
+    return name.startswith("gemm_") or name.startswith("gram_ns_fused")
 
 
 def log(*a):
@@ -105,7 +111,12 @@ def copy_calibration():
 
 def kernel_source_hash(kernel: str) -> str:
     """Hash of the source file that holds this kernel's device code."""
-    f = "gemm_f16.hip" if kernel.startswith("gemm_") else "rows.hip"
+    if kernel.startswith("gemm_"):
+        f = "gemm_f16.hip"
+    elif kernel.startswith("gram_ns_fused"):
+        f = "gram_small.hip"
+    else:
+        f = "rows.hip"
     with open(os.path.join(ROOT, "orthogonalizing_optimizer_amd", "csrc", f), "rb") as fh:
         return hashlib.sha256(fh.read()).hexdigest()[:16]
 
@@ -277,7 +288,7 @@ def main():
             (f"{st['tflops']:7.1f} TFLOP/s ({100 * st['frac_fp16_peak']:.1f}% fp16 peak)"
              if st["flops"] > 0 else f"{st['gbs']:7.1f} GB/s ({100 * st['frac_hbm']:.1f}% HBM)"))
 
-    gemm = [st for nm, st in kernels.items() if nm.startswith("gemm_")]
+    gemm = [st for nm, st in kernels.items() if is_ns_kernel(nm)]
     gemm_flops = sum(st["flops"] for st in gemm) / max(1, args.steps)
     gemm_ms = sum(st["ms"] for st in gemm) / max(1, args.steps)
     gram_tflops = gemm_flops / (gemm_ms * 1e-3) / 1e12 if gemm_ms > 0 else None

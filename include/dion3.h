@@ -78,6 +78,7 @@ typedef struct {
   float abc[DION3_MAX_ITERS][3];
   float eps;
   int32_t method;   /* DION3_NS_GRAM (default) or DION3_NS_STANDARD */
+  int32_t path;     /* DION3_PATH_AUTO (default), _TILED or _FUSED */
 } dion3_ns_cfg;
 
 /* method: DION3_NS_GRAM iterates on the Gram matrix (the level-1 paragraph);
@@ -86,6 +87,22 @@ typedef struct {
  * (the Muon baseline the pages compare against; restarts do not apply). */
 #define DION3_NS_GRAM 0
 #define DION3_NS_STANDARD 1
+
+/* path (Gram method only): how the Gram iteration is launched.
+ * DION3_PATH_TILED: one tiled MFMA product per step of the iteration (about
+ *   20 launches per call, every grid spread over the whole GPU).
+ * DION3_PATH_FUSED: one launch, one workgroup per matrix running the whole
+ *   iteration with R, Z, Q in LDS; only when the Gram side min(k, m) is at
+ *   most 128, else DION3_ERR_UNSUPPORTED.  Its result is bitwise identical
+ *   to the tiled path (same products, same accumulation order, same
+ *   roundings).
+ * DION3_PATH_AUTO: the fused path where it is allowed and expected to be
+ *   faster (Gram side <= 128 and enough matrices or short enough rows for
+ *   one workgroup each), the tiled path otherwise.
+ * The standard method always runs tiled. */
+#define DION3_PATH_AUTO 0
+#define DION3_PATH_TILED 1
+#define DION3_PATH_FUSED 2
 
 /* Default schedule: Gram Newton-Schulz, 5 iterations of Muon's quintic
  * (3.4445, -4.7750, 2.0315), one restart at iteration 3, eps = 1e-7. */

@@ -38,11 +38,14 @@ class NsCfg(ctypes.Structure):
     _fields_ = [("iters", ctypes.c_int32), ("n_restart", ctypes.c_int32),
                 ("restart_at", ctypes.c_int32 * MAX_RESTARTS),
                 ("abc", (ctypes.c_float * 3) * MAX_ITERS), ("eps", ctypes.c_float),
-                ("method", ctypes.c_int32)]
+                ("method", ctypes.c_int32), ("path", ctypes.c_int32)]
 
 
 NS_GRAM = 0
 NS_STANDARD = 1
+PATH_AUTO = 0
+PATH_TILED = 1
+PATH_FUSED = 2
 
 
 _lib = None
@@ -111,12 +114,15 @@ def _check(status: int, where: str):
 
 def ns_cfg(iters: int = 5, restart_at: Sequence[int] = (3,),
            coeffs: Optional[Sequence[Tuple[float, float, float]]] = None,
-           eps: float = 1e-7, method: int = NS_GRAM) -> NsCfg:
+           eps: float = 1e-7, method: int = NS_GRAM, path: int = PATH_AUTO) -> NsCfg:
     """Build a dion3_ns_cfg (validated by the library at call time).
-    method: NS_GRAM (Gram Newton-Schulz) or NS_STANDARD (iteration on X)."""
+    method: NS_GRAM (Gram Newton-Schulz) or NS_STANDARD (iteration on X).
+    path: PATH_AUTO, PATH_TILED (one product per launch) or PATH_FUSED (the
+    whole iteration in one launch; Gram side min(k, m) <= 128 only)."""
     cfg = NsCfg()
     lib().dion3_ns_cfg_default(ctypes.byref(cfg))
     cfg.method = method
+    cfg.path = path
     if len(restart_at) > MAX_RESTARTS or iters > MAX_ITERS:
         raise ValueError("too many restarts or iterations")
     cfg.iters = iters

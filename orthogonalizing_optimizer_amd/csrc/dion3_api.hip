@@ -88,6 +88,8 @@ dion3_status check_cfg(const dion3_ns_cfg* c) {
   }
   if (!(c->eps >= 0.0f) || !isfinite(c->eps)) return DION3_ERR_ARG;
   if (c->method != DION3_NS_GRAM && c->method != DION3_NS_STANDARD) return DION3_ERR_ARG;
+  if (c->path != DION3_PATH_AUTO && c->path != DION3_PATH_TILED && c->path != DION3_PATH_FUSED)
+    return DION3_ERR_ARG;
   for (int t = 0; t < c->iters; ++t)
     for (int j = 0; j < 3; ++j)
       if (!isfinite(c->abc[t][j])) return DION3_ERR_ARG;
@@ -222,8 +224,55 @@ hipError_t rect(const Plan& P, const f16* Q, const XPair& x, const XPair& y, boo
 // matrix here is a polynomial in the first Gram, so all products commute,
 // are symmetric, and only their lower triangles are computed.  The final
 // product hands O to `sink` (the row-sparse update and/or O_out).
+// Algorithmic flops of the whole Gram iteration on unpadded sizes, with the
+// symmetric products counted at half (lower triangle), as the tiled
+// launches record them.
+double gram_ns_flops(const Plan& P, const dion3_ns_cfg& cfg) {
+  const double sv = s_of(P), L = L_of(P), B = P.B;
+  double f = B * sv * sv * L;               // first Gram
+  bool q_identity = true;
+  for (int t = 1; t <= cfg.iters; ++t) {
+    if (restart_at(cfg, t)) {
+      if (!q_identity) f += 2.0 * B * sv * sv * L;
+      f += B * sv * sv * L;
+      q_identity = true;
+    }
+    f += B * sv * sv * sv;                  // Z
+    if (!q_identity) f += B * sv * sv * sv; // Q <- Z Q
+    q_identity = false;
+    if (t < cfg.iters && !restart_at(cfg, t + 1)) f += 2.0 * B * sv * sv * sv;
+  }
+  return f + 2.0 * B * sv * sv * L;         // O = Q X
+}
+
+// The fused one-launch path covers Gram sides that pad to one 128 tile.  It
+// runs one workgroup per matrix, so its time grows with the row length L
+// (measured on MI355X, whole Gram iteration: 67 us at L = 512, 153 us at
+// 2048, 265 us at 4096, 490 us at 8192, flat in the batch up to 256
+// matrices) while the tiled launches cost about 210 us at small sizes and
+// spread long rows over many CUs.  Measured crossovers: the fused path wins
+// up to L = 2048 at any batch, up to 4096 from 16 matrices on, and up to
+// 8192 from 64 matrices on.
+bool use_fused(const Plan& P, const dion3_ns_cfg& cfg) {
+  if (cfg.path == DION3_PATH_TILED || P.sp != kTile) return false;
+  if (cfg.path == DION3_PATH_FUSED) return true;
+  return P.Lp <= 2048 || (P.Lp <= 4096 && P.B >= 16) || (P.Lp <= 8192 && P.B >= 64);
+}
+
+// The fused path was asked for explicitly but the Gram side exceeds 128.
+bool path_ok(const Plan& P, const dion3_ns_cfg& cfg) {
+  return !(cfg.method == DION3_NS_GRAM && cfg.path == DION3_PATH_FUSED && P.sp != kTile);
+}
+
 dion3_status gram_ns(const Plan& P, const dion3_ns_cfg& cfg, const Bufs& bf,
                      const UpdateSink& sink, hipStream_t s) {
+  if (use_fused(P, cfg)) {
+    HIP_TRY(launch_gram_ns_small(
+        (f16*)xmath(P, bf.a), (f16*)xmathT(P, bf.a), (f16*)xmath(P, bf.b), (f16*)xmathT(P, bf.b),
+        P.kp * P.mp, P.B, (int)P.Lp, P.tr, cfg, sink.W, sink.ldw, sink.idx, sink.lr, sink.Oout,
+        (int)P.k, (int)P.m, (int)P.n, gram_ns_flops(P, cfg), s));
+    return DION3_OK;
+  }
   XPair x = bf.a, xalt = bf.b;
   f16 *R = bf.R, *Z = bf.Z, *Tm = bf.T, *Q = bf.Q0, *Qn = bf.Q1;
   HIP_TRY(gram(P, x, R, s));
@@ -324,7 +373,7 @@ dion3_status step_impl(BatchPtr<float> W, BatchPtr<float> M, BatchPtr<const floa
   dion3_status st = check_cfg(&cfg);
   if (st != DION3_OK) return st;
   const Plan P = make_plan(batch, n, m, k);
-  if (!plan_fits(P)) return DION3_ERR_UNSUPPORTED;
+  if (!plan_fits(P) || !path_ok(P, cfg)) return DION3_ERR_UNSUPPORTED;
   st = check_ws(P, ws, ws_bytes, P.total);
   if (st != DION3_OK) return st;
 
@@ -487,7 +536,7 @@ dion3_status dion3_gram_ns(const uint16_t* X, uint16_t* O, int32_t batch, int64_
   dion3_status st = check_cfg(&cfg);
   if (st != DION3_OK) return st;
   const Plan P = make_plan(batch, k, m, k);
-  if (!plan_fits(P)) return DION3_ERR_UNSUPPORTED;
+  if (!plan_fits(P) || !path_ok(P, cfg)) return DION3_ERR_UNSUPPORTED;
   st = check_ws(P, ws, ws_bytes, P.total);
   if (st != DION3_OK) return st;
   hipStream_t s = (hipStream_t)stream;

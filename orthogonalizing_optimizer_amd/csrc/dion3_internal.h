@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/dion3.h"
+
 namespace dion3 {
 
 typedef _Float16 f16;
@@ -95,5 +97,15 @@ hipError_t launch_gather_f32(BatchPtr<float> M, int batch, int n, int m, long lo
 hipError_t launch_gather_f16(BatchPtr<const f16> Xin, int batch, int m, long long ld, int k,
                              const double* scale, f16* X, f16* XT, long long sX, int kp, int mp,
                              hipStream_t s);
+
+// The whole Gram Newton-Schulz (the schedule in cfg) for matrices whose Gram
+// side pads to 128, one workgroup per matrix: X_math [128][Lp] and its
+// transpose XT [Lp][128] per matrix at stride sX (halves), Y/YT the second
+// pair written by a restart.  The result goes to the fused update (W, idx,
+// lr; rows layout = X_math, or its transpose when tr) and/or Oout [k][m].
+hipError_t launch_gram_ns_small(f16* X, f16* XT, f16* Y, f16* YT, long long sX, int batch, int Lp,
+                                bool tr, const dion3_ns_cfg& cfg, BatchPtr<float> W, long long ldw,
+                                const int* idx, float lr, f16* Oout, int kval, int mval, int nrows,
+                                double trace_flops, hipStream_t s);
 
 }  // namespace dion3

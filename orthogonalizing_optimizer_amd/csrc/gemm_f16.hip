@@ -349,8 +349,14 @@ __global__ __launch_bounds__(C::NT, (C::BM == 256 ? 1 : 2)) void k_gemm(GemmArgs
           if (Db && gr < p.M && gc < p.N) dv = *(const half4*)(Db + (long long)gc * p.ldd + gr);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            val[e] = val[e] * p.alpha + p.beta * (float)dv[e];
+            val[e] = __builtin_fmaf(val[e], p.alpha, p.beta * (float)dv[e]);
             if (gr + e == gc) val[e] += p.gamma;
+            // Keep the fp32 result as written (round to fp32, then to fp16):
+            // otherwise the compiler may fuse the fma with the conversion
+            // into one mixed-precision fma that rounds once, in some
+            // elements only, and the fused small-matrix kernel would no
+            // longer match bit for bit.
+            asm("" : "+v"(val[e]));
           }
         }
 #pragma unroll

@@ -1,0 +1,433 @@
+// Whole Gram Newton-Schulz in one workgroup per matrix, for Gram sides of at
+// most 128 ("Dion3: Full-Stack Orthogonal Updates", agihunt.info, level-1
+// paragraph).  Small matrices would otherwise pay one launch per product
+// (about 20 per step, each a few microseconds of fixed cost); here R, Z, Q
+// and T stay in LDS (4 x 34 KB), 64-wide K slices of X stream through an
+// 18 KB staging buffer with a register prefetch of several slices, and the final
+// product feeds the row-sparse update directly (its output blocks staged in
+// the LDS matrices that are free by then).
+//
+// 4 waves in a 2 x 2 grid over the 128 x 128 output, each wave 64 x 64 as
+// 2 x 2 v_mfma_f32_32x32x16_f16.  Every element accumulates its k-slices in
+// increasing order and goes through the same fp32 epilogue as the tiled
+// kernels, and each symmetric result takes at (i, j) and (j, i) the value
+// the tiled kernels compute for the lower triangle, so the result equals
+// the tiled path bit for bit.  Symmetric outputs are written without a
+// mirror pass: the lower-left wave stores its block transposed (one 8-byte
+// run per 4 accumulators) into the upper-right quadrant, the upper-right
+// wave computes the lower-left block with its operands exchanged (exact
+// fp16 products commute) and stores it transposed into the lower-left
+// quadrant, and the two diagonal waves store their lower triangles both
+// ways.
+#include "../../include/dion3.h"
+#include "dion3_internal.h"
+
+namespace dion3 {
+namespace {
+
+constexpr int S = 128;           // padded Gram side
+constexpr int SL = S + 8;        // LDS row stride of the s x s matrices (halves)
+constexpr int BK = 64;           // K slice of X
+constexpr int XL = BK + 8;       // LDS row stride of the staging buffer
+constexpr int NT = 256;
+constexpr int kLdsHalves = 4 * S * SL + S * XL;   // 154 KB
+// Register prefetch depth (K slices held in registers) of the two streamed
+// products: four for the Gram; two for the multiply-back, whose epilogue
+// leaves no room for more without spills.
+constexpr int kGramDepth = 4;
+constexpr int kRectDepth = 2;
+
+typedef f16 half8 __attribute__((ext_vector_type(8)));
+typedef f16 half4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+struct SmallArgs {
+  // X_math (128 x Lp, row stride Lp) and its transpose (Lp x 128), then the
+  // second pair the restart writes into; per-matrix stride sX halves
+  f16 *X, *XT, *Y, *YT;
+  long long sX;
+  int Lp;
+  int tr;                        // X_math is the transpose of the selected rows (k > m)
+  dion3_ns_cfg cfg;
+  BatchPtr<float> W;
+  long long ldw;
+  const int* idx;
+  float lr;
+  f16* Oout;
+  int kval, mval, nrows;
+};
+
+// A wave of the 2 x 2 grid: quadrant (wm, wn) of the output.
+struct Wave {
+  int lane, tid, wm, wn;
+  __device__ bool diag() const { return wm == wn; }
+};
+
+__device__ __forceinline__ void zero_acc(floatx16 (&acc)[2][2]) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+}
+
+// acc[i][j] += P[pr + 32 i + ..][k] * Q[qr + 32 j + ..][k] over k < KN, both
+// operands K-contiguous in LDS with row strides LP, LQ.
+template <int LP, int LQ, int KN>
+__device__ __forceinline__ void mma(const f16* P, int pr, const f16* Q, int qr, int lane,
+                                    floatx16 (&acc)[2][2]) {
+  const f16* p_s = P + (pr + (lane & 31)) * LP + (lane >> 5) * 8;
+  const f16* q_s = Q + (qr + (lane & 31)) * LQ + (lane >> 5) * 8;
+  // fragments double-buffered: those of slice kk + 16 are requested before
+  // the MFMAs of slice kk, so the LDS latency hides behind them
+  half8 pf[2][2], qf[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) pf[0][i] = *(const half8*)(p_s + i * 32 * LP);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) qf[0][j] = *(const half8*)(q_s + j * 32 * LQ);
+#pragma unroll
+  for (int kk = 0; kk < KN; kk += 16) {
+    const int cb = (kk >> 4) & 1;
+    if (kk + 16 < KN) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) pf[cb ^ 1][i] = *(const half8*)(p_s + i * 32 * LP + kk + 16);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) qf[cb ^ 1][j] = *(const half8*)(q_s + j * 32 * LQ + kk + 16);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pf[cb][i], qf[cb][j], acc[i][j], 0, 0, 0);
+  }
+}
+
+// The symmetric product's operands for this wave (see the file comment).
+template <int LA, int KN>
+__device__ __forceinline__ void mma_sym(const f16* A, const f16* B, const Wave& w,
+                                        floatx16 (&acc)[2][2]) {
+  if (w.wm == 0 && w.wn == 1)
+    mma<LA, LA, KN>(B, 0, A, 64, w.lane, acc);
+  else
+    mma<LA, LA, KN>(A, w.wm * 64, B, w.wn * 64, w.lane, acc);
+}
+
+// Epilogue of a symmetric product into `out` (LDS, stride SL):
+// value = alpha acc + beta D + gamma I (POLY) or acc, rounded to fp32 and
+// then fp16, stored at both (r, c) and (c, r) as the lower element's value.
+// Accumulator (i, j, v) of lane l is element (p + v % 4, q) with
+// p = 32 i + 8 (v / 4) + 4 (l / 32) and q = 32 j + l % 32 (plus the wave's
+// row and column bases).  Every block is stored transposed (one 8-byte run
+// per 4 accumulators), which puts the lower values into the upper triangle;
+// the lower triangle of the off-diagonal quadrant comes from the swapped
+// wave, that of the strictly lower blocks of the diagonal quadrants from
+// direct stores, and that of the four diagonal 32 x 32 blocks from a short
+// copy of their upper halves after a barrier.  The caller's barrier follows.
+template <bool POLY>
+__device__ __forceinline__ void epi_sym(f16* out, const floatx16 (&acc)[2][2], float alpha,
+                                        const f16* D, float beta, float gamma, const Wave& w) {
+  const bool swap = (w.wm == 0 && w.wn == 1);
+  const int pr = swap ? 0 : w.wm * 64, qr = swap ? 64 : w.wn * 64;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      if (w.diag() && i < j) continue;          // upper block of a diagonal quadrant
+#pragma unroll
+      for (int v4 = 0; v4 < 4; ++v4) {
+        const int p = pr + i * 32 + 8 * v4 + 4 * (w.lane >> 5);
+        const int q = qr + j * 32 + (w.lane & 31);
+        float val[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) val[e] = acc[i][j][4 * v4 + e];
+        if (POLY) {
+          const half4 d = *(const half4*)(D + q * SL + p);   // D[p + e][q] (D symmetric)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            val[e] = __builtin_fmaf(val[e], alpha, beta * (float)d[e]);
+            if (p + e == q) val[e] += gamma;
+            asm("" : "+v"(val[e]));   // fp32 rounding, then fp16, as in the tiled kernels
+          }
+        }
+        half4 h;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) h[e] = (f16)val[e];
+        *(half4*)(out + q * SL + p) = h;
+        if (w.diag() && i > j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) out[(p + e) * SL + q] = h[e];
+      }
+    }
+  __syncthreads();
+  if (w.diag()) {
+    // lower triangle of the diagonal blocks (b, b), b = 2 wm, 2 wm + 1: the
+    // element (x, y), x > y, takes (y, x); the others rewrite their own value
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      const int base = w.wm * 64 + blk * 32;
+      f16 v[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int id = w.lane + 64 * e, x = id >> 5, y = id & 31;
+        const int sx = x > y ? y : x, sy = x > y ? x : y;
+        v[e] = out[(base + sx) * SL + base + sy];
+      }
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int id = w.lane + 64 * e, x = id >> 5, y = id & 31;
+        out[(base + x) * SL + base + y] = v[e];
+      }
+    }
+  }
+}
+
+// out = alpha A B + beta D + gamma I (POLY) or A B, all symmetric s x s in
+// LDS.  out may be A or B: the product is finished before anything is
+// written.
+template <bool POLY>
+__device__ __forceinline__ void symm_lds(f16* out, const f16* A, const f16* B, const f16* D,
+                                         float alpha, float beta, float gamma, const Wave& w) {
+  floatx16 acc[2][2];
+  zero_acc(acc);
+  mma_sym<SL, S>(A, B, w, acc);
+  __syncthreads();
+  epi_sym<POLY>(out, acc, alpha, D, beta, gamma, w);
+  __syncthreads();
+}
+
+// Streams 128-row x 64-half slices of a K-contiguous global matrix through
+// the LDS staging buffer.  Slice t covers rows row0(t).. and columns
+// col0(t)..; each thread moves 4 chunks of 8 halves.
+struct Slices {
+  const f16* src;
+  int ld;
+  __device__ __forceinline__ void load(half8 (&r)[4], int row0, int col0, int tid) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + NT * i;
+      r[i] = *(const half8*)(src + (long long)(row0 + (c >> 3)) * ld + col0 + (c & 7) * 8);
+    }
+  }
+};
+
+__device__ __forceinline__ void lds_store(f16* xs, const half8 (&r)[4], int tid) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = tid + NT * i;
+    *(half8*)(xs + (c >> 3) * XL + (c & 7) * 8) = r[i];
+  }
+}
+
+// Runs consume(t) for t = 0 .. n-1 with K slice t in the staging buffer,
+// the slices arriving through a ring of D register sets (D - 1 slices in
+// flight while one is multiplied).  coord(t, row0, col0) places slice t.
+template <int D, class Coord, class Consume>
+__device__ __forceinline__ void stream_slices(const Slices& sl, int n, f16* xs, int tid,
+                                              Coord coord, Consume consume) {
+  half8 r[D][4];
+#pragma unroll
+  for (int u = 0; u < D; ++u)
+    if (u < n) {
+      int r0, c0;
+      coord(u, r0, c0);
+      sl.load(r[u], r0, c0, tid);
+    }
+  for (int t = 0; t < n; t += D) {
+#pragma unroll
+    for (int u = 0; u < D; ++u) {
+      if (t + u < n) {
+        __syncthreads();                     // the previous slice is consumed
+        lds_store(xs, r[u], tid);
+        if (t + u + D < n) {
+          int r0, c0;
+          coord(t + u + D, r0, c0);
+          sl.load(r[u], r0, c0, tid);
+        }
+        __syncthreads();
+        consume(t + u);
+      }
+    }
+  }
+}
+
+// R = X X^T (K = Lp), X from global (rows layout, row stride Lp).
+__device__ __forceinline__ void gram_small(f16* R, f16* xs, const f16* X, int Lp, const Wave& w) {
+  const Slices sl = {X, Lp};
+  floatx16 acc[2][2];
+  zero_acc(acc);
+  stream_slices<kGramDepth>(
+      sl, Lp / BK, xs, w.tid, [](int t, int& r0, int& c0) { r0 = 0; c0 = t * BK; },
+      [&](int) { mma_sym<XL, BK>(xs, xs, w, acc); });
+  __syncthreads();
+  epi_sym<false>(R, acc, 1.0f, nullptr, 0.0f, 0.0f, w);
+  __syncthreads();
+}
+
+// One 8-wide chunk of O in rows layout (row orow, columns ocol..ocol+7)
+// goes to the row-sparse update: W[idx[orow]][ocol..] -= lr * O and
+// optionally O_out = O; the same arithmetic as the tiled kernels' update.
+__device__ __forceinline__ void sink8(const SmallArgs& p, int b, int orow, int ocol,
+                                      const half8& v) {
+  if (orow >= p.kval || ocol >= p.mval) return;
+  const bool full = ocol + 8 <= p.mval;
+  if (p.Oout) {
+    f16* o = p.Oout + ((long long)b * p.kval + orow) * p.mval + ocol;
+    if (full && ((uintptr_t)o & 15) == 0) {
+      *(half8*)o = v;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (ocol + e < p.mval) o[e] = v[e];
+    }
+  }
+  if (p.W.ptrs || p.W.base) {
+    const int row = p.idx[(long long)b * p.kval + orow];
+    if (row < 0 || row >= p.nrows) return;
+    float* wp = p.W.get(b) + (long long)row * p.ldw + ocol;
+    if (full && ((uintptr_t)wp & 15) == 0) {
+      float4 w0 = ((float4*)wp)[0], w1 = ((float4*)wp)[1];
+      w0.x = __builtin_fmaf(-p.lr, (float)v[0], w0.x);
+      w0.y = __builtin_fmaf(-p.lr, (float)v[1], w0.y);
+      w0.z = __builtin_fmaf(-p.lr, (float)v[2], w0.z);
+      w0.w = __builtin_fmaf(-p.lr, (float)v[3], w0.w);
+      w1.x = __builtin_fmaf(-p.lr, (float)v[4], w1.x);
+      w1.y = __builtin_fmaf(-p.lr, (float)v[5], w1.y);
+      w1.z = __builtin_fmaf(-p.lr, (float)v[6], w1.z);
+      w1.w = __builtin_fmaf(-p.lr, (float)v[7], w1.w);
+      ((float4*)wp)[0] = w0;
+      ((float4*)wp)[1] = w1;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (ocol + e < p.mval) wp[e] = __builtin_fmaf(-p.lr, (float)v[e], wp[e]);
+    }
+  }
+}
+
+// Y = Q X_math over the L side in 128-wide column blocks (two K slices of
+// X^T each).  Each 128 x 128 block is staged in two free s x s buffers (SA
+// in the math layout, SB transposed) and leaves in 16-byte runs: to Y and
+// YT (restart) or, in rows layout, into the update (final).
+__device__ __forceinline__ void rect_small(const f16* Q, f16* xs, f16* SA, f16* SB, const f16* XT,
+                                           int Lp, f16* Y, f16* YT, const SmallArgs& p, int b,
+                                           bool final_pass, const Wave& w) {
+  const Slices sl = {XT, S};
+  const bool rows = !final_pass || !p.tr, cols = !final_pass || p.tr;
+  floatx16 acc[2][2];
+  auto coord = [](int t, int& r0, int& c0) { r0 = (t >> 1) * S; c0 = (t & 1) * BK; };
+  auto consume = [&](int t) {
+    if ((t & 1) == 0) {
+      zero_acc(acc);
+      mma<SL, XL, BK>(Q, w.wm * 64, xs, w.wn * 64, w.lane, acc);
+      return;
+    }
+    mma<SL, XL, BK>(Q + BK, w.wm * 64, xs, w.wn * 64, w.lane, acc);
+    const int j0 = (t >> 1) * S;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+        for (int v4 = 0; v4 < 4; ++v4) {
+          const int r = w.wm * 64 + i * 32 + 8 * v4 + 4 * (w.lane >> 5);   // rows r..r+3
+          const int c = w.wn * 64 + jj * 32 + (w.lane & 31);               // block column
+          half4 h;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) h[e] = (f16)acc[i][jj][4 * v4 + e];
+          if (rows)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) SA[(r + e) * SL + c] = h[e];
+          if (cols) *(half4*)(SB + c * SL + r) = h;
+        }
+    __syncthreads();
+    // 128 rows x 16 chunks of 8 halves per layout, 8 chunks per thread
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int e = w.tid + NT * i, row = e >> 4, ch = (e & 15) * 8;
+      if (!final_pass) {
+        *(half8*)(Y + (long long)row * Lp + j0 + ch) = *(const half8*)(SA + row * SL + ch);
+        *(half8*)(YT + (long long)(j0 + row) * S + ch) = *(const half8*)(SB + row * SL + ch);
+      } else if (!p.tr) {   // rows layout = math layout: O[row][j0 + ch..]
+        sink8(p, b, row, j0 + ch, *(const half8*)(SA + row * SL + ch));
+      } else {              // rows layout = transposed: O[j0 + row][ch..]
+        sink8(p, b, j0 + row, ch, *(const half8*)(SB + row * SL + ch));
+      }
+    }
+  };
+  stream_slices<kRectDepth>(sl, 2 * (Lp / S), xs, w.tid, coord, consume);
+  __syncthreads();
+}
+
+__device__ __forceinline__ bool is_restart(const dion3_ns_cfg& c, int t) {
+  for (int i = 0; i < c.n_restart; ++i)
+    if (c.restart_at[i] == t) return true;
+  return false;
+}
+
+__global__ __launch_bounds__(NT, 1) void k_gram_ns_small(SmallArgs p) {
+  __shared__ __attribute__((aligned(16))) f16 lds[kLdsHalves];
+  f16* xs = lds + 4 * S * SL;
+  const int b = blockIdx.x;
+  Wave w;
+  w.tid = threadIdx.x;
+  w.lane = w.tid & 63;
+  w.wm = (w.tid >> 6) >> 1;
+  w.wn = (w.tid >> 6) & 1;
+  f16* X = p.X + (long long)b * p.sX;
+  f16* XT = p.XT + (long long)b * p.sX;
+  f16* Y = p.Y + (long long)b * p.sX;
+  f16* YT = p.YT + (long long)b * p.sX;
+
+  f16 *R = lds, *Z = lds + S * SL, *Q = lds + 2 * S * SL, *T = lds + 3 * S * SL;
+  gram_small(R, xs, X, p.Lp, w);
+  bool q_identity = true;
+  const int iters = p.cfg.iters;
+  for (int t = 1; t <= iters; ++t) {
+    if (is_restart(p.cfg, t)) {      // X <- Q X, R <- X X^T, Q <- I
+      if (!q_identity) {
+        rect_small(Q, xs, R, T, XT, p.Lp, Y, YT, p, b, false, w);
+        f16* tx = X; X = Y; Y = tx;
+        f16* tt = XT; XT = YT; YT = tt;
+      }
+      gram_small(R, xs, X, p.Lp, w);
+      q_identity = true;
+    }
+    const float a = p.cfg.abc[t - 1][0], bb = p.cfg.abc[t - 1][1], c = p.cfg.abc[t - 1][2];
+    symm_lds<true>(Z, R, R, R, c, bb, a, w);            // Z = a I + b R + c R^2
+    f16* Zv;
+    if (q_identity) {                                    // Q = I: adopt Z
+      f16* tmp = Q; Q = Z; Z = tmp;
+      Zv = Q;
+      q_identity = false;
+    } else {
+      symm_lds<false>(Q, Z, Q, nullptr, 1.0f, 0.0f, 0.0f, w);   // Q <- Z Q
+      Zv = Z;
+    }
+    if (t < iters && !is_restart(p.cfg, t + 1)) {      // R <- Z R Z
+      symm_lds<false>(T, Zv, R, nullptr, 1.0f, 0.0f, 0.0f, w);
+      symm_lds<false>(R, T, Zv, nullptr, 1.0f, 0.0f, 0.0f, w);
+    }
+  }
+  rect_small(Q, xs, R, T, XT, p.Lp, Y, YT, p, b, true, w);
+}
+
+}  // namespace
+
+hipError_t launch_gram_ns_small(f16* X, f16* XT, f16* Y, f16* YT, long long sX, int batch, int Lp,
+                                bool tr, const dion3_ns_cfg& cfg, BatchPtr<float> W, long long ldw,
+                                const int* idx, float lr, f16* Oout, int kval, int mval, int nrows,
+                                double trace_flops, hipStream_t s) {
+  if (Lp < S || Lp % S != 0 || batch < 1) return hipErrorInvalidValue;
+  SmallArgs p;
+  p.X = X; p.XT = XT; p.Y = Y; p.YT = YT; p.sX = sX;
+  p.Lp = Lp; p.tr = tr ? 1 : 0;
+  p.cfg = cfg;
+  p.W = W; p.ldw = ldw; p.idx = idx; p.lr = lr; p.Oout = Oout;
+  p.kval = kval; p.mval = mval; p.nrows = nrows;
+  TraceScope trace("gram_ns_fused_128", trace_flops, 0.0, s);
+  hipLaunchKernelGGL(k_gram_ns_small, dim3(batch), dim3(NT), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace dion3

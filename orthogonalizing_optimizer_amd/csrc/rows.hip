@@ -150,29 +150,33 @@ __device__ int block_exclusive_scan(int v, int* sh, int& total) {
 }
 
 // One workgroup per matrix.  Scores are non-negative doubles, so their bit
-// patterns order like the values; an MSB-first 8-bit radix select finds the
-// k-th largest key T exactly, then rows with key > T and the lowest-index
-// rows with key == T are taken, compacted in index order.
+// patterns order like the values; an MSB-first 8-bit radix select narrows
+// the k-th largest key down to a prefix P of its top bytes (mask): rows with
+// masked key > P are taken, and of the rows with masked key == P the
+// lowest-index need_eq ones, compacted in index order.  The select stops as
+// soon as every remaining candidate is taken (for distinct scores after two
+// or three bytes); the set is the same as with the full 64-bit threshold.
 __global__ __launch_bounds__(TK_THREADS) void k_topk(const double* __restrict__ l1,
                                                      const double* __restrict__ sq, int n, int k,
                                                      int* __restrict__ idx,
                                                      double* __restrict__ scale, double eps) {
   __shared__ unsigned hist[256];
+  __shared__ unsigned wsum_sh[4];
   __shared__ int scan_sh[TK_THREADS];
   __shared__ double red_sh[TK_THREADS];
   __shared__ unsigned long long prefix_sh;
-  __shared__ int rem_sh;
+  __shared__ int rem_sh, done_sh;
 
   const int b = blockIdx.x, tid = threadIdx.x;
   const double* __restrict__ sc = l1 + (long long)b * n;
   const double* __restrict__ q = sq + (long long)b * n;
   int* __restrict__ out = idx + (long long)b * k;
 
-  unsigned long long T = 0;
+  unsigned long long T = 0, mask = 0;
   int need_eq = 0;
   const bool all = (k >= n);
   if (!all) {
-    unsigned long long prefix = 0, mask = 0;
+    unsigned long long prefix = 0;
     int rem = k;
     for (int shift = 56; shift >= 0; shift -= 8) {
       for (int i = tid; i < 256; i += TK_THREADS) hist[i] = 0;
@@ -182,20 +186,37 @@ __global__ __launch_bounds__(TK_THREADS) void k_topk(const double* __restrict__ 
         if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
       }
       __syncthreads();
-      if (tid == 0) {
-        int cum = 0, d = 255;
-        for (; d > 0; --d) {
-          if (cum + (int)hist[d] >= rem) break;
-          cum += (int)hist[d];
+      // The digit: the largest d whose count of candidates with digit >= d
+      // reaches rem.  Thread t < 256 holds digit 255 - t; an inclusive scan
+      // over t (in-wave shuffles, then the wave totals) gives those counts.
+      const int d = 255 - tid;
+      unsigned h = 0, incl = 0;
+      if (tid < 256) {
+        h = hist[d];
+        incl = h;
+        for (int o = 1; o < 64; o <<= 1) {
+          const unsigned t = __shfl_up(incl, o, 64);
+          if ((tid & 63) >= o) incl += t;
         }
-        prefix_sh = prefix | ((unsigned long long)d << shift);
-        rem_sh = rem - cum;
+        if ((tid & 63) == 63) wsum_sh[tid >> 6] = incl;
+      }
+      __syncthreads();
+      if (tid < 256) {
+        for (int w = 0; w < (tid >> 6); ++w) incl += wsum_sh[w];
+        const unsigned excl = incl - h;       // candidates with a larger digit
+        if (excl < (unsigned)rem && incl >= (unsigned)rem) {   // exactly one thread
+          prefix_sh = prefix | ((unsigned long long)d << shift);
+          rem_sh = rem - (int)excl;
+          done_sh = (h == (unsigned)(rem - (int)excl));
+        }
       }
       __syncthreads();
       prefix = prefix_sh;
       rem = rem_sh;
       mask |= 255ull << shift;
+      const bool done = done_sh != 0;
       __syncthreads();
+      if (done) break;
     }
     T = prefix;
     need_eq = rem;
@@ -207,7 +228,7 @@ __global__ __launch_bounds__(TK_THREADS) void k_topk(const double* __restrict__ 
   int n_eq = 0;
   if (!all)
     for (int i = c0; i < c1; ++i)
-      n_eq += ((unsigned long long)__double_as_longlong(sc[i]) == T);
+      n_eq += (((unsigned long long)__double_as_longlong(sc[i]) & mask) == T);
   int tot;
   const int eq_start = all ? 0 : block_exclusive_scan(n_eq, scan_sh, tot);
   int n_sel = 0;
@@ -215,7 +236,7 @@ __global__ __launch_bounds__(TK_THREADS) void k_topk(const double* __restrict__ 
   for (int i = c0; i < c1; ++i) {
     bool take = all;
     if (!all) {
-      const unsigned long long key = (unsigned long long)__double_as_longlong(sc[i]);
+      const unsigned long long key = (unsigned long long)__double_as_longlong(sc[i]) & mask;
       take = key > T || (key == T && eqb < need_eq);
       eqb += (key == T);
     }
@@ -229,7 +250,7 @@ __global__ __launch_bounds__(TK_THREADS) void k_topk(const double* __restrict__ 
   for (int i = c0; i < c1; ++i) {
     bool take = all;
     if (!all) {
-      const unsigned long long key = (unsigned long long)__double_as_longlong(sc[i]);
+      const unsigned long long key = (unsigned long long)__double_as_longlong(sc[i]) & mask;
       take = key > T || (key == T && eqb < need_eq);
       eqb += (key == T);
     }

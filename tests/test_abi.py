@@ -61,7 +61,7 @@ def test_k_from_fraction_edges():
 def test_default_cfg():
     cfg = d3.default_cfg()
     assert cfg.iters == 5 and cfg.n_restart == 1 and cfg.restart_at[0] == 3
-    assert cfg.method == d3.NS_GRAM
+    assert cfg.method == d3.NS_GRAM and cfg.path == d3.PATH_AUTO
     assert abs(cfg.abc[0][0] - 3.4445) < 1e-6 and abs(cfg.abc[4][2] - 2.0315) < 1e-6
     assert abs(cfg.eps - 1e-7) < 1e-12
 
@@ -120,6 +120,24 @@ def test_step_rejects_bad_arguments_before_launch():
     assert _step(lib, cfg=bad) == ERR_ARG
     assert _step(lib, cfg=_cfg(eps=-1.0)) == ERR_ARG
     assert _step(lib, cfg=_cfg(method=2)) == ERR_ARG
+    assert _step(lib, cfg=_cfg(path=3)) == ERR_ARG
+    assert _step(lib, cfg=_cfg(path=-1)) == ERR_ARG
+
+
+def test_fused_path_needs_gram_side_of_at_most_128():
+    lib = d3.lib()
+    fused = _cfg(path=d3.PATH_FUSED)
+    # Gram side min(k, m) = 200 pads to 256: refused before any launch
+    assert _step(lib, n=400, m=300, ld=300, k=200, cfg=fused) == ERR_UNSUP
+    assert _step(lib, n=400, m=200, ld=200, k=300, cfg=fused) == ERR_UNSUP
+    # the standard method ignores the path
+    std = _cfg(path=d3.PATH_FUSED, method=d3.NS_STANDARD)
+    assert _step(lib, n=400, m=300, ld=300, k=200, cfg=std, ws=FAKE + 16) == ERR_WS
+    # min(k, m) <= 128 passes the path check and fails later on the workspace
+    assert _step(lib, n=400, m=300, ld=300, k=128, cfg=fused, ws=FAKE + 16) == ERR_WS
+    assert _step(lib, n=400, m=100, ld=100, k=300, cfg=fused, ws=FAKE + 16) == ERR_WS
+    X = FAKE
+    assert lib.dion3_gram_ns(X, X, 1, 129, 129, ctypes.byref(fused), FAKE, 1 << 30, None) == ERR_UNSUP
 
 
 def test_step_rejects_bad_workspace_before_launch():

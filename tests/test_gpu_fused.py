@@ -1,0 +1,141 @@
+"""The fused one-launch Gram iteration (Gram side min(k, m) <= 128, one
+workgroup per matrix): bitwise equal to the tiled launches on the same
+inputs, within the oracle tolerance, and under every schedule shape."""
+import sys
+
+import numpy as np
+import pytest
+
+from oracle import dion3_oracle as orc
+from tests.parity import O_TOL, check_step, rel
+from workloads import host_gaussian, host_lowrank
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+import orthogonalizing_optimizer_amd as d3  # noqa: E402
+
+DEV = "cuda:0"
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def run_step(W, M, k, lr, mu, cfg):
+    Wd, Md = dev(W), dev(M)
+    idx, O = d3.step(Wd, Md, k, lr, mu, cfg, return_idx=True, return_O=True)
+    torch.cuda.synchronize()
+    return Wd.cpu().numpy(), Md.cpu().numpy(), idx.cpu().numpy(), O.cpu().numpy()
+
+
+def same(a, b):
+    return np.asarray(a).tobytes() == np.asarray(b).tobytes()
+
+
+# (n, m, k): k <= m with the Gram on X X^T, k > m with X^T X (m <= 128),
+# ragged sides, one row, one column, long rows (L = 4096)
+FUSED_STEP_CASES = [(128, 512, 32), (300, 200, 75), (512, 512, 128), (1024, 96, 512),
+                    (200, 128, 200), (64, 4096, 16), (130, 1, 5), (1, 16, 1), (129, 129, 128)]
+
+
+@pytest.mark.parametrize("n,m,k", FUSED_STEP_CASES)
+def test_fused_step_equals_tiled_bitwise(n, m, k):
+    say("fused step", n, m, k)
+    W = host_gaussian((n, m), [40, n, m], std=0.02)
+    M = host_gaussian((n, m), [41, n, m])
+    ft = run_step(W, M, k, 0.04, 0.95, d3.ns_cfg(path=d3.PATH_FUSED))
+    tt = run_step(W, M, k, 0.04, 0.95, d3.ns_cfg(path=d3.PATH_TILED))
+    for a, b, what in zip(ft, tt, ("W", "M", "idx", "O")):
+        assert same(a, b), what
+    err = check_step(W, M, *ft, k, 0.04, 0.95)
+    print(f"{n}x{m} k={k}: fused O rel err {err:.3e}", flush=True)
+
+
+@pytest.mark.parametrize("iters,restarts", [(5, ()), (5, (2, 4)), (3, (2,)), (7, (3, 6)), (1, ()),
+                                            (16, (4, 8, 12, 16))])
+def test_fused_schedules(iters, restarts):
+    say("fused schedule", iters, restarts)
+    X = dev(host_gaussian((3, 96, 333), [42, iters]).astype(np.float16))
+    co = [orc.MUON_COEFFS] * iters
+    fused = d3.gram_ns(X, d3.ns_cfg(iters=iters, restart_at=restarts, coeffs=co,
+                                    path=d3.PATH_FUSED)).cpu().numpy()
+    tiled = d3.gram_ns(X, d3.ns_cfg(iters=iters, restart_at=restarts, coeffs=co,
+                                    path=d3.PATH_TILED)).cpu().numpy()
+    assert same(fused, tiled)
+    Xh = X.cpu().numpy()
+    if iters <= 7:    # the quintic's fixed point: longer schedules only stay near it
+        for b in range(3):
+            ref = orc.ns_gram(Xh[b].astype(np.float64), co, restarts)
+            assert rel(fused[b], ref) <= O_TOL
+
+
+def test_fused_transposed_gram_ns():
+    """k > m: the Gram is X^T X and the multiply-back runs along k."""
+    say("fused gram_ns k>m")
+    X = dev(host_gaussian((2, 700, 100), 43).astype(np.float16))
+    fused = d3.gram_ns(X, d3.ns_cfg(path=d3.PATH_FUSED)).cpu().numpy()
+    tiled = d3.gram_ns(X, d3.ns_cfg(path=d3.PATH_TILED)).cpu().numpy()
+    assert same(fused, tiled)
+    Xh = X.cpu().numpy()
+    for b in range(2):
+        assert rel(fused[b], orc.ns_gram(Xh[b].astype(np.float64), orc.default_coeffs(), (3,))) <= O_TOL
+
+
+def test_fused_restart_on_lowrank():
+    """Ill-conditioned input: the restart lives inside the fused kernel too."""
+    say("fused lowrank")
+    M = host_lowrank(100, 2048, 44)
+    Xn = (M.astype(np.float64) / np.linalg.norm(M.astype(np.float64))).astype(np.float16)
+    ref = orc.ns_gram(Xn.astype(np.float64), orc.default_coeffs(), (3,))
+    fused = d3.gram_ns(dev(Xn), d3.ns_cfg(path=d3.PATH_FUSED)).cpu().numpy()
+    tiled = d3.gram_ns(dev(Xn), d3.ns_cfg(path=d3.PATH_TILED)).cpu().numpy()
+    assert same(fused, tiled)
+    print(f"lowrank 100x2048 fused rel err {rel(fused, ref):.3e}", flush=True)
+    assert rel(fused, ref) <= O_TOL
+
+
+def test_fused_megabatch_equals_tiled_bitwise():
+    """Many matrices in one launch (one workgroup each)."""
+    say("fused megabatch")
+    B, n, m, k = 40, 256, 384, 64
+    Ws = [host_gaussian((n, m), [45, b], std=0.02) for b in range(B)]
+    Ms = [host_gaussian((n, m), [46, b]) for b in range(B)]
+    outs = []
+    for path in (d3.PATH_FUSED, d3.PATH_TILED):
+        Wd, Md = [dev(w) for w in Ws], [dev(x) for x in Ms]
+        idx, O = d3.step_megabatch(Wd, Md, k, 0.04, 0.95, d3.ns_cfg(path=path),
+                                   return_idx=True, return_O=True)
+        torch.cuda.synchronize()
+        outs.append(([w.cpu().numpy() for w in Wd], [x.cpu().numpy() for x in Md],
+                     idx.cpu().numpy(), O.cpu().numpy()))
+    (Wf, Mf, If, Of), (Wt, Mt, It, Ot) = outs
+    assert same(If, It) and same(Of, Ot)
+    for b in range(B):
+        assert same(Wf[b], Wt[b]) and same(Mf[b], Mt[b]), b
+    for b in (0, B - 1):
+        check_step(Ws[b], Ms[b], Wf[b], Mf[b], If[b], Of[b], k, 0.04, 0.95)
+
+
+def test_fused_trace_records_one_launch():
+    say("fused trace")
+    W = dev(host_gaussian((300, 500), 47, std=0.02))
+    M = dev(host_gaussian((300, 500), 48))
+    cfg = d3.ns_cfg(path=d3.PATH_FUSED)
+    d3.step(W, M, 75, 0.04, 0.95, cfg)
+    torch.cuda.synchronize()
+    d3.trace_enable(64)
+    try:
+        d3.step(W, M, 75, 0.04, 0.95, cfg)
+        recs = d3.trace_records()
+    finally:
+        d3.trace_disable()
+    assert [r[0] for r in recs] == ["row_score", "topk", "gather", "gram_ns_fused_128"]
+    s_, L_ = 75.0, 500.0
+    assert recs[3][2] == pytest.approx(6 * s_ * s_ * L_ + 14 * s_ ** 3)
+    assert recs[3][1] > 0

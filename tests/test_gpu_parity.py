@@ -339,11 +339,12 @@ def test_timing_trace_records_every_kernel():
     say("trace")
     W = dev(host_gaussian((300, 500), 27, std=0.02))
     M = dev(host_gaussian((300, 500), 28))
-    d3.step(W, M, 75, 0.04, 0.95)          # warm
+    tiled = d3.ns_cfg(path=d3.PATH_TILED)
+    d3.step(W, M, 75, 0.04, 0.95, tiled)          # warm
     torch.cuda.synchronize()
     d3.trace_enable(256)
     try:
-        d3.step(W, M, 75, 0.04, 0.95)
+        d3.step(W, M, 75, 0.04, 0.95, tiled)
         recs = d3.trace_records()
     finally:
         d3.trace_disable()
