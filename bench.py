@@ -240,18 +240,22 @@ def main():
     if not args.no_trace:
         d3.trace_enable(launches_per_step * args.steps + 64)
     stream = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # one event before the first step and one after each step: the mean over
+    # the whole timed region is the reported value; the per-step times give
+    # its spread
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
-    e0.record(stream)
-    for _ in range(args.steps):
+    evs[0].record(stream)
+    for i in range(args.steps):
         if graph is not None:
             graph.replay()
         else:
             one_step()
-    e1.record(stream)
+        evs[i + 1].record(stream)
     torch.cuda.synchronize()
-    ms_total = e0.elapsed_time(e1)
+    ms_total = evs[0].elapsed_time(evs[-1])
     ms_per_step = ms_total / args.steps
+    step_ms = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
 
     # per-kernel statistics over the timed region
     kernels = {}
@@ -381,6 +385,9 @@ def main():
             "hip_graph": bool(args.graph),
         },
         "matrices_per_s": round(wl.n_matrices / (ms_per_step * 1e-3), 1),
+        "step_ms": {"median": round(float(np.median(step_ms)), 4),
+                    "p10": round(float(np.percentile(step_ms, 10)), 4),
+                    "p90": round(float(np.percentile(step_ms, 90)), 4)},
         "gram_ns_tflops": round(gram_tflops, 2) if gram_tflops else None,
         "gram_ns_frac_fp16_peak": round(gram_tflops / FP16_PEAK_TFLOPS, 4) if gram_tflops else None,
         "effective_standard_ns_tflops": round(eff_flops / (ms_per_step * 1e-3) / 1e12, 2),

@@ -108,6 +108,10 @@ typedef struct {
  * (3.4445, -4.7750, 2.0315), one restart at iteration 3, eps = 1e-7. */
 DION3_API void dion3_ns_cfg_default(dion3_ns_cfg* cfg);
 
+/* sizeof(dion3_ns_cfg) as this library was built, so that a binding can
+ * check its own copy of the struct before passing one. */
+DION3_API size_t dion3_ns_cfg_size(void);
+
 /* k = ceil(f * n) (level-3 paragraph of the agihunt summary), computed in
  * exact rationals: f is read as the nearest fraction with denominator
  * <= 2^20 (so 0.07 * 100 gives 7, not 8).  The result is clamped to [1, n].

@@ -56,6 +56,7 @@ def _declare(lib):
     vp, i32, i64, f32, f64, sz = c.c_void_p, c.c_int32, c.c_int64, c.c_float, c.c_double, c.c_size_t
     sig = {
         "dion3_version": (c.c_int, []),
+        "dion3_ns_cfg_size": (sz, []),
         "dion3_ns_cfg_default": (None, [c.POINTER(NsCfg)]),
         "dion3_k_from_fraction": (i64, [f64, i64]),
         "dion3_workspace_size": (c.c_int, [i32, i64, i64, i64, c.POINTER(sz)]),
@@ -86,7 +87,7 @@ def _declare(lib):
     return lib
 
 
-EXPORTED = ("dion3_version", "dion3_ns_cfg_default", "dion3_k_from_fraction",
+EXPORTED = ("dion3_version", "dion3_ns_cfg_size", "dion3_ns_cfg_default", "dion3_k_from_fraction",
             "dion3_workspace_size", "dion3_row_select", "dion3_gram_ns", "dion3_step",
             "dion3_step_megabatch", "dion3_step_accum", "dion3_step_megabatch_accum",
             "dion3_syrk_f16", "dion3_symm_f16", "dion3_trace_enable",
@@ -101,7 +102,11 @@ def lib():
         if not os.path.exists(LIB_PATH):
             raise ImportError(f"{LIB_PATH} is missing: build it with "
                               "`python -m orthogonalizing_optimizer_amd.build`")
-        _lib = _declare(ctypes.CDLL(LIB_PATH))
+        loaded = _declare(ctypes.CDLL(LIB_PATH))
+        if loaded.dion3_ns_cfg_size() != ctypes.sizeof(NsCfg):
+            raise ImportError(f"{LIB_PATH}: dion3_ns_cfg is {loaded.dion3_ns_cfg_size()} bytes, "
+                              f"the binding's NsCfg {ctypes.sizeof(NsCfg)}: rebuild the library")
+        _lib = loaded
     return _lib
 
 
@@ -192,7 +197,21 @@ class Workspace:
         return base + off, self.buf.numel() - off
 
 
-_default_ws = Workspace()
+# Default workspaces, one per (device, stream): calls on different streams
+# never share scratch memory.  Each is kept (and grown as needed) until the
+# process ends; pass ``ws`` to manage the memory yourself.
+_default_ws: dict = {}
+
+
+def _ws_for(ws: Optional[Workspace], device) -> Workspace:
+    if ws is not None:
+        return ws
+    torch = _torch()
+    key = (str(device), torch.cuda.current_stream(device).cuda_stream)
+    w = _default_ws.get(key)
+    if w is None:
+        w = _default_ws[key] = Workspace()
+    return w
 
 
 def _req(t, dtype, name):
@@ -214,7 +233,7 @@ def row_select(M, k: int, return_scores: bool = False, ws: Optional[Workspace] =
     ld = Mb.stride(1)
     idx = torch.empty((B, k), dtype=torch.int32, device=M.device)
     scores = torch.empty((B, n), dtype=torch.float64, device=M.device) if return_scores else None
-    p, nb = (ws or _default_ws).get(workspace_size(B, n, m, k), M.device)
+    p, nb = _ws_for(ws, M.device).get(workspace_size(B, n, m, k), M.device)
     _check(lib().dion3_row_select(Mb.data_ptr(), B, n, m, ld, k, idx.data_ptr(), _ptr(scores), p,
                                   nb, _stream(M.device)), "dion3_row_select")
     if M.dim() == 2:
@@ -232,7 +251,7 @@ def gram_ns(X, cfg: Optional[NsCfg] = None, ws: Optional[Workspace] = None):
     Xb = X.unsqueeze(0) if X.dim() == 2 else X
     B, k, m = Xb.shape
     O = torch.empty_like(Xb)
-    p, nb = (ws or _default_ws).get(workspace_size(B, k, m, k), X.device)
+    p, nb = _ws_for(ws, X.device).get(workspace_size(B, k, m, k), X.device)
     _check(lib().dion3_gram_ns(Xb.data_ptr(), O.data_ptr(), B, k, m,
                                ctypes.byref(cfg) if cfg is not None else None, p, nb,
                                _stream(X.device)), "dion3_gram_ns")
@@ -257,7 +276,7 @@ def step(W, M, k: int, lr: float, mu: float, cfg: Optional[NsCfg] = None,
     n, m = M.shape
     idx = torch.empty(k, dtype=torch.int32, device=M.device) if return_idx else None
     O = torch.empty((k, m), dtype=torch.float16, device=M.device) if return_O else None
-    p, nb = (ws or _default_ws).get(workspace_size(1, n, m, k), M.device)
+    p, nb = _ws_for(ws, M.device).get(workspace_size(1, n, m, k), M.device)
     c = ctypes.byref(cfg) if cfg is not None else None
     if G is None:
         _check(lib().dion3_step(W.data_ptr(), M.data_ptr(), n, m, M.stride(0), k, lr, mu, c,
@@ -299,7 +318,7 @@ def step_megabatch(Ws, Ms, k: int, lr: float, mu: float, cfg: Optional[NsCfg] = 
         ptrs = (pointer_array(Ws, dev), pointer_array(Ms, dev))
     idx = torch.empty((B, k), dtype=torch.int32, device=dev) if return_idx else None
     O = torch.empty((B, k, m), dtype=torch.float16, device=dev) if return_O else None
-    p, nb = (ws or _default_ws).get(workspace_size(B, n, m, k), dev)
+    p, nb = _ws_for(ws, dev).get(workspace_size(B, n, m, k), dev)
     c = ctypes.byref(cfg) if cfg is not None else None
     if Gs is None and gptrs is None:
         _check(lib().dion3_step_megabatch(ptrs[0].data_ptr(), ptrs[1].data_ptr(), B, n, m, stride[0],

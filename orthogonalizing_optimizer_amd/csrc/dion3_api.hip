@@ -455,6 +455,8 @@ extern "C" {
 
 int dion3_version(void) { return 1; }
 
+size_t dion3_ns_cfg_size(void) { return sizeof(dion3_ns_cfg); }
+
 void dion3_ns_cfg_default(dion3_ns_cfg* cfg) {
   if (!cfg) return;
   memset(cfg, 0, sizeof(*cfg));

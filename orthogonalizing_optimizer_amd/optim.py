@@ -39,13 +39,16 @@ class Dion3Step:
         for w, m in zip(weights, momenta):
             if w.dim() != 2 or w.shape != m.shape:
                 raise ValueError("Dion3 steps 2-D matrices with same-shape momentum")
+            if w.stride() != m.stride() or w.stride(1) != 1 or w.device != m.device:
+                raise ValueError("W and M must share strides and device, with contiguous rows")
             key = (tuple(w.shape), w.stride(0), str(w.device))
             self.groups.setdefault(key, {"W": [], "M": []})
             self.groups[key]["W"].append(w)
             self.groups[key]["M"].append(m)
-        self.ws = _lib.Workspace()
+        self.ws: Dict[str, _lib.Workspace] = {}     # one per device, shared by its groups
         for key, g in self.groups.items():
             dev = g["M"][0].device
+            g["ws"] = self.ws.setdefault(str(dev), _lib.Workspace())
             g["ptrs"] = (_lib.pointer_array(g["W"], dev), _lib.pointer_array(g["M"], dev))
             g["k"] = _lib.k_from_fraction(float(self.fraction), key[0][0])
 
@@ -65,4 +68,4 @@ class Dion3Step:
         for key, g in self.groups.items():
             Gs = [gmap[id(w)] for w in g["W"]] if gmap is not None else None
             _lib.step_megabatch(g["W"], g["M"], g["k"], self.lr_eff, self.mu, self.cfg,
-                                ws=self.ws, ptrs=g["ptrs"], Gs=Gs)
+                                ws=g["ws"], ptrs=g["ptrs"], Gs=Gs)

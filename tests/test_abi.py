@@ -184,3 +184,15 @@ def test_binding_refuses_cpu_tensors():
         d3.step(torch.zeros(4, 4), torch.zeros(4, 4), 2, 0.1, 0.9)
     with pytest.raises(TypeError):
         d3.gram_ns(torch.zeros(4, 4, dtype=torch.float16))
+
+
+def test_binding_struct_matches_library():
+    assert d3.lib().dion3_ns_cfg_size() == ctypes.sizeof(d3.NsCfg)
+
+
+def test_dion3step_rejects_mismatched_strides_before_any_device_work():
+    torch = pytest.importorskip("torch")
+    W = torch.zeros(4, 6)
+    M = torch.zeros(6, 4).t()          # same shape, column-major strides
+    with pytest.raises(ValueError):
+        d3.Dion3Step([W], [M])

@@ -157,6 +157,28 @@ def test_step_standard_method(n, m, k):
     assert M1[mask].tobytes() == ref["M"][mask].tobytes()
 
 
+def test_default_workspaces_are_per_stream():
+    """Calls on two streams without an explicit workspace must not share
+    scratch memory: results equal the sequential ones bit for bit."""
+    say("default workspace per stream")
+    X1 = dev(host_gaussian((3, 200, 700), 60).astype(np.float16))
+    X2 = dev(host_gaussian((3, 200, 700), 61).astype(np.float16))
+    ref1, ref2 = d3.gram_ns(X1).cpu().numpy(), d3.gram_ns(X2).cpu().numpy()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    outs = []
+    for _ in range(3):
+        with torch.cuda.stream(s1):
+            o1 = d3.gram_ns(X1)
+        with torch.cuda.stream(s2):
+            o2 = d3.gram_ns(X2)
+        outs.append((o1, o2))
+    torch.cuda.synchronize()
+    for o1, o2 in outs:
+        assert o1.cpu().numpy().tobytes() == ref1.tobytes()
+        assert o2.cpu().numpy().tobytes() == ref2.tobytes()
+
+
 def test_gram_ns_deterministic():
     say("gram_ns twice")
     X = dev(host_gaussian((3, 200, 700), 6).astype(np.float16))
