@@ -8,7 +8,8 @@ import sys
 import numpy as np
 import pytest
 
-from tests.parity import check_step
+from oracle import dion3_oracle as orc
+from tests.parity import check_step, rel
 from workloads import MU, WORKLOADS, device_workload
 
 pytestmark = pytest.mark.gpu
@@ -36,8 +37,16 @@ def test_fullsize_group(wl_name, group):
     idx, O = d3.step_megabatch(Ws, Ms, k, wl.lr, MU, return_idx=True, return_O=True)
     torch.cuda.synchronize()
     for j in picks:
-        err = check_step(W0[j], M0[j], Ws[j].cpu().numpy(), Ms[j].cpu().numpy(),
-                         idx[j].cpu().numpy(), O[j].cpu().numpy(), k, wl.lr, MU)
-        print(f"{wl.name} group {group} matrix {j}: k={k}, O rel err {err:.3e}", flush=True)
+        S, Oj = idx[j].cpu().numpy(), O[j].cpu().numpy()
+        err = check_step(W0[j], M0[j], Ws[j].cpu().numpy(), Ms[j].cpu().numpy(), S, Oj, k,
+                         wl.lr, MU)
+        # the kernel's own share of the error: the oracle on the fp16 X the
+        # gather writes (fp32 rows times fp32(1 / (||X|| + eps)), rounded)
+        Xs = M0[j][S]
+        scale = 1.0 / (np.sqrt(np.sum(Xs.astype(np.float64) ** 2)) + 1e-7)
+        X16 = (Xs * np.float32(scale)).astype(np.float16).astype(np.float64)
+        e16 = rel(Oj, orc.ns_gram(X16, orc.default_coeffs(), (3,)))
+        print(f"{wl.name} group {group} matrix {j}: k={k}, O rel err {err:.3e} against the "
+              f"fp64 oracle, {e16:.3e} against the oracle on the fp16-rounded input", flush=True)
     del Ws, Ms, idx, O
     torch.cuda.empty_cache()
