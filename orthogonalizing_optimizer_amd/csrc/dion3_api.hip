@@ -73,8 +73,14 @@ bool dims_ok(long long v) { return v >= 1 && v <= DION3_MAX_DIM; }
 // The products address each matrix through a buffer resource with 32-bit
 // byte offsets, so every padded per-matrix operand must stay below 2^31 bytes.
 constexpr long long kMaxOperandBytes = 1LL << 31;
+// The grid of every product (128-wide tiles at most, times the batch) must
+// also fit a launch, checked here so that no kernel runs before a refusal.
+constexpr long long kMaxGrid = 0x7fffffffLL;
 bool plan_fits(const Plan& P) {
-  return P.kp * P.mp * 2 < kMaxOperandBytes && P.sp * P.sp * 2 < kMaxOperandBytes;
+  const long long ts = P.sp / kTile, tl = P.Lp / kTile;
+  const long long tiles = ts * (ts + 1) / 2 > ts * tl ? ts * (ts + 1) / 2 : ts * tl;
+  return P.kp * P.mp * 2 < kMaxOperandBytes && P.sp * P.sp * 2 < kMaxOperandBytes &&
+         tiles * P.B <= kMaxGrid;
 }
 
 dion3_status check_cfg(const dion3_ns_cfg* c) {

@@ -82,6 +82,10 @@ def test_workspace_size_layout():
     # padded selected block of 2^31 bytes or more: rejected (32-bit buffer offsets)
     assert d3.lib().dion3_workspace_size(1, 1 << 16, 1 << 15, 1 << 15, ctypes.byref(out)) == ERR_UNSUP
     assert d3.lib().dion3_workspace_size(1, 1 << 16, 1 << 14, 1 << 15, ctypes.byref(out)) == 0
+    # a product grid beyond 2^31 - 1 blocks (65408 128-tiles per matrix times 65535 matrices):
+    # refused up front, before any kernel could run
+    assert d3.lib().dion3_workspace_size(65535, 16384, 65408, 16384, ctypes.byref(out)) == ERR_UNSUP
+    assert d3.lib().dion3_workspace_size(1, 16384, 65408, 16384, ctypes.byref(out)) == 0
 
 
 def _cfg(**kw):
