@@ -54,7 +54,9 @@ typedef enum {
   DION3_ERR_UNSUPPORTED = -3,  /* a shape beyond the library's limits: a dimension above
                                   DION3_MAX_DIM, or a zero-padded per-matrix block (the selected
                                   rows, padded to multiples of 128, or the Gram side) of 2^31
-                                  bytes or more */
+                                  bytes or more, or a product whose 128 x 128 output tiles over
+                                  the whole batch exceed 2^31 - 1; with DION3_PATH_FUSED, also a
+                                  Gram side min(k, m) above 128 */
   DION3_ERR_HIP = -4           /* a HIP call or launch failed; see dion3_last_hip_error() */
 } dion3_status;
 
