@@ -7,9 +7,9 @@ from ._lib import (NS_GRAM, NS_STANDARD, PATH_AUTO, PATH_FUSED, PATH_TILED, Dion
                    ns_cfg, pointer_array, row_select, status_string, step, step_megabatch,
                    symm_f16, syrk_f16, trace_disable, trace_enable, trace_records, trace_reset,
                    workspace_size)
-from .optim import Dion3Step
+from .optim import Dion3, Dion3Step
 
 __all__ = ["NS_GRAM", "NS_STANDARD", "PATH_AUTO", "PATH_FUSED", "PATH_TILED", "Dion3Error", "NsCfg", "Workspace", "default_cfg", "gram_ns", "k_from_fraction", "lib",
            "ns_cfg", "pointer_array", "row_select", "status_string", "step", "step_megabatch",
            "symm_f16", "syrk_f16", "trace_disable", "trace_enable", "trace_records", "trace_reset",
-           "workspace_size", "Dion3Step"]
+           "workspace_size", "Dion3", "Dion3Step"]

@@ -69,3 +69,64 @@ class Dion3Step:
             Gs = [gmap[id(w)] for w in g["W"]] if gmap is not None else None
             _lib.step_megabatch(g["W"], g["M"], g["k"], self.lr_eff, self.mu, self.cfg,
                                 ws=g["ws"], ptrs=g["ptrs"], Gs=Gs)
+
+
+def _optimizer_base():
+    import torch
+    return torch.optim.Optimizer
+
+
+class Dion3(_optimizer_base()):
+    """torch.optim-style Dion3 for 2-D fp32 parameters.
+
+    Each parameter p with a gradient keeps a momentum buffer M (fp32, zero at
+    first).  ``step()`` runs, per parameter group and per (shape, strides,
+    device), one megabatched library call: M <- M + grad (fused into the row
+    scoring), top-k row selection with k = ceil(f n), Gram Newton-Schulz on
+    the selected rows, p[S] -= lr / sqrt(f) * O and M[S] *= mu ("Dion3:
+    Full-Stack Orthogonal Updates", agihunt.info, level-3 paragraph: error
+    feedback keeps the unselected rows of M for a later step; level-4:
+    megabatching by shape).  Parameters that are not 2-D fp32 matrices with
+    contiguous rows are refused: route them to another optimizer.
+    """
+
+    def __init__(self, params, lr: float = 0.02, fraction=Fraction(1, 4), mu: float = 0.95,
+                 cfg: Optional[_lib.NsCfg] = None):
+        if lr <= 0 or not (0 < float(fraction) <= 1) or not (0 <= mu <= 1):
+            raise ValueError("need lr > 0, 0 < fraction <= 1 and 0 <= mu <= 1")
+        super().__init__(params, dict(lr=lr, fraction=fraction, mu=mu))
+        import torch
+        for group in self.param_groups:
+            for p in group["params"]:
+                if p.dim() != 2 or p.dtype != torch.float32 or p.stride(1) != 1:
+                    raise ValueError("Dion3 steps 2-D fp32 matrices with contiguous rows")
+        self.cfg = cfg
+        self._ws: Dict[str, _lib.Workspace] = {}
+
+    def step(self, closure=None):
+        import torch
+        loss = None
+        if closure is not None:
+            with torch.enable_grad():
+                loss = closure()
+        with torch.no_grad():
+            for group in self.param_groups:
+                f = float(group["fraction"])
+                buckets: "OrderedDict[Tuple, List]" = OrderedDict()
+                for p in group["params"]:
+                    if p.grad is None:
+                        continue
+                    if p.grad.stride() != p.stride():
+                        raise ValueError("a gradient must have its parameter's strides")
+                    st = self.state[p]
+                    if "momentum" not in st:   # the parameter's own strides
+                        st["momentum"] = torch.empty_strided(p.shape, p.stride(), dtype=p.dtype,
+                                                             device=p.device).zero_()
+                    buckets.setdefault((tuple(p.shape), p.stride(), str(p.device)), []).append(p)
+                for (shape, _, dev), ps in buckets.items():
+                    k = _lib.k_from_fraction(f, shape[0])
+                    ws = self._ws.setdefault(dev, _lib.Workspace())
+                    _lib.step_megabatch(ps, [self.state[p]["momentum"] for p in ps], k,
+                                        group["lr"] / math.sqrt(f), group["mu"], self.cfg, ws=ws,
+                                        Gs=[p.grad for p in ps])
+        return loss

@@ -200,3 +200,20 @@ def test_dion3step_rejects_mismatched_strides_before_any_device_work():
     M = torch.zeros(6, 4).t()          # same shape, column-major strides
     with pytest.raises(ValueError):
         d3.Dion3Step([W], [M])
+
+
+def test_dion3_optimizer_refuses_what_it_cannot_step():
+    torch = pytest.importorskip("torch")
+    with pytest.raises(ValueError):
+        d3.Dion3([torch.nn.Parameter(torch.zeros(4))])              # not a matrix
+    with pytest.raises(ValueError):
+        d3.Dion3([torch.nn.Parameter(torch.zeros(4, 6, dtype=torch.float64))])
+    with pytest.raises(ValueError):
+        d3.Dion3([torch.nn.Parameter(torch.zeros(6, 4).t())])       # columns contiguous
+    with pytest.raises(ValueError):
+        d3.Dion3([torch.nn.Parameter(torch.zeros(4, 6))], fraction=0.0)
+    p = torch.nn.Parameter(torch.zeros(4, 6))
+    opt = d3.Dion3([p])
+    p.grad = torch.ones(4, 6)
+    with pytest.raises(TypeError):                                  # host tensors: no CPU path
+        opt.step()

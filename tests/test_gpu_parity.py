@@ -402,3 +402,32 @@ def test_dion3step_groups_by_shape():
         ref = orc.dion3_step(W0[i], M0[i], k, 0.04, 0.9)
         assert rel(Ws[i].cpu().numpy() - W0[i], ref["W"] - W0[i]) <= O_TOL
         assert Ms[i].cpu().numpy().tobytes() == ref["M"].tobytes()
+
+
+def test_dion3_optimizer_two_steps():
+    """torch.optim-style Dion3: momentum accumulates the gradient (M <- M + G),
+    then the step; two steps on two shapes against the oracle."""
+    say("Dion3 optimizer")
+    shapes = [(96, 64), (64, 96), (96, 64)]
+    params = [torch.nn.Parameter(dev(host_gaussian(sh, [80, i], std=0.02)))
+              for i, sh in enumerate(shapes)]
+    opt = d3.Dion3(params, lr=0.02, fraction=0.25, mu=0.9)
+    W = [p.detach().cpu().numpy().copy() for p in params]
+    M = [np.zeros(sh, np.float32) for sh in shapes]
+    for it in range(2):
+        G = [host_gaussian(sh, [81, it, i]) for i, sh in enumerate(shapes)]
+        for p, g in zip(params, G):
+            p.grad = dev(g)
+        opt.step()
+        torch.cuda.synchronize()
+        for i, (p, sh) in enumerate(zip(params, shapes)):
+            k = orc.k_from_fraction(0.25, sh[0])
+            ref = orc.dion3_step(W[i], M[i] + G[i], k, 0.04, 0.9)
+            W1 = p.detach().cpu().numpy()
+            M1 = opt.state[p]["momentum"].cpu().numpy()
+            changed = np.nonzero(np.any(W1 != W[i], axis=1))[0]
+            assert np.array_equal(changed, ref["S"]), (it, i)
+            assert M1.tobytes() == ref["M"].tobytes(), (it, i)
+            assert rel(W1 - W[i], ref["W"] - W[i]) <= O_TOL, (it, i)
+            W[i], M[i] = W1, M1
+
