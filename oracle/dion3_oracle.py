@@ -44,9 +44,13 @@ Readings where the pages are silent (each is also a row of the design notes):
   buffer and only the selected ones are decayed after use ([AGI] level-3
   paragraph), so the buffer is a running sum.
 
+* per-neuron normalization (no formula on the pages): see
+  normalize_neurons.
+
 Parity pins for every function live in tests/test_oracle.py (SVD polar
 factor, the scalar Newton-Schulz map on singular values, Gram NS against
-standard NS, brute-force selection, the pages' FLOP figures).
+standard NS, brute-force selection, the pages' FLOP figures, and for the
+normalization its invariants and a hand-worked example).
 """
 from __future__ import annotations
 
@@ -225,13 +229,57 @@ def ns_gram(X, coeffs: Sequence[Tuple[float, float, float]],
     return O.T if tr else O
 
 
+# ------------------------------------------------------------- per-neuron normalization
+
+def normalize_neurons(O: np.ndarray, S: np.ndarray, V: np.ndarray, beta2: float,
+                      eps: float) -> Tuple[np.ndarray, np.ndarray]:
+    """Per-neuron normalization of the orthogonalized update.
+
+    The pages say only that Dion3 inherits NorMuon's per-neuron normalization
+    ([QSA] section "Dion3's fastest path is a combined systems stack") and
+    that it runs in float32 ([AGI] limitations paragraph); they give no
+    formula.  Reading taken here, for the rows S of one matrix with the
+    orthogonalized rows O (k x m) and a float32 second-moment state V (one
+    entry per row of the matrix):
+
+      q_i = mean_j O_ij^2                       (mean square of row i)
+      V[S_i] <- beta2 V[S_i] + (1 - beta2) q_i  (stored as float32; rows
+                                                 outside S keep their state)
+      U_i = O_i / (sqrt(V[S_i]) + eps)
+      U  <- U ||O||_F / ||U||_F                 (the update keeps O's norm, so
+                                                 the step size keeps its
+                                                 meaning, eta ~ 1/sqrt(f))
+
+    Returns (U, V') with U the update that takes O's place.
+    """
+    O = np.asarray(O, np.float64)
+    S = np.asarray(S, np.int64)
+    V = np.asarray(V)
+    if V.dtype != np.float32 or V.ndim != 1:
+        raise TypeError("V must be a float32 vector")
+    if not (0.0 <= beta2 < 1.0) or not eps >= 0.0:
+        raise ValueError("need 0 <= beta2 < 1 and eps >= 0")
+    k, m = O.shape
+    if S.shape != (k,):
+        raise ValueError("one state row per row of O")
+    sq = (O * O).sum(axis=1)
+    v = (beta2 * V[S].astype(np.float64) + (1.0 - beta2) * (sq / m)).astype(np.float32)
+    V_new = V.copy()
+    V_new[S] = v
+    U = O / (np.sqrt(v.astype(np.float64)) + eps)[:, None]
+    nU = np.linalg.norm(U)
+    U = U * (np.sqrt(sq.sum()) / nU) if nU > 0 else np.zeros_like(O)
+    return U, V_new
+
+
 # ------------------------------------------------------------- the step
 
 def dion3_step(W: np.ndarray, M: np.ndarray, k: int, lr: float, mu: float,
                coeffs: Optional[Sequence[Tuple[float, float, float]]] = None,
                restart_at: Iterable[int] = DEFAULT_RESTART_AT, eps: float = DEFAULT_EPS,
                S_override: Optional[np.ndarray] = None, method: str = "gram",
-               G: Optional[np.ndarray] = None) -> dict:
+               G: Optional[np.ndarray] = None,
+               norm: Optional[Tuple[np.ndarray, float, float]] = None) -> dict:
     """One Dion3 step on one matrix ([AGI] level-3 paragraph, [ABS]).
 
     1. score rows by l1 and keep the k best (ties: lowest index);
@@ -242,6 +290,8 @@ def dion3_step(W: np.ndarray, M: np.ndarray, k: int, lr: float, mu: float,
        rows untouched (error feedback keeps them for later steps).
 
     With a gradient G, the buffer first accumulates it: M <- fl32(M + G).
+    With norm = (V, beta2, eps) the update is the per-neuron normalized U of
+    normalize_neurons in place of O, and the new state is returned as "V".
 
     Returns W' (fp64 on S, the input bytes elsewhere), M' (fp32), S, O and
     the normalized fp64 submatrix that entered the iteration.
@@ -280,11 +330,18 @@ def dion3_step(W: np.ndarray, M: np.ndarray, k: int, lr: float, mu: float,
     else:
         raise ValueError(method)
 
+    out = {}
+    U = O
+    if norm is not None:
+        V, beta2, neps = norm
+        U, out["V"] = normalize_neurons(O, S, V, beta2, neps)
+        out["U"] = U
     W_new = W.astype(np.float64)
-    W_new[S] = W_new[S] - float(lr) * O
+    W_new[S] = W_new[S] - float(lr) * U
     M_new = M.copy()
     mu32 = np.float64(np.float32(mu))
     M_new[S] = (mu32 * M[S].astype(np.float64)).astype(np.float32)
-    return {"W": W_new, "M": M_new, "S": S, "O": O, "l1": l1, "sq": sq,
-            "X": _normalize(X, eps)}
+    out.update({"W": W_new, "M": M_new, "S": S, "O": O, "l1": l1, "sq": sq,
+                "X": _normalize(X, eps)})
+    return out
 

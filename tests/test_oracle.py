@@ -315,3 +315,120 @@ def test_flop_figures_of_the_pages():
     # restart at iteration 3 costs exactly 3 (alpha - 1) s^3 more
     fr, _ = _flops(s, L, (3,))
     assert fr - fg == d["restart_extra_flops_coeff"] * (d["alpha"] - 1) * s ** 3
+
+
+# ------------------------------------------------------------- per-neuron normalization
+# (no formula on the pages: the reading is stated in normalize_neurons; these
+# pins fix its invariants and one example worked by hand)
+
+def _norm_case(seed, k=6, m=10, n=9):
+    rng = np.random.default_rng(seed)
+    O = rng.standard_normal((k, m))
+    S = np.sort(rng.choice(n, size=k, replace=False))
+    V = rng.uniform(0.01, 1.0, n).astype(np.float32)
+    return O, S, V
+
+
+def test_normalize_keeps_frobenius_norm():
+    for seed in range(5):
+        O, S, V = _norm_case(seed)
+        U, _ = orc.normalize_neurons(O, S, V, 0.9, 1e-8)
+        assert abs(np.linalg.norm(U) - np.linalg.norm(O)) <= 1e-12 * np.linalg.norm(O)
+
+
+def test_normalize_beta0_equalizes_rows():
+    """beta2 = 0 and eps = 0: every row is divided by its own RMS, so after the
+    norm-preserving rescale all rows have norm ||O||_F / sqrt(k)."""
+    O, S, V = _norm_case(11)
+    U, _ = orc.normalize_neurons(O, S, V, 0.0, 0.0)
+    want = np.linalg.norm(O) / np.sqrt(O.shape[0])
+    assert np.allclose(np.linalg.norm(U, axis=1), want, rtol=1e-7)   # V is stored as fp32
+
+
+def test_normalize_is_identity_on_equal_rows_at_steady_state():
+    """Rows of equal mean square whose state already equals that mean square:
+    the division is one common factor, which the rescale removes."""
+    rng = np.random.default_rng(12)
+    Q, _ = np.linalg.qr(rng.standard_normal((16, 5)))
+    O = Q.T                                   # 5 orthonormal rows of length 16
+    S = np.array([1, 3, 4, 7, 8])
+    V = np.full(10, 1.0 / 16, np.float32)     # mean square of a unit row of 16
+    U, V1 = orc.normalize_neurons(O, S, V, 0.95, 0.0)
+    assert np.allclose(U, O, atol=1e-6)
+    assert np.allclose(V1, V, rtol=1e-6)
+
+
+def test_normalize_worked_example():
+    """O = [[3, 4], [0, 5]] (m = 2), rows S = {0, 1}, V = [1, 2, 9], beta2 = 1/2,
+    eps = 0, worked by hand:
+      q = [25/2, 25/2];  v = [1/2 + 25/4, 1 + 25/4] = [6.75, 7.25];
+      U_hat = [[3, 4] / sqrt(6.75), [0, 5] / sqrt(7.25)];
+      ||U_hat||^2 = 25/6.75 + 25/7.25 = 7.15197956577...;
+      U = U_hat * sqrt(50 / 7.15197956577...), i.e.
+      U = [[3.05310147, 4.07080196], [0, 4.90990253]]; V' = [6.75, 7.25, 9]."""
+    O = np.array([[3.0, 4.0], [0.0, 5.0]])
+    U, V1 = orc.normalize_neurons(O, np.array([0, 1]), np.array([1, 2, 9], np.float32), 0.5, 0.0)
+    assert np.allclose(U, [[3.05310147, 4.07080196], [0.0, 4.90990253]], atol=5e-8)
+    assert V1.tolist() == [6.75, 7.25, 9.0]
+
+
+def test_normalize_state_of_unselected_rows_untouched():
+    O, S, V = _norm_case(13)
+    _, V1 = orc.normalize_neurons(O, S, V, 0.9, 1e-8)
+    rest = np.setdiff1d(np.arange(V.size), S)
+    assert V1[rest].tobytes() == V[rest].tobytes()
+    assert V1.dtype == np.float32
+
+
+def test_normalize_permutation_equivariant():
+    O, S, V = _norm_case(14)
+    p = np.random.default_rng(15).permutation(O.shape[0])
+    U, V1 = orc.normalize_neurons(O, S, V, 0.8, 1e-6)
+    Up, V1p = orc.normalize_neurons(O[p], S[p], V, 0.8, 1e-6)
+    assert np.allclose(Up, U[p], atol=1e-12)
+    assert V1p.tobytes() == V1.tobytes()
+
+
+def test_normalize_homogeneous_at_beta0():
+    O, S, V = _norm_case(16)
+    U, _ = orc.normalize_neurons(O, S, V, 0.0, 0.0)
+    U3, _ = orc.normalize_neurons(3.0 * O, S, V, 0.0, 0.0)
+    assert np.allclose(U3, 3.0 * U, rtol=1e-6)
+
+
+def test_normalize_rejects_bad_input():
+    O, S, V = _norm_case(17)
+    with pytest.raises(TypeError):
+        orc.normalize_neurons(O, S, V.astype(np.float64), 0.9, 1e-8)
+    with pytest.raises(ValueError):
+        orc.normalize_neurons(O, S, V, 1.0, 1e-8)
+    with pytest.raises(ValueError):
+        orc.normalize_neurons(O, S, V, 0.9, -1.0)
+
+
+def test_step_with_normalization_updates_by_u():
+    rng = np.random.default_rng(18)
+    W = (rng.standard_normal((40, 24)) * 0.02).astype(np.float32)
+    M = rng.standard_normal((40, 24)).astype(np.float32)
+    V = np.zeros(40, np.float32)
+    ref = orc.dion3_step(W, M, 10, 0.04, 0.95, norm=(V, 0.95, 1e-8))
+    S = ref["S"]
+    assert np.allclose(ref["W"][S] - W[S], -0.04 * ref["U"], atol=1e-12)
+    assert abs(np.linalg.norm(ref["U"]) - np.linalg.norm(ref["O"])) <= 1e-10
+    assert ref["V"][np.setdiff1d(np.arange(40), S)].tobytes() == bytes(4 * 30)
+    # a zero momentum gives a zero update (and a decayed, still zero, state)
+    ref0 = orc.dion3_step(W, np.zeros_like(M), 10, 0.04, 0.95, norm=(V, 0.95, 1e-8))
+    assert not np.any(ref0["U"])
+
+
+def test_normalize_worked_example_ema_weights_and_eps():
+    """The example above with beta2 = 0.9: v = [0.9 + 1.25, 1.8 + 1.25] =
+    [2.15, 3.05] (a swapped weighting would give 11.35); and with beta2 = 1/2,
+    eps = 1: U_hat = O / (sqrt(v) + 1) = [[3, 4] / 3.598076, [0, 5] / 3.692582],
+    rescaled to norm sqrt(50): [[3.038633, 4.051510], [0, 4.934772]]."""
+    O = np.array([[3.0, 4.0], [0.0, 5.0]])
+    V = np.array([1, 2, 9], np.float32)
+    _, V1 = orc.normalize_neurons(O, np.array([0, 1]), V, 0.9, 0.0)
+    assert V1.tolist() == np.array([2.15, 3.05, 9.0], np.float32).tolist()
+    U, _ = orc.normalize_neurons(O, np.array([0, 1]), V, 0.5, 1.0)
+    assert np.allclose(U, [[3.038633, 4.051510], [0.0, 4.934772]], rtol=0, atol=1e-6)
