@@ -245,7 +245,8 @@ def normalize_neurons(O: np.ndarray, S: np.ndarray, V: np.ndarray, beta2: float,
       q_i = mean_j O_ij^2                       (mean square of row i)
       V[S_i] <- beta2 V[S_i] + (1 - beta2) q_i  (stored as float32; rows
                                                  outside S keep their state)
-      U_i = O_i / (sqrt(V[S_i]) + eps)
+      U_i = O_i / (sqrt(V[S_i]) + eps)          (0 when that is 0 / 0: a zero
+                                                 row with a zero state)
       U  <- U ||O||_F / ||U||_F                 (the update keeps O's norm, so
                                                  the step size keeps its
                                                  meaning, eta ~ 1/sqrt(f))
@@ -266,7 +267,9 @@ def normalize_neurons(O: np.ndarray, S: np.ndarray, V: np.ndarray, beta2: float,
     v = (beta2 * V[S].astype(np.float64) + (1.0 - beta2) * (sq / m)).astype(np.float32)
     V_new = V.copy()
     V_new[S] = v
-    U = O / (np.sqrt(v.astype(np.float64)) + eps)[:, None]
+    d = np.sqrt(v.astype(np.float64)) + eps
+    # d = 0 needs v = 0 and eps = 0, so the row of O is zero: its update is zero
+    U = np.divide(O, d[:, None], out=np.zeros_like(O), where=d[:, None] > 0)
     nU = np.linalg.norm(U)
     U = U * (np.sqrt(sq.sum()) / nU) if nU > 0 else np.zeros_like(O)
     return U, V_new

@@ -432,3 +432,10 @@ def test_normalize_worked_example_ema_weights_and_eps():
     assert V1.tolist() == np.array([2.15, 3.05, 9.0], np.float32).tolist()
     U, _ = orc.normalize_neurons(O, np.array([0, 1]), V, 0.5, 1.0)
     assert np.allclose(U, [[3.038633, 4.051510], [0.0, 4.934772]], rtol=0, atol=1e-6)
+
+
+def test_normalize_zero_row_with_zero_state_and_eps():
+    O = np.array([[0.0, 0.0], [0.0, 5.0]])
+    U, V1 = orc.normalize_neurons(O, np.array([0, 1]), np.zeros(2, np.float32), 0.5, 0.0)
+    assert np.all(np.isfinite(U)) and not np.any(U[0])
+    assert np.allclose(U[1], [0.0, 5.0])
