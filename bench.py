@@ -43,6 +43,9 @@ KERNEL_SYMBOLS = {
     "topk": "k_topk",
     "gather": "k_gather<float, true>",
     "gram_ns_fused_128": "k_gram_ns_small",
+    "norm_rows": "k_norm_rows",
+    "norm_scale": "k_norm_scale",
+    "norm_update": "k_norm_update",
 }
 
 
@@ -67,6 +70,9 @@ def parse():
                    help="gram: Gram Newton-Schulz (the step); standard: the iteration on X itself "
                         "(the Muon baseline, on the same kernels)")
     p.add_argument("--no-trace", action="store_true")
+    p.add_argument("--normalize", action="store_true",
+                   help="per-neuron normalization of the update (fp32 second moment per row, "
+                        "beta2 = 0.95, eps = 1e-8) through dion3_step_megabatch_norm")
     p.add_argument("--accumulate", action="store_true",
                    help="each step first accumulates a gradient into the momentum (M <- M + G, "
                         "fused into the row scoring); gradients are fixed seeded N(0, 0.1^2)")
@@ -115,6 +121,8 @@ def kernel_source_hash(kernel: str) -> str:
         f = "gemm_f16.hip"
     elif kernel.startswith("gram_ns_fused"):
         f = "gram_small.hip"
+    elif kernel.startswith("norm_"):
+        f = "normalize.hip"
     else:
         f = "rows.hip"
     with open(os.path.join(ROOT, "orthogonalizing_optimizer_amd", "csrc", f), "rb") as fh:
@@ -183,6 +191,7 @@ def main():
 
     groups = []
     grads = {}
+    norms = {}
     max_ws = 0
     for gi, (g, Ws, Ms) in enumerate(data):
         k = d3.k_from_fraction(float(wl.fraction), g.n)
@@ -194,6 +203,9 @@ def main():
             gen.manual_seed(7000 + gi)
             Gs = [torch.randn(M.shape, generator=gen, device=dev).mul_(0.1) for M in Ms]
             grads[gi] = (Gs, d3.pointer_array(Gs, dev))
+        if args.normalize:
+            Vs = [torch.zeros(g.n, dtype=torch.float32, device=dev) for _ in Ms]
+            norms[gi] = (Vs, d3.pointer_array(Vs, dev))
     nstreams = max(1, min(args.streams, len(groups)))
     if nstreams == 1:
         ws = d3.Workspace()
@@ -211,15 +223,19 @@ def main():
         if nstreams == 1:
             for gi, (g, Ws, Ms, k, ptrs) in enumerate(groups):
                 gp = grads[gi][1] if gi in grads else None
-                d3.step_megabatch(Ws, Ms, k, lr, mu, cfg, ws=wss[gi], ptrs=ptrs, gptrs=gp)
+                nrm = (norms[gi][0], 0.95, 1e-8) if gi in norms else None
+                d3.step_megabatch(Ws, Ms, k, lr, mu, cfg, ws=wss[gi], ptrs=ptrs, gptrs=gp,
+                                  norm=nrm, vptrs=norms[gi][1] if gi in norms else None)
             return
         main = torch.cuda.current_stream()
         for st in side:
             st.wait_stream(main)
         for gi, (g, Ws, Ms, k, ptrs) in enumerate(groups):
             gp = grads[gi][1] if gi in grads else None
+            nrm = (norms[gi][0], 0.95, 1e-8) if gi in norms else None
             with torch.cuda.stream(side[gi % nstreams]):
-                d3.step_megabatch(Ws, Ms, k, lr, mu, cfg, ws=wss[gi], ptrs=ptrs, gptrs=gp)
+                d3.step_megabatch(Ws, Ms, k, lr, mu, cfg, ws=wss[gi], ptrs=ptrs, gptrs=gp,
+                                  norm=nrm, vptrs=norms[gi][1] if gi in norms else None)
         for st in side:
             main.wait_stream(st)
 
@@ -236,7 +252,7 @@ def main():
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
-    launches_per_step = sum(3 + 1 + 2 * (1 + cfg.n_restart) + 4 * cfg.iters for _ in groups)
+    launches_per_step = sum(3 + 1 + 2 * (1 + cfg.n_restart) + 4 * cfg.iters + 3 for _ in groups)
     if not args.no_trace:
         d3.trace_enable(launches_per_step * args.steps + 64)
     stream = torch.cuda.current_stream()
@@ -382,6 +398,7 @@ def main():
             "parallelism": "single GPU, one megabatched call per shape group" +
                            (f", groups on {nstreams} streams" if nstreams > 1 else ""),
             "gradient_accumulation": bool(args.accumulate),
+            "per_neuron_normalization": bool(args.normalize),
             "hip_graph": bool(args.graph),
         },
         "matrices_per_s": round(wl.n_matrices / (ms_per_step * 1e-3), 1),

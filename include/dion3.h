@@ -182,6 +182,38 @@ DION3_API dion3_status dion3_step_megabatch_accum(float* const* W, float* const*
                                                   int32_t* idx_out, uint16_t* O_out, void* ws,
                                                   size_t ws_bytes, void* stream);
 
+/* Per-neuron normalization of the update.  The pages say that Dion3
+ * inherits NorMuon's per-neuron normalization ("Dion3 Cuts Muon Optimizer
+ * Time by Up to 6x", quasa.io, section "Dion3's fastest path is a combined
+ * systems stack") and that it runs in float32 ("Dion3: Full-Stack
+ * Orthogonal Updates", agihunt.info, limitations paragraph), without a
+ * formula.  Reading implemented: for the selected rows S and orthogonalized
+ * rows O (k x m) of one matrix with a float32 state V (n entries, one per
+ * row, caller-owned, zero before the first step):
+ *   q_i = mean_j O_ij^2;  V[S_i] <- beta2 V[S_i] + (1 - beta2) q_i;
+ *   U_i = O_i / (sqrt(V[S_i]) + eps)  (0 for a zero row with zero state);
+ *   U <- U ||O||_F / ||U||_F  (the step keeps O's norm);
+ *   W[S] <- W[S] - lr U.  Rows of V outside S are not written. */
+typedef struct {
+  float beta2;   /* 0 <= beta2 < 1 */
+  float eps;     /* >= 0, added to sqrt(V) */
+} dion3_norm_cfg;
+
+/* The megabatch step with per-neuron normalization.  W, M, V are DEVICE
+ * arrays of `batch` device pointers (V[b]: n floats); G is NULL or such an
+ * array of gradients accumulated first as in dion3_step_megabatch_accum.
+ * O_out, when not NULL, receives O before the normalization.  The workspace
+ * is the one dion3_workspace_size gives for the same shapes.
+ * DION3_ERR_ARG also for a NULL V or norm, beta2 outside [0, 1) or eps < 0. */
+DION3_API dion3_status dion3_step_megabatch_norm(float* const* W, float* const* M,
+                                                 const float* const* G, float* const* V,
+                                                 int32_t batch, int64_t n, int64_t m, int64_t ld,
+                                                 int64_t k, float lr, float mu,
+                                                 const dion3_ns_cfg* cfg,
+                                                 const dion3_norm_cfg* norm, int32_t* idx_out,
+                                                 uint16_t* O_out, void* ws, size_t ws_bytes,
+                                                 void* stream);
+
 /* The symmetric products of the level-2 paragraph, usable on their own.
  *
  * dion3_syrk_f16: R[b] = A[b] A[b]^T for `batch` fp16 matrices A[b]

@@ -41,6 +41,11 @@ class NsCfg(ctypes.Structure):
                 ("method", ctypes.c_int32), ("path", ctypes.c_int32)]
 
 
+class NormCfg(ctypes.Structure):
+    """Mirror of dion3_norm_cfg (per-neuron normalization of the update)."""
+    _fields_ = [("beta2", ctypes.c_float), ("eps", ctypes.c_float)]
+
+
 NS_GRAM = 0
 NS_STANDARD = 1
 PATH_AUTO = 0
@@ -70,6 +75,9 @@ def _declare(lib):
                                        c.POINTER(NsCfg), vp, vp, vp, sz, vp]),
         "dion3_step_megabatch_accum": (c.c_int, [vp, vp, vp, i32, i64, i64, i64, i64, f32, f32,
                                                  c.POINTER(NsCfg), vp, vp, vp, sz, vp]),
+        "dion3_step_megabatch_norm": (c.c_int, [vp, vp, vp, vp, i32, i64, i64, i64, i64, f32, f32,
+                                                c.POINTER(NsCfg), c.POINTER(NormCfg), vp, vp, vp,
+                                                sz, vp]),
         "dion3_syrk_f16": (c.c_int, [vp, vp, i32, i64, i64, i64, i64, vp]),
         "dion3_symm_f16": (c.c_int, [vp, vp, vp, vp, i32, i64, i64, f32, f32, f32, vp]),
         "dion3_trace_enable": (c.c_int, [i32]),
@@ -90,6 +98,7 @@ def _declare(lib):
 EXPORTED = ("dion3_version", "dion3_ns_cfg_size", "dion3_ns_cfg_default", "dion3_k_from_fraction",
             "dion3_workspace_size", "dion3_row_select", "dion3_gram_ns", "dion3_step",
             "dion3_step_megabatch", "dion3_step_accum", "dion3_step_megabatch_accum",
+            "dion3_step_megabatch_norm",
             "dion3_syrk_f16", "dion3_symm_f16", "dion3_trace_enable",
             "dion3_trace_count", "dion3_trace_reset", "dion3_trace_record", "dion3_status_string",
             "dion3_last_hip_error")
@@ -296,11 +305,14 @@ def pointer_array(tensors, device):
 
 def step_megabatch(Ws, Ms, k: int, lr: float, mu: float, cfg: Optional[NsCfg] = None,
                    return_idx: bool = False, return_O: bool = False,
-                   ws: Optional[Workspace] = None, ptrs=None, Gs=None, gptrs=None):
+                   ws: Optional[Workspace] = None, ptrs=None, Gs=None, gptrs=None, norm=None,
+                   vptrs=None):
     """One Dion3 step on a group of same-shape matrices in one call.
     ``ptrs`` may carry cached (W pointer array, M pointer array).  With
     gradients ``Gs`` (or their cached pointer array ``gptrs``), each M <- M + G
-    first, fused into the row scoring."""
+    first, fused into the row scoring.  With ``norm = (Vs, beta2, eps)`` the
+    update is normalized per neuron (Vs: one fp32 [n] state per matrix,
+    updated in place; ``vptrs`` may carry their cached pointer array)."""
     torch = _torch()
     if len(Ws) != len(Ms) or not Ws:
         raise ValueError("need equally many W and M matrices")
@@ -320,7 +332,24 @@ def step_megabatch(Ws, Ms, k: int, lr: float, mu: float, cfg: Optional[NsCfg] = 
     O = torch.empty((B, k, m), dtype=torch.float16, device=dev) if return_O else None
     p, nb = _ws_for(ws, dev).get(workspace_size(B, n, m, k), dev)
     c = ctypes.byref(cfg) if cfg is not None else None
-    if Gs is None and gptrs is None:
+    if norm is not None:
+        Vs, beta2, eps = norm
+        if len(Vs) != B:
+            raise ValueError("need one state vector per matrix")
+        for v in Vs:
+            _req(v, torch.float32, "V")
+            if v.dim() != 1 or v.shape[0] != n or v.stride(0) != 1:
+                raise ValueError("each state must be a contiguous fp32 vector of n entries")
+        if vptrs is None:
+            vptrs = pointer_array(Vs, dev)
+        if Gs is not None and gptrs is None:
+            gptrs = pointer_array(Gs, dev)
+        nc = NormCfg(float(beta2), float(eps))
+        _check(lib().dion3_step_megabatch_norm(
+            ptrs[0].data_ptr(), ptrs[1].data_ptr(), gptrs.data_ptr() if gptrs is not None else None,
+            vptrs.data_ptr(), B, n, m, stride[0], k, lr, mu, c, ctypes.byref(nc), _ptr(idx), _ptr(O),
+            p, nb, _stream(dev)), "dion3_step_megabatch_norm")
+    elif Gs is None and gptrs is None:
         _check(lib().dion3_step_megabatch(ptrs[0].data_ptr(), ptrs[1].data_ptr(), B, n, m, stride[0],
                                           k, lr, mu, c, _ptr(idx), _ptr(O), p, nb, _stream(dev)),
                "dion3_step_megabatch")

@@ -365,12 +365,24 @@ dion3_status orthogonalize(const Plan& P, const dion3_ns_cfg& cfg, const Bufs& b
                                          : gram_ns(P, cfg, bf, sink, s);
 }
 
+// The X pair that the orthogonalization no longer reads once it has started
+// its last product: every restart (Gram) or every iteration but the last
+// (standard) swaps the two pairs, starting from the first.
+const XPair& free_pair(const dion3_ns_cfg& cfg, const Bufs& bf) {
+  const int swaps = cfg.method == DION3_NS_STANDARD ? cfg.iters - 1 : cfg.n_restart;
+  return swaps % 2 == 0 ? bf.b : bf.a;
+}
+
 dion3_status step_impl(BatchPtr<float> W, BatchPtr<float> M, BatchPtr<const float> G, int batch,
                        long long n, long long m,
                        long long ld, long long k, float lr, float mu, const dion3_ns_cfg* cfg_in,
                        int32_t* idx_out, uint16_t* O_out, void* ws, size_t ws_bytes,
-                       void* stream) {
+                       void* stream, BatchPtr<float> V = {nullptr, 0, nullptr},
+                       const dion3_norm_cfg* norm = nullptr) {
   if (batch < 1 || batch > DION3_MAX_BATCH) return DION3_ERR_ARG;
+  if (norm && (!(V.base || V.ptrs) || !(norm->beta2 >= 0.0f && norm->beta2 < 1.0f) ||
+               !(norm->eps >= 0.0f) || !isfinite(norm->eps)))
+    return DION3_ERR_ARG;
   if (!dims_ok(n) || !dims_ok(m) || !dims_ok(k)) return DION3_ERR_UNSUPPORTED;
   if (k > n || ld < m) return DION3_ERR_ARG;
   if (!isfinite(lr) || !isfinite(mu)) return DION3_ERR_ARG;
@@ -410,9 +422,24 @@ dion3_status step_impl(BatchPtr<float> W, BatchPtr<float> M, BatchPtr<const floa
     HIP_TRY(launch_gather_f32(M, batch, (int)n, (int)m, ld, idx, (int)k, scale, mu, true, bf.a.X,
                               bf.a.XT, P.kp * P.mp, (int)P.kp, (int)P.mp, s));
   }
-  const UpdateSink sink = {W, ld, idx, lr, (f16*)O_out};
-  st = orthogonalize(P, cfg, bf, sink, s);
-  if (st != DION3_OK) return st;
+  if (!norm) {
+    const UpdateSink sink = {W, ld, idx, lr, (f16*)O_out};
+    st = orthogonalize(P, cfg, bf, sink, s);
+    if (st != DION3_OK) return st;
+  } else {
+    // O (rows layout [batch][k][m]) into the free X buffer, then the
+    // per-neuron normalization and the update; the row statistics reuse the
+    // score region and the per-matrix scale the norm region
+    f16* Obuf = free_pair(cfg, bf).X;
+    const UpdateSink sink = {{nullptr, 0, nullptr}, 0, idx, lr, Obuf};
+    st = orthogonalize(P, cfg, bf, sink, s);
+    if (st != DION3_OK) return st;
+    HIP_TRY(launch_normalize(Obuf, batch, (int)k, (int)m, idx, V, norm->beta2, norm->eps, W, ld, lr,
+                             (float2*)l1, scale, s));
+    if (O_out)
+      HIP_TRY(hipMemcpyAsync(O_out, Obuf, (size_t)batch * k * m * sizeof(uint16_t),
+                             hipMemcpyDeviceToDevice, s));
+  }
   if (idx_out)
     HIP_TRY(hipMemcpyAsync(idx_out, idx, (size_t)batch * k * sizeof(int32_t),
                            hipMemcpyDeviceToDevice, s));
@@ -604,6 +631,19 @@ dion3_status dion3_step_megabatch_accum(float* const* W, float* const* M, const 
   BatchPtr<const float> Gb = {nullptr, 0, G};
   return step_impl(Wb, Mb, Gb, batch, n, m, ld, k, lr, mu, cfg, idx_out, O_out, ws, ws_bytes,
                    stream);
+}
+
+dion3_status dion3_step_megabatch_norm(float* const* W, float* const* M, const float* const* G,
+                                       float* const* V, int32_t batch, int64_t n, int64_t m,
+                                       int64_t ld, int64_t k, float lr, float mu,
+                                       const dion3_ns_cfg* cfg, const dion3_norm_cfg* norm,
+                                       int32_t* idx_out, uint16_t* O_out, void* ws,
+                                       size_t ws_bytes, void* stream) {
+  if (!W || !M || !V || !norm) return DION3_ERR_ARG;
+  BatchPtr<float> Wb = {nullptr, 0, W}, Mb = {nullptr, 0, M}, Vb = {nullptr, 0, V};
+  BatchPtr<const float> Gb = {nullptr, 0, G};
+  return step_impl(Wb, Mb, Gb, batch, n, m, ld, k, lr, mu, cfg, idx_out, O_out, ws, ws_bytes,
+                   stream, Vb, norm);
 }
 
 dion3_status dion3_syrk_f16(const uint16_t* A, uint16_t* R, int32_t batch, int64_t rows,

@@ -108,4 +108,11 @@ hipError_t launch_gram_ns_small(f16* X, f16* XT, f16* Y, f16* YT, long long sX, 
                                 const int* idx, float lr, f16* Oout, int kval, int mval, int nrows,
                                 double trace_flops, hipStream_t s);
 
+// Per-neuron normalization of O ([batch][k][m] fp16, rows layout) and the
+// update W[idx[i]] -= lr * U_i; V holds one fp32 state per row of each
+// matrix; stats ([batch][k]) and g ([batch]) are scratch.
+hipError_t launch_normalize(const f16* O, int batch, int k, int m, const int* idx,
+                            BatchPtr<float> V, float beta2, float eps, BatchPtr<float> W,
+                            long long ldw, float lr, float2* stats, double* g, hipStream_t s);
+
 }  // namespace dion3

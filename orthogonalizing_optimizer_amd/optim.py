@@ -88,13 +88,22 @@ class Dion3(_optimizer_base()):
     feedback keeps the unselected rows of M for a later step; level-4:
     megabatching by shape).  Parameters that are not 2-D fp32 matrices with
     contiguous rows are refused: route them to another optimizer.
+
+    With ``normalize=True`` the update is normalized per neuron (row) with a
+    float32 second-moment state per row (``beta2``, ``eps``), the reading of
+    the pages' "per-neuron normalization inherited from NorMuon" stated in
+    include/dion3.h at dion3_norm_cfg.
     """
 
     def __init__(self, params, lr: float = 0.02, fraction=Fraction(1, 4), mu: float = 0.95,
-                 cfg: Optional[_lib.NsCfg] = None):
+                 cfg: Optional[_lib.NsCfg] = None, normalize: bool = False,
+                 beta2: float = 0.95, eps: float = 1e-8):
         if lr <= 0 or not (0 < float(fraction) <= 1) or not (0 <= mu <= 1):
             raise ValueError("need lr > 0, 0 < fraction <= 1 and 0 <= mu <= 1")
-        super().__init__(params, dict(lr=lr, fraction=fraction, mu=mu))
+        if normalize and not (0 <= beta2 < 1 and eps >= 0):
+            raise ValueError("need 0 <= beta2 < 1 and eps >= 0")
+        super().__init__(params, dict(lr=lr, fraction=fraction, mu=mu, normalize=normalize,
+                                      beta2=beta2, eps=eps))
         import torch
         for group in self.param_groups:
             for p in group["params"]:
@@ -122,11 +131,18 @@ class Dion3(_optimizer_base()):
                     if "momentum" not in st:   # the parameter's own strides
                         st["momentum"] = torch.empty_strided(p.shape, p.stride(), dtype=p.dtype,
                                                              device=p.device).zero_()
+                    if group["normalize"] and "second_moment" not in st:
+                        st["second_moment"] = torch.zeros(p.shape[0], dtype=torch.float32,
+                                                          device=p.device)
                     buckets.setdefault((tuple(p.shape), p.stride(), str(p.device)), []).append(p)
                 for (shape, _, dev), ps in buckets.items():
                     k = _lib.k_from_fraction(f, shape[0])
                     ws = self._ws.setdefault(dev, _lib.Workspace())
+                    norm = None
+                    if group["normalize"]:
+                        norm = ([self.state[p]["second_moment"] for p in ps], group["beta2"],
+                                group["eps"])
                     _lib.step_megabatch(ps, [self.state[p]["momentum"] for p in ps], k,
                                         group["lr"] / math.sqrt(f), group["mu"], self.cfg, ws=ws,
-                                        Gs=[p.grad for p in ps])
+                                        Gs=[p.grad for p in ps], norm=norm)
         return loss

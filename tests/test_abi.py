@@ -217,3 +217,24 @@ def test_dion3_optimizer_refuses_what_it_cannot_step():
     p.grad = torch.ones(4, 6)
     with pytest.raises(TypeError):                                  # host tensors: no CPU path
         opt.step()
+
+
+def test_norm_step_rejects_bad_arguments_before_launch():
+    lib = d3.lib()
+    nb = d3.workspace_size(1, 64, 32, 16)
+    good = d3.NormCfg(0.95, 1e-8)
+
+    def call(V=FAKE, norm=good):
+        return lib.dion3_step_megabatch_norm(FAKE, FAKE, None, V, 1, 64, 32, 32, 16, 0.04, 0.95,
+                                             None, ctypes.byref(norm) if norm else None, None,
+                                             None, FAKE, nb, None)
+    assert call(V=None) == ERR_ARG
+    assert call(norm=None) == ERR_ARG
+    assert call(norm=d3.NormCfg(1.0, 1e-8)) == ERR_ARG
+    assert call(norm=d3.NormCfg(-0.1, 1e-8)) == ERR_ARG
+    assert call(norm=d3.NormCfg(0.9, -1.0)) == ERR_ARG
+    assert call(norm=d3.NormCfg(0.9, float("nan"))) == ERR_ARG
+    # valid normalization arguments pass on to the workspace check
+    assert lib.dion3_step_megabatch_norm(FAKE, FAKE, None, FAKE, 1, 64, 32, 32, 16, 0.04, 0.95,
+                                         None, ctypes.byref(good), None, None, FAKE + 16, nb,
+                                         None) == ERR_WS

@@ -1,0 +1,112 @@
+"""Per-neuron normalization of the update (dion3_step_megabatch_norm)
+against the oracle: the normalization arithmetic tightly, on the GPU's own
+orthogonalized rows, and the whole step against the fp64 oracle at the
+step's tolerance; fused and tiled Gram paths, k > m, gradient accumulation,
+and the torch.optim-style optimizer."""
+import sys
+
+import numpy as np
+import pytest
+
+from oracle import dion3_oracle as orc
+from tests.parity import O_TOL, check_selection, rel
+from workloads import host_gaussian
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+import orthogonalizing_optimizer_amd as d3  # noqa: E402
+
+DEV = "cuda:0"
+BETA2, EPS, LR, MU = 0.9, 1e-8, 0.04, 0.95
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+# (n, m, k): fused path (Gram side <= 128), tiled, k > m (transposed Gram), ragged
+CASES = [(200, 300, 50), (700, 520, 300), (500, 96, 300), (130, 257, 129), (64, 64, 64)]
+
+
+@pytest.mark.parametrize("n,m,k", CASES)
+@pytest.mark.parametrize("accumulate", [False, True])
+def test_norm_step(n, m, k, accumulate):
+    say("norm step", n, m, k, accumulate)
+    B = 3
+    Ws = [host_gaussian((n, m), [100, n, b], std=0.02) for b in range(B)]
+    Ms = [host_gaussian((n, m), [101, n, b]) for b in range(B)]
+    Gs = [host_gaussian((n, m), [102, n, b]) for b in range(B)] if accumulate else None
+    rng = np.random.default_rng(n + m)
+    Vs = [rng.uniform(0.0, 0.01, n).astype(np.float32) for _ in range(B)]
+    Wd, Md, Vd = [dev(w) for w in Ws], [dev(x) for x in Ms], [dev(v) for v in Vs]
+    Gd = [dev(g) for g in Gs] if accumulate else None
+    idx, O = d3.step_megabatch(Wd, Md, k, LR, MU, Gs=Gd, norm=(Vd, BETA2, EPS), return_idx=True,
+                               return_O=True)
+    torch.cuda.synchronize()
+    for b in range(B):
+        M0 = Ms[b] + Gs[b] if accumulate else Ms[b]
+        S, Ob = idx[b].cpu().numpy(), O[b].cpu().numpy().astype(np.float64)
+        W1, M1, V1 = Wd[b].cpu().numpy(), Md[b].cpu().numpy(), Vd[b].cpu().numpy()
+        assert np.array_equal(S, check_selection(S, M0, k))
+        # the normalization on the GPU's own O: tight
+        U_ref, V_ref = orc.normalize_neurons(Ob, S, Vs[b], BETA2, EPS)
+        rest = np.setdiff1d(np.arange(n), S)
+        assert V1[rest].tobytes() == Vs[b][rest].tobytes()
+        assert np.max(np.abs(V1[S] - V_ref[S]) / V_ref[S]) <= 1e-5
+        assert W1[rest].tobytes() == Ws[b][rest].tobytes()
+        assert rel(W1[S] - Ws[b][S], -LR * U_ref) <= 1e-5
+        # the whole step against the fp64 oracle
+        ref = orc.dion3_step(Ws[b], M0, k, LR, MU, norm=(Vs[b], BETA2, EPS))
+        assert M1.tobytes() == ref["M"].tobytes()
+        assert rel(Ob, ref["O"]) <= O_TOL
+        assert rel(W1[S] - Ws[b][S], ref["W"][S] - Ws[b][S]) <= O_TOL
+
+
+def test_norm_step_equal_across_paths():
+    """The fused and tiled Gram paths give the same O bit for bit, so the
+    normalized step is bitwise the same too."""
+    say("norm paths")
+    n, m, k = 300, 200, 75
+    W = host_gaussian((n, m), 103, std=0.02)
+    M = host_gaussian((n, m), 104)
+    outs = []
+    for p in (d3.PATH_FUSED, d3.PATH_TILED):
+        Wd, Md, Vd = [dev(W)], [dev(M)], [torch.zeros(n, device=DEV)]
+        d3.step_megabatch(Wd, Md, k, LR, MU, d3.ns_cfg(path=p), norm=(Vd, BETA2, EPS))
+        torch.cuda.synchronize()
+        outs.append((Wd[0].cpu().numpy(), Vd[0].cpu().numpy()))
+    assert outs[0][0].tobytes() == outs[1][0].tobytes()
+    assert outs[0][1].tobytes() == outs[1][1].tobytes()
+
+
+def test_dion3_optimizer_normalized_two_steps():
+    say("Dion3 optimizer, normalized")
+    shapes = [(96, 64), (64, 96)]
+    params = [torch.nn.Parameter(dev(host_gaussian(sh, [105, i], std=0.02)))
+              for i, sh in enumerate(shapes)]
+    opt = d3.Dion3(params, lr=0.02, fraction=0.25, mu=0.9, normalize=True, beta2=BETA2, eps=EPS)
+    W = [p.detach().cpu().numpy().copy() for p in params]
+    M = [np.zeros(sh, np.float32) for sh in shapes]
+    V = [np.zeros(sh[0], np.float32) for sh in shapes]
+    for it in range(2):
+        G = [host_gaussian(sh, [106, it, i]) for i, sh in enumerate(shapes)]
+        for p, g in zip(params, G):
+            p.grad = dev(g)
+        opt.step()
+        torch.cuda.synchronize()
+        for i, (p, sh) in enumerate(zip(params, shapes)):
+            k = orc.k_from_fraction(0.25, sh[0])
+            ref = orc.dion3_step(W[i], M[i] + G[i], k, 0.04, 0.9, norm=(V[i], BETA2, EPS))
+            W1 = p.detach().cpu().numpy()
+            M1 = opt.state[p]["momentum"].cpu().numpy()
+            V1 = opt.state[p]["second_moment"].cpu().numpy()
+            assert M1.tobytes() == ref["M"].tobytes(), (it, i)
+            assert rel(W1 - W[i], ref["W"] - W[i]) <= O_TOL, (it, i)
+            assert rel(V1, ref["V"]) <= 2e-2, (it, i)
+            W[i], M[i], V[i] = W1, M1, V1
