@@ -61,8 +61,10 @@ def log(*a):
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=10)
-    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--steps", type=int, default=None,
+                   help="timed steps (default: 50 for the small workloads c1-c3, 10 otherwise)")
+    p.add_argument("--warmup", type=int, default=None,
+                   help="untimed steps first (default: 5 for c1-c3, 2 otherwise)")
     p.add_argument("--workload", default="c4",
                    help="c1, c2, c3, c4 (7B f=1/4), c4h (7B f=1/2), c4f (7B f=1), c5")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -168,6 +170,11 @@ def main():
     torch.cuda.set_device(0)
     dev = "cuda:0"
     wl = WORKLOADS[args.workload]
+    small = args.workload in ("c1", "c2", "c3")
+    if args.steps is None:
+        args.steps = 50 if small else 10
+    if args.warmup is None:
+        args.warmup = 5 if small else 2
     cfg = d3.default_cfg()
     if args.method == "standard":
         cfg.method = d3.NS_STANDARD
