@@ -194,6 +194,7 @@ struct UpdateSink {
   const int* idx;
   float lr;
   f16* Oout;
+  long long sO;   // elements between consecutive matrices' O blocks (>= k * m)
 };
 
 // Y_math = Q X_math.  The restart needs Y in both layouts.  The final
@@ -217,6 +218,7 @@ hipError_t rect(const Plan& P, const f16* Q, const XPair& x, const XPair& y, boo
     d.C = nullptr;
     d.CT = nullptr;
     d.W = sink->W; d.ldw = sink->ldw; d.idx = sink->idx; d.lr = sink->lr; d.Oout = sink->Oout;
+    d.sO = sink->sO;
     d.kval = (int)P.k; d.mval = (int)P.m; d.nrows = (int)P.n;
   }
   d.M = (int)P.sp; d.N = (int)P.Lp; d.K = (int)P.sp; d.batch = P.B;
@@ -276,6 +278,7 @@ dion3_status gram_ns(const Plan& P, const dion3_ns_cfg& cfg, const Bufs& bf,
     HIP_TRY(launch_gram_ns_small(
         (f16*)xmath(P, bf.a), (f16*)xmathT(P, bf.a), (f16*)xmath(P, bf.b), (f16*)xmathT(P, bf.b),
         P.kp * P.mp, P.B, (int)P.Lp, P.tr, cfg, sink.W, sink.ldw, sink.idx, sink.lr, sink.Oout,
+        sink.sO,
         (int)P.k, (int)P.m, (int)P.n, gram_ns_flops(P, cfg), s));
     return DION3_OK;
   }
@@ -336,6 +339,7 @@ hipError_t ns_update(const Plan& P, const f16* B, const XPair& x, const XPair& y
     d.C = nullptr;
     d.CT = nullptr;
     d.W = sink->W; d.ldw = sink->ldw; d.idx = sink->idx; d.lr = sink->lr; d.Oout = sink->Oout;
+    d.sO = sink->sO;
     d.kval = (int)P.k; d.mval = (int)P.m; d.nrows = (int)P.n;
   }
   d.M = (int)P.sp; d.N = (int)P.Lp; d.K = (int)P.sp; d.batch = P.B;
@@ -423,22 +427,26 @@ dion3_status step_impl(BatchPtr<float> W, BatchPtr<float> M, BatchPtr<const floa
                               bf.a.XT, P.kp * P.mp, (int)P.kp, (int)P.mp, s));
   }
   if (!norm) {
-    const UpdateSink sink = {W, ld, idx, lr, (f16*)O_out};
+    const UpdateSink sink = {W, ld, idx, lr, (f16*)O_out, k * m};
     st = orthogonalize(P, cfg, bf, sink, s);
     if (st != DION3_OK) return st;
   } else {
-    // O (rows layout [batch][k][m]) into the free X buffer, then the
+    // O into the free X buffer, each matrix's rows [k][m] inside that
+    // matrix's own padded block (so that in the fused one-launch path no
+    // workgroup writes where another matrix is still being read), then the
     // per-neuron normalization and the update; the row statistics reuse the
     // score region and the per-matrix scale the norm region
     f16* Obuf = free_pair(cfg, bf).X;
-    const UpdateSink sink = {{nullptr, 0, nullptr}, 0, idx, lr, Obuf};
+    const long long sO = P.kp * P.mp;
+    const UpdateSink sink = {{nullptr, 0, nullptr}, 0, idx, lr, Obuf, sO};
     st = orthogonalize(P, cfg, bf, sink, s);
     if (st != DION3_OK) return st;
-    HIP_TRY(launch_normalize(Obuf, batch, (int)k, (int)m, idx, V, norm->beta2, norm->eps, W, ld, lr,
-                             (float2*)l1, scale, s));
+    HIP_TRY(launch_normalize(Obuf, sO, batch, (int)k, (int)m, idx, V, norm->beta2, norm->eps, W, ld,
+                             lr, (float2*)l1, scale, s));
     if (O_out)
-      HIP_TRY(hipMemcpyAsync(O_out, Obuf, (size_t)batch * k * m * sizeof(uint16_t),
-                             hipMemcpyDeviceToDevice, s));
+      HIP_TRY(hipMemcpy2DAsync(O_out, (size_t)k * m * sizeof(uint16_t), Obuf,
+                               (size_t)sO * sizeof(uint16_t), (size_t)k * m * sizeof(uint16_t),
+                               (size_t)batch, hipMemcpyDeviceToDevice, s));
   }
   if (idx_out)
     HIP_TRY(hipMemcpyAsync(idx_out, idx, (size_t)batch * k * sizeof(int32_t),
@@ -585,7 +593,7 @@ dion3_status dion3_gram_ns(const uint16_t* X, uint16_t* O, int32_t batch, int64_
   HIP_TRY(launch_topk(nullptr, sq, batch, (int)k, (int)k, idx, scale, (double)cfg.eps, s));
   HIP_TRY(launch_gather_f16(Xb, batch, (int)m, m, (int)k, scale, bf.a.X, bf.a.XT, P.kp * P.mp,
                             (int)P.kp, (int)P.mp, s));
-  const UpdateSink sink = {{nullptr, 0, nullptr}, 0, idx, 0.0f, (f16*)O};
+  const UpdateSink sink = {{nullptr, 0, nullptr}, 0, idx, 0.0f, (f16*)O, k * m};
   st = orthogonalize(P, cfg, bf, sink, s);
   if (st != DION3_OK) return st;
   return DION3_OK;

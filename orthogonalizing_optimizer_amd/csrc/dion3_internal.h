@@ -51,13 +51,15 @@ struct GemmDesc {
   // layout (the C pass when sink == 1, the CT pass when sink == 2) is not
   // stored; instead, for output row r < kval and column c < mval,
   //   W[b][idx[b][r]][c] = fma(-lr, O[r][c], W[...])   (when W has pointers)
-  //   Oout[b][r][c] = O[r][c]                         (when Oout is set).
+  //   Oout[b * sO + r * mval + c] = O[r][c]           (when Oout is set;
+  //                                                    sO >= kval * mval).
   int sink;
   BatchPtr<float> W;
   long long ldw;
   const int* idx;
   float lr;
   f16* Oout;
+  long long sO;            // elements between the Oout blocks of consecutive matrices
   int kval, mval, nrows;   // nrows: rows of W (row indices outside are skipped)
 };
 // Launches the product; records it in the timing trace (when enabled) under
@@ -102,16 +104,19 @@ hipError_t launch_gather_f16(BatchPtr<const f16> Xin, int batch, int m, long lon
 // side pads to 128, one workgroup per matrix: X_math [128][Lp] and its
 // transpose XT [Lp][128] per matrix at stride sX (halves), Y/YT the second
 // pair written by a restart.  The result goes to the fused update (W, idx,
-// lr; rows layout = X_math, or its transpose when tr) and/or Oout [k][m].
+// lr; rows layout = X_math, or its transpose when tr) and/or Oout ([k][m]
+// per matrix, matrices sO elements apart).
 hipError_t launch_gram_ns_small(f16* X, f16* XT, f16* Y, f16* YT, long long sX, int batch, int Lp,
                                 bool tr, const dion3_ns_cfg& cfg, BatchPtr<float> W, long long ldw,
-                                const int* idx, float lr, f16* Oout, int kval, int mval, int nrows,
+                                const int* idx, float lr, f16* Oout, long long sO, int kval,
+                                int mval, int nrows,
                                 double trace_flops, hipStream_t s);
 
-// Per-neuron normalization of O ([batch][k][m] fp16, rows layout) and the
+// Per-neuron normalization of O ([k][m] fp16 rows per matrix, matrices sO
+// elements apart) and the
 // update W[idx[i]] -= lr * U_i; V holds one fp32 state per row of each
 // matrix; stats ([batch][k]) and g ([batch]) are scratch.
-hipError_t launch_normalize(const f16* O, int batch, int k, int m, const int* idx,
+hipError_t launch_normalize(const f16* O, long long sO, int batch, int k, int m, const int* idx,
                             BatchPtr<float> V, float beta2, float eps, BatchPtr<float> W,
                             long long ldw, float lr, float2* stats, double* g, hipStream_t s);
 

@@ -43,17 +43,19 @@ struct GemmArgs {
   const int* idx;
   float lr;
   f16* Oout;
+  long long sO;
   int kval, mval, nrows;
 };
 
 // One 8-wide chunk of the output in rows layout (row r, columns c..c+7)
 // goes to the fused update instead of memory: W[idx[r]][c..] -= lr * O and
-// optionally O_out[r][c..] = O.
+// optionally O_out[r][c..] = O (matrix b's rows start sO elements after
+// matrix b-1's).
 __device__ __forceinline__ void sink_chunk(const GemmArgs& p, int b, int r, int c, const half8& v) {
   if (r >= p.kval || c >= p.mval) return;
   const bool full = c + 8 <= p.mval;
   if (p.Oout) {
-    f16* o = p.Oout + ((long long)b * p.kval + r) * p.mval + c;
+    f16* o = p.Oout + (long long)b * p.sO + (long long)r * p.mval + c;
     if (full && ((uintptr_t)o & 15) == 0) {
       *(half8*)o = v;
     } else {
@@ -455,6 +457,7 @@ hipError_t launch(const GemmDesc& d, hipStream_t s) {
   p.total = (int)total;
   p.alpha = d.alpha; p.beta = d.beta; p.gamma = d.gamma;
   p.sink = d.sink; p.W = d.W; p.ldw = d.ldw; p.idx = d.idx; p.lr = d.lr; p.Oout = d.Oout;
+  p.sO = d.sO;
   p.kval = d.kval; p.mval = d.mval; p.nrows = d.nrows;
   hipLaunchKernelGGL((k_gemm<C, ROLE, LOWER, EPI>), dim3(p.total), dim3(C::NT), 0, s, p);
   return hipGetLastError();

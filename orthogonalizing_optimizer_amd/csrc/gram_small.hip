@@ -54,6 +54,7 @@ struct SmallArgs {
   const int* idx;
   float lr;
   f16* Oout;
+  long long sO;                  // elements between consecutive matrices' O blocks
   int kval, mval, nrows;
 };
 
@@ -272,7 +273,7 @@ __device__ __forceinline__ void sink8(const SmallArgs& p, int b, int orow, int o
   if (orow >= p.kval || ocol >= p.mval) return;
   const bool full = ocol + 8 <= p.mval;
   if (p.Oout) {
-    f16* o = p.Oout + ((long long)b * p.kval + orow) * p.mval + ocol;
+    f16* o = p.Oout + (long long)b * p.sO + (long long)orow * p.mval + ocol;
     if (full && ((uintptr_t)o & 15) == 0) {
       *(half8*)o = v;
     } else {
@@ -416,14 +417,14 @@ __global__ __launch_bounds__(NT, 1) void k_gram_ns_small(SmallArgs p) {
 
 hipError_t launch_gram_ns_small(f16* X, f16* XT, f16* Y, f16* YT, long long sX, int batch, int Lp,
                                 bool tr, const dion3_ns_cfg& cfg, BatchPtr<float> W, long long ldw,
-                                const int* idx, float lr, f16* Oout, int kval, int mval, int nrows,
-                                double trace_flops, hipStream_t s) {
+                                const int* idx, float lr, f16* Oout, long long sO, int kval,
+                                int mval, int nrows, double trace_flops, hipStream_t s) {
   if (Lp < S || Lp % S != 0 || batch < 1) return hipErrorInvalidValue;
   SmallArgs p;
   p.X = X; p.XT = XT; p.Y = Y; p.YT = YT; p.sX = sX;
   p.Lp = Lp; p.tr = tr ? 1 : 0;
   p.cfg = cfg;
-  p.W = W; p.ldw = ldw; p.idx = idx; p.lr = lr; p.Oout = Oout;
+  p.W = W; p.ldw = ldw; p.idx = idx; p.lr = lr; p.Oout = Oout; p.sO = sO;
   p.kval = kval; p.mval = mval; p.nrows = nrows;
   TraceScope trace("gram_ns_fused_128", trace_flops, 0.0, s);
   hipLaunchKernelGGL(k_gram_ns_small, dim3(batch), dim3(NT), 0, s, p);

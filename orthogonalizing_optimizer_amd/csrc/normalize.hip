@@ -28,17 +28,18 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// Row stats of O (rows layout [b][k][m], contiguous): s_i = sum of squares
-// (fp32 lanes, fixed butterfly), the state update and r_i.
-__global__ __launch_bounds__(256) void k_norm_rows(const f16* __restrict__ O, int k, int m,
-                                                   const int* __restrict__ idx, BatchPtr<float> V,
+// Row stats of O (rows [k][m] per matrix, matrices sO apart): s_i = sum of
+// squares (fp32 lanes, fixed butterfly), the state update and r_i.
+__global__ __launch_bounds__(256) void k_norm_rows(const f16* __restrict__ O, long long sO, int k,
+                                                   int m, const int* __restrict__ idx,
+                                                   BatchPtr<float> V,
                                                    float beta2, float eps,
                                                    float2* __restrict__ stats) {
   const int b = blockIdx.y;
   const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (i >= k) return;                       // whole waves leave together
-  const f16* __restrict__ row = O + ((long long)b * k + i) * m;
+  const f16* __restrict__ row = O + (long long)b * sO + (long long)i * m;
   float acc = 0.0f;
   const bool vec = ((uintptr_t)row & 15) == 0;
   int j = 0;
@@ -91,8 +92,8 @@ __global__ __launch_bounds__(256) void k_norm_scale(const float2* __restrict__ s
 
 // W[idx[i]][j] = fma(-lr g r_i, O_ij, W[idx[i]][j]): one workgroup per 4 rows
 // of O, 64 lanes along a row, 4 columns per lane per pass.
-__global__ __launch_bounds__(256) void k_norm_update(const f16* __restrict__ O, int k, int m,
-                                                     const int* __restrict__ idx,
+__global__ __launch_bounds__(256) void k_norm_update(const f16* __restrict__ O, long long sO, int k,
+                                                     int m, const int* __restrict__ idx,
                                                      BatchPtr<float> W, long long ldw, float lr,
                                                      const float2* __restrict__ stats,
                                                      const double* __restrict__ g) {
@@ -101,7 +102,7 @@ __global__ __launch_bounds__(256) void k_norm_update(const f16* __restrict__ O, 
   const int lane = threadIdx.x & 63;
   if (i >= k) return;
   const float c = -lr * (float)g[b] * stats[(long long)b * k + i].y;
-  const f16* __restrict__ src = O + ((long long)b * k + i) * m;
+  const f16* __restrict__ src = O + (long long)b * sO + (long long)i * m;
   float* __restrict__ w = W.get(b) + (long long)idx[(long long)b * k + i] * ldw;
   for (int j = 4 * lane; j < m; j += 4 * 64) {
     if (j + 3 < m && ((uintptr_t)(w + j) & 15) == 0) {
@@ -112,21 +113,23 @@ __global__ __launch_bounds__(256) void k_norm_update(const f16* __restrict__ O, 
       x.w = __builtin_fmaf(c, (float)src[j + 3], x.w);
       *(float4*)(w + j) = x;
     } else {
-      for (int e = 0; e < 4 && j + e < m; ++e) w[j + e] = __builtin_fmaf(c, (float)src[j + e], w[j + e]);
+      for (int e = 0; e < 4 && j + e < m; ++e)
+        w[j + e] = __builtin_fmaf(c, (float)src[j + e], w[j + e]);
     }
   }
 }
 
 }  // namespace
 
-hipError_t launch_normalize(const f16* O, int batch, int k, int m, const int* idx,
+hipError_t launch_normalize(const f16* O, long long sO, int batch, int k, int m, const int* idx,
                             BatchPtr<float> V, float beta2, float eps, BatchPtr<float> W,
                             long long ldw, float lr, float2* stats, double* g, hipStream_t s) {
   const dim3 grid((k + 3) / 4, batch);
   const double km = (double)batch * k * m;
   {
     TraceScope ts("norm_rows", 0.0, km * 2.0, s);
-    hipLaunchKernelGGL(k_norm_rows, grid, dim3(256), 0, s, O, k, m, idx, V, beta2, eps, stats);
+    hipLaunchKernelGGL(k_norm_rows, grid, dim3(256), 0, s, O, sO, k, m, idx, V, beta2, eps,
+                       stats);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -137,7 +140,8 @@ hipError_t launch_normalize(const f16* O, int batch, int k, int m, const int* id
     if (e != hipSuccess) return e;
   }
   TraceScope ts("norm_update", 0.0, km * 10.0, s);
-  hipLaunchKernelGGL(k_norm_update, grid, dim3(256), 0, s, O, k, m, idx, W, ldw, lr, stats, g);
+  hipLaunchKernelGGL(k_norm_update, grid, dim3(256), 0, s, O, sO, k, m, idx, W, ldw, lr, stats,
+                     g);
   return hipGetLastError();
 }
 
