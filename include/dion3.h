@@ -30,6 +30,10 @@
  *   - Concurrent calls are safe when their workspaces and outputs are
  *     disjoint.  The library's only mutable global state is the thread-local
  *     last HIP error and the optional timing trace (dion3_trace_*).
+ *   - Within one call the matrices written (W, M and, for the normalized
+ *     step, V; every matrix of a megabatch) must not overlap each other in
+ *     memory; W and M must not alias.  Inputs that are only read (G, and X
+ *     of dion3_gram_ns) may alias outputs: they are consumed first.
  */
 #ifndef DION3_H
 #define DION3_H
