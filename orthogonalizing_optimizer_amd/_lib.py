@@ -269,11 +269,18 @@ def gram_ns(X, cfg: Optional[NsCfg] = None, ws: Optional[Workspace] = None):
 
 def step(W, M, k: int, lr: float, mu: float, cfg: Optional[NsCfg] = None,
          return_idx: bool = False, return_O: bool = False, ws: Optional[Workspace] = None,
-         G=None):
+         G=None, norm=None):
     """One Dion3 step on one matrix, in place on W and M (fp32, [n, m]).
     With G (same shape and strides as M), M <- M + G first, fused into the
-    row scoring."""
+    row scoring.  With norm = (V, beta2, eps) (V: fp32 [n] state, updated in
+    place) the update is normalized per neuron, through the megabatch entry
+    point with one matrix."""
     torch = _torch()
+    if norm is not None:
+        V, beta2, eps = norm
+        idx, O = step_megabatch([W], [M], k, lr, mu, cfg, return_idx, return_O, ws,
+                                Gs=None if G is None else [G], norm=([V], beta2, eps))
+        return (idx[0] if idx is not None else None), (O[0] if O is not None else None)
     _req(W, torch.float32, "W")
     _req(M, torch.float32, "M")
     if W.shape != M.shape or W.dim() != 2 or W.stride() != M.stride() or W.stride(1) != 1:

@@ -132,3 +132,20 @@ def test_norm_fused_many_matrices_equals_tiled():
         outs.append((Wd.cpu().numpy(), Vd.cpu().numpy(), O.cpu().numpy()))
     for a, b in zip(outs[0], outs[1]):
         assert a.tobytes() == b.tobytes()
+
+
+def test_norm_single_matrix_equals_megabatch():
+    say("norm single vs megabatch")
+    n, m, k = 300, 200, 75
+    W = host_gaussian((n, m), 108, std=0.02)
+    M = host_gaussian((n, m), 109)
+    Wa, Ma, Va = dev(W), dev(M), torch.zeros(n, device=DEV)
+    idx_a, O_a = d3.step(Wa, Ma, k, LR, MU, norm=(Va, BETA2, EPS), return_idx=True, return_O=True)
+    Wb, Mb, Vb = dev(W), dev(M), torch.zeros(n, device=DEV)
+    idx_b, O_b = d3.step_megabatch([Wb], [Mb], k, LR, MU, norm=([Vb], BETA2, EPS),
+                                   return_idx=True, return_O=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(idx_a.cpu().numpy(), idx_b[0].cpu().numpy())
+    assert O_a.cpu().numpy().tobytes() == O_b[0].cpu().numpy().tobytes()
+    for x, y in ((Wa, Wb), (Ma, Mb), (Va, Vb)):
+        assert x.cpu().numpy().tobytes() == y.cpu().numpy().tobytes()
