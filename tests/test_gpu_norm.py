@@ -149,3 +149,25 @@ def test_norm_single_matrix_equals_megabatch():
     assert O_a.cpu().numpy().tobytes() == O_b[0].cpu().numpy().tobytes()
     for x, y in ((Wa, Wb), (Ma, Mb), (Va, Vb)):
         assert x.cpu().numpy().tobytes() == y.cpu().numpy().tobytes()
+
+
+@pytest.mark.parametrize("iters,restarts,method,path", [
+    (5, (), d3.NS_GRAM, d3.PATH_TILED), (5, (3,), d3.NS_GRAM, d3.PATH_TILED),
+    (7, (3, 6), d3.NS_GRAM, d3.PATH_TILED), (7, (3, 6), d3.NS_GRAM, d3.PATH_FUSED),
+    (5, (), d3.NS_GRAM, d3.PATH_FUSED), (5, (), d3.NS_STANDARD, d3.PATH_AUTO),
+    (4, (), d3.NS_STANDARD, d3.PATH_AUTO)])
+def test_norm_o_buffer_never_aliases_the_iteration(iters, restarts, method, path):
+    """O goes to the X pair the iteration no longer reads; which pair that is
+    depends on the parity of restarts (Gram) or iterations (standard).  For
+    every parity the normalized path's O equals the plain path's bit for bit."""
+    say("norm O buffer", iters, restarts, method, path)
+    n, m, k = 300, 200, 75 if path != d3.PATH_TILED else 150
+    W = host_gaussian((n, m), [110, iters], std=0.02)
+    M = host_gaussian((n, m), [111, iters])
+    cfg = d3.ns_cfg(iters=iters, restart_at=restarts, coeffs=[orc.MUON_COEFFS] * iters,
+                    method=method, path=path)
+    _, O_plain = d3.step(dev(W), dev(M), k, LR, MU, cfg, return_O=True)
+    _, O_norm = d3.step(dev(W), dev(M), k, LR, MU, cfg, return_O=True,
+                        norm=(torch.zeros(n, device=DEV), BETA2, EPS))
+    torch.cuda.synchronize()
+    assert O_norm.cpu().numpy().tobytes() == O_plain.cpu().numpy().tobytes()
