@@ -238,3 +238,21 @@ def test_norm_step_rejects_bad_arguments_before_launch():
     assert lib.dion3_step_megabatch_norm(FAKE, FAKE, None, FAKE, 1, 64, 32, 32, 16, 0.04, 0.95,
                                          None, ctypes.byref(good), None, None, FAKE + 16, nb,
                                          None) == ERR_WS
+
+
+def test_header_compiles_as_c99_and_host_calls_work_from_c(tmp_path):
+    """The ABI from plain C: gcc -std=c99 -Wall -Werror against include/dion3.h,
+    linked to the built library, host-only calls (no device work)."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not available")
+    pkg = os.path.join(ROOT, "orthogonalizing_optimizer_amd")
+    exe = str(tmp_path / "abi_check")
+    cmd = [gcc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-I", os.path.join(ROOT, "include"),
+           os.path.join(ROOT, "tests", "c", "abi_check.c"), "-o", exe, "-L", pkg, "-ldion3",
+           "-Wl,-rpath," + pkg, "-lm"]
+    subprocess.run(cmd, check=True)
+    out = subprocess.run([exe], check=True, capture_output=True, text=True)
+    assert "c abi ok" in out.stdout
