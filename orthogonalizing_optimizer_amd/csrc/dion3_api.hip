@@ -151,6 +151,11 @@ double L_of(const Plan& P) { return dbl(P.tr ? P.k : P.m); }
 // The Gram side works on X_math (sp x Lp): the selected rows when k <= m,
 // their transpose when k > m.  Its row-form copy has row stride Lp and its
 // transpose (Lp x sp) row stride sp.
+// Inner dimension of a product over an unpadded extent: the padded
+// operands are zero past it (the Gram-side cross terms between the real and
+// the padded block are zero too), so only K steps that touch it are run.
+int k_loop(double extent) { return (int)pad_to((long long)extent, kKStep); }
+
 const f16* xmath(const Plan& P, const XPair& x) { return P.tr ? x.XT : x.X; }
 const f16* xmathT(const Plan& P, const XPair& x) { return P.tr ? x.X : x.XT; }
 
@@ -162,7 +167,7 @@ hipError_t gram(const Plan& P, const XPair& x, f16* R, hipStream_t s) {
   d.role = kRoleGram;
   d.A = d.B = xmath(P, x); d.sA = d.sB = P.kp * P.mp; d.lda = d.ldb = (int)P.Lp;
   d.C = R; d.sC = P.sp * P.sp; d.ldc = (int)P.sp;
-  d.M = d.N = (int)P.sp; d.K = (int)P.Lp; d.batch = P.B;
+  d.M = d.N = (int)P.sp; d.K = k_loop(L_of(P)); d.batch = P.B;
   d.lower = true; d.epilogue = false;
   d.alpha = 1.0f;
   return launch_gemm(d, s);
@@ -180,7 +185,7 @@ hipError_t symm(const Plan& P, const f16* A, const f16* B, const f16* D, f16* C,
   d.B = B; d.sB = ss; d.ldb = (int)P.sp;
   d.C = C; d.sC = ss; d.ldc = (int)P.sp;
   d.D = D; d.sD = ss; d.ldd = (int)P.sp;
-  d.M = d.N = d.K = (int)P.sp; d.batch = P.B;
+  d.M = d.N = (int)P.sp; d.K = k_loop(sv); d.batch = P.B;
   d.lower = true; d.epilogue = epi;
   d.alpha = alpha; d.beta = beta; d.gamma = gamma;
   return launch_gemm(d, s);
@@ -221,7 +226,7 @@ hipError_t rect(const Plan& P, const f16* Q, const XPair& x, const XPair& y, boo
     d.sO = sink->sO;
     d.kval = (int)P.k; d.mval = (int)P.m; d.nrows = (int)P.n;
   }
-  d.M = (int)P.sp; d.N = (int)P.Lp; d.K = (int)P.sp; d.batch = P.B;
+  d.M = (int)P.sp; d.N = (int)P.Lp; d.K = k_loop(sv); d.batch = P.B;
   d.lower = false; d.epilogue = false;
   d.alpha = 1.0f;
   return launch_gemm(d, s);

@@ -25,6 +25,11 @@ constexpr int kTile = 128;
 
 inline long long pad_to(long long x, long long p) { return (x + p - 1) / p * p; }
 
+// K advances through every GEMM 64 at a time.  A product whose inner
+// dimension is padded past the next multiple of 64 only reads the padding's
+// zero cross terms there, so its K loop stops at that multiple.
+constexpr int kKStep = 64;
+
 // C = alpha * A * B^T (+ beta * D + gamma * I when `epilogue`), batched.
 //  A is M x K stored A[m * lda + k]; B is N x K stored B[n * ldb + k].
 //  Rows outside M (or N) read as zero; outputs outside M x N are not written.
