@@ -108,6 +108,114 @@ struct Cfg {
 typedef Cfg<256, 2, 4, 1> CfgL;   // large tile, 8 waves of 128 x 64 (2 waves per SIMD)
 typedef Cfg<128, 2, 2, 2> CfgS;   // small tile
 
+// The fused update for one staged tile (S: the fp16 tile in LDS, row stride
+// C::EP).  SINK 1: output rows are the tile's rows (O row m0 + r); SINK 2:
+// they are its columns (O row n0 + c).  Each thread owns NCH 8-wide chunks
+// at fixed positions; it loads the selected-row indices of all of them
+// first, then the W rows of BATCH chunks at a time, and only then does the
+// fma and the stores, so the global round trips overlap instead of running
+// one after another per chunk.  Chunks at a ragged column end, or W rows
+// that are not 16-byte aligned, take sink_chunk's element path.
+template <class C, int SINK>
+__device__ __forceinline__ void sink_tile(const GemmArgs& p, int b, int m0, int n0,
+                                          const f16* __restrict__ S, int tid) {
+  constexpr int NCH = C::BM * C::BN / 8 / C::NT;
+  constexpr int BATCH = 8;
+  static_assert(NCH % BATCH == 0, "chunk batches");
+  constexpr int CPR = C::BN / 8;   // SINK 1: chunks per staged row
+  static_assert(C::NT % CPR == 0 && C::NT % C::BN == 0, "fixed chunk columns per thread");
+  float* __restrict__ Wb = (p.W.ptrs || p.W.base) ? p.W.get(b) : nullptr;
+  const bool vec = Wb && ((uintptr_t)Wb & 15) == 0 && (p.ldw & 3) == 0;
+  const int* __restrict__ ib = p.idx + (long long)b * p.kval;
+  // output row and first column of chunk q, and its place in S
+  auto where = [&](int q, int& gr, int& gc, int& sr, int& sc) {
+    if (SINK == 1) {
+      sr = tid / CPR + q * (C::NT / CPR);
+      sc = (tid % CPR) * 8;
+      gr = m0 + sr;
+      gc = n0 + sc;
+    } else {
+      sc = tid % C::BN;
+      sr = (tid / C::BN + q * (C::NT / C::BN)) * 8;
+      gr = n0 + sc;
+      gc = m0 + sr;
+    }
+  };
+  auto staged = [&](int sr, int sc) {
+    half8 v;
+    if (SINK == 1) {
+      v = *(const half8*)(S + sr * C::EP + sc);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = S[(sr + k) * C::EP + sc];
+    }
+    return v;
+  };
+  int row[NCH];
+  if (SINK == 1) {
+#pragma unroll
+    for (int q = 0; q < NCH; ++q) {
+      int gr, gc, sr, sc;
+      where(q, gr, gc, sr, sc);
+      row[q] = gr < p.kval ? ib[gr] : -1;
+    }
+  } else {
+    int gr, gc, sr, sc;
+    where(0, gr, gc, sr, sc);
+    const int r = gr < p.kval ? ib[gr] : -1;
+#pragma unroll
+    for (int q = 0; q < NCH; ++q) row[q] = r;
+  }
+#pragma unroll
+  for (int q0 = 0; q0 < NCH; q0 += BATCH) {
+    float4 w0[BATCH], w1[BATCH];
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u) {
+      int gr, gc, sr, sc;
+      where(q0 + u, gr, gc, sr, sc);
+      const int r = row[q0 + u];
+      if (vec && r >= 0 && r < p.nrows && gc + 8 <= p.mval) {
+        const float4* w = (const float4*)(Wb + (long long)r * p.ldw + gc);
+        w0[u] = w[0];
+        w1[u] = w[1];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u) {
+      int gr, gc, sr, sc;
+      where(q0 + u, gr, gc, sr, sc);
+      if (gr >= p.kval || gc >= p.mval) continue;
+      const half8 v = staged(sr, sc);
+      const int r = row[q0 + u];
+      if (!(vec && r >= 0 && r < p.nrows && gc + 8 <= p.mval)) {
+        sink_chunk(p, b, gr, gc, v);
+        continue;
+      }
+      if (p.Oout) {
+        f16* o = p.Oout + (long long)b * p.sO + (long long)gr * p.mval + gc;
+        if (((uintptr_t)o & 15) == 0) {
+          *(half8*)o = v;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) o[e] = v[e];
+        }
+      }
+      float4 a = w0[u], c = w1[u];
+      a.x = __builtin_fmaf(-p.lr, (float)v[0], a.x);
+      a.y = __builtin_fmaf(-p.lr, (float)v[1], a.y);
+      a.z = __builtin_fmaf(-p.lr, (float)v[2], a.z);
+      a.w = __builtin_fmaf(-p.lr, (float)v[3], a.w);
+      c.x = __builtin_fmaf(-p.lr, (float)v[4], c.x);
+      c.y = __builtin_fmaf(-p.lr, (float)v[5], c.y);
+      c.z = __builtin_fmaf(-p.lr, (float)v[6], c.z);
+      c.w = __builtin_fmaf(-p.lr, (float)v[7], c.w);
+      float4* w = (float4*)(Wb + (long long)r * p.ldw + gc);
+      w[0] = a;
+      w[1] = c;
+    }
+  }
+}
+
 __device__ __forceinline__ void tri_index(int t, int& bi, int& bj) {
   int i = (int)((sqrtf(8.0f * (float)t + 1.0f) - 1.0f) * 0.5f);
   while (i * (i + 1) / 2 > t) --i;
@@ -463,15 +571,23 @@ __global__ __launch_bounds__(C::NT, (C::BM == 256 ? 1 : 2)) void k_gemm(GemmArgs
     __syncthreads();
   }
 
+  if constexpr (!LOWER) {
+    if (p.sink == 1) {
+      sink_tile<C, 1>(p, b, m0, n0, S, tid);
+      return;
+    }
+    if (p.sink == 2) {
+      sink_tile<C, 2>(p, b, m0, n0, S, tid);
+      return;
+    }
+  }
   f16* __restrict__ Cb = p.C ? p.C + (long long)b * p.sC : nullptr;
-  if (Cb || (!LOWER && p.sink == 1)) {   // rows: C[m0 + r][n0 + c]
+  if (Cb) {   // rows: C[m0 + r][n0 + c]
     for (int e = tid; e < C::BM * (C::BN / 8); e += C::NT) {
       const int r = e / (C::BN / 8), c8 = e - r * (C::BN / 8);
       const int gr = m0 + r, gc = n0 + c8 * 8;
       if (gr < p.M && gc < p.N) {
-        const half8 v = *(const half8*)(S + r * C::EP + c8 * 8);
-        if (!LOWER && p.sink == 1) sink_chunk(p, b, gr, gc, v);
-        else *(half8*)(Cb + (long long)gr * p.ldc + gc) = v;
+        *(half8*)(Cb + (long long)gr * p.ldc + gc) = *(const half8*)(S + r * C::EP + c8 * 8);
       }
     }
   }
@@ -485,7 +601,7 @@ __global__ __launch_bounds__(C::NT, (C::BM == 256 ? 1 : 2)) void k_gemm(GemmArgs
     Tb = p.CT + (long long)b * p.sCT;
     ldt = p.ldct;
   }
-  if (Tb || (!LOWER && p.sink == 2)) {
+  if (Tb) {
     for (int e = tid; e < C::BN * (C::BM / 8); e += C::NT) {
       const int r8 = e / C::BN, c = e - r8 * C::BN;
       const int gr = n0 + c, gc = m0 + r8 * 8;
@@ -493,8 +609,7 @@ __global__ __launch_bounds__(C::NT, (C::BM == 256 ? 1 : 2)) void k_gemm(GemmArgs
         half8 v;
 #pragma unroll
         for (int k = 0; k < 8; ++k) v[k] = S[(r8 * 8 + k) * C::EP + c];
-        if (!LOWER && p.sink == 2) sink_chunk(p, b, gr, gc, v);
-        else *(half8*)(Tb + (long long)gr * ldt + gc) = v;
+        *(half8*)(Tb + (long long)gr * ldt + gc) = v;
       }
     }
   }
@@ -551,7 +666,7 @@ hipError_t launch_gemm(const GemmDesc& d, hipStream_t s) {
   if (d.M % 128 || d.N % 128 || d.K % BK || d.K <= 0 || d.batch <= 0) return hipErrorInvalidValue;
   if (d.lower && (d.M != d.N || d.CT || !d.C)) return hipErrorInvalidValue;
   if (!d.lower && !d.C && !d.CT && !d.sink) return hipErrorInvalidValue;
-  if (d.sink && (d.lower || (d.sink == 1 && d.C) || (d.sink == 2 && d.CT))) return hipErrorInvalidValue;
+  if (d.sink && (d.lower || d.C || d.CT || (d.sink != 1 && d.sink != 2))) return hipErrorInvalidValue;
   switch (d.role) {
     case kRoleGram:
       if (!d.lower || d.epilogue) break;
