@@ -48,6 +48,7 @@ struct GemmArgs {
   f16* Oout;
   long long sO;
   int kval, mval, nrows;
+  int tcols;   // column outputs through a column-major restaging of the tile
 };
 
 // One 8-wide chunk of the output in rows layout (row r, columns c..c+7)
@@ -521,7 +522,7 @@ __global__ __launch_bounds__(C::NT, (C::BM == 256 ? 1 : 2)) void k_gemm(GemmArgs
                                      fb0, acc);
   }
 
-  // Epilogue: final fp32 value (alpha, D, gamma I) -> fp16 tile in LDS.
+  // Epilogue: final fp32 value (alpha, D, gamma I) -> fp16, kept in registers.
   // Accumulator layout of the 32x32 MFMA: lane l, value v holds row
   // 8*(v/4) + 4*(l/32) + v%4, column l%32 of its 32x32 block, so each lane
   // owns runs of 4 consecutive rows of one column.  The 4 values
@@ -530,7 +531,7 @@ __global__ __launch_bounds__(C::NT, (C::BM == 256 ? 1 : 2)) void k_gemm(GemmArgs
   // transposed copy of X for the standard-iteration update.
   typedef f16 half4 __attribute__((ext_vector_type(4)));
   const f16* __restrict__ Db = EPI && p.D ? p.D + (long long)b * p.sD : nullptr;
-  f16* S = lds;
+  half4 hv[C::FM][C::FN][4];
 #pragma unroll
   for (int i = 0; i < C::FM; ++i)
 #pragma unroll
@@ -559,40 +560,13 @@ __global__ __launch_bounds__(C::NT, (C::BM == 256 ? 1 : 2)) void k_gemm(GemmArgs
           }
         }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) S[(r + e) * C::EP + c] = (f16)val[e];
+        for (int e = 0; e < 4; ++e) hv[i][j][v4][e] = (f16)val[e];
       }
-  __syncthreads();
-  if (LOWER && bi == bj) {
-    // diagonal tile: the upper half takes the mirror of the lower half
-    for (int e = tid; e < C::BM * C::BM; e += C::NT) {
-      const int r = e / C::BM, c = e - r * C::BM;
-      if (r < c) S[r * C::EP + c] = S[c * C::EP + r];
-    }
-    __syncthreads();
-  }
 
-  if constexpr (!LOWER) {
-    if (p.sink == 1) {
-      sink_tile<C, 1>(p, b, m0, n0, S, tid);
-      return;
-    }
-    if (p.sink == 2) {
-      sink_tile<C, 2>(p, b, m0, n0, S, tid);
-      return;
-    }
-  }
+  // Outputs: rows (C[m0 + r][n0 + c], or the fused update) and columns (the
+  // mirror of an off-diagonal lower tile into C, or the transposed output
+  // CT[n0 + c][m0 + r]).
   f16* __restrict__ Cb = p.C ? p.C + (long long)b * p.sC : nullptr;
-  if (Cb) {   // rows: C[m0 + r][n0 + c]
-    for (int e = tid; e < C::BM * (C::BN / 8); e += C::NT) {
-      const int r = e / (C::BN / 8), c8 = e - r * (C::BN / 8);
-      const int gr = m0 + r, gc = n0 + c8 * 8;
-      if (gr < p.M && gc < p.N) {
-        *(half8*)(Cb + (long long)gr * p.ldc + gc) = *(const half8*)(S + r * C::EP + c8 * 8);
-      }
-    }
-  }
-  // columns: the mirror of an off-diagonal lower tile into C, or the
-  // transposed output CT[n0 + c][m0 + r]
   f16* __restrict__ Tb = nullptr;
   int ldt = 0;
   if (LOWER) {
@@ -601,16 +575,87 @@ __global__ __launch_bounds__(C::NT, (C::BM == 256 ? 1 : 2)) void k_gemm(GemmArgs
     Tb = p.CT + (long long)b * p.sCT;
     ldt = p.ldct;
   }
-  if (Tb) {
-    for (int e = tid; e < C::BN * (C::BM / 8); e += C::NT) {
-      const int r8 = e / C::BN, c = e - r8 * C::BN;
-      const int gr = n0 + c, gc = m0 + r8 * 8;
-      if (gr < p.N && gc < p.M) {
-        half8 v;
+  const bool tcols = Tb && p.tcols;
+  f16* S = lds;
+  if (Cb || (!LOWER && p.sink) || (Tb && !tcols)) {
+    // the tile row-major in LDS, row stride C::EP
 #pragma unroll
-        for (int k = 0; k < 8; ++k) v[k] = S[(r8 * 8 + k) * C::EP + c];
-        *(half8*)(Tb + (long long)gr * ldt + gc) = v;
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+        for (int v4 = 0; v4 < 4; ++v4) {
+          const int r = wm * C::WTM + i * 32 + 8 * v4 + 4 * (lane >> 5);
+          const int c = wn * C::WTN + j * 32 + (lane & 31);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) S[(r + e) * C::EP + c] = hv[i][j][v4][e];
+        }
+    __syncthreads();
+    if (LOWER && bi == bj) {
+      // diagonal tile: the upper half takes the mirror of the lower half
+      for (int e = tid; e < C::BM * C::BM; e += C::NT) {
+        const int r = e / C::BM, c = e - r * C::BM;
+        if (r < c) S[r * C::EP + c] = S[c * C::EP + r];
       }
+      __syncthreads();
+    }
+    if constexpr (!LOWER) {
+      if (p.sink == 1) {
+        sink_tile<C, 1>(p, b, m0, n0, S, tid);
+        return;
+      }
+      if (p.sink == 2) {
+        sink_tile<C, 2>(p, b, m0, n0, S, tid);
+        return;
+      }
+    }
+    if (Cb) {
+      for (int e = tid; e < C::BM * (C::BN / 8); e += C::NT) {
+        const int r = e / (C::BN / 8), c8 = e - r * (C::BN / 8);
+        const int gr = m0 + r, gc = n0 + c8 * 8;
+        if (gr < p.M && gc < p.N)
+          *(half8*)(Cb + (long long)gr * p.ldc + gc) = *(const half8*)(S + r * C::EP + c8 * 8);
+      }
+    }
+    if (Tb && !tcols) {
+      // columns read from the row-major tile, consecutive lanes on
+      // consecutive output rows
+      for (int e = tid; e < C::BN * (C::BM / 8); e += C::NT) {
+        const int r8 = e / C::BN, c = e - r8 * C::BN;
+        const int gr = n0 + c, gc = m0 + r8 * 8;
+        if (gr < p.N && gc < p.M) {
+          half8 v;
+#pragma unroll
+          for (int k = 0; k < 8; ++k) v[k] = S[(r8 * 8 + k) * C::EP + c];
+          *(half8*)(Tb + (long long)gr * ldt + gc) = v;
+        }
+      }
+    }
+  }
+  if (tcols) {
+    // the tile again, column-major (St[c][r], row stride EPT: each lane's
+    // run of 4 rows of one column is one 8-byte write), then written with
+    // consecutive lanes on consecutive 8-wide chunks of one output row
+    constexpr int EPT = C::BM + 8;
+    static_assert(C::BN * EPT <= C::LDS, "column-major staging fits");
+    if (Cb) __syncthreads();
+    f16* St = lds;
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+        for (int v4 = 0; v4 < 4; ++v4) {
+          const int r = wm * C::WTM + i * 32 + 8 * v4 + 4 * (lane >> 5);
+          const int c = wn * C::WTN + j * 32 + (lane & 31);
+          *(half4*)(St + c * EPT + r) = hv[i][j][v4];
+        }
+    __syncthreads();
+    for (int e = tid; e < C::BN * (C::BM / 8); e += C::NT) {
+      const int c = e / (C::BM / 8), r8 = e - c * (C::BM / 8);
+      const int gr = n0 + c, gc = m0 + r8 * 8;
+      if (gr < p.N && gc < p.M)
+        *(half8*)(Tb + (long long)gr * ldt + gc) = *(const half8*)(St + c * EPT + r8 * 8);
     }
   }
 }
@@ -632,6 +677,11 @@ hipError_t launch(const GemmDesc& d, hipStream_t s) {
   p.sink = d.sink; p.W = d.W; p.ldw = d.ldw; p.idx = d.idx; p.lr = d.lr; p.Oout = d.Oout;
   p.sO = d.sO;
   p.kval = d.kval; p.mval = d.mval; p.nrows = d.nrows;
+  // The column-major restaging costs two more barriers and an LDS pass; it
+  // pays for the transposed output always and for the symmetric mirror once
+  // K is long (measured: +10 % on 64 x 2816^2 symmetric products, -3 % at
+  // 1024^2).
+  p.tcols = (!LOWER || d.K >= 2048) ? 1 : 0;
   hipLaunchKernelGGL((k_gemm<C, ROLE, LOWER, EPI>), dim3(p.total), dim3(C::NT), 0, s, p);
   return hipGetLastError();
 }
