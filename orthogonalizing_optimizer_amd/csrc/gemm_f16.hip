@@ -530,7 +530,36 @@ __global__ __launch_bounds__(C::NT, (C::BM == 256 ? 1 : 2)) void k_gemm(GemmArgs
   // transposed addend: D itself when it is symmetric (the polynomial), the
   // transposed copy of X for the standard-iteration update.
   typedef f16 half4 __attribute__((ext_vector_type(4)));
-  const f16* __restrict__ Db = EPI && p.D ? p.D + (long long)b * p.sD : nullptr;
+  typedef int int2v __attribute__((ext_vector_type(2)));
+  // The addend's 32 runs per lane are loaded before any of them is used, so
+  // their latencies overlap.  They go through a buffer resource bounded by
+  // D's N rows: columns gc >= N read as zero without a branch; rows gr >= M
+  // belong to outputs that are never stored.
+  half4 dvs[C::FM][C::FN][4];
+  if (EPI) {
+    if (p.D) {
+      const __amdgpu_buffer_rsrc_t Dr = operand_rsrc(p.D + (long long)b * p.sD, p.N, p.ldd);
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+          for (int v4 = 0; v4 < 4; ++v4) {
+            const int gr = m0 + wm * C::WTM + i * 32 + 8 * v4 + 4 * (lane >> 5);
+            const int gc = min(n0 + wn * C::WTN + j * 32 + (lane & 31), p.N);
+            const unsigned off = (unsigned)(gc * p.ldd + gr) * 2u;   // D is under 2^31 bytes
+            const int2v raw = __builtin_amdgcn_raw_buffer_load_b64(Dr, off, 0, 0);
+            dvs[i][j][v4] = __builtin_bit_cast(half4, raw);
+          }
+    } else {
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+          for (int v4 = 0; v4 < 4; ++v4) dvs[i][j][v4] = half4{};
+    }
+  }
   half4 hv[C::FM][C::FN][4];
 #pragma unroll
   for (int i = 0; i < C::FM; ++i)
@@ -545,8 +574,7 @@ __global__ __launch_bounds__(C::NT, (C::BM == 256 ? 1 : 2)) void k_gemm(GemmArgs
         for (int e = 0; e < 4; ++e) val[e] = acc[i][j][4 * v4 + e];
         if (EPI) {
           const int gr = m0 + r, gc = n0 + c;
-          half4 dv = {};
-          if (Db && gr < p.M && gc < p.N) dv = *(const half4*)(Db + (long long)gc * p.ldd + gr);
+          const half4 dv = dvs[i][j][v4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             val[e] = __builtin_fmaf(val[e], p.alpha, p.beta * (float)dv[e]);
