@@ -33,11 +33,11 @@ KERNEL_SYMBOLS = {
     "gemm_symm_256": "k_gemm<Cfg<256, 2, 4, 1>, 2, true, false>",
     "gemm_rect_256": "k_gemm<Cfg<256, 2, 4, 1>, 3, false, false>",
     "gemm_nsx_256": "k_gemm<Cfg<256, 2, 4, 1>, 4, false, true>",
-    "gemm_nsx_128": "k_gemm<Cfg<128, 2, 2, 2>, 4, false, true>",
-    "gemm_gram_128": "k_gemm<Cfg<128, 2, 2, 2>, 0, true, false>",
-    "gemm_poly_128": "k_gemm<Cfg<128, 2, 2, 2>, 1, true, true>",
-    "gemm_symm_128": "k_gemm<Cfg<128, 2, 2, 2>, 2, true, false>",
-    "gemm_rect_128": "k_gemm<Cfg<128, 2, 2, 2>, 3, false, false>",
+    "gemm_nsx_128": "k_gemm<Cfg<128, 2, 2, 1>, 4, false, true>",
+    "gemm_gram_128": "k_gemm<Cfg<128, 2, 2, 1>, 0, true, false>",
+    "gemm_poly_128": "k_gemm<Cfg<128, 2, 2, 1>, 1, true, true>",
+    "gemm_symm_128": "k_gemm<Cfg<128, 2, 2, 1>, 2, true, false>",
+    "gemm_rect_128": "k_gemm<Cfg<128, 2, 2, 1>, 3, false, false>",
     "row_score": "k_row_score_f32",
     "accum_score": "k_accum_score_f32",
     "topk": "k_topk",

@@ -14,12 +14,13 @@
 // K advances 64 at a time through two LDS buffers (rows padded by 8 halves:
 // conflict-free 16-byte fragment reads).  Operands arrive through raw buffer
 // loads (rows past the matrix read as zero) into a register prefetch of one
-// K step (large tile; its 128 accumulators leave no room for more at two
-// waves per SIMD) or two K steps (small tile); the next tile's LDS stores
-// and global loads are issued at the start of each step's MFMAs.  In the
-// large tile the instruction order of each k-slice is fixed by hand (see
-// mma_step) and the next step's first fragments are read under the current
-// step's last MFMAs.  The epilogue
+// K step (the large tile's 128 accumulators leave no room for more at two
+// waves per SIMD; a second set in the small tile spilled once the fragments
+// were carried across steps); the next tile's LDS stores and global loads
+// are issued at the start of each step's MFMAs.  The
+// instruction order of each k-slice is fixed by hand (see mma_step) and the
+// next step's first fragments are read under the current step's last MFMAs.
+// The epilogue
 // stages the fp16 tile in LDS and writes it with 16-byte stores as rows, and
 // for the mirrored (symmetric) or transposed outputs as columns.
 #include "dion3_internal.h"
@@ -96,6 +97,7 @@ template <int BM_, int WAVES_M, int WAVES_N, int PF_>
 struct Cfg {
   static constexpr int BM = BM_, BN = BM_;
   static constexpr int PF = PF_;                         // K steps of register prefetch
+  static_assert(PF == 1, "the K loop carries one register set");
   static constexpr int NT = 64 * WAVES_M * WAVES_N;
   static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
   static constexpr int FM = WTM / 32, FN = WTN / 32;
@@ -107,7 +109,7 @@ struct Cfg {
 };
 
 typedef Cfg<256, 2, 4, 1> CfgL;   // large tile, 8 waves of 128 x 64 (2 waves per SIMD)
-typedef Cfg<128, 2, 2, 2> CfgS;   // small tile
+typedef Cfg<128, 2, 2, 1> CfgS;   // small tile
 
 // The fused update for one staged tile (S: the fp16 tile in LDS, row stride
 // C::EP).  SINK 1: output rows are the tile's rows (O row m0 + r); SINK 2:
@@ -256,26 +258,6 @@ __device__ __forceinline__ void lstore(f16* __restrict__ s, int tid, const half8
   }
 }
 
-template <class C>
-__device__ __forceinline__ void mma_stage(const f16* __restrict__ st, int wm, int wn, int lane,
-                                          floatx16 (&acc)[C::FM][C::FN]) {
-  const f16* a_s = st + (wm * C::WTM + (lane & 31)) * LDSK + (lane >> 5) * 8;
-  const f16* b_s = st + (C::BM + wn * C::WTN + (lane & 31)) * LDSK + (lane >> 5) * 8;
-#pragma unroll
-  for (int kk = 0; kk < BK / 16; ++kk) {
-    half8 af[C::FM], bf[C::FN];
-#pragma unroll
-    for (int i = 0; i < C::FM; ++i) af[i] = *(const half8*)(a_s + i * 32 * LDSK + kk * 16);
-#pragma unroll
-    for (int j = 0; j < C::FN; ++j) bf[j] = *(const half8*)(b_s + j * 32 * LDSK + kk * 16);
-#pragma unroll
-    for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-      for (int j = 0; j < C::FN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
-  }
-}
-
 // Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
 constexpr int kSgMfma = 0x008, kSgVmemRead = 0x020, kSgDsRead = 0x100, kSgDsWrite = 0x200;
 
@@ -315,7 +297,8 @@ __device__ __forceinline__ void mma_step(const f16* __restrict__ st, f16* __rest
                                          int boff, half8 (&fa0)[C::FM], half8 (&fb0)[C::FN],
                                          floatx16 (&acc)[C::FM][C::FN]) {
   constexpr int NS = BK / 16, NR = C::FM + C::FN, NM = C::FM * C::FN;
-  static_assert(NM >= NR && NM == 2 * C::CH, "slice schedules assume these counts");
+  constexpr int WPM = 2 * C::CH / NM;   // LDS writes (and global loads) per MFMA in slice 0
+  static_assert(NM >= NR && WPM * NM == 2 * C::CH, "slice schedules assume these counts");
   const f16* a_s = st + aoff;
   const f16* b_s = st + boff;
   half8 af[2][C::FM], bf[2][C::FN];
@@ -361,8 +344,8 @@ __device__ __forceinline__ void mma_step(const f16* __restrict__ st, f16* __rest
 #pragma unroll
       for (int q = 0; q < NM; ++q) {
         __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSgDsWrite, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSgVmemRead, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSgDsWrite, WPM, 0);
+        __builtin_amdgcn_sched_group_barrier(kSgVmemRead, WPM, 0);
       }
     } else {
 #pragma unroll
@@ -370,7 +353,7 @@ __device__ __forceinline__ void mma_step(const f16* __restrict__ st, f16* __rest
         __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
         __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(kSgMfma, NM - NR, 0);
+      if constexpr (NM > NR) __builtin_amdgcn_sched_group_barrier(kSgMfma, NM - NR, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -422,66 +405,7 @@ __global__ __launch_bounds__(C::NT, (C::BM == 256 ? 1 : 2)) void k_gemm(GemmArgs
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
   const int nk = p.K / BK;
-  if constexpr (C::PF == 2) {
-    // Two register sets; set s holds the tile of K step t with t % 2 == s.
-    // Step t multiplies LDS stage t%2 and stores tile t+1 into the other
-    // stage; after the barrier its register set is refilled with tile t+3.
-    half8 ra0[C::CH], rb0[C::CH], ra1[C::CH], rb1[C::CH];
-    gload<C>(Ab, p.lda, m0, 0, tid, ra0);
-    gload<C>(Bb, p.ldb, n0, 0, tid, rb0);
-    lstore<C>(lds, tid, ra0);
-    lstore<C>(lds + C::BM * LDSK, tid, rb0);
-    if (nk > 1) {
-      gload<C>(Ab, p.lda, m0, BK, tid, ra1);
-      gload<C>(Bb, p.ldb, n0, BK, tid, rb1);
-    }
-    if (nk > 2) {
-      gload<C>(Ab, p.lda, m0, 2 * BK, tid, ra0);
-      gload<C>(Bb, p.ldb, n0, 2 * BK, tid, rb0);
-    }
-    __syncthreads();
-    // while four or more steps remain every store and load happens: no
-    // branch in the loop body; the tail below keeps
-    // the conditions
-    int kt0 = 0;
-    for (; kt0 + 4 < nk; kt0 += 2) {
-      mma_stage<C>(lds, wm, wn, lane, acc);
-      lstore<C>(lds + C::STAGE, tid, ra1);
-      lstore<C>(lds + C::STAGE + C::BM * LDSK, tid, rb1);
-      __syncthreads();
-      gload<C>(Ab, p.lda, m0, (kt0 + 3) * BK, tid, ra1);
-      gload<C>(Bb, p.ldb, n0, (kt0 + 3) * BK, tid, rb1);
-      mma_stage<C>(lds + C::STAGE, wm, wn, lane, acc);
-      lstore<C>(lds, tid, ra0);
-      lstore<C>(lds + C::BM * LDSK, tid, rb0);
-      __syncthreads();
-      gload<C>(Ab, p.lda, m0, (kt0 + 4) * BK, tid, ra0);
-      gload<C>(Bb, p.ldb, n0, (kt0 + 4) * BK, tid, rb0);
-    }
-    for (int kt = kt0; kt < nk; kt += 2) {
-      mma_stage<C>(lds, wm, wn, lane, acc);
-      if (kt + 1 < nk) {
-        lstore<C>(lds + C::STAGE, tid, ra1);
-        lstore<C>(lds + C::STAGE + C::BM * LDSK, tid, rb1);
-      }
-      __syncthreads();
-      if (kt + 3 < nk) {
-        gload<C>(Ab, p.lda, m0, (kt + 3) * BK, tid, ra1);
-        gload<C>(Bb, p.ldb, n0, (kt + 3) * BK, tid, rb1);
-      }
-      if (kt + 1 >= nk) break;
-      mma_stage<C>(lds + C::STAGE, wm, wn, lane, acc);
-      if (kt + 2 < nk) {
-        lstore<C>(lds, tid, ra0);
-        lstore<C>(lds + C::BM * LDSK, tid, rb0);
-      }
-      __syncthreads();
-      if (kt + 4 < nk) {
-        gload<C>(Ab, p.lda, m0, (kt + 4) * BK, tid, ra0);
-        gload<C>(Bb, p.ldb, n0, (kt + 4) * BK, tid, rb0);
-      }
-    }
-  } else {
+  {
     // One register set.  Step t multiplies stage t%2; at its start tile t+1
     // goes from the registers into the other stage (free since the barrier
     // that ended step t-1) and tile t+2 is requested into the registers.
