@@ -1,0 +1,82 @@
+"""GPU: the symmetric GEMM entry points on every code path their launches
+can take: the 256 tile (at least 512 lower 256-tiles per launch) and the
+128 tile; a ragged last tile row (a side that is a multiple of 128 but not
+of 256); K below 2048 (columns read from the row-major staging) and from
+2048 up (columns restaged column-major); diagonal and off-diagonal tiles.
+Each case checks sampled matrices against the fp64 product and every
+matrix for exact symmetry (the upper triangle is the mirror of the lower)."""
+import sys
+
+import numpy as np
+import pytest
+
+from tests.parity import rel
+from workloads import host_gaussian
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+import orthogonalizing_optimizer_amd as d3  # noqa: E402
+
+DEV = "cuda:0"
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def lower_tiles(side, tile):
+    t = (side + tile - 1) // tile
+    return t * (t + 1) // 2
+
+
+# (batch, rows, cols) and the path each case takes:
+#   52 x 1024 x 2304: 256 tile (520 lower tiles), K >= 2048
+#   35 x 1152 x 1024: 256 tile (525), ragged last tile row, K < 2048
+#   2 x 384 x 2560:   128 tile, ragged for the 256 rule, K >= 2048
+#   3 x 640 x 640:    128 tile, K < 2048
+SYRK_CASES = [(52, 1024, 2304), (35, 1152, 1024), (2, 384, 2560), (3, 640, 640)]
+
+
+@pytest.mark.parametrize("B,rows,cols", SYRK_CASES)
+def test_syrk_every_tile_path(B, rows, cols):
+    big = lower_tiles(rows, 256) * B >= 512
+    say("syrk paths", B, rows, cols, "256 tile" if big else "128 tile",
+        "K >= 2048" if cols >= 2048 else "K < 2048")
+    A = (host_gaussian((B, rows, cols), [60, B, rows, cols]) * 0.03).astype(np.float16)
+    R = d3.syrk_f16(dev(A)).cpu().numpy()
+    for b in range(B):
+        assert np.array_equal(R[b], R[b].T), b
+    for b in sorted({0, B // 2, B - 1}):
+        A64 = A[b].astype(np.float64)
+        assert rel(R[b], A64 @ A64.T) <= 2e-3, b
+
+
+# (batch, side): 15 x 2048 takes the 256 tile (540 lower tiles) with K = 2048;
+# 4 x 2048 the 128 tile with K = 2048; 35 x 1152 the 256 tile, ragged, K < 2048
+SYMM_CASES = [(15, 2048), (4, 2048), (35, 1152)]
+
+
+@pytest.mark.parametrize("B,s", SYMM_CASES)
+def test_symm_poly_every_tile_path(B, s):
+    big = lower_tiles(s, 256) * B >= 512
+    say("symm poly paths", B, s, "256 tile" if big else "128 tile")
+    G = host_gaussian((B, s, s), [61, B, s])
+    A = ((G + G.transpose(0, 2, 1)) * (0.5 / np.sqrt(s))).astype(np.float16)   # symmetric
+    a, b_, c = 3.4445, -4.7750, 2.0315
+    Ad = dev(A)
+    C = d3.symm_f16(Ad, Ad, Ad, alpha=c, beta=b_, gamma=a).cpu().numpy()
+    P = d3.symm_f16(Ad, Ad).cpu().numpy()
+    for i in range(B):
+        assert np.array_equal(C[i], C[i].T), i
+        assert np.array_equal(P[i], P[i].T), i
+    for i in sorted({0, B - 1}):
+        Af = A[i].astype(np.float64)
+        A2 = Af @ Af
+        assert rel(P[i], A2) <= 2e-3, i
+        assert rel(C[i], c * A2 + b_ * Af + a * np.eye(s)) <= 2e-3, i
