@@ -431,3 +431,32 @@ def test_dion3_optimizer_two_steps():
             assert rel(W1 - W[i], ref["W"] - W[i]) <= O_TOL, (it, i)
             W[i], M[i] = W1, M1
 
+
+
+# (n, m, ld, k) through the tiled path: the fused update's element path for
+# rows that are not 16-byte aligned (odd ld) and ragged last chunks (m % 8),
+# its vector path (ld % 4 == 0), with the output rows as the tile's rows
+# (k <= m) and as its columns (k > m)
+TILED_UPDATE_CASES = [(300, 203, 207, 150), (400, 77, 81, 250), (512, 520, 520, 200),
+                      (333, 1000, 1003, 300), (260, 96, 100, 100)]
+
+
+@pytest.mark.parametrize("n,m,ld,k", TILED_UPDATE_CASES)
+def test_tiled_update_alignment_and_layouts(n, m, ld, k):
+    say("tiled update", n, m, ld, k)
+    Wb = dev(host_gaussian((n, ld), [70, n, m], std=0.02))
+    Mb = dev(host_gaussian((n, ld), [71, n, m]))
+    W0, M0 = Wb.cpu().numpy().copy(), Mb.cpu().numpy().copy()
+    cfg = d3.ns_cfg(path=d3.PATH_TILED)
+    idx, O = d3.step(Wb[:, :m], Mb[:, :m], k, 0.04, 0.95, cfg, return_idx=True, return_O=True)
+    W1, M1 = Wb.cpu().numpy(), Mb.cpu().numpy()
+    assert W1[:, m:].tobytes() == W0[:, m:].tobytes() and M1[:, m:].tobytes() == M0[:, m:].tobytes()
+    check_step(np.ascontiguousarray(W0[:, :m]), np.ascontiguousarray(M0[:, :m]),
+               np.ascontiguousarray(W1[:, :m]), np.ascontiguousarray(M1[:, :m]),
+               idx.cpu().numpy(), O.cpu().numpy(), k, 0.04, 0.95)
+    if min(k, m) <= 128:   # the fused kernel covers this Gram side: same bits
+        Wf, Mf = dev(W0), dev(M0)
+        idf, Of = d3.step(Wf[:, :m], Mf[:, :m], k, 0.04, 0.95, d3.ns_cfg(path=d3.PATH_FUSED),
+                          return_idx=True, return_O=True)
+        assert Wf.cpu().numpy().tobytes() == W1.tobytes()
+        assert Of.cpu().numpy().tobytes() == O.cpu().numpy().tobytes()
