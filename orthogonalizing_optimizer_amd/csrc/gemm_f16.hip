@@ -454,27 +454,45 @@ __global__ __launch_bounds__(C::NT, (C::BM == 256 ? 1 : 2)) void k_gemm(GemmArgs
   // transposed addend: D itself when it is symmetric (the polynomial), the
   // transposed copy of X for the standard-iteration update.
   typedef f16 half4 __attribute__((ext_vector_type(4)));
-  typedef int int2v __attribute__((ext_vector_type(2)));
-  // The addend's 32 runs per lane are loaded before any of them is used, so
-  // their latencies overlap.  They go through a buffer resource bounded by
-  // D's N rows: columns gc >= N read as zero without a branch; rows gr >= M
-  // belong to outputs that are never stored.
+  // The addend D is read as the block D[n0 + c][m0 + r]: each lane needs,
+  // for its run of rows r..r+3 of column c, the 4 contiguous halves
+  // D[n0 + c][m0 + r .. + 3].  The block is staged in LDS (row stride DST)
+  // with coalesced 16-byte loads, 32 lanes per D row, through a buffer
+  // resource bounded by D's N rows (rows n0 + c >= N read as zero; columns
+  // past M belong to outputs that are never stored), then each run is one
+  // 8-byte LDS read.  The LDS is free here: the last K step's barrier came
+  // after every operand read.
   half4 dvs[C::FM][C::FN][4];
   if (EPI) {
+    constexpr int DST = C::BM + 8;
+    static_assert(C::BN * DST <= C::LDS, "addend block fits");
     if (p.D) {
       const __amdgpu_buffer_rsrc_t Dr = operand_rsrc(p.D + (long long)b * p.sD, p.N, p.ldd);
+      constexpr int NCHD = C::BN * (C::BM / 8) / C::NT;   // 16-byte chunks per thread
+      int4v dchunk[NCHD];
+#pragma unroll
+      for (int q = 0; q < NCHD; ++q) {
+        const int e = tid + q * C::NT, c = e / (C::BM / 8), r8 = e % (C::BM / 8);
+        const unsigned off = (unsigned)(min(n0 + c, p.N) * p.ldd + m0 + 8 * r8) * 2u;
+        dchunk[q] = __builtin_amdgcn_raw_buffer_load_b128(Dr, off, 0, 0);
+      }
+#pragma unroll
+      for (int q = 0; q < NCHD; ++q) {
+        const int e = tid + q * C::NT, c = e / (C::BM / 8), r8 = e % (C::BM / 8);
+        *(int4v*)(lds + c * DST + 8 * r8) = dchunk[q];
+      }
+      __syncthreads();
 #pragma unroll
       for (int i = 0; i < C::FM; ++i)
 #pragma unroll
         for (int j = 0; j < C::FN; ++j)
 #pragma unroll
           for (int v4 = 0; v4 < 4; ++v4) {
-            const int gr = m0 + wm * C::WTM + i * 32 + 8 * v4 + 4 * (lane >> 5);
-            const int gc = min(n0 + wn * C::WTN + j * 32 + (lane & 31), p.N);
-            const unsigned off = (unsigned)(gc * p.ldd + gr) * 2u;   // D is under 2^31 bytes
-            const int2v raw = __builtin_amdgcn_raw_buffer_load_b64(Dr, off, 0, 0);
-            dvs[i][j][v4] = __builtin_bit_cast(half4, raw);
+            const int r = wm * C::WTM + i * 32 + 8 * v4 + 4 * (lane >> 5);
+            const int c = wn * C::WTN + j * 32 + (lane & 31);
+            dvs[i][j][v4] = *(const half4*)(lds + c * DST + r);
           }
+      __syncthreads();   // the staging below reuses the LDS
     } else {
 #pragma unroll
       for (int i = 0; i < C::FM; ++i)
