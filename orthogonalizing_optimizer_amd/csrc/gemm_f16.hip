@@ -33,7 +33,6 @@ constexpr int LDSK = BK + 8;   // halves per LDS operand row
 
 typedef f16 half8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 struct GemmArgs {
   const f16* A; const f16* B; f16* C; f16* CT; const f16* D;
@@ -118,8 +117,7 @@ typedef Cfg<128, 2, 2, 1> CfgS;   // small tile
 // at fixed positions; it loads the selected-row indices of all of them
 // first, then the W rows of BATCH chunks at a time, and only then does the
 // fma and the stores, so the global round trips overlap instead of running
-// one after another per chunk.  W is touched once per step, so its loads and
-// stores carry the nontemporal hint (multiply-back about 1 % faster).  Chunks at a ragged column end, or W rows
+// one after another per chunk.  Chunks at a ragged column end, or W rows
 // that are not 16-byte aligned, take sink_chunk's element path.
 template <class C, int SINK>
 __device__ __forceinline__ void sink_tile(const GemmArgs& p, int b, int m0, int n0,
@@ -180,10 +178,9 @@ __device__ __forceinline__ void sink_tile(const GemmArgs& p, int b, int m0, int 
       where(q0 + u, gr, gc, sr, sc);
       const int r = row[q0 + u];
       if (vec && r >= 0 && r < p.nrows && gc + 8 <= p.mval) {
-        const f32x4* w = (const f32x4*)(Wb + (long long)r * p.ldw + gc);
-        const f32x4 x0 = __builtin_nontemporal_load(w), x1 = __builtin_nontemporal_load(w + 1);
-        w0[u] = make_float4(x0[0], x0[1], x0[2], x0[3]);
-        w1[u] = make_float4(x1[0], x1[1], x1[2], x1[3]);
+        const float4* w = (const float4*)(Wb + (long long)r * p.ldw + gc);
+        w0[u] = w[0];
+        w1[u] = w[1];
       }
     }
 #pragma unroll
@@ -215,9 +212,9 @@ __device__ __forceinline__ void sink_tile(const GemmArgs& p, int b, int m0, int 
       c.y = __builtin_fmaf(-p.lr, (float)v[5], c.y);
       c.z = __builtin_fmaf(-p.lr, (float)v[6], c.z);
       c.w = __builtin_fmaf(-p.lr, (float)v[7], c.w);
-      f32x4* w = (f32x4*)(Wb + (long long)r * p.ldw + gc);
-      __builtin_nontemporal_store(f32x4{a.x, a.y, a.z, a.w}, w);
-      __builtin_nontemporal_store(f32x4{c.x, c.y, c.z, c.w}, w + 1);
+      float4* w = (float4*)(Wb + (long long)r * p.ldw + gc);
+      w[0] = a;
+      w[1] = c;
     }
   }
 }
