@@ -281,9 +281,10 @@ __global__ __launch_bounds__(TK_THREADS) void k_topk(const double* __restrict__ 
 // row of M, writes X in rows layout directly and, through an LDS tile, its
 // transpose XT (eight lanes per 128-byte run of an XT row), so that every
 // product of the Gram iteration reads K-contiguous operands; with DECAY it
-// also writes the rows of M back times mu.  Every access is a single-use
-// stream far larger than the caches, so the fp32 loads and all stores carry
-// the nontemporal hint (measured on the 7B set: 10-15 % less kernel time than
+// also writes the rows of M back times mu.  The rows of M are read and
+// written once, and X and XT (read again only by the next products) are far
+// larger than the caches, so the fp32 loads and all stores carry the
+// nontemporal hint (measured on the 7B set: 10-15 % less kernel time than
 // plain accesses with one thread per XT run, bitwise the same outputs).
 constexpr int GR = 64, GC = 256, GPAD = 8;
 
