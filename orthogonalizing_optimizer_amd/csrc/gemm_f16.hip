@@ -562,10 +562,28 @@ __global__ __launch_bounds__(C::NT, (C::BM == 256 ? 1 : 2)) void k_gemm(GemmArgs
         }
     __syncthreads();
     if (LOWER && bi == bj) {
-      // diagonal tile: the upper half takes the mirror of the lower half
-      for (int e = tid; e < C::BM * C::BM; e += C::NT) {
-        const int r = e / C::BM, c = e - r * C::BM;
-        if (r < c) S[r * C::EP + c] = S[c * C::EP + r];
+      // diagonal tile: the upper half takes the mirror of the lower half.
+      // Reads touch only the lower triangle and writes only the upper one,
+      // so each thread reads a batch of MB values before writing any of
+      // them: the LDS round trips overlap instead of running one after
+      // another (a dependent read and write per element had made diagonal
+      // tiles' epilogues about twice as long as the others').
+      constexpr int ITER = C::BM * C::BM / C::NT;
+      constexpr int MB = 16;
+      static_assert(ITER % MB == 0, "mirror batches");
+#pragma unroll
+      for (int i0 = 0; i0 < ITER; i0 += MB) {
+        f16 v[MB];
+#pragma unroll
+        for (int u = 0; u < MB; ++u) {
+          const int e = tid + (i0 + u) * C::NT, r = e / C::BM, c = e - r * C::BM;
+          v[u] = r < c ? S[c * C::EP + r] : (f16)0.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < MB; ++u) {
+          const int e = tid + (i0 + u) * C::NT, r = e / C::BM, c = e - r * C::BM;
+          if (r < c) S[r * C::EP + c] = v[u];
+        }
       }
       __syncthreads();
     }
