@@ -548,45 +548,49 @@ __global__ __launch_bounds__(C::NT, (C::BM == 256 ? 1 : 2)) void k_gemm(GemmArgs
   const bool tcols = Tb && p.tcols;
   f16* S = lds;
   if (Cb || (!LOWER && p.sink) || (Tb && !tcols)) {
-    // the tile row-major in LDS, row stride C::EP
-#pragma unroll
-    for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-      for (int j = 0; j < C::FN; ++j)
-#pragma unroll
-        for (int v4 = 0; v4 < 4; ++v4) {
-          const int r = wm * C::WTM + i * 32 + 8 * v4 + 4 * (lane >> 5);
-          const int c = wn * C::WTN + j * 32 + (lane & 31);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) S[(r + e) * C::EP + c] = hv[i][j][v4][e];
-        }
-    __syncthreads();
+    // the tile row-major in LDS, row stride C::EP.  A diagonal tile of a
+    // symmetric product keeps its lower triangle (diagonal included) and
+    // fills the upper one with the mirror of the lower values in the same
+    // pass: a lane's run of 4 rows r..r+3 of column c lies below the
+    // diagonal where r + e > c, and then goes to row c, columns r + e (one
+    // 8-byte write when the whole run is below).  The two sets of positions
+    // are disjoint, so one barrier covers both.
+    // (The two cases are separate loops: a per-element test in the common
+    // one slowed every tile's staging.)
     if (LOWER && bi == bj) {
-      // diagonal tile: the upper half takes the mirror of the lower half.
-      // Reads touch only the lower triangle and writes only the upper one,
-      // so each thread reads a batch of MB values before writing any of
-      // them: the LDS round trips overlap instead of running one after
-      // another (a dependent read and write per element had made diagonal
-      // tiles' epilogues about twice as long as the others').
-      constexpr int ITER = C::BM * C::BM / C::NT;
-      constexpr int MB = 16;
-      static_assert(ITER % MB == 0, "mirror batches");
 #pragma unroll
-      for (int i0 = 0; i0 < ITER; i0 += MB) {
-        f16 v[MB];
+      for (int i = 0; i < C::FM; ++i)
 #pragma unroll
-        for (int u = 0; u < MB; ++u) {
-          const int e = tid + (i0 + u) * C::NT, r = e / C::BM, c = e - r * C::BM;
-          v[u] = r < c ? S[c * C::EP + r] : (f16)0.0f;
-        }
+        for (int j = 0; j < C::FN; ++j)
 #pragma unroll
-        for (int u = 0; u < MB; ++u) {
-          const int e = tid + (i0 + u) * C::NT, r = e / C::BM, c = e - r * C::BM;
-          if (r < c) S[r * C::EP + c] = v[u];
-        }
-      }
-      __syncthreads();
+          for (int v4 = 0; v4 < 4; ++v4) {
+            const int r = wm * C::WTM + i * 32 + 8 * v4 + 4 * (lane >> 5);
+            const int c = wn * C::WTN + j * 32 + (lane & 31);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (r + e >= c) S[(r + e) * C::EP + c] = hv[i][j][v4][e];
+            if (r > c) {
+              *(half4*)(S + c * C::EP + r) = hv[i][j][v4];
+            } else if (r + 3 > c) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                if (r + e > c) S[c * C::EP + r + e] = hv[i][j][v4][e];
+            }
+          }
+    } else {
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+          for (int v4 = 0; v4 < 4; ++v4) {
+            const int r = wm * C::WTM + i * 32 + 8 * v4 + 4 * (lane >> 5);
+            const int c = wn * C::WTN + j * 32 + (lane & 31);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) S[(r + e) * C::EP + c] = hv[i][j][v4][e];
+          }
     }
+    __syncthreads();
     if constexpr (!LOWER) {
       if (p.sink == 1) {
         sink_tile<C, 1>(p, b, m0, n0, S, tid);
