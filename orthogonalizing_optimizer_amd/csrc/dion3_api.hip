@@ -188,6 +188,7 @@ hipError_t symm(const Plan& P, const f16* A, const f16* B, const f16* D, f16* C,
   d.M = d.N = (int)P.sp; d.K = k_loop(sv); d.batch = P.B;
   d.lower = true; d.epilogue = epi;
   d.alpha = alpha; d.beta = beta; d.gamma = gamma;
+  d.gdiag = (int)sv;   // the identity of the unpadded Gram side only
   return launch_gemm(d, s);
 }
 

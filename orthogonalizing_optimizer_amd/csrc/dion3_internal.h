@@ -51,6 +51,12 @@ struct GemmDesc {
   int M, N, K, batch;
   bool lower, epilogue;
   float alpha, beta, gamma;
+  // gamma is added on the diagonal elements (i, i) with i < gdiag only (0:
+  // all of them).  The Gram-side products pass the unpadded side, so the
+  // zero padding block stays exactly zero instead of growing as a power of
+  // the polynomial's constant term (which overflows fp16 after about nine
+  // iterations without a restart and then turns the cross terms into NaN).
+  int gdiag;
   double trace_flops;   // algorithmic flops of this launch, for the timing trace
   // Fused row-sparse update (rectangular products only): the output in rows
   // layout (the C pass when sink == 1, the CT pass when sink == 2) is not

@@ -41,6 +41,7 @@ struct GemmArgs {
   int M, N, K;
   int tilesM, tilesN, tilesPerMat, total;
   float alpha, beta, gamma;
+  int gdiag;   // gamma only on diagonal elements below this index
   int sink;
   BatchPtr<float> W;
   long long ldw;
@@ -520,7 +521,7 @@ __global__ __launch_bounds__(C::NT, (C::BM == 256 ? 1 : 2)) void k_gemm(GemmArgs
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             val[e] = __builtin_fmaf(val[e], p.alpha, p.beta * (float)dv[e]);
-            if (gr + e == gc) val[e] += p.gamma;
+            if (gr + e == gc && gc < p.gdiag) val[e] += p.gamma;
             // Keep the fp32 result as written (round to fp32, then to fp16):
             // otherwise the compiler may fuse the fma with the conversion
             // into one mixed-precision fma that rounds once, in some
@@ -666,6 +667,7 @@ hipError_t launch(const GemmDesc& d, hipStream_t s) {
   if (total <= 0 || total > 0x7fffffffLL) return hipErrorInvalidValue;
   p.total = (int)total;
   p.alpha = d.alpha; p.beta = d.beta; p.gamma = d.gamma;
+  p.gdiag = d.gdiag > 0 ? d.gdiag : d.M;
   p.sink = d.sink; p.W = d.W; p.ldw = d.ldw; p.idx = d.idx; p.lr = d.lr; p.Oout = d.Oout;
   p.sO = d.sO;
   p.kval = d.kval; p.mval = d.mval; p.nrows = d.nrows;

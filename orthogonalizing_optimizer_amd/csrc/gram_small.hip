@@ -127,7 +127,8 @@ __device__ __forceinline__ void mma_sym(const f16* A, const f16* B, const Wave& 
 // copy of their upper halves after a barrier.  The caller's barrier follows.
 template <bool POLY>
 __device__ __forceinline__ void epi_sym(f16* out, const floatx16 (&acc)[2][2], float alpha,
-                                        const f16* D, float beta, float gamma, const Wave& w) {
+                                        const f16* D, float beta, float gamma, const Wave& w,
+                                        int gd) {
   const bool swap = (w.wm == 0 && w.wn == 1);
   const int pr = swap ? 0 : w.wm * 64, qr = swap ? 64 : w.wn * 64;
 #pragma unroll
@@ -147,7 +148,7 @@ __device__ __forceinline__ void epi_sym(f16* out, const floatx16 (&acc)[2][2], f
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             val[e] = __builtin_fmaf(val[e], alpha, beta * (float)d[e]);
-            if (p + e == q) val[e] += gamma;
+            if (p + e == q && q < gd) val[e] += gamma;   // identity of the real block only
             asm("" : "+v"(val[e]));   // fp32 rounding, then fp16, as in the tiled kernels
           }
         }
@@ -185,15 +186,25 @@ __device__ __forceinline__ void epi_sym(f16* out, const floatx16 (&acc)[2][2], f
 
 // out = alpha A B + beta D + gamma I (POLY) or A B, all symmetric s x s in
 // LDS.  out may be A or B: the product is finished before anything is
-// written.
+// written.  The inner dimension runs to kn, the Gram side rounded up to 32:
+// past it every operand of the real block is zero padding, so the real
+// block's sums are the same bits (its accumulators start at +0, and adding
+// exact zeros changes no value and no sign), and the padding block, which
+// no real output ever reads, stays zero.
 template <bool POLY>
 __device__ __forceinline__ void symm_lds(f16* out, const f16* A, const f16* B, const f16* D,
-                                         float alpha, float beta, float gamma, const Wave& w) {
+                                         float alpha, float beta, float gamma, const Wave& w,
+                                         int kn, int sreal) {
   floatx16 acc[2][2];
   zero_acc(acc);
-  mma_sym<SL, S>(A, B, w, acc);
+  if (kn <= 32)
+    mma_sym<SL, 32>(A, B, w, acc);
+  else if (kn <= 64)
+    mma_sym<SL, 64>(A, B, w, acc);
+  else
+    mma_sym<SL, S>(A, B, w, acc);
   __syncthreads();
-  epi_sym<POLY>(out, acc, alpha, D, beta, gamma, w);
+  epi_sym<POLY>(out, acc, alpha, D, beta, gamma, w, sreal);
   __syncthreads();
 }
 
@@ -261,7 +272,7 @@ __device__ __forceinline__ void gram_small(f16* R, f16* xs, const f16* X, int Lp
       sl, Lp / BK, xs, w.tid, [](int t, int& r0, int& c0) { r0 = 0; c0 = t * BK; },
       [&](int) { mma_sym<XL, BK>(xs, xs, w, acc); });
   __syncthreads();
-  epi_sym<false>(R, acc, 1.0f, nullptr, 0.0f, 0.0f, w);
+  epi_sym<false>(R, acc, 1.0f, nullptr, 0.0f, 0.0f, w, S);
   __syncthreads();
 }
 
@@ -312,7 +323,7 @@ __device__ __forceinline__ void sink8(const SmallArgs& p, int b, int orow, int o
 // YT (restart) or, in rows layout, into the update (final).
 __device__ __forceinline__ void rect_small(const f16* Q, f16* xs, f16* SA, f16* SB, const f16* XT,
                                            int Lp, f16* Y, f16* YT, const SmallArgs& p, int b,
-                                           bool final_pass, const Wave& w) {
+                                           bool final_pass, const Wave& w, int kn) {
   const Slices sl = {XT, S};
   const bool rows = !final_pass || !p.tr, cols = !final_pass || p.tr;
   floatx16 acc[2][2];
@@ -323,7 +334,9 @@ __device__ __forceinline__ void rect_small(const f16* Q, f16* xs, f16* SA, f16* 
       mma<SL, XL, BK>(Q, w.wm * 64, xs, w.wn * 64, w.lane, acc);
       return;
     }
-    mma<SL, XL, BK>(Q + BK, w.wm * 64, xs, w.wn * 64, w.lane, acc);
+    // Q's columns from 64 on are zero padding when the Gram side is at
+    // most 64 (see symm_lds)
+    if (kn > BK) mma<SL, XL, BK>(Q + BK, w.wm * 64, xs, w.wn * 64, w.lane, acc);
     const int j0 = (t >> 1) * S;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -381,13 +394,17 @@ __global__ __launch_bounds__(NT, 1) void k_gram_ns_small(SmallArgs p) {
   f16* YT = p.YT + (long long)b * p.sX;
 
   f16 *R = lds, *Z = lds + S * SL, *Q = lds + 2 * S * SL, *T = lds + 3 * S * SL;
+  // the unpadded Gram side, and the inner extent of the s x s products: that
+  // side rounded up to 32
+  const int sreal = p.tr ? p.mval : p.kval;
+  const int kn = (sreal + 31) / 32 * 32;
   gram_small(R, xs, X, p.Lp, w);
   bool q_identity = true;
   const int iters = p.cfg.iters;
   for (int t = 1; t <= iters; ++t) {
     if (is_restart(p.cfg, t)) {      // X <- Q X, R <- X X^T, Q <- I
       if (!q_identity) {
-        rect_small(Q, xs, R, T, XT, p.Lp, Y, YT, p, b, false, w);
+        rect_small(Q, xs, R, T, XT, p.Lp, Y, YT, p, b, false, w, kn);
         f16* tx = X; X = Y; Y = tx;
         f16* tt = XT; XT = YT; YT = tt;
       }
@@ -395,22 +412,22 @@ __global__ __launch_bounds__(NT, 1) void k_gram_ns_small(SmallArgs p) {
       q_identity = true;
     }
     const float a = p.cfg.abc[t - 1][0], bb = p.cfg.abc[t - 1][1], c = p.cfg.abc[t - 1][2];
-    symm_lds<true>(Z, R, R, R, c, bb, a, w);            // Z = a I + b R + c R^2
+    symm_lds<true>(Z, R, R, R, c, bb, a, w, kn, sreal);            // Z = a I + b R + c R^2
     f16* Zv;
     if (q_identity) {                                    // Q = I: adopt Z
       f16* tmp = Q; Q = Z; Z = tmp;
       Zv = Q;
       q_identity = false;
     } else {
-      symm_lds<false>(Q, Z, Q, nullptr, 1.0f, 0.0f, 0.0f, w);   // Q <- Z Q
+      symm_lds<false>(Q, Z, Q, nullptr, 1.0f, 0.0f, 0.0f, w, kn, sreal);   // Q <- Z Q
       Zv = Z;
     }
     if (t < iters && !is_restart(p.cfg, t + 1)) {      // R <- Z R Z
-      symm_lds<false>(T, Zv, R, nullptr, 1.0f, 0.0f, 0.0f, w);
-      symm_lds<false>(R, T, Zv, nullptr, 1.0f, 0.0f, 0.0f, w);
+      symm_lds<false>(T, Zv, R, nullptr, 1.0f, 0.0f, 0.0f, w, kn, sreal);
+      symm_lds<false>(R, T, Zv, nullptr, 1.0f, 0.0f, 0.0f, w, kn, sreal);
     }
   }
-  rect_small(Q, xs, R, T, XT, p.Lp, Y, YT, p, b, true, w);
+  rect_small(Q, xs, R, T, XT, p.Lp, Y, YT, p, b, true, w, kn);
 }
 
 }  // namespace

@@ -75,6 +75,36 @@ def test_fused_schedules(iters, restarts):
             assert rel(fused[b], ref) <= O_TOL
 
 
+def _polar(a):
+    u, _, vt = np.linalg.svd(np.asarray(a, np.float64), full_matrices=False)
+    return u @ vt
+
+
+@pytest.mark.parametrize("k,m", [(96, 333), (100, 300), (300, 100)])
+def test_long_schedule_without_restart_stays_finite(k, m):
+    """Twelve Muon iterations with no restart on a Gram side that pads to
+    128: the identity term of the polynomial goes on the real diagonal only,
+    so the zero padding block stays zero.  (Added on the padded diagonal too,
+    it grew as 3.4445^t, overflowed fp16 after nine iterations and turned the
+    cross terms, and then O, into NaN.)  Both paths must agree bit for bit,
+    keep the singular values in the band the quintic holds them in (the
+    oracle's are in [0.68, 1.14] for these inputs), and keep the polar factor
+    of X."""
+    say("long schedule", k, m)
+    iters = 12
+    X = host_gaussian((2, k, m), [43, k, m]).astype(np.float16)
+    co = [orc.MUON_COEFFS] * iters
+    outs = [d3.gram_ns(dev(X), d3.ns_cfg(iters=iters, restart_at=(), coeffs=co, path=path))
+            .cpu().numpy() for path in (d3.PATH_FUSED, d3.PATH_TILED)]
+    assert same(outs[0], outs[1])
+    O = outs[0].astype(np.float64)
+    assert np.isfinite(O).all()
+    for b in range(2):
+        sv = np.linalg.svd(O[b], compute_uv=False)
+        assert 0.6 <= sv.min() and sv.max() <= 1.25, (sv.min(), sv.max())
+        assert rel(_polar(O[b]), _polar(X[b])) <= O_TOL
+
+
 def test_fused_transposed_gram_ns():
     """k > m: the Gram is X^T X and the multiply-back runs along k."""
     say("fused gram_ns k>m")
