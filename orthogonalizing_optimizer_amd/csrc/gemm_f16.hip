@@ -50,7 +50,6 @@ struct GemmArgs {
   f16* Oout;
   long long sO;
   int kval, mval, nrows;
-  int tcols;   // column outputs through a column-major restaging of the tile
 };
 
 // One 8-wide chunk of the output in rows layout (row r, columns c..c+7)
@@ -546,9 +545,14 @@ __global__ __launch_bounds__(C::NT, (C::BM == 256 ? 1 : 2)) void k_gemm(GemmArgs
     Tb = p.CT + (long long)b * p.sCT;
     ldt = p.ldct;
   }
-  const bool tcols = Tb && p.tcols;
+  // Column outputs (Tb) always go through a column-major restaging of the
+  // tile.  (Reading them from the row-major staging, 8 strided halves per
+  // chunk, had been kept for symmetric products with K < 2048; since the
+  // diagonal mirror moved into the staging pass the restaging is as fast or
+  // faster there too: 1B step -2.5 %, 14B symmetric products +5 %.)
+  const bool tcols = Tb != nullptr;
   f16* S = lds;
-  if (Cb || (!LOWER && p.sink) || (Tb && !tcols)) {
+  if (Cb || (!LOWER && p.sink)) {
     // the tile row-major in LDS, row stride C::EP.  A diagonal tile of a
     // symmetric product keeps its lower triangle (diagonal included) and
     // fills the upper one with the mirror of the lower values in the same
@@ -610,20 +614,6 @@ __global__ __launch_bounds__(C::NT, (C::BM == 256 ? 1 : 2)) void k_gemm(GemmArgs
           *(half8*)(Cb + (long long)gr * p.ldc + gc) = *(const half8*)(S + r * C::EP + c8 * 8);
       }
     }
-    if (Tb && !tcols) {
-      // columns read from the row-major tile, consecutive lanes on
-      // consecutive output rows
-      for (int e = tid; e < C::BN * (C::BM / 8); e += C::NT) {
-        const int r8 = e / C::BN, c = e - r8 * C::BN;
-        const int gr = n0 + c, gc = m0 + r8 * 8;
-        if (gr < p.N && gc < p.M) {
-          half8 v;
-#pragma unroll
-          for (int k = 0; k < 8; ++k) v[k] = S[(r8 * 8 + k) * C::EP + c];
-          *(half8*)(Tb + (long long)gr * ldt + gc) = v;
-        }
-      }
-    }
   }
   if (tcols) {
     // the tile again, column-major (St[c][r], row stride EPT: each lane's
@@ -671,11 +661,6 @@ hipError_t launch(const GemmDesc& d, hipStream_t s) {
   p.sink = d.sink; p.W = d.W; p.ldw = d.ldw; p.idx = d.idx; p.lr = d.lr; p.Oout = d.Oout;
   p.sO = d.sO;
   p.kval = d.kval; p.mval = d.mval; p.nrows = d.nrows;
-  // The column-major restaging costs two more barriers and an LDS pass; it
-  // pays for the transposed output always and for the symmetric mirror once
-  // K is long (measured: +10 % on 64 x 2816^2 symmetric products, -3 % at
-  // 1024^2).
-  p.tcols = (!LOWER || d.K >= 2048) ? 1 : 0;
   hipLaunchKernelGGL((k_gemm<C, ROLE, LOWER, EPI>), dim3(p.total), dim3(C::NT), 0, s, p);
   return hipGetLastError();
 }
