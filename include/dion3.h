@@ -246,7 +246,8 @@ DION3_API dion3_status dion3_symm_f16(const uint16_t* A, const uint16_t* B, cons
  * kernels).  Records past the capacity are dropped.  capacity <= 0 stops and
  * frees the trace.  dion3_trace_record(i, ...) waits for record i's second
  * event and returns its kernel name (a static string), elapsed ms, flops and
- * bytes.  The trace is process-wide; it is meant for one benchmarking thread. */
+ * bytes; it returns DION3_ERR_HIP when recording either event of that pair
+ * failed.  The trace is process-wide; it is meant for one benchmarking thread. */
 DION3_API dion3_status dion3_trace_enable(int32_t capacity);
 DION3_API int32_t dion3_trace_count(void);
 DION3_API void dion3_trace_reset(void);

@@ -15,6 +15,7 @@ struct TraceRec {
   const char* name;
   double flops, bytes;
   hipEvent_t e0, e1;
+  bool ok;   // both events were recorded
 };
 
 std::mutex g_mu;
@@ -33,13 +34,14 @@ TraceScope::TraceScope(const char* name, double flops, double bytes, hipStream_t
   r.name = name;
   r.flops = flops;
   r.bytes = bytes;
-  hipEventRecord(r.e0, s);
+  r.ok = hipEventRecord(r.e0, s) == hipSuccess;
 }
 
 TraceScope::~TraceScope() {
   if (slot < 0) return;
   std::lock_guard<std::mutex> lk(g_mu);
-  hipEventRecord(g_recs[slot].e1, stream);
+  TraceRec& r = g_recs[slot];
+  if (r.ok) r.ok = hipEventRecord(r.e1, stream) == hipSuccess;
 }
 
 }  // namespace dion3
@@ -50,9 +52,9 @@ extern "C" {
 
 dion3_status dion3_trace_enable(int32_t capacity) {
   std::lock_guard<std::mutex> lk(g_mu);
-  for (TraceRec& r : g_recs) {
-    hipEventDestroy(r.e0);
-    hipEventDestroy(r.e1);
+  for (TraceRec& r : g_recs) {   // nothing to do about a failed destroy
+    (void)hipEventDestroy(r.e0);
+    (void)hipEventDestroy(r.e1);
   }
   g_recs.clear();
   g_count = 0;
@@ -86,7 +88,7 @@ dion3_status dion3_trace_record(int32_t i, const char** name, double* ms, double
   std::lock_guard<std::mutex> lk(g_mu);
   if (i < 0 || i >= g_count || !name || !ms || !flops || !bytes) return DION3_ERR_ARG;
   TraceRec& r = g_recs[i];
-  if (hipEventSynchronize(r.e1) != hipSuccess) return DION3_ERR_HIP;
+  if (!r.ok || hipEventSynchronize(r.e1) != hipSuccess) return DION3_ERR_HIP;
   float t = 0.0f;
   if (hipEventElapsedTime(&t, r.e0, r.e1) != hipSuccess) return DION3_ERR_HIP;
   *name = r.name;
