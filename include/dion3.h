@@ -53,14 +53,19 @@ extern "C" {
 
 typedef enum {
   DION3_OK = 0,
-  DION3_ERR_ARG = -1,          /* a null required pointer or an out-of-range size/parameter */
+  DION3_ERR_ARG = -1,          /* a null required pointer or an out-of-range size/parameter:
+                                  any size below 1, k outside [1, n], ld < m, a schedule outside
+                                  its stated ranges.  Sizes are checked in that order, so k = 0
+                                  or k > n is an argument error even where n or m also exceeds
+                                  DION3_MAX_DIM */
   DION3_ERR_WORKSPACE = -2,    /* ws is NULL, misaligned or smaller than dion3_workspace_size() */
-  DION3_ERR_UNSUPPORTED = -3,  /* a shape beyond the library's limits: a dimension above
-                                  DION3_MAX_DIM, or a zero-padded per-matrix block (the selected
-                                  rows, padded to multiples of 128, or the Gram side) of 2^31
-                                  bytes or more, or a product whose 128 x 128 output tiles over
-                                  the whole batch exceed 2^31 - 1; with DION3_PATH_FUSED, also a
-                                  Gram side min(k, m) above 128 */
+  DION3_ERR_UNSUPPORTED = -3,  /* a shape beyond the library's limits (sizes that are
+                                  otherwise valid): a dimension above DION3_MAX_DIM, or a
+                                  zero-padded per-matrix block (the selected rows, padded to
+                                  multiples of 128, or the Gram side) of 2^31 bytes or more, or
+                                  a product whose 128 x 128 output tiles over the whole batch
+                                  exceed 2^31 - 1; with DION3_PATH_FUSED, also a Gram side
+                                  min(k, m) above 128 */
   DION3_ERR_HIP = -4           /* a HIP call or launch failed; see dion3_last_hip_error() */
 } dion3_status;
 

@@ -24,8 +24,8 @@ Sources (the pages are cited by title and paragraph):
   stack" (error feedback; a full fraction reduces to Muon in exact
   arithmetic).
 * [ABS] the paper abstract ("Dion3: Full-Stack Orthogonal Updates", as
-  reproduced on arxivlens.com and scholarbro.com): select only a fraction of
-  the momentum matrix's rows to orthogonalize at each step.
+  reproduced on arxivlens.com and scholarbro.com): the step orthogonalizes a
+  subset of the momentum rows rather than the whole matrix.
 
 Readings where the pages are silent (each is also a row of the design notes):
 

@@ -68,7 +68,14 @@ Plan make_plan(int B, long long n, long long m, long long k) {
   return P;
 }
 
-bool dims_ok(long long v) { return v >= 1 && v <= DION3_MAX_DIM; }
+// Size checks of the step's entry points, in the order the header states:
+// a size below 1 or k outside [1, n] is an argument error; only sizes that
+// are valid but above DION3_MAX_DIM are unsupported.
+dion3_status check_dims(long long n, long long m, long long k) {
+  if (n < 1 || m < 1 || k < 1 || k > n) return DION3_ERR_ARG;
+  if (n > DION3_MAX_DIM || m > DION3_MAX_DIM) return DION3_ERR_UNSUPPORTED;
+  return DION3_OK;
+}
 
 // The products address each matrix through a buffer resource with 32-bit
 // byte offsets, so every padded per-matrix operand must stay below 2^31 bytes.
@@ -393,12 +400,13 @@ dion3_status step_impl(BatchPtr<float> W, BatchPtr<float> M, BatchPtr<const floa
   if (norm && (!(V.base || V.ptrs) || !(norm->beta2 >= 0.0f && norm->beta2 < 1.0f) ||
                !(norm->eps >= 0.0f) || !isfinite(norm->eps)))
     return DION3_ERR_ARG;
-  if (!dims_ok(n) || !dims_ok(m) || !dims_ok(k)) return DION3_ERR_UNSUPPORTED;
-  if (k > n || ld < m) return DION3_ERR_ARG;
+  dion3_status st = check_dims(n, m, k);
+  if (st != DION3_OK) return st;
+  if (ld < m) return DION3_ERR_ARG;
   if (!isfinite(lr) || !isfinite(mu)) return DION3_ERR_ARG;
   dion3_ns_cfg cfg;
   if (cfg_in) cfg = *cfg_in; else dion3_ns_cfg_default(&cfg);
-  dion3_status st = check_cfg(&cfg);
+  st = check_cfg(&cfg);
   if (st != DION3_OK) return st;
   const Plan P = make_plan(batch, n, m, k);
   if (!plan_fits(P) || !path_ok(P, cfg)) return DION3_ERR_UNSUPPORTED;
@@ -543,8 +551,8 @@ int64_t dion3_k_from_fraction(double f, int64_t n) {
 dion3_status dion3_workspace_size(int32_t batch, int64_t n, int64_t m, int64_t k, size_t* bytes) {
   if (!bytes) return DION3_ERR_ARG;
   if (batch < 1 || batch > DION3_MAX_BATCH) return DION3_ERR_ARG;
-  if (!dims_ok(n) || !dims_ok(m) || !dims_ok(k)) return DION3_ERR_UNSUPPORTED;
-  if (k > n) return DION3_ERR_ARG;
+  const dion3_status st = check_dims(n, m, k);
+  if (st != DION3_OK) return st;
   const Plan P = make_plan(batch, n, m, k);
   if (!plan_fits(P)) return DION3_ERR_UNSUPPORTED;
   *bytes = P.total;
@@ -556,10 +564,11 @@ dion3_status dion3_row_select(const float* M, int32_t batch, int64_t n, int64_t 
                               void* stream) {
   if (!M || !idx) return DION3_ERR_ARG;
   if (batch < 1 || batch > DION3_MAX_BATCH) return DION3_ERR_ARG;
-  if (!dims_ok(n) || !dims_ok(m) || !dims_ok(k)) return DION3_ERR_UNSUPPORTED;
-  if (k > n || ld < m) return DION3_ERR_ARG;
+  dion3_status st = check_dims(n, m, k);
+  if (st != DION3_OK) return st;
+  if (ld < m) return DION3_ERR_ARG;
   const Plan P = make_plan(batch, n, m, k);
-  dion3_status st = check_ws(P, ws, ws_bytes, P.o_Xa);
+  st = check_ws(P, ws, ws_bytes, P.o_Xa);
   if (st != DION3_OK) return st;
   hipStream_t s = (hipStream_t)stream;
   char* w = (char*)ws;
@@ -579,10 +588,11 @@ dion3_status dion3_gram_ns(const uint16_t* X, uint16_t* O, int32_t batch, int64_
                            const dion3_ns_cfg* cfg_in, void* ws, size_t ws_bytes, void* stream) {
   if (!X || !O) return DION3_ERR_ARG;
   if (batch < 1 || batch > DION3_MAX_BATCH) return DION3_ERR_ARG;
-  if (!dims_ok(k) || !dims_ok(m)) return DION3_ERR_UNSUPPORTED;
+  dion3_status st = check_dims(k, m, k);
+  if (st != DION3_OK) return st;
   dion3_ns_cfg cfg;
   if (cfg_in) cfg = *cfg_in; else dion3_ns_cfg_default(&cfg);
-  dion3_status st = check_cfg(&cfg);
+  st = check_cfg(&cfg);
   if (st != DION3_OK) return st;
   const Plan P = make_plan(batch, k, m, k);
   if (!plan_fits(P) || !path_ok(P, cfg)) return DION3_ERR_UNSUPPORTED;
@@ -664,7 +674,8 @@ dion3_status dion3_syrk_f16(const uint16_t* A, uint16_t* R, int32_t batch, int64
                             int64_t cols, int64_t lda, int64_t ldr, void* stream) {
   if (!A || !R) return DION3_ERR_ARG;
   if (batch < 1 || batch > DION3_MAX_BATCH) return DION3_ERR_ARG;
-  if (!dims_ok(rows) || !dims_ok(cols)) return DION3_ERR_UNSUPPORTED;
+  if (rows < 1 || cols < 1) return DION3_ERR_ARG;
+  if (rows > DION3_MAX_DIM || cols > DION3_MAX_DIM) return DION3_ERR_UNSUPPORTED;
   if (rows % kTile || cols % kTile || lda < cols || ldr < rows || lda % 8 || ldr % 8)
     return DION3_ERR_ARG;
   if (rows * lda * 2 >= kMaxOperandBytes || rows * ldr * 2 >= kMaxOperandBytes)
@@ -687,7 +698,8 @@ dion3_status dion3_symm_f16(const uint16_t* A, const uint16_t* B, const uint16_t
                             float gamma, void* stream) {
   if (!A || !B || !C || (beta != 0.0f && !D)) return DION3_ERR_ARG;
   if (batch < 1 || batch > DION3_MAX_BATCH) return DION3_ERR_ARG;
-  if (!dims_ok(s)) return DION3_ERR_UNSUPPORTED;
+  if (s < 1) return DION3_ERR_ARG;
+  if (s > DION3_MAX_DIM) return DION3_ERR_UNSUPPORTED;
   if (s % kTile || ld < s || ld % 8) return DION3_ERR_ARG;
   if (s * ld * 2 >= kMaxOperandBytes) return DION3_ERR_UNSUPPORTED;
   if (!isfinite(alpha) || !isfinite(beta) || !isfinite(gamma)) return DION3_ERR_ARG;

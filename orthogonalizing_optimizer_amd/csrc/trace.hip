@@ -64,7 +64,12 @@ dion3_status dion3_trace_enable(int32_t capacity) {
   g_recs.resize(capacity);
   for (int i = 0; i < capacity; ++i) {
     TraceRec& r = g_recs[i];
-    if (hipEventCreate(&r.e0) != hipSuccess || hipEventCreate(&r.e1) != hipSuccess) {
+    if (hipEventCreate(&r.e0) != hipSuccess) {
+      g_recs.resize(i);
+      return DION3_ERR_HIP;
+    }
+    if (hipEventCreate(&r.e1) != hipSuccess) {
+      (void)hipEventDestroy(r.e0);   // this slot's first event; nothing to do if it fails
       g_recs.resize(i);
       return DION3_ERR_HIP;
     }

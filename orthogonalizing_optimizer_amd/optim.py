@@ -22,8 +22,9 @@ class Dion3Step:
     k = ceil(f n), Gram Newton-Schulz on the selected rows, the row-sparse
     update W[S] -= lr_eff * O with lr_eff = lr / sqrt(f) (level-3 paragraph:
     eta proportional to 1/sqrt(f)) and the decay M[S] *= mu.  The momentum M
-    is the optimizer state; accumulating gradients into it is left to the
-    caller.
+    is the optimizer state.  ``step(grads)`` first accumulates one gradient
+    per weight into it (M <- M + G, fused into the row scoring); ``step()``
+    starts from M as it is.
     """
 
     def __init__(self, weights: Sequence, momenta: Sequence, lr: float = 0.02,

@@ -35,7 +35,14 @@ int main(void) {
   EXPECT(dion3_workspace_size(1, 128, 512, 32, &bytes) == DION3_OK && bytes > 0);
   EXPECT(dion3_workspace_size(4, 128, 512, 32, &bytes4) == DION3_OK && bytes4 > 3 * bytes);
   EXPECT(dion3_workspace_size(1, 10, 10, 11, &bytes) == DION3_ERR_ARG);
-  EXPECT(dion3_workspace_size(1, 0, 10, 1, &bytes) == DION3_ERR_UNSUPPORTED);
+  EXPECT(dion3_workspace_size(1, 0, 10, 1, &bytes) == DION3_ERR_ARG);
+  EXPECT(dion3_workspace_size(1, 10, 10, 0, &bytes) == DION3_ERR_ARG);
+  EXPECT(dion3_workspace_size(1, (1 << 20) + 1, 10, 0, &bytes) == DION3_ERR_ARG);
+  EXPECT(dion3_workspace_size(1, (1 << 20) + 1, 10, 1, &bytes) == DION3_ERR_UNSUPPORTED);
+  EXPECT(dion3_step((float*)ws, (float*)ws, 64, 32, 32, 0, 0.04f, 0.95f, NULL, NULL, NULL, ws,
+                    1u << 30, NULL) == DION3_ERR_ARG);
+  EXPECT(dion3_step((float*)ws, (float*)ws, 64, 32, 32, 65, 0.04f, 0.95f, NULL, NULL, NULL, ws,
+                    1u << 30, NULL) == DION3_ERR_ARG);
 
   /* argument errors are reported before any launch */
   EXPECT(dion3_step(NULL, NULL, 64, 32, 32, 16, 0.04f, 0.95f, NULL, NULL, NULL, ws, 1u << 30,

@@ -79,6 +79,9 @@ def test_workspace_size_layout():
         d3.workspace_size(0, 10, 10, 1)
     out = ctypes.c_size_t()
     assert d3.lib().dion3_workspace_size(1, (1 << 20) + 1, 4, 1, ctypes.byref(out)) == ERR_UNSUP
+    assert d3.lib().dion3_workspace_size(1, 10, 10, 0, ctypes.byref(out)) == ERR_ARG
+    assert d3.lib().dion3_workspace_size(1, 10, 0, 1, ctypes.byref(out)) == ERR_ARG
+    assert d3.lib().dion3_workspace_size(1, (1 << 20) + 1, 4, 0, ctypes.byref(out)) == ERR_ARG
     # padded selected block of 2^31 bytes or more: rejected (32-bit buffer offsets)
     assert d3.lib().dion3_workspace_size(1, 1 << 16, 1 << 15, 1 << 15, ctypes.byref(out)) == ERR_UNSUP
     assert d3.lib().dion3_workspace_size(1, 1 << 16, 1 << 14, 1 << 15, ctypes.byref(out)) == 0
@@ -107,8 +110,16 @@ def test_step_rejects_bad_arguments_before_launch():
     lib = d3.lib()
     assert _step(lib, W=None) == ERR_ARG
     assert _step(lib, M=None) == ERR_ARG
-    assert _step(lib, k=0) == ERR_UNSUP
+    assert _step(lib, k=0) == ERR_ARG
+    assert _step(lib, k=-3) == ERR_ARG
     assert _step(lib, k=65) == ERR_ARG
+    assert _step(lib, n=0, k=1, nbytes=1 << 30) == ERR_ARG
+    assert _step(lib, m=0, ld=8, nbytes=1 << 30) == ERR_ARG
+    # a size below 1 or k > n is an argument error even when another size is
+    # beyond the library's limit
+    assert _step(lib, n=(1 << 20) + 1, k=0) == ERR_ARG
+    assert _step(lib, n=(1 << 20) + 1, k=(1 << 20) + 2) == ERR_ARG
+    assert _step(lib, n=(1 << 20) + 1, k=4, nbytes=1 << 30) == ERR_UNSUP
     assert _step(lib, ld=31) == ERR_ARG
     assert _step(lib, lr=float("inf")) == ERR_ARG
     assert _step(lib, cfg=_cfg(iters=0)) == ERR_ARG
@@ -165,6 +176,12 @@ def test_other_entry_points_validate():
                                           None, FAKE, 1 << 30, None) == ERR_ARG
     assert lib.dion3_row_select(None, 1, 8, 8, 8, 2, FAKE, None, FAKE, 1 << 30, None) == ERR_ARG
     assert lib.dion3_row_select(FAKE, 1, 8, 8, 8, 9, FAKE, None, FAKE, 1 << 30, None) == ERR_ARG
+    assert lib.dion3_row_select(FAKE, 1, 8, 8, 8, 0, FAKE, None, FAKE, 1 << 30, None) == ERR_ARG
+    assert lib.dion3_gram_ns(FAKE, FAKE, 1, 0, 8, cfg, FAKE, 1 << 30, None) == ERR_ARG
+    assert lib.dion3_gram_ns(FAKE, FAKE, 1, 8, 0, cfg, FAKE, 1 << 30, None) == ERR_ARG
+    assert lib.dion3_syrk_f16(FAKE, FAKE, 1, 0, 128, 128, 128, None) == ERR_ARG
+    assert lib.dion3_symm_f16(FAKE, FAKE, None, FAKE + 512, 1, 0, 128, 1.0, 0.0, 0.0,
+                              None) == ERR_ARG
     assert lib.dion3_row_select(FAKE, 1, 8, 8, 8, 2, FAKE, None, FAKE, 0, None) == ERR_WS
     assert lib.dion3_gram_ns(None, FAKE, 1, 8, 8, cfg, FAKE, 1 << 30, None) == ERR_ARG
     assert lib.dion3_gram_ns(FAKE, FAKE, 1, 8, 8, cfg, FAKE, 16, None) == ERR_WS

@@ -1,8 +1,9 @@
 """GPU parity at the workloads' full sizes, in the launch configuration the
 benchmark times: one megabatched call over a whole shape group of the 1B,
 7B (f = 1/4 and f = 1/2) and 14B ill-conditioned weight sets.  The oracle
-checks the first and the last matrix of the group (the oracle runs one fp64
-matrix at a time)."""
+runs one fp64 matrix at a time, so it checks a sample of each group: its
+first and last matrix ("ends") and two more drawn with a seeded generator
+("random"), each pair in a test of its own."""
 import sys
 
 import numpy as np
@@ -19,18 +20,30 @@ import orthogonalizing_optimizer_amd as d3  # noqa: E402
 
 DEV = "cuda:0"
 
-CASES = [("c3", 0), ("c3", 1), ("c3", 2), ("c4", 0), ("c4", 1), ("c4", 2), ("c4h", 1),
-         ("c5", 0), ("c5", 1), ("c5", 2)]
+GROUPS = [("c3", 0), ("c3", 1), ("c3", 2), ("c4", 0), ("c4", 1), ("c4", 2),
+          ("c4h", 0), ("c4h", 1), ("c4h", 2), ("c5", 0), ("c5", 1), ("c5", 2)]
+CASES = [(w, g, s) for (w, g) in GROUPS for s in ("ends", "random")]
 
 
-@pytest.mark.parametrize("wl_name,group", CASES)
-def test_fullsize_group(wl_name, group):
+def sample(wl, group, which):
+    """Matrix indices of a group checked by the oracle: the first and last, or
+    two others drawn from a generator seeded by the workload and group."""
+    count = wl.groups[group].count
+    if which == "ends":
+        return sorted({0, count - 1})
+    inner = np.arange(1, count - 1)
+    rng = np.random.default_rng([wl.seed_base, group, 2])
+    return sorted(int(j) for j in rng.choice(inner, size=min(2, len(inner)), replace=False))
+
+
+@pytest.mark.parametrize("wl_name,group,which", CASES)
+def test_fullsize_group(wl_name, group, which):
     wl = WORKLOADS[wl_name]
     g = wl.groups[group]
-    print(f"[case] {wl.name} group {group}: {g.count} x {g.n}x{g.m}", flush=True)
+    picks = sample(wl, group, which)
+    print(f"[case] {wl.name} group {group}: {g.count} x {g.n}x{g.m}, matrices {picks}", flush=True)
     sys.stdout.flush()
     (_, Ws, Ms), = device_workload(wl, DEV, groups=[group])
-    picks = sorted({0, g.count - 1})
     W0 = {j: Ws[j].cpu().numpy() for j in picks}
     M0 = {j: Ms[j].cpu().numpy() for j in picks}
     k = d3.k_from_fraction(float(wl.fraction), g.n)
