@@ -38,6 +38,8 @@ KERNEL_SYMBOLS = {
     "gemm_poly_128": "k_gemm<Cfg<128, 2, 2, 1>, 1, true, true>",
     "gemm_symm_128": "k_gemm<Cfg<128, 2, 2, 1>, 2, true, false>",
     "gemm_rect_128": "k_gemm<Cfg<128, 2, 2, 1>, 3, false, false>",
+    "gemm_back_256": "k_gemm<Cfg<256, 2, 4, 1>, 5, false, false>",
+    "gemm_back_128": "k_gemm<Cfg<128, 2, 2, 1>, 5, false, false>",
     "row_score": "k_row_score_f32",
     "accum_score": "k_accum_score_f32",
     "topk": "k_topk",
@@ -74,7 +76,7 @@ def parse():
     p.add_argument("--no-trace", action="store_true")
     p.add_argument("--normalize", action="store_true",
                    help="per-neuron normalization of the update (fp32 second moment per row, "
-                        "beta2 = 0.95, eps = 1e-8) through dion3_step_megabatch_norm")
+                        "beta2 = 0.95, eps = 1e-8), the norm argument of dion3_step_groups")
     p.add_argument("--accumulate", action="store_true",
                    help="each step first accumulates a gradient into the momentum (M <- M + G, "
                         "fused into the row scoring); gradients are fixed seeded N(0, 0.1^2)")
@@ -89,6 +91,12 @@ def parse():
     p.add_argument("--graph", action="store_true",
                    help="capture one whole step (every group's launches) in a HIP graph and time "
                         "its replays (the per-kernel trace is then off)")
+    p.add_argument("--per-group", action="store_true",
+                   help="one library call per shape group (dion3_step_megabatch's launch "
+                        "sequence) instead of one call for all groups")
+    p.add_argument("--also-fraction", default="1/2",
+                   help="for the 7B set (c4), also step the same resident matrices at this "
+                        "fraction and report it in a sub-object (\"none\" to skip)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 2 GiB device-to-device copy (a known-size kernel for "
                         "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE) and print its GB/s")
@@ -147,6 +155,111 @@ def load_traffic(kernel: str, workload: str):
         return None
 
 
+def kernel_stats(records, steps):
+    """Per-kernel totals over the timed region, from the library's trace, and
+    per (kernel, work per launch), which tells the shapes apart."""
+    kernels, by_shape = {}, {}
+    for name, ms, fl, by in records:
+        for table, key in ((kernels, name), (by_shape, (name, fl, by))):
+            st = table.setdefault(key, {"launches": 0, "ms": 0.0, "flops": 0.0, "bytes": 0.0})
+            st["launches"] += 1
+            st["ms"] += ms
+            st["flops"] += fl
+            st["bytes"] += by
+    for table in (kernels, by_shape):
+        for st in table.values():
+            t = st["ms"] * 1e-3
+            st["avg_us"] = 1e3 * st["ms"] / st["launches"]
+            st["ms_per_step"] = st["ms"] / steps
+            st["tflops"] = st["flops"] / t / 1e12 if st["flops"] > 0 else 0.0
+            st["gbs"] = st["bytes"] / t / 1e9 if st["bytes"] > 0 else 0.0
+            st["frac_fp16_peak"] = st["tflops"] / FP16_PEAK_TFLOPS
+            st["frac_hbm"] = st["gbs"] / HBM_PEAK_GBS
+            # the roofline of a kernel that does both: the larger of its flop
+            # time and its byte time at the peaks, over its measured time
+            st["bound"] = "mfma" if st["frac_fp16_peak"] >= st["frac_hbm"] else "hbm"
+            st["frac_roofline"] = max(st["frac_fp16_peak"], st["frac_hbm"])
+    return kernels, by_shape
+
+
+def roofline_of(kernels, workload):
+    """The roofline object of the dominant kernel (most time per step)."""
+    if not kernels:
+        return None
+    dom = max(kernels, key=lambda nm: kernels[nm]["ms"])
+    st = kernels[dom]
+    if st["bound"] == "mfma":
+        r = {"bound": "mfma", "achieved": round(st["tflops"], 2), "peak": FP16_PEAK_TFLOPS,
+             "unit": "TFLOP/s", "frac": round(st["frac_fp16_peak"], 4)}
+        work = st["flops"] / st["launches"]
+    else:
+        r = {"bound": "hbm", "achieved": round(st["gbs"], 1), "peak": HBM_PEAK_GBS,
+             "unit": "GB/s", "frac": round(st["frac_hbm"], 4)}
+        work = st["bytes"] / st["launches"]
+    r["traffic"] = load_traffic(dom, workload)
+    r["kernel"] = KERNEL_SYMBOLS.get(dom, dom)
+    r["avg_launch_us"] = round(st["avg_us"], 2)
+    r["work_per_launch"] = work
+    return r
+
+
+def multiply_back_of(kernels):
+    """The final multiply-back with the fused row-sparse update, against both
+    of its bounds: its flops (2 s^2 L) and its bytes (X and Q read, the
+    selected rows of W read and written)."""
+    names = [nm for nm in kernels if nm.startswith("gemm_back_")]
+    if not names:
+        return None
+    st = {"launches": 0, "ms": 0.0, "flops": 0.0, "bytes": 0.0}
+    for nm in names:
+        for key in st:
+            st[key] += kernels[nm][key]
+    t = st["ms"] * 1e-3
+    tf, gb = st["flops"] / t / 1e12, st["bytes"] / t / 1e9
+    return {"kernels": [KERNEL_SYMBOLS.get(nm, nm) for nm in names],
+            "avg_launch_us": round(1e3 * st["ms"] / st["launches"], 2),
+            "tflops": round(tf, 2), "frac_fp16_peak": round(tf / FP16_PEAK_TFLOPS, 4),
+            "gbs": round(gb, 1), "frac_hbm": round(gb / HBM_PEAK_GBS, 4),
+            "bound": "mfma" if tf / FP16_PEAK_TFLOPS >= gb / HBM_PEAK_GBS else "hbm",
+            "frac_roofline": round(max(tf / FP16_PEAK_TFLOPS, gb / HBM_PEAK_GBS), 4)}
+
+
+def cpu_baseline_of(samples, fraction, lr, mu, method, budget_s):
+    """The fp64 oracle on a bounded sample of the matrices, scaled to one
+    whole-model step."""
+    from oracle import dion3_oracle as orc
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    per_group = {}
+    t_cpu = 0.0
+    used = 0
+    for g, W0, M0 in samples:
+        key = (g.n, g.m, g.count)
+        if t_cpu >= budget_s and key in per_group:
+            continue
+        k = orc.k_from_fraction(fraction, g.n)
+        t = time.perf_counter()
+        orc.dion3_step(W0, M0, k, lr, mu, method=method)
+        dt = time.perf_counter() - t
+        t_cpu += dt
+        used += 1
+        per_group.setdefault(key, []).append(dt)
+    cpu_ms = 1e3 * sum(g[2] * (sum(v) / len(v)) for g, v in per_group.items())
+    log(f"cpu oracle (f = {fraction}): {t_cpu:.1f}s for {used} matrices -> {cpu_ms:.0f} ms/model "
+        f"step ({threads} BLAS threads, os.cpu_count()={os.cpu_count()})")
+    return {"value": round(cpu_ms, 1), "unit": "ms per model step", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{used} matrices of the set ("
+                      + ", ".join(f"{len(v)} x {n}x{m}" for (n, m, c), v in per_group.items()) +
+                      f"), fp64 NumPy oracle, {t_cpu:.1f}s of CPU work; the mean time per matrix "
+                      "of each shape group is scaled by the group's matrix count to one "
+                      "whole-model step"}
+
+
 def main():
     args = parse()
     if args.copy_calibration:
@@ -157,6 +270,8 @@ def main():
               "build runs the step on a single MI355X (multi-GPU sharding is a design note only). "
               "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+
+    from fractions import Fraction
 
     import numpy as np
     import torch
@@ -179,7 +294,6 @@ def main():
     if args.method == "standard":
         cfg.method = d3.NS_STANDARD
     mu = 0.95
-    lr = wl.lr
 
     t_gen = time.time()
     data = device_workload(wl, dev)
@@ -196,197 +310,141 @@ def main():
                 if j < g.count:
                     samples.append((g, Ws[j].cpu().numpy(), Ms[j].cpu().numpy()))
 
-    groups = []
-    grads = {}
-    norms = {}
-    max_ws = 0
+    grads, norms = {}, {}
     for gi, (g, Ws, Ms) in enumerate(data):
-        k = d3.k_from_fraction(float(wl.fraction), g.n)
-        ptrs = (d3.pointer_array(Ws, dev), d3.pointer_array(Ms, dev))
-        groups.append((g, Ws, Ms, k, ptrs))
-        max_ws = max(max_ws, d3.workspace_size(len(Ms), g.n, g.m, k))
         if args.accumulate:
             gen = torch.Generator(device=dev)
             gen.manual_seed(7000 + gi)
-            Gs = [torch.randn(M.shape, generator=gen, device=dev).mul_(0.1) for M in Ms]
-            grads[gi] = (Gs, d3.pointer_array(Gs, dev))
+            grads[gi] = [torch.randn(M.shape, generator=gen, device=dev).mul_(0.1) for M in Ms]
         if args.normalize:
-            Vs = [torch.zeros(g.n, dtype=torch.float32, device=dev) for _ in Ms]
-            norms[gi] = (Vs, d3.pointer_array(Vs, dev))
-    nstreams = max(1, min(args.streams, len(groups)))
-    if nstreams == 1:
-        ws = d3.Workspace()
-        ws.get(max_ws, dev)
-        wss = [ws] * len(groups)
-    else:
-        wss = []
-        for g, Ws, Ms, k, ptrs in groups:
-            w_ = d3.Workspace()
-            w_.get(d3.workspace_size(len(Ms), g.n, g.m, k), dev)
-            wss.append(w_)
-    side = [torch.cuda.Stream() for _ in range(nstreams)] if nstreams > 1 else []
+            norms[gi] = [torch.zeros(g.n, dtype=torch.float32, device=dev) for _ in Ms]
+    norm = (0.95, 1e-8) if args.normalize else None
+    ws = d3.Workspace()
 
-    def one_step():
-        if nstreams == 1:
-            for gi, (g, Ws, Ms, k, ptrs) in enumerate(groups):
-                gp = grads[gi][1] if gi in grads else None
-                nrm = (norms[gi][0], 0.95, 1e-8) if gi in norms else None
-                d3.step_megabatch(Ws, Ms, k, lr, mu, cfg, ws=wss[gi], ptrs=ptrs, gptrs=gp,
-                                  norm=nrm, vptrs=norms[gi][1] if gi in norms else None)
-            return
-        main = torch.cuda.current_stream()
-        for st in side:
-            st.wait_stream(main)
-        for gi, (g, Ws, Ms, k, ptrs) in enumerate(groups):
-            gp = grads[gi][1] if gi in grads else None
-            nrm = (norms[gi][0], 0.95, 1e-8) if gi in norms else None
-            with torch.cuda.stream(side[gi % nstreams]):
-                d3.step_megabatch(Ws, Ms, k, lr, mu, cfg, ws=wss[gi], ptrs=ptrs, gptrs=gp,
-                                  norm=nrm, vptrs=norms[gi][1] if gi in norms else None)
-        for st in side:
-            main.wait_stream(st)
+    def run(fraction):
+        """Warm-up, then the timed steps at this fraction; returns the
+        result fields of that run."""
+        lr = 0.02 / math.sqrt(float(fraction))
+        groups = []
+        for gi, (g, Ws, Ms) in enumerate(data):
+            k = d3.k_from_fraction(float(fraction), g.n)
+            groups.append(d3.Group(Ws, Ms, k, lr, Gs=grads.get(gi), Vs=norms.get(gi)))
+        nstreams = max(1, min(args.streams, len(groups)))
+        per_group = args.per_group or nstreams > 1
+        if per_group:
+            wss = [ws] * len(groups) if nstreams == 1 else [d3.Workspace() for _ in groups]
+            side = [torch.cuda.Stream() for _ in range(nstreams)] if nstreams > 1 else []
+        ws.get(d3.workspace_size_groups(groups, cfg), dev)
 
-    for _ in range(args.warmup):
-        one_step()
-    torch.cuda.synchronize()
+        def one_step():
+            if not per_group:
+                d3.step_groups(groups, mu, cfg, norm=norm, ws=ws)
+                return
+            if nstreams == 1:
+                for gr, w_ in zip(groups, wss):
+                    d3.step_groups([gr], mu, cfg, norm=norm, ws=w_)
+                return
+            main_s = torch.cuda.current_stream()
+            for st in side:
+                st.wait_stream(main_s)
+            for gi, gr in enumerate(groups):
+                with torch.cuda.stream(side[gi % nstreams]):
+                    d3.step_groups([gr], mu, cfg, norm=norm, ws=wss[gi])
+            for st in side:
+                main_s.wait_stream(st)
 
-    graph = None
-    if args.graph:
-        args.no_trace = True
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
+        for _ in range(args.warmup):
             one_step()
         torch.cuda.synchronize()
-        graph.replay()
-        torch.cuda.synchronize()
-    launches_per_step = sum(3 + 1 + 2 * (1 + cfg.n_restart) + 4 * cfg.iters + 3 for _ in groups)
-    if not args.no_trace:
-        d3.trace_enable(launches_per_step * args.steps + 64)
-    stream = torch.cuda.current_stream()
-    # one event before the first step and one after each step: the mean over
-    # the whole timed region is the reported value; the per-step times give
-    # its spread
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-    torch.cuda.synchronize()
-    evs[0].record(stream)
-    for i in range(args.steps):
-        if graph is not None:
+        graph = None
+        no_trace = args.no_trace
+        if args.graph:
+            no_trace = True
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                one_step()
+            torch.cuda.synchronize()
             graph.replay()
-        else:
-            one_step()
-        evs[i + 1].record(stream)
-    torch.cuda.synchronize()
-    ms_total = evs[0].elapsed_time(evs[-1])
-    ms_per_step = ms_total / args.steps
-    step_ms = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
+            torch.cuda.synchronize()
+        launches_per_step = len(groups) * (3 + 2 * (1 + cfg.n_restart) + 5 * cfg.iters + 8)
+        if not no_trace:
+            d3.trace_enable(launches_per_step * args.steps + 64)
+        stream = torch.cuda.current_stream()
+        # one event before the first step and one after each step: the mean
+        # over the whole timed region is the reported value; the per-step
+        # times give its spread
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        torch.cuda.synchronize()
+        evs[0].record(stream)
+        for i in range(args.steps):
+            if graph is not None:
+                graph.replay()
+            else:
+                one_step()
+            evs[i + 1].record(stream)
+        torch.cuda.synchronize()
+        ms_per_step = evs[0].elapsed_time(evs[-1]) / args.steps
+        step_ms = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
+        kernels, by_shape = {}, {}
+        if not no_trace:
+            kernels, by_shape = kernel_stats(d3.trace_records(), args.steps)
+            d3.trace_disable()
+        log(f"-- {wl.name} at f = {fraction}: {ms_per_step:.3f} ms per step")
+        for (name, fl, by), st in sorted(by_shape.items()):
+            rate = (f"{st['tflops']:7.1f} TFLOP/s" if fl > 0 else "") + \
+                   (f"  {st['gbs']:7.1f} GB/s" if by > 0 else "")
+            log(f"  {name:18s} x{st['launches'] / args.steps:4.1f}/step  avg {st['avg_us']:9.1f} us"
+                f"  ms/step {st['ms_per_step']:7.3f}  {rate}  roofline {st['frac_roofline']:.3f}"
+                f" ({st['bound']})")
+        for name, st in kernels.items():
+            log(f"  {name:18s} launches/step {st['launches'] / args.steps:5.1f}  "
+                f"avg {st['avg_us']:9.1f} us  ms/step {st['ms_per_step']:8.3f}  "
+                f"{st['tflops']:7.1f} TFLOP/s ({100 * st['frac_fp16_peak']:.1f}% fp16)  "
+                f"{st['gbs']:7.1f} GB/s ({100 * st['frac_hbm']:.1f}% HBM)")
+        gemm = [st for nm, st in kernels.items() if is_ns_kernel(nm)]
+        gemm_flops = sum(st["flops"] for st in gemm) / max(1, args.steps)
+        gemm_ms = sum(st["ms"] for st in gemm) / max(1, args.steps)
+        gram_tflops = gemm_flops / (gemm_ms * 1e-3) / 1e12 if gemm_ms > 0 else None
+        # standard-NS dense-equivalent work (a labelled "effective" number only)
+        eff_flops = 0.0
+        for gr in groups:
+            s_, L_ = min(gr.k, gr.m), max(gr.k, gr.m)
+            eff_flops += gr.batch * cfg.iters * (4.0 * s_ * s_ * L_ + 2.0 * s_ ** 3)
+        cpu = (cpu_baseline_of(samples, fraction, lr, mu, args.method, args.cpu_seconds)
+               if samples else None)
+        return {
+            "ms_per_step": round(ms_per_step, 3),
+            "k": [gr.k for gr in groups], "lr": round(lr, 6),
+            "matrices_per_s": round(wl.n_matrices / (ms_per_step * 1e-3), 1),
+            "step_ms": {"median": round(float(np.median(step_ms)), 4),
+                        "p10": round(float(np.percentile(step_ms, 10)), 4),
+                        "p90": round(float(np.percentile(step_ms, 90)), 4)},
+            "gram_ns_tflops": round(gram_tflops, 2) if gram_tflops else None,
+            "gram_ns_frac_fp16_peak": round(gram_tflops / FP16_PEAK_TFLOPS, 4) if gram_tflops
+            else None,
+            "effective_standard_ns_tflops": round(eff_flops / (ms_per_step * 1e-3) / 1e12, 2),
+            "roofline": roofline_of(kernels, args.workload if fraction == wl.fraction else
+                                    {"1/2": "c4h", "1": "c4f"}.get(str(fraction))),
+            "multiply_back": multiply_back_of(kernels),
+            "cpu_baseline": cpu,
+            "kernels": {nm: {kk: (round(v, 4) if isinstance(v, float) else v)
+                             for kk, v in st.items()} for nm, st in kernels.items()},
+        }
 
-    # per-kernel statistics over the timed region
-    kernels = {}
-    by_group = {}
-    if not args.no_trace:
-        gi = -1
-        for name, ms, fl, by in d3.trace_records():
-            if name in ("row_score", "accum_score"):   # every group's launch sequence starts so
-                gi = (gi + 1) % len(groups)
-            for table, key in ((kernels, name), (by_group, (gi, name))):
-                st = table.setdefault(key, {"launches": 0, "ms": 0.0, "flops": 0.0, "bytes": 0.0})
-                st["launches"] += 1
-                st["ms"] += ms
-                st["flops"] += fl
-                st["bytes"] += by
-        d3.trace_disable()
-    for (gi, name), st in sorted(by_group.items()):
-        g = groups[gi][0]
-        rate = (f"{st['flops'] / (st['ms'] * 1e-3) / 1e12:7.1f} TFLOP/s" if st["flops"] > 0 else
-                f"{st['bytes'] / (st['ms'] * 1e-3) / 1e9:7.1f} GB/s")
-        log(f"  group {gi} ({g.count}x{g.n}x{g.m}, k={groups[gi][3]}) {name:10s} "
-            f"avg {1e3 * st['ms'] / st['launches']:9.1f} us  ms/step {st['ms'] / args.steps:7.3f}  {rate}")
-    for name, st in kernels.items():
-        st["avg_us"] = 1e3 * st["ms"] / st["launches"]
-        if st["flops"] > 0:
-            st["tflops"] = st["flops"] / (st["ms"] * 1e-3) / 1e12
-            st["frac_fp16_peak"] = st["tflops"] / FP16_PEAK_TFLOPS
-        else:
-            st["gbs"] = st["bytes"] / (st["ms"] * 1e-3) / 1e9
-            st["frac_hbm"] = st["gbs"] / HBM_PEAK_GBS
-        st["ms_per_step"] = st["ms"] / args.steps
-        log(f"  {name:10s} launches/step {st['launches'] / args.steps:5.1f}  "
-            f"avg {st['avg_us']:9.1f} us  ms/step {st['ms_per_step']:8.3f}  " +
-            (f"{st['tflops']:7.1f} TFLOP/s ({100 * st['frac_fp16_peak']:.1f}% fp16 peak)"
-             if st["flops"] > 0 else f"{st['gbs']:7.1f} GB/s ({100 * st['frac_hbm']:.1f}% HBM)"))
-
-    gemm = [st for nm, st in kernels.items() if is_ns_kernel(nm)]
-    gemm_flops = sum(st["flops"] for st in gemm) / max(1, args.steps)
-    gemm_ms = sum(st["ms"] for st in gemm) / max(1, args.steps)
-    gram_tflops = gemm_flops / (gemm_ms * 1e-3) / 1e12 if gemm_ms > 0 else None
-
-    # standard-NS dense-equivalent work (a labelled "effective" number only)
-    eff_flops = 0.0
-    for g, Ws, Ms, k, ptrs in groups:
-        s, L = min(k, g.m), max(k, g.m)
-        eff_flops += g.count * cfg.iters * (4.0 * s * s * L + 2.0 * s ** 3)
-
-    roofline = None
-    if kernels:
-        dom = max(kernels, key=lambda nm: kernels[nm]["ms"])
-        st = kernels[dom]
-        per_launch_work = (st["flops"] if st["flops"] > 0 else st["bytes"]) / st["launches"]
-        if st["flops"] > 0:
-            roofline = {"bound": "mfma", "achieved": round(st["tflops"], 2),
-                        "peak": FP16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                        "frac": round(st["tflops"] / FP16_PEAK_TFLOPS, 4)}
-        else:
-            roofline = {"bound": "hbm", "achieved": round(st["gbs"], 1), "peak": HBM_PEAK_GBS,
-                        "unit": "GB/s", "frac": round(st["gbs"] / HBM_PEAK_GBS, 4)}
-        roofline["traffic"] = load_traffic(dom, args.workload)
-        roofline["kernel"] = KERNEL_SYMBOLS.get(dom, dom)
-        roofline["avg_launch_us"] = round(st["avg_us"], 2)
-        roofline["work_per_launch"] = per_launch_work
-
-    # CPU baseline: the fp64 oracle on a bounded sample, scaled to the model
-    cpu_baseline = None
-    if samples:
-        from oracle import dion3_oracle as orc
-        try:
-            from threadpoolctl import threadpool_info
-            threads = max([i.get("num_threads", 1) for i in threadpool_info()
-                           if i.get("user_api") == "blas"] or [1])
-        except Exception:
-            threads = os.cpu_count() or 1
-        per_group = {}
-        t_cpu = 0.0
-        used = 0
-        for g, W0, M0 in samples:
-            key = (g.n, g.m, g.count)
-            if t_cpu >= args.cpu_seconds and key in per_group:
-                continue
-            k = orc.k_from_fraction(wl.fraction, g.n)
-            t = time.perf_counter()
-            orc.dion3_step(W0, M0, k, lr, mu, method=args.method)
-            dt = time.perf_counter() - t
-            t_cpu += dt
-            used += 1
-            per_group.setdefault(key, []).append(dt)
-        cpu_ms = 1e3 * sum(g[2] * (sum(v) / len(v)) for g, v in per_group.items())
-        cpu_baseline = {"value": round(cpu_ms, 1), "unit": "ms per model step",
-                        "cores": threads, "kind": "oracle",
-                        "sample": f"{used} matrices of the set ("
-                                  + ", ".join(f"{len(v)} x {n}x{m}" for (n, m, c), v in
-                                              per_group.items()) +
-                                  f"), fp64 NumPy oracle, {t_cpu:.1f}s of CPU work; the mean time "
-                                  "per matrix of each shape group is scaled by the group's "
-                                  "matrix count to one whole-model step"}
-        log(f"cpu oracle: {t_cpu:.1f}s for {used} matrices -> {cpu_ms:.0f} ms/model step "
-            f"({threads} BLAS threads, os.cpu_count()={os.cpu_count()})")
+    head = run(wl.fraction)
+    extra = None
+    also = None if args.also_fraction in ("", "none") else Fraction(args.also_fraction)
+    if also is not None and args.workload == "c4" and also != wl.fraction:
+        extra = run(also)
 
     out = {
         "metric": METRIC,
-        "value": round(ms_per_step, 3),
+        "value": head["ms_per_step"],
         "unit": "ms",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 3),
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
@@ -398,28 +456,34 @@ def main():
             "params": wl.n_params,
             "shape_groups": [f"{g.count}x{g.n}x{g.m}" for g in wl.groups],
             "fraction": str(wl.fraction),
-            "k": [k for (_, _, _, k, _) in groups],
-            "lr": lr, "mu": mu, "ns_iters": cfg.iters,
+            "k": head["k"],
+            "lr": head["lr"], "mu": mu, "ns_iters": cfg.iters,
             "restart_at": [cfg.restart_at[i] for i in range(cfg.n_restart)],
             "state_dtype": "fp32 W and M; fp16 X, Gram, polynomials and O with fp32 accumulation",
-            "parallelism": "single GPU, one megabatched call per shape group" +
-                           (f", groups on {nstreams} streams" if nstreams > 1 else ""),
+            "parallelism": "single GPU, " + (
+                "one megabatched call per shape group" if (args.per_group or args.streams > 1)
+                else "one call for all shape groups (groups with equal Gram sides share their "
+                     "s x s products' launches)") +
+                (f", groups on {args.streams} streams" if args.streams > 1 else ""),
             "gradient_accumulation": bool(args.accumulate),
             "per_neuron_normalization": bool(args.normalize),
             "hip_graph": bool(args.graph),
         },
-        "matrices_per_s": round(wl.n_matrices / (ms_per_step * 1e-3), 1),
-        "step_ms": {"median": round(float(np.median(step_ms)), 4),
-                    "p10": round(float(np.percentile(step_ms, 10)), 4),
-                    "p90": round(float(np.percentile(step_ms, 90)), 4)},
-        "gram_ns_tflops": round(gram_tflops, 2) if gram_tflops else None,
-        "gram_ns_frac_fp16_peak": round(gram_tflops / FP16_PEAK_TFLOPS, 4) if gram_tflops else None,
-        "effective_standard_ns_tflops": round(eff_flops / (ms_per_step * 1e-3) / 1e12, 2),
-        "roofline": roofline,
-        "cpu_baseline": cpu_baseline,
-        "kernels": {nm: {kk: (round(v, 4) if isinstance(v, float) else v) for kk, v in st.items()}
-                    for nm, st in kernels.items()},
     }
+    for key in ("matrices_per_s", "step_ms", "gram_ns_tflops", "gram_ns_frac_fp16_peak",
+                "effective_standard_ns_tflops", "roofline", "multiply_back", "cpu_baseline",
+                "kernels"):
+        out[key] = head[key]
+    if extra is not None:
+        # the same resident matrices stepped at the other fraction the pages
+        # quote for this model (the timed region and protocol are the same)
+        out["at_fraction_" + str(also).replace("/", "_")] = {
+            "workload": wl.name.replace("f" + str(wl.fraction), "f" + str(also)),
+            "fraction": str(also),
+            **{key: extra[key] for key in ("ms_per_step", "k", "lr", "matrices_per_s", "step_ms",
+                                           "gram_ns_tflops", "gram_ns_frac_fp16_peak",
+                                           "effective_standard_ns_tflops", "roofline",
+                                           "multiply_back", "cpu_baseline")}}
     print(json.dumps(out), flush=True)
 
 

@@ -73,6 +73,7 @@ typedef enum {
 #define DION3_MAX_RESTARTS 4
 #define DION3_MAX_DIM (1 << 20)   /* n, m, k each at most this */
 #define DION3_MAX_BATCH 65535
+#define DION3_MAX_GROUPS 64       /* shape groups in one dion3_step_groups call */
 
 /* Newton-Schulz schedule.  Iteration t (1-based) uses the quintic
  * coefficients abc[t-1] = (a, b, c): Z = a I + b R + c R^2.  An iteration
@@ -222,6 +223,53 @@ DION3_API dion3_status dion3_step_megabatch_norm(float* const* W, float* const* 
                                                  const dion3_norm_cfg* norm, int32_t* idx_out,
                                                  uint16_t* O_out, void* ws, size_t ws_bytes,
                                                  void* stream);
+
+/* One shape group of a whole-model step (dion3_step_groups): `batch`
+ * matrices of n x m (row stride ld) with k selected rows each and step size
+ * lr.  W, M (and G, V when used) are DEVICE arrays of `batch` device
+ * pointers, as in dion3_step_megabatch_accum / _norm.  G: NULL, or the
+ * gradients accumulated first (M <- M + G).  V: the per-neuron
+ * normalization states (n floats per matrix); required when the call is
+ * given a dion3_norm_cfg, ignored otherwise.  idx_out ([batch][k] int32) and
+ * O_out ([batch][k][m] fp16) are optional outputs as in the megabatch call. */
+typedef struct {
+  float* const* W;
+  float* const* M;
+  const float* const* G;
+  float* const* V;
+  int64_t n, m, ld, k;
+  int32_t batch;
+  float lr;
+  int32_t* idx_out;
+  uint16_t* O_out;
+} dion3_group;
+
+/* sizeof(dion3_group) as this library was built (for bindings). */
+DION3_API size_t dion3_group_size(void);
+
+/* Workspace bytes for dion3_step_groups over these groups and this schedule
+ * (cfg NULL: the default).  Only the sizes of each group are read.  The
+ * status codes are those of dion3_step_groups' shape checks. */
+DION3_API dion3_status dion3_workspace_size_groups(const dion3_group* groups, int32_t ngroups,
+                                                   const dion3_ns_cfg* cfg, size_t* bytes);
+
+/* The step over a whole model's shape groups in one call (the host array
+ * `groups`, 1 <= ngroups <= DION3_MAX_GROUPS).  Megabatching ("Dion3:
+ * Full-Stack Orthogonal Updates", agihunt.info, level-4 paragraph) carried
+ * one level further on one GPU: groups whose Gram sides are equal (s =
+ * min(k, m); e.g. the attention and down-projection matrices of a
+ * transformer at one fraction) run their s x s products, the polynomial and
+ * the symmetric products of the level-2 paragraph, as one launch over the
+ * matrices of all of them; each group's products that read its selected
+ * rows (the Grams and the multiply-backs) run per group.  norm: NULL, or the
+ * per-neuron normalization of dion3_step_megabatch_norm for every group.
+ * Results equal calling dion3_step_megabatch (_accum, _norm) once per group
+ * with the same arguments, bit for bit.  Matrices written by different
+ * groups must not overlap.  All checks (every group, then the workspace)
+ * run before the first launch. */
+DION3_API dion3_status dion3_step_groups(const dion3_group* groups, int32_t ngroups, float mu,
+                                         const dion3_ns_cfg* cfg, const dion3_norm_cfg* norm,
+                                         void* ws, size_t ws_bytes, void* stream);
 
 /* The symmetric products of the level-2 paragraph, usable on their own.
  *

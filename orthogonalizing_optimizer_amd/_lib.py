@@ -46,6 +46,15 @@ class NormCfg(ctypes.Structure):
     _fields_ = [("beta2", ctypes.c_float), ("eps", ctypes.c_float)]
 
 
+class GroupDesc(ctypes.Structure):
+    """Mirror of dion3_group (one shape group of a grouped step)."""
+    _fields_ = [("W", ctypes.c_void_p), ("M", ctypes.c_void_p), ("G", ctypes.c_void_p),
+                ("V", ctypes.c_void_p), ("n", ctypes.c_int64), ("m", ctypes.c_int64),
+                ("ld", ctypes.c_int64), ("k", ctypes.c_int64), ("batch", ctypes.c_int32),
+                ("lr", ctypes.c_float), ("idx_out", ctypes.c_void_p), ("O_out", ctypes.c_void_p)]
+
+
+MAX_GROUPS = 64
 NS_GRAM = 0
 NS_STANDARD = 1
 PATH_AUTO = 0
@@ -78,6 +87,11 @@ def _declare(lib):
         "dion3_step_megabatch_norm": (c.c_int, [vp, vp, vp, vp, i32, i64, i64, i64, i64, f32, f32,
                                                 c.POINTER(NsCfg), c.POINTER(NormCfg), vp, vp, vp,
                                                 sz, vp]),
+        "dion3_group_size": (sz, []),
+        "dion3_workspace_size_groups": (c.c_int, [c.POINTER(GroupDesc), i32, c.POINTER(NsCfg),
+                                                  c.POINTER(sz)]),
+        "dion3_step_groups": (c.c_int, [c.POINTER(GroupDesc), i32, f32, c.POINTER(NsCfg),
+                                        c.POINTER(NormCfg), vp, sz, vp]),
         "dion3_syrk_f16": (c.c_int, [vp, vp, i32, i64, i64, i64, i64, vp]),
         "dion3_symm_f16": (c.c_int, [vp, vp, vp, vp, i32, i64, i64, f32, f32, f32, vp]),
         "dion3_trace_enable": (c.c_int, [i32]),
@@ -98,7 +112,8 @@ def _declare(lib):
 EXPORTED = ("dion3_version", "dion3_ns_cfg_size", "dion3_ns_cfg_default", "dion3_k_from_fraction",
             "dion3_workspace_size", "dion3_row_select", "dion3_gram_ns", "dion3_step",
             "dion3_step_megabatch", "dion3_step_accum", "dion3_step_megabatch_accum",
-            "dion3_step_megabatch_norm",
+            "dion3_step_megabatch_norm", "dion3_group_size", "dion3_workspace_size_groups",
+            "dion3_step_groups",
             "dion3_syrk_f16", "dion3_symm_f16", "dion3_trace_enable",
             "dion3_trace_count", "dion3_trace_reset", "dion3_trace_record", "dion3_status_string",
             "dion3_last_hip_error")
@@ -115,6 +130,10 @@ def lib():
         if loaded.dion3_ns_cfg_size() != ctypes.sizeof(NsCfg):
             raise ImportError(f"{LIB_PATH}: dion3_ns_cfg is {loaded.dion3_ns_cfg_size()} bytes, "
                               f"the binding's NsCfg {ctypes.sizeof(NsCfg)}: rebuild the library")
+        if loaded.dion3_group_size() != ctypes.sizeof(GroupDesc):
+            raise ImportError(f"{LIB_PATH}: dion3_group is {loaded.dion3_group_size()} bytes, "
+                              f"the binding's GroupDesc {ctypes.sizeof(GroupDesc)}: rebuild the "
+                              "library")
         _lib = loaded
     return _lib
 
@@ -368,6 +387,87 @@ def step_megabatch(Ws, Ms, k: int, lr: float, mu: float, cfg: Optional[NsCfg] = 
                                                 _ptr(idx), _ptr(O), p, nb, _stream(dev)),
                "dion3_step_megabatch_accum")
     return idx, O
+
+
+class Group:
+    """One shape group of a grouped step: same-shape fp32 matrices W and M
+    (contiguous rows, equal strides), k selected rows each, step size lr.
+    Optional: gradients Gs (accumulated first) and per-neuron states Vs (fp32
+    [n] each).  The device pointer arrays are built once and kept; build a
+    new Group if the tensors change."""
+
+    def __init__(self, Ws, Ms, k: int, lr: float, Gs=None, Vs=None):
+        torch = _torch()
+        if len(Ws) != len(Ms) or not Ws:
+            raise ValueError("need equally many W and M matrices")
+        if Gs is not None and len(Gs) != len(Ms):
+            raise ValueError("need one gradient per matrix")
+        if Vs is not None and len(Vs) != len(Ms):
+            raise ValueError("need one state vector per matrix")
+        shape, stride = Ms[0].shape, Ms[0].stride()
+        for t in list(Ws) + list(Ms) + list(Gs or []):
+            _req(t, torch.float32, "W/M/G")
+            if t.shape != shape or t.stride() != stride or t.dim() != 2 or t.stride(1) != 1:
+                raise ValueError("all matrices must share shape and strides with contiguous rows")
+        self.n, self.m = shape
+        for v in Vs or []:
+            _req(v, torch.float32, "V")
+            if v.dim() != 1 or v.shape[0] != self.n or v.stride(0) != 1:
+                raise ValueError("each state must be a contiguous fp32 vector of n entries")
+        self.device = Ms[0].device
+        self.Ws, self.Ms, self.Gs, self.Vs = list(Ws), list(Ms), Gs, Vs
+        self.k, self.lr, self.ld, self.batch = int(k), float(lr), stride[0], len(Ms)
+        self.ptrs = (pointer_array(Ws, self.device), pointer_array(Ms, self.device))
+        self.gptrs = pointer_array(Gs, self.device) if Gs is not None else None
+        self.vptrs = pointer_array(Vs, self.device) if Vs is not None else None
+
+    def desc(self, idx=None, O=None) -> GroupDesc:
+        return GroupDesc(self.ptrs[0].data_ptr(), self.ptrs[1].data_ptr(),
+                         self.gptrs.data_ptr() if self.gptrs is not None else None,
+                         self.vptrs.data_ptr() if self.vptrs is not None else None,
+                         self.n, self.m, self.ld, self.k, self.batch, self.lr, _ptr(idx), _ptr(O))
+
+
+def workspace_size_groups(groups: Sequence[Group], cfg: Optional[NsCfg] = None) -> int:
+    arr = (GroupDesc * len(groups))(*[g.desc() for g in groups])
+    out = ctypes.c_size_t(0)
+    _check(lib().dion3_workspace_size_groups(arr, len(groups),
+                                             ctypes.byref(cfg) if cfg is not None else None,
+                                             ctypes.byref(out)), "dion3_workspace_size_groups")
+    return int(out.value)
+
+
+def step_groups(groups: Sequence[Group], mu: float, cfg: Optional[NsCfg] = None, norm=None,
+                return_idx: bool = False, return_O: bool = False,
+                ws: Optional[Workspace] = None):
+    """One Dion3 step over several shape groups in one call (groups with
+    equal Gram sides share their s x s products' launches).  norm: None or
+    (beta2, eps), with every group carrying its states Vs.  Returns one
+    (idx, O) pair per group (None unless asked for)."""
+    torch = _torch()
+    if not groups:
+        raise ValueError("need at least one group")
+    dev = groups[0].device
+    if any(g.device != dev for g in groups):
+        raise ValueError("all groups must be on one device")
+    if norm is not None and any(g.vptrs is None for g in groups):
+        raise ValueError("the normalized step needs the states Vs of every group")
+    outs = []
+    for g in groups:
+        idx = torch.empty((g.batch, g.k), dtype=torch.int32, device=dev) if return_idx else None
+        O = torch.empty((g.batch, g.k, g.m), dtype=torch.float16, device=dev) if return_O else None
+        outs.append((idx, O))
+    arr = (GroupDesc * len(groups))(*[g.desc(i, o) for g, (i, o) in zip(groups, outs)])
+    c = ctypes.byref(cfg) if cfg is not None else None
+    need = ctypes.c_size_t(0)
+    _check(lib().dion3_workspace_size_groups(arr, len(groups), c, ctypes.byref(need)),
+           "dion3_workspace_size_groups")
+    p, nb = _ws_for(ws, dev).get(int(need.value), dev)
+    nc = NormCfg(float(norm[0]), float(norm[1])) if norm is not None else None
+    _check(lib().dion3_step_groups(arr, len(groups), float(mu), c,
+                                   ctypes.byref(nc) if nc is not None else None, p, nb,
+                                   _stream(dev)), "dion3_step_groups")
+    return outs
 
 
 def syrk_f16(A):

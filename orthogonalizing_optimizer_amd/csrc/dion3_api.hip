@@ -26,46 +26,114 @@ dion3_status hip_fail(hipError_t e) {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Workspace layout for `B` matrices of n x m with k selected rows.  The
-// selected rows X live in zero-padded fp16 blocks per matrix, both in rows
-// layout [kp][mp] and transposed [mp][kp], so that every product reads
-// K-contiguous operands; the s x s Gram-side matrices are zero-padded to
-// sp x sp.  Zero padding is exact for Gram Newton-Schulz: the padded block
-// stays decoupled from the real one and its output rows and columns are zero.
-struct Plan {
+// Shapes of one group of B same-shape matrices (n x m, k selected rows).
+// The selected rows X live in zero-padded fp16 blocks per matrix, both in
+// rows layout [kp][mp] and transposed [mp][kp], so that every product reads
+// K-contiguous operands; the Gram side s = min(k, m) pads to sp and the
+// other side L = max(k, m) to Lp.  Zero padding is exact for Gram
+// Newton-Schulz: the padded block stays decoupled from the real one and its
+// output rows and columns are zero.
+struct Shape {
   int B;
   long long n, m, k;
   bool tr;                 // k > m: the Gram is X^T X (s = m)
   long long kp, mp, sp, Lp;
-  size_t o_l1, o_sq, o_idx, o_scale, o_Xa, o_XaT, o_Xb, o_XbT, o_R, o_Z, o_T, o_Q0, o_Q1, total;
 };
 
-Plan make_plan(int B, long long n, long long m, long long k) {
-  Plan P;
+Shape make_shape(int B, long long n, long long m, long long k) {
+  Shape P;
   P.B = B; P.n = n; P.m = m; P.k = k;
   P.tr = k > m;
   P.kp = pad_to(k, kTile);
   P.mp = pad_to(m, kTile);
   P.sp = P.tr ? P.mp : P.kp;
   P.Lp = P.tr ? P.kp : P.mp;
+  return P;
+}
+
+// Workspace regions of one group: fp64 l1 and sum of squares per row, the
+// selected indices, the per-matrix scale and two X pairs (ping-pong for the
+// restart).
+struct GroupLayout {
+  Shape P;
+  size_t o_l1, o_sq, o_idx, o_scale, o_Xa, o_XaT, o_Xb, o_XbT;
+  int side;              // its Gram-side set, or -1 (the fused path needs none)
+  long long side_off;    // its first matrix inside that set
+};
+
+// Gram-side buffers R, Z, T, Q, Q' ([batch][sp][sp] fp16 each) of the groups
+// whose Gram sides are equal (same s, hence same sp): their s x s products,
+// the polynomial and the symmetric products of the level-2 paragraph, run
+// as one launch over the matrices of all of them.
+struct SideLayout {
+  long long sp, s;
+  int batch;
+  size_t o_R, o_Z, o_T, o_Q0, o_Q1;
+};
+
+struct CallLayout {
+  int ng, nside;
+  GroupLayout g[DION3_MAX_GROUPS];
+  SideLayout sd[DION3_MAX_GROUPS];
+  size_t total;
+};
+
+long long side_of(const Shape& P) { return P.tr ? P.m : P.k; }
+
+// Regions in order: every group's rows and X pairs, then the side sets.  A
+// group with no_side[g] set gets no side set; the others join the set of
+// their Gram side.
+void make_layout(CallLayout& L, int ng, const Shape* shapes, const bool* no_side) {
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
-  P.o_l1 = take((size_t)B * n * 8);
-  P.o_sq = take((size_t)B * n * 8);
-  P.o_idx = take((size_t)B * k * 4);
-  P.o_scale = take((size_t)B * 8);
-  const size_t xb = (size_t)B * P.kp * P.mp * 2, sb = (size_t)B * P.sp * P.sp * 2;
-  P.o_Xa = take(xb);
-  P.o_XaT = take(xb);
-  P.o_Xb = take(xb);
-  P.o_XbT = take(xb);
-  P.o_R = take(sb);
-  P.o_Z = take(sb);
-  P.o_T = take(sb);
-  P.o_Q0 = take(sb);
-  P.o_Q1 = take(sb);
-  P.total = off;
-  return P;
+  L.ng = ng;
+  L.nside = 0;
+  for (int i = 0; i < ng; ++i) {
+    GroupLayout& G = L.g[i];
+    const Shape& P = shapes[i];
+    G.P = P;
+    G.o_l1 = take((size_t)P.B * P.n * 8);
+    G.o_sq = take((size_t)P.B * P.n * 8);
+    G.o_idx = take((size_t)P.B * P.k * 4);
+    G.o_scale = take((size_t)P.B * 8);
+    const size_t xb = (size_t)P.B * P.kp * P.mp * 2;
+    G.o_Xa = take(xb);
+    G.o_XaT = take(xb);
+    G.o_Xb = take(xb);
+    G.o_XbT = take(xb);
+    G.side = -1;
+    G.side_off = 0;
+    if (no_side[i]) continue;
+    int j = 0;
+    while (j < L.nside && !(L.sd[j].sp == P.sp && L.sd[j].s == side_of(P))) ++j;
+    if (j == L.nside) {
+      L.sd[j].sp = P.sp;
+      L.sd[j].s = side_of(P);
+      L.sd[j].batch = 0;
+      ++L.nside;
+    }
+    G.side = j;
+    G.side_off = L.sd[j].batch;
+    L.sd[j].batch += P.B;
+  }
+  for (int j = 0; j < L.nside; ++j) {
+    SideLayout& S = L.sd[j];
+    const size_t sb = (size_t)S.batch * S.sp * S.sp * 2;
+    S.o_R = take(sb);
+    S.o_Z = take(sb);
+    S.o_T = take(sb);
+    S.o_Q0 = take(sb);
+    S.o_Q1 = take(sb);
+  }
+  L.total = off;
+}
+
+// The layout of a one-group call: always with a side set, so that its size
+// does not depend on the schedule (dion3_workspace_size takes no cfg).
+void make_single_layout(CallLayout& L, int B, long long n, long long m, long long k) {
+  const Shape P = make_shape(B, n, m, k);
+  const bool no_side = false;
+  make_layout(L, 1, &P, &no_side);
 }
 
 // Size checks of the step's entry points, in the order the header states:
@@ -83,11 +151,20 @@ constexpr long long kMaxOperandBytes = 1LL << 31;
 // The grid of every product (128-wide tiles at most, times the batch) must
 // also fit a launch, checked here so that no kernel runs before a refusal.
 constexpr long long kMaxGrid = 0x7fffffffLL;
-bool plan_fits(const Plan& P) {
+bool shape_fits(const Shape& P) {
   const long long ts = P.sp / kTile, tl = P.Lp / kTile;
   const long long tiles = ts * (ts + 1) / 2 > ts * tl ? ts * (ts + 1) / 2 : ts * tl;
   return P.kp * P.mp * 2 < kMaxOperandBytes && P.sp * P.sp * 2 < kMaxOperandBytes &&
          tiles * P.B <= kMaxGrid;
+}
+bool layout_fits(const CallLayout& L) {
+  for (int i = 0; i < L.ng; ++i)
+    if (!shape_fits(L.g[i].P)) return false;
+  for (int j = 0; j < L.nside; ++j) {
+    const long long ts = L.sd[j].sp / kTile;
+    if (ts * (ts + 1) / 2 * L.sd[j].batch > kMaxGrid) return false;
+  }
+  return true;
 }
 
 dion3_status check_cfg(const dion3_ns_cfg* c) {
@@ -109,8 +186,13 @@ dion3_status check_cfg(const dion3_ns_cfg* c) {
   return DION3_OK;
 }
 
-dion3_status check_ws(const Plan& P, void* ws, size_t ws_bytes, size_t need) {
-  (void)P;
+dion3_status check_norm(const dion3_norm_cfg* norm) {
+  if (!(norm->beta2 >= 0.0f && norm->beta2 < 1.0f) || !(norm->eps >= 0.0f) || !isfinite(norm->eps))
+    return DION3_ERR_ARG;
+  return DION3_OK;
+}
+
+dion3_status check_ws(void* ws, size_t ws_bytes, size_t need) {
   if (!ws || ((uintptr_t)ws & 255) != 0) return DION3_ERR_WORKSPACE;
   if (ws_bytes < need) return DION3_ERR_WORKSPACE;
   return DION3_OK;
@@ -129,31 +211,11 @@ struct XPair {
   f16 *X, *XT;
 };
 
-struct Bufs {
-  XPair a, b;
-  f16 *R, *Z, *T, *Q0, *Q1;
-};
-
-Bufs carve(const Plan& P, void* ws) {
-  char* w = (char*)ws;
-  Bufs b;
-  b.a.X = (f16*)(w + P.o_Xa);
-  b.a.XT = (f16*)(w + P.o_XaT);
-  b.b.X = (f16*)(w + P.o_Xb);
-  b.b.XT = (f16*)(w + P.o_XbT);
-  b.R = (f16*)(w + P.o_R);
-  b.Z = (f16*)(w + P.o_Z);
-  b.T = (f16*)(w + P.o_T);
-  b.Q0 = (f16*)(w + P.o_Q0);
-  b.Q1 = (f16*)(w + P.o_Q1);
-  return b;
-}
-
 double dbl(long long v) { return (double)v; }
 
 // Unpadded Gram-side sizes: s = min(k, m), L = max(k, m).
-double s_of(const Plan& P) { return dbl(P.tr ? P.m : P.k); }
-double L_of(const Plan& P) { return dbl(P.tr ? P.k : P.m); }
+double s_of(const Shape& P) { return dbl(P.tr ? P.m : P.k); }
+double L_of(const Shape& P) { return dbl(P.tr ? P.k : P.m); }
 
 // The Gram side works on X_math (sp x Lp): the selected rows when k <= m,
 // their transpose when k > m.  Its row-form copy has row stride Lp and its
@@ -163,36 +225,39 @@ double L_of(const Plan& P) { return dbl(P.tr ? P.k : P.m); }
 // the padded block are zero too), so only K steps that touch it are run.
 int k_loop(double extent) { return (int)pad_to((long long)extent, kKStep); }
 
-const f16* xmath(const Plan& P, const XPair& x) { return P.tr ? x.XT : x.X; }
-const f16* xmathT(const Plan& P, const XPair& x) { return P.tr ? x.X : x.XT; }
+const f16* xmath(const Shape& P, const XPair& x) { return P.tr ? x.XT : x.X; }
+const f16* xmathT(const Shape& P, const XPair& x) { return P.tr ? x.X : x.XT; }
 
 // R = X_math X_math^T.
-hipError_t gram(const Plan& P, const XPair& x, f16* R, hipStream_t s) {
-  const double sv = s_of(P);
+hipError_t gram(const Shape& P, const XPair& x, f16* R, hipStream_t s) {
+  const double sv = s_of(P), L = L_of(P);
   GemmDesc d = {};
-  d.trace_flops = P.B * sv * sv * L_of(P);
+  d.trace_flops = P.B * sv * sv * L;
+  d.trace_bytes = 2.0 * P.B * sv * (L + sv);          // read X, write R
   d.role = kRoleGram;
   d.A = d.B = xmath(P, x); d.sA = d.sB = P.kp * P.mp; d.lda = d.ldb = (int)P.Lp;
   d.C = R; d.sC = P.sp * P.sp; d.ldc = (int)P.sp;
-  d.M = d.N = (int)P.sp; d.K = k_loop(L_of(P)); d.batch = P.B;
+  d.M = d.N = (int)P.sp; d.K = k_loop(L); d.batch = P.B;
   d.lower = true; d.epilogue = false;
   d.alpha = 1.0f;
   return launch_gemm(d, s);
 }
 
-// C = alpha A B + beta D + gamma I for symmetric commuting s x s matrices.
-hipError_t symm(const Plan& P, const f16* A, const f16* B, const f16* D, f16* C, float alpha,
+// C = alpha A B + beta D + gamma I for symmetric commuting s x s matrices,
+// over every matrix of a side set.
+hipError_t symm(const SideLayout& S, const f16* A, const f16* B, const f16* D, f16* C, float alpha,
                 float beta, float gamma, bool epi, hipStream_t s) {
-  const double sv = s_of(P);
+  const double sv = dbl(S.s);
   GemmDesc d = {};
-  d.trace_flops = P.B * sv * sv * sv;
+  d.trace_flops = S.batch * sv * sv * sv;
+  d.trace_bytes = (epi ? 4.0 : 6.0) * S.batch * sv * sv;   // read A (= B = D) or A and B, write C
   d.role = epi ? kRolePoly : kRoleSymm;
-  const long long ss = P.sp * P.sp;
-  d.A = A; d.sA = ss; d.lda = (int)P.sp;
-  d.B = B; d.sB = ss; d.ldb = (int)P.sp;
-  d.C = C; d.sC = ss; d.ldc = (int)P.sp;
-  d.D = D; d.sD = ss; d.ldd = (int)P.sp;
-  d.M = d.N = (int)P.sp; d.K = k_loop(sv); d.batch = P.B;
+  const long long ss = S.sp * S.sp;
+  d.A = A; d.sA = ss; d.lda = (int)S.sp;
+  d.B = B; d.sB = ss; d.ldb = (int)S.sp;
+  d.C = C; d.sC = ss; d.ldc = (int)S.sp;
+  d.D = D; d.sD = ss; d.ldd = (int)S.sp;
+  d.M = d.N = (int)S.sp; d.K = k_loop(sv); d.batch = S.batch;
   d.lower = true; d.epilogue = epi;
   d.alpha = alpha; d.beta = beta; d.gamma = gamma;
   d.gdiag = (int)sv;   // the identity of the unpadded Gram side only
@@ -210,29 +275,39 @@ struct UpdateSink {
   long long sO;   // elements between consecutive matrices' O blocks (>= k * m)
 };
 
+void set_sink(GemmDesc& d, const Shape& P, const UpdateSink& sink) {
+  // rows layout is the math layout when k <= m (the C pass) and its
+  // transpose when k > m (the CT pass)
+  d.sink = P.tr ? 2 : 1;
+  d.C = nullptr;
+  d.CT = nullptr;
+  d.W = sink.W; d.ldw = sink.ldw; d.idx = sink.idx; d.lr = sink.lr; d.Oout = sink.Oout;
+  d.sO = sink.sO;
+  d.kval = (int)P.k; d.mval = (int)P.m; d.nrows = (int)P.n;
+}
+
 // Y_math = Q X_math.  The restart needs Y in both layouts.  The final
 // product (sink set) stores nothing: its rows-layout output goes straight
 // into the update of W (and O_out).
-hipError_t rect(const Plan& P, const f16* Q, const XPair& x, const XPair& y, bool both,
+hipError_t rect(const Shape& P, const f16* Q, const XPair& x, const XPair& y, bool both,
                 hipStream_t s, const UpdateSink* sink = nullptr) {
-  const double sv = s_of(P);
+  const double sv = s_of(P), L = L_of(P);
   GemmDesc d = {};
-  d.trace_flops = 2.0 * P.B * sv * sv * L_of(P);
-  d.role = kRoleRect;
+  d.trace_flops = 2.0 * P.B * sv * sv * L;
+  d.role = sink ? kRoleBack : kRoleRect;
   d.A = Q; d.sA = P.sp * P.sp; d.lda = (int)P.sp;
   d.B = xmathT(P, x); d.sB = P.kp * P.mp; d.ldb = (int)P.sp;
   const bool want_math = both || !P.tr, want_mathT = both || P.tr;
   d.C = want_math ? (f16*)xmath(P, y) : nullptr; d.sC = P.kp * P.mp; d.ldc = (int)P.Lp;
   d.CT = want_mathT ? (f16*)xmathT(P, y) : nullptr; d.sCT = P.kp * P.mp; d.ldct = (int)P.sp;
   if (sink) {
-    // rows layout is the math layout when k <= m (the C pass) and its
-    // transpose when k > m (the CT pass)
-    d.sink = P.tr ? 2 : 1;
-    d.C = nullptr;
-    d.CT = nullptr;
-    d.W = sink->W; d.ldw = sink->ldw; d.idx = sink->idx; d.lr = sink->lr; d.Oout = sink->Oout;
-    d.sO = sink->sO;
-    d.kval = (int)P.k; d.mval = (int)P.m; d.nrows = (int)P.n;
+    set_sink(d, P, *sink);
+    // read Q and X, read and write the selected rows of W (fp32), and write
+    // O when asked
+    const bool w = sink->W.ptrs || sink->W.base;
+    d.trace_bytes = P.B * (2.0 * sv * sv + (2.0 + (w ? 8.0 : 0.0) + (sink->Oout ? 2.0 : 0.0)) * sv * L);
+  } else {
+    d.trace_bytes = P.B * (2.0 * sv * sv + 4.0 * sv * L);   // read Q and X, write Y
   }
   d.M = (int)P.sp; d.N = (int)P.Lp; d.K = k_loop(sv); d.batch = P.B;
   d.lower = false; d.epilogue = false;
@@ -240,15 +315,10 @@ hipError_t rect(const Plan& P, const f16* Q, const XPair& x, const XPair& y, boo
   return launch_gemm(d, s);
 }
 
-// Gram Newton-Schulz on the normalized, padded X held in bufs.a ("Dion3:
-// Full-Stack Orthogonal Updates", agihunt.info, level-1 paragraph).  Every
-// matrix here is a polynomial in the first Gram, so all products commute,
-// are symmetric, and only their lower triangles are computed.  The final
-// product hands O to `sink` (the row-sparse update and/or O_out).
 // Algorithmic flops of the whole Gram iteration on unpadded sizes, with the
 // symmetric products counted at half (lower triangle), as the tiled
 // launches record them.
-double gram_ns_flops(const Plan& P, const dion3_ns_cfg& cfg) {
+double gram_ns_flops(const Shape& P, const dion3_ns_cfg& cfg) {
   const double sv = s_of(P), L = L_of(P), B = P.B;
   double f = B * sv * sv * L;               // first Gram
   bool q_identity = true;
@@ -274,71 +344,95 @@ double gram_ns_flops(const Plan& P, const dion3_ns_cfg& cfg) {
 // spread long rows over many CUs.  Measured crossovers: the fused path wins
 // up to L = 2048 at any batch, up to 4096 from 16 matrices on, and up to
 // 8192 from 64 matrices on.
-bool use_fused(const Plan& P, const dion3_ns_cfg& cfg) {
+bool use_fused(const Shape& P, const dion3_ns_cfg& cfg) {
+  if (cfg.method != DION3_NS_GRAM) return false;
   if (cfg.path == DION3_PATH_TILED || P.sp != kTile) return false;
   if (cfg.path == DION3_PATH_FUSED) return true;
   return P.Lp <= 2048 || (P.Lp <= 4096 && P.B >= 16) || (P.Lp <= 8192 && P.B >= 64);
 }
 
 // The fused path was asked for explicitly but the Gram side exceeds 128.
-bool path_ok(const Plan& P, const dion3_ns_cfg& cfg) {
+bool path_ok(const Shape& P, const dion3_ns_cfg& cfg) {
   return !(cfg.method == DION3_NS_GRAM && cfg.path == DION3_PATH_FUSED && P.sp != kTile);
 }
 
-dion3_status gram_ns(const Plan& P, const dion3_ns_cfg& cfg, const Bufs& bf,
-                     const UpdateSink& sink, hipStream_t s) {
-  if (use_fused(P, cfg)) {
-    HIP_TRY(launch_gram_ns_small(
-        (f16*)xmath(P, bf.a), (f16*)xmathT(P, bf.a), (f16*)xmath(P, bf.b), (f16*)xmathT(P, bf.b),
-        P.kp * P.mp, P.B, (int)P.Lp, P.tr, cfg, sink.W, sink.ldw, sink.idx, sink.lr, sink.Oout,
-        sink.sO,
-        (int)P.k, (int)P.m, (int)P.n, gram_ns_flops(P, cfg), s));
-    return DION3_OK;
+// One group inside the orthogonalization: its layout, its current and free
+// X pairs and where its result goes.
+struct GroupRun {
+  const GroupLayout* G;
+  XPair x, xalt;
+  UpdateSink sink;
+};
+
+void swap_pairs(GroupRun* r, int nr) {
+  for (int i = 0; i < nr; ++i) {
+    XPair t = r[i].x;
+    r[i].x = r[i].xalt;
+    r[i].xalt = t;
   }
-  XPair x = bf.a, xalt = bf.b;
-  f16 *R = bf.R, *Z = bf.Z, *Tm = bf.T, *Q = bf.Q0, *Qn = bf.Q1;
-  HIP_TRY(gram(P, x, R, s));
+}
+
+// The Gram-side matrices of one group inside its set's buffer.
+f16* slice(f16* base, const SideLayout& S, const GroupLayout& G) {
+  return base + G.side_off * S.sp * S.sp;
+}
+
+// Gram Newton-Schulz on the normalized, padded X of every group of one side
+// set ("Dion3: Full-Stack Orthogonal Updates", agihunt.info, level-1
+// paragraph).  Every matrix here is a polynomial in the first Gram, so all
+// products commute, are symmetric, and only their lower triangles are
+// computed.  The products that read X (the Grams, the restart's X <- Q X
+// and the final multiply-back) run per group; the s x s products run once
+// over the whole set.  The final product hands O to each group's sink.
+dion3_status gram_ns_set(const dion3_ns_cfg& cfg, const SideLayout& S, char* w, GroupRun* r, int nr,
+                         hipStream_t s) {
+  f16 *R = (f16*)(w + S.o_R), *Z = (f16*)(w + S.o_Z), *Tm = (f16*)(w + S.o_T);
+  f16 *Q = (f16*)(w + S.o_Q0), *Qn = (f16*)(w + S.o_Q1);
+  for (int i = 0; i < nr; ++i) HIP_TRY(gram(r[i].G->P, r[i].x, slice(R, S, *r[i].G), s));
   bool q_identity = true;
   const int T = cfg.iters;
   for (int t = 1; t <= T; ++t) {
     if (restart_at(cfg, t)) {      // X <- Q X, R <- X X^T, Q <- I
       if (!q_identity) {
-        HIP_TRY(rect(P, Q, x, xalt, true, s));
-        XPair tmp = x; x = xalt; xalt = tmp;
+        for (int i = 0; i < nr; ++i)
+          HIP_TRY(rect(r[i].G->P, slice(Q, S, *r[i].G), r[i].x, r[i].xalt, true, s));
+        swap_pairs(r, nr);
       }
-      HIP_TRY(gram(P, x, R, s));
+      for (int i = 0; i < nr; ++i) HIP_TRY(gram(r[i].G->P, r[i].x, slice(R, S, *r[i].G), s));
       q_identity = true;
     }
     const float a = cfg.abc[t - 1][0], b = cfg.abc[t - 1][1], c = cfg.abc[t - 1][2];
     // Z = a I + b R + c R^2  (the "A^2 + B" product)
-    HIP_TRY(symm(P, R, R, R, Z, c, b, a, true, s));
+    HIP_TRY(symm(S, R, R, R, Z, c, b, a, true, s));
     f16* Zv;
     if (q_identity) {           // Q <- Z Q with Q = I: just adopt Z
       f16* tmp = Q; Q = Z; Z = tmp;
       Zv = Q;
       q_identity = false;
     } else {
-      HIP_TRY(symm(P, Z, Q, nullptr, Qn, 1.0f, 0.0f, 0.0f, false, s));
+      HIP_TRY(symm(S, Z, Q, nullptr, Qn, 1.0f, 0.0f, 0.0f, false, s));
       f16* tmp = Q; Q = Qn; Qn = tmp;
       Zv = Z;
     }
     if (t < T && !restart_at(cfg, t + 1)) {   // R <- Z R Z
-      HIP_TRY(symm(P, Zv, R, nullptr, Tm, 1.0f, 0.0f, 0.0f, false, s));
-      HIP_TRY(symm(P, Tm, Zv, nullptr, R, 1.0f, 0.0f, 0.0f, false, s));
+      HIP_TRY(symm(S, Zv, R, nullptr, Tm, 1.0f, 0.0f, 0.0f, false, s));
+      HIP_TRY(symm(S, Tm, Zv, nullptr, R, 1.0f, 0.0f, 0.0f, false, s));
     }
   }
-  HIP_TRY(rect(P, Q, x, xalt, false, s, &sink));
+  for (int i = 0; i < nr; ++i)
+    HIP_TRY(rect(r[i].G->P, slice(Q, S, *r[i].G), r[i].x, r[i].xalt, false, s, &r[i].sink));
   return DION3_OK;
 }
 
 // Standard quintic Newton-Schulz on X itself (the iteration the Gram form
 // replaces, level-1 paragraph): A = X X^T, B = b A + c A^2, X <- a X + B X.
 // The last update goes to `sink`.
-hipError_t ns_update(const Plan& P, const f16* B, const XPair& x, const XPair& y, float a,
+hipError_t ns_update(const Shape& P, const f16* B, const XPair& x, const XPair& y, float a,
                      bool both, hipStream_t s, const UpdateSink* sink) {
-  const double sv = s_of(P);
+  const double sv = s_of(P), L = L_of(P);
   GemmDesc d = {};
-  d.trace_flops = 2.0 * P.B * sv * sv * L_of(P);
+  d.trace_flops = 2.0 * P.B * sv * sv * L;
+  d.trace_bytes = P.B * (2.0 * sv * sv + 4.0 * sv * L);
   d.role = kRoleNsX;
   d.A = B; d.sA = P.sp * P.sp; d.lda = (int)P.sp;
   d.B = xmathT(P, x); d.sB = P.kp * P.mp; d.ldb = (int)P.sp;
@@ -347,125 +441,200 @@ hipError_t ns_update(const Plan& P, const f16* B, const XPair& x, const XPair& y
   const bool want_math = both || !P.tr, want_mathT = both || P.tr;
   d.C = want_math ? (f16*)xmath(P, y) : nullptr; d.sC = P.kp * P.mp; d.ldc = (int)P.Lp;
   d.CT = want_mathT ? (f16*)xmathT(P, y) : nullptr; d.sCT = P.kp * P.mp; d.ldct = (int)P.sp;
-  if (sink) {
-    d.sink = P.tr ? 2 : 1;
-    d.C = nullptr;
-    d.CT = nullptr;
-    d.W = sink->W; d.ldw = sink->ldw; d.idx = sink->idx; d.lr = sink->lr; d.Oout = sink->Oout;
-    d.sO = sink->sO;
-    d.kval = (int)P.k; d.mval = (int)P.m; d.nrows = (int)P.n;
-  }
+  if (sink) set_sink(d, P, *sink);
   d.M = (int)P.sp; d.N = (int)P.Lp; d.K = (int)P.sp; d.batch = P.B;
   return launch_gemm(d, s);
 }
 
-dion3_status standard_ns(const Plan& P, const dion3_ns_cfg& cfg, const Bufs& bf,
-                         const UpdateSink& sink, hipStream_t s) {
-  XPair x = bf.a, xalt = bf.b;
+dion3_status standard_ns_set(const dion3_ns_cfg& cfg, const SideLayout& S, char* w, GroupRun* r,
+                             int nr, hipStream_t s) {
+  f16 *R = (f16*)(w + S.o_R), *Z = (f16*)(w + S.o_Z);
   for (int t = 1; t <= cfg.iters; ++t) {
     const float a = cfg.abc[t - 1][0], b = cfg.abc[t - 1][1], c = cfg.abc[t - 1][2];
-    HIP_TRY(gram(P, x, bf.R, s));                                  // A = X X^T
-    HIP_TRY(symm(P, bf.R, bf.R, bf.R, bf.Z, c, b, 0.0f, true, s));  // B = b A + c A^2
-    if (t < cfg.iters) {
-      HIP_TRY(ns_update(P, bf.Z, x, xalt, a, true, s, nullptr));
-      XPair tmp = x; x = xalt; xalt = tmp;
-    } else {
-      HIP_TRY(ns_update(P, bf.Z, x, xalt, a, false, s, &sink));
-    }
+    for (int i = 0; i < nr; ++i) HIP_TRY(gram(r[i].G->P, r[i].x, slice(R, S, *r[i].G), s));  // A = X X^T
+    HIP_TRY(symm(S, R, R, R, Z, c, b, 0.0f, true, s));                                        // B = b A + c A^2
+    const bool last = t == cfg.iters;
+    for (int i = 0; i < nr; ++i)
+      HIP_TRY(ns_update(r[i].G->P, slice(Z, S, *r[i].G), r[i].x, r[i].xalt, a, !last, s,
+                        last ? &r[i].sink : nullptr));
+    if (!last) swap_pairs(r, nr);
   }
   return DION3_OK;
 }
 
-dion3_status orthogonalize(const Plan& P, const dion3_ns_cfg& cfg, const Bufs& bf,
-                           const UpdateSink& sink, hipStream_t s) {
-  return cfg.method == DION3_NS_STANDARD ? standard_ns(P, cfg, bf, sink, s)
-                                         : gram_ns(P, cfg, bf, sink, s);
+// The orthogonalization of every group of a call: groups on the fused
+// path one launch each, then each side set with its member groups.
+dion3_status orthogonalize(const CallLayout& L, const dion3_ns_cfg& cfg, char* w, GroupRun* runs,
+                           hipStream_t s) {
+  for (int i = 0; i < L.ng; ++i) {
+    const Shape& P = L.g[i].P;
+    if (!use_fused(P, cfg)) continue;
+    const GroupRun& r = runs[i];
+    HIP_TRY(launch_gram_ns_small((f16*)xmath(P, r.x), (f16*)xmathT(P, r.x), (f16*)xmath(P, r.xalt),
+                                 (f16*)xmathT(P, r.xalt), P.kp * P.mp, P.B, (int)P.Lp, P.tr, cfg,
+                                 r.sink.W, r.sink.ldw, r.sink.idx, r.sink.lr, r.sink.Oout,
+                                 r.sink.sO, (int)P.k, (int)P.m, (int)P.n, gram_ns_flops(P, cfg),
+                                 s));
+  }
+  for (int j = 0; j < L.nside; ++j) {
+    GroupRun members[DION3_MAX_GROUPS];
+    int nr = 0;
+    for (int i = 0; i < L.ng; ++i)
+      if (L.g[i].side == j && !use_fused(L.g[i].P, cfg)) members[nr++] = runs[i];
+    if (nr == 0) continue;
+    const dion3_status st = cfg.method == DION3_NS_STANDARD
+                                ? standard_ns_set(cfg, L.sd[j], w, members, nr, s)
+                                : gram_ns_set(cfg, L.sd[j], w, members, nr, s);
+    if (st != DION3_OK) return st;
+  }
+  return DION3_OK;
 }
 
 // The X pair that the orthogonalization no longer reads once it has started
 // its last product: every restart (Gram) or every iteration but the last
 // (standard) swaps the two pairs, starting from the first.
-const XPair& free_pair(const dion3_ns_cfg& cfg, const Bufs& bf) {
+bool free_pair_is_b(const dion3_ns_cfg& cfg) {
   const int swaps = cfg.method == DION3_NS_STANDARD ? cfg.iters - 1 : cfg.n_restart;
-  return swaps % 2 == 0 ? bf.b : bf.a;
+  return swaps % 2 == 0;
 }
 
-dion3_status step_impl(BatchPtr<float> W, BatchPtr<float> M, BatchPtr<const float> G, int batch,
-                       long long n, long long m,
-                       long long ld, long long k, float lr, float mu, const dion3_ns_cfg* cfg_in,
-                       int32_t* idx_out, uint16_t* O_out, void* ws, size_t ws_bytes,
-                       void* stream, BatchPtr<float> V = {nullptr, 0, nullptr},
-                       const dion3_norm_cfg* norm = nullptr) {
+XPair pair_a(const GroupLayout& G, char* w) { return {(f16*)(w + G.o_Xa), (f16*)(w + G.o_XaT)}; }
+XPair pair_b(const GroupLayout& G, char* w) { return {(f16*)(w + G.o_Xb), (f16*)(w + G.o_XbT)}; }
+
+// One group's arguments in a step call.
+struct GroupArgs {
+  BatchPtr<float> W, M;
+  BatchPtr<const float> G;   // gradients accumulated first, or none
+  BatchPtr<float> V;         // per-neuron normalization state, or none
+  long long ld;
+  float lr;
+  int32_t* idx_out;
+  uint16_t* O_out;
+};
+
+// The whole step for every group of a call: rows (score, select, gather
+// with decay) group by group, the orthogonalization, then the per-neuron
+// normalization (when `norm` is set) and the index copies.  Every check has
+// been made before this runs.
+dion3_status run_step(const CallLayout& L, const GroupArgs* A, float mu, const dion3_ns_cfg& cfg,
+                      const dion3_norm_cfg* norm, char* w, hipStream_t s) {
+  GroupRun runs[DION3_MAX_GROUPS];
+  for (int i = 0; i < L.ng; ++i) {
+    const GroupLayout& G = L.g[i];
+    const Shape& P = G.P;
+    const GroupArgs& a = A[i];
+    double* l1 = (double*)(w + G.o_l1);
+    double* sq = (double*)(w + G.o_sq);
+    int* idx = (int*)(w + G.o_idx);
+    double* scale = (double*)(w + G.o_scale);
+    const bool all = (P.k == P.n);
+    const double Bd = P.B, nm = dbl(P.n) * dbl(P.m), km = dbl(P.k) * dbl(P.m);
+    const int n = (int)P.n, m = (int)P.m, k = (int)P.k;
+    BatchPtr<const float> Mc = {a.M.base, a.M.stride, (const float* const*)a.M.ptrs};
+    if (a.G.base || a.G.ptrs) {   // accumulate the gradient into the buffer while scoring
+      TraceScope ts("accum_score", 0.0, Bd * nm * 12.0, s);
+      HIP_TRY(launch_accum_score_f32(a.M, a.G, P.B, n, m, a.ld, all ? nullptr : l1, sq, s));
+    } else {
+      TraceScope ts("row_score", 0.0, Bd * nm * 4.0, s);
+      HIP_TRY(launch_row_score_f32(Mc, P.B, n, m, a.ld, all ? nullptr : l1, sq, s));
+    }
+    {
+      TraceScope ts("topk", 0.0, Bd * dbl(P.n) * 16.0, s);
+      HIP_TRY(launch_topk(l1, sq, P.B, n, k, idx, scale, (double)cfg.eps, s));
+    }
+    const XPair xa = pair_a(G, w), xb = pair_b(G, w);
+    {
+      TraceScope ts("gather", 0.0, Bd * km * 10.0, s);
+      HIP_TRY(launch_gather_f32(a.M, P.B, n, m, a.ld, idx, k, scale, mu, true, xa.X, xa.XT,
+                                P.kp * P.mp, (int)P.kp, (int)P.mp, s));
+    }
+    GroupRun& r = runs[i];
+    r.G = &G;
+    r.x = xa;
+    r.xalt = xb;
+    if (!norm) {
+      r.sink = {a.W, a.ld, idx, a.lr, (f16*)a.O_out, P.k * P.m};
+    } else {
+      // O into the free X buffer, each matrix's rows [k][m] inside that
+      // matrix's own padded block (so that in the fused one-launch path no
+      // workgroup writes where another matrix may still be read)
+      f16* Obuf = free_pair_is_b(cfg) ? xb.X : xa.X;
+      r.sink = {{nullptr, 0, nullptr}, 0, idx, a.lr, Obuf, P.kp * P.mp};
+    }
+  }
+  dion3_status st = orthogonalize(L, cfg, w, runs, s);
+  if (st != DION3_OK) return st;
+  for (int i = 0; i < L.ng; ++i) {
+    const GroupLayout& G = L.g[i];
+    const Shape& P = G.P;
+    const GroupArgs& a = A[i];
+    int* idx = (int*)(w + G.o_idx);
+    if (norm) {
+      // the row statistics reuse the score region and the per-matrix scale
+      // the norm region
+      const f16* Obuf = runs[i].sink.Oout;
+      const long long sO = runs[i].sink.sO;
+      HIP_TRY(launch_normalize(Obuf, sO, P.B, (int)P.k, (int)P.m, idx, a.V, norm->beta2, norm->eps,
+                               a.W, a.ld, a.lr, (float2*)(w + G.o_l1), (double*)(w + G.o_scale),
+                               s));
+      if (a.O_out)
+        HIP_TRY(hipMemcpy2DAsync(a.O_out, (size_t)P.k * P.m * sizeof(uint16_t), Obuf,
+                                 (size_t)sO * sizeof(uint16_t), (size_t)P.k * P.m * sizeof(uint16_t),
+                                 (size_t)P.B, hipMemcpyDeviceToDevice, s));
+    }
+    if (a.idx_out)
+      HIP_TRY(hipMemcpyAsync(a.idx_out, idx, (size_t)P.B * P.k * sizeof(int32_t),
+                             hipMemcpyDeviceToDevice, s));
+  }
+  return DION3_OK;
+}
+
+// The checks shared by every one-group step entry point, then the step.
+dion3_status step_one(const GroupArgs& a, int batch, long long n, long long m, long long k,
+                      float mu, const dion3_ns_cfg* cfg_in, const dion3_norm_cfg* norm, void* ws,
+                      size_t ws_bytes, void* stream) {
   if (batch < 1 || batch > DION3_MAX_BATCH) return DION3_ERR_ARG;
-  if (norm && (!(V.base || V.ptrs) || !(norm->beta2 >= 0.0f && norm->beta2 < 1.0f) ||
-               !(norm->eps >= 0.0f) || !isfinite(norm->eps)))
-    return DION3_ERR_ARG;
+  if (norm && (!(a.V.base || a.V.ptrs) || check_norm(norm) != DION3_OK)) return DION3_ERR_ARG;
   dion3_status st = check_dims(n, m, k);
   if (st != DION3_OK) return st;
-  if (ld < m) return DION3_ERR_ARG;
-  if (!isfinite(lr) || !isfinite(mu)) return DION3_ERR_ARG;
+  if (a.ld < m) return DION3_ERR_ARG;
+  if (!isfinite(a.lr) || !isfinite(mu)) return DION3_ERR_ARG;
   dion3_ns_cfg cfg;
   if (cfg_in) cfg = *cfg_in; else dion3_ns_cfg_default(&cfg);
   st = check_cfg(&cfg);
   if (st != DION3_OK) return st;
-  const Plan P = make_plan(batch, n, m, k);
-  if (!plan_fits(P) || !path_ok(P, cfg)) return DION3_ERR_UNSUPPORTED;
-  st = check_ws(P, ws, ws_bytes, P.total);
+  CallLayout L;
+  make_single_layout(L, batch, n, m, k);
+  if (!layout_fits(L) || !path_ok(L.g[0].P, cfg)) return DION3_ERR_UNSUPPORTED;
+  st = check_ws(ws, ws_bytes, L.total);
   if (st != DION3_OK) return st;
+  return run_step(L, &a, mu, cfg, norm, (char*)ws, (hipStream_t)stream);
+}
 
-  hipStream_t s = (hipStream_t)stream;
-  char* w = (char*)ws;
-  double* l1 = (double*)(w + P.o_l1);
-  double* sq = (double*)(w + P.o_sq);
-  int* idx = (int*)(w + P.o_idx);
-  double* scale = (double*)(w + P.o_scale);
-  const Bufs bf = carve(P, ws);
-  const bool all = (k == n);
-
-  BatchPtr<const float> Mc = {M.base, M.stride, (const float* const*)M.ptrs};
-  const double Bd = batch, nm = dbl(n) * dbl(m), km = dbl(k) * dbl(m);
-  if (G.base || G.ptrs) {   // accumulate the gradient into the buffer while scoring
-    TraceScope ts("accum_score", 0.0, Bd * nm * 12.0, s);
-    HIP_TRY(launch_accum_score_f32(M, G, batch, (int)n, (int)m, ld, all ? nullptr : l1, sq, s));
-  } else {
-    TraceScope ts("row_score", 0.0, Bd * nm * 4.0, s);
-    HIP_TRY(launch_row_score_f32(Mc, batch, (int)n, (int)m, ld, all ? nullptr : l1, sq, s));
+// Layout of a grouped call.  Groups that take the fused path get no side set;
+// the others share one per Gram side.
+dion3_status group_layout(CallLayout& L, const dion3_group* groups, int32_t ngroups,
+                          const dion3_ns_cfg& cfg) {
+  if (!groups || ngroups < 1 || ngroups > DION3_MAX_GROUPS) return DION3_ERR_ARG;
+  Shape shapes[DION3_MAX_GROUPS];
+  bool no_side[DION3_MAX_GROUPS];
+  dion3_status worst = DION3_OK;
+  for (int i = 0; i < ngroups; ++i) {
+    const dion3_group& g = groups[i];
+    if (g.batch < 1 || g.batch > DION3_MAX_BATCH) return DION3_ERR_ARG;
+    const dion3_status st = check_dims(g.n, g.m, g.k);
+    if (st == DION3_ERR_ARG) return st;
+    if (st != DION3_OK) worst = st;
+    if (g.ld < g.m) return DION3_ERR_ARG;
   }
-  {
-    TraceScope ts("topk", 0.0, Bd * dbl(n) * 16.0, s);
-    HIP_TRY(launch_topk(l1, sq, batch, (int)n, (int)k, idx, scale, (double)cfg.eps, s));
+  if (worst != DION3_OK) return worst;
+  for (int i = 0; i < ngroups; ++i) {
+    shapes[i] = make_shape(groups[i].batch, groups[i].n, groups[i].m, groups[i].k);
+    if (!path_ok(shapes[i], cfg)) return DION3_ERR_UNSUPPORTED;
+    no_side[i] = use_fused(shapes[i], cfg);
   }
-  {
-    TraceScope ts("gather", 0.0, Bd * km * 10.0, s);
-    HIP_TRY(launch_gather_f32(M, batch, (int)n, (int)m, ld, idx, (int)k, scale, mu, true, bf.a.X,
-                              bf.a.XT, P.kp * P.mp, (int)P.kp, (int)P.mp, s));
-  }
-  if (!norm) {
-    const UpdateSink sink = {W, ld, idx, lr, (f16*)O_out, k * m};
-    st = orthogonalize(P, cfg, bf, sink, s);
-    if (st != DION3_OK) return st;
-  } else {
-    // O into the free X buffer, each matrix's rows [k][m] inside that
-    // matrix's own padded block (so that in the fused one-launch path no
-    // workgroup writes where another matrix is still being read), then the
-    // per-neuron normalization and the update; the row statistics reuse the
-    // score region and the per-matrix scale the norm region
-    f16* Obuf = free_pair(cfg, bf).X;
-    const long long sO = P.kp * P.mp;
-    const UpdateSink sink = {{nullptr, 0, nullptr}, 0, idx, lr, Obuf, sO};
-    st = orthogonalize(P, cfg, bf, sink, s);
-    if (st != DION3_OK) return st;
-    HIP_TRY(launch_normalize(Obuf, sO, batch, (int)k, (int)m, idx, V, norm->beta2, norm->eps, W, ld,
-                             lr, (float2*)l1, scale, s));
-    if (O_out)
-      HIP_TRY(hipMemcpy2DAsync(O_out, (size_t)k * m * sizeof(uint16_t), Obuf,
-                               (size_t)sO * sizeof(uint16_t), (size_t)k * m * sizeof(uint16_t),
-                               (size_t)batch, hipMemcpyDeviceToDevice, s));
-  }
-  if (idx_out)
-    HIP_TRY(hipMemcpyAsync(idx_out, idx, (size_t)batch * k * sizeof(int32_t),
-                           hipMemcpyDeviceToDevice, s));
-  return DION3_OK;
+  make_layout(L, ngroups, shapes, no_side);
+  return layout_fits(L) ? DION3_OK : DION3_ERR_UNSUPPORTED;
 }
 
 // Best rational approximation p/q of x = mant / 2^e with q <= qmax
@@ -553,9 +722,10 @@ dion3_status dion3_workspace_size(int32_t batch, int64_t n, int64_t m, int64_t k
   if (batch < 1 || batch > DION3_MAX_BATCH) return DION3_ERR_ARG;
   const dion3_status st = check_dims(n, m, k);
   if (st != DION3_OK) return st;
-  const Plan P = make_plan(batch, n, m, k);
-  if (!plan_fits(P)) return DION3_ERR_UNSUPPORTED;
-  *bytes = P.total;
+  CallLayout L;
+  make_single_layout(L, batch, n, m, k);
+  if (!layout_fits(L)) return DION3_ERR_UNSUPPORTED;
+  *bytes = L.total;
   return DION3_OK;
 }
 
@@ -567,14 +737,16 @@ dion3_status dion3_row_select(const float* M, int32_t batch, int64_t n, int64_t 
   dion3_status st = check_dims(n, m, k);
   if (st != DION3_OK) return st;
   if (ld < m) return DION3_ERR_ARG;
-  const Plan P = make_plan(batch, n, m, k);
-  st = check_ws(P, ws, ws_bytes, P.o_Xa);
+  CallLayout L;
+  make_single_layout(L, batch, n, m, k);
+  const GroupLayout& G = L.g[0];
+  st = check_ws(ws, ws_bytes, G.o_Xa);   // the row regions only
   if (st != DION3_OK) return st;
   hipStream_t s = (hipStream_t)stream;
   char* w = (char*)ws;
-  double* l1 = (double*)(w + P.o_l1);
-  double* sq = (double*)(w + P.o_sq);
-  double* scale = (double*)(w + P.o_scale);
+  double* l1 = (double*)(w + G.o_l1);
+  double* sq = (double*)(w + G.o_sq);
+  double* scale = (double*)(w + G.o_scale);
   BatchPtr<const float> Mb = {M, n * ld, nullptr};
   HIP_TRY(launch_row_score_f32(Mb, batch, (int)n, (int)m, ld, l1, sq, s));
   HIP_TRY(launch_topk(l1, sq, batch, (int)n, (int)k, idx, scale, 0.0, s));
@@ -594,34 +766,38 @@ dion3_status dion3_gram_ns(const uint16_t* X, uint16_t* O, int32_t batch, int64_
   if (cfg_in) cfg = *cfg_in; else dion3_ns_cfg_default(&cfg);
   st = check_cfg(&cfg);
   if (st != DION3_OK) return st;
-  const Plan P = make_plan(batch, k, m, k);
-  if (!plan_fits(P) || !path_ok(P, cfg)) return DION3_ERR_UNSUPPORTED;
-  st = check_ws(P, ws, ws_bytes, P.total);
+  CallLayout L;
+  make_single_layout(L, batch, k, m, k);
+  const GroupLayout& G = L.g[0];
+  if (!layout_fits(L) || !path_ok(G.P, cfg)) return DION3_ERR_UNSUPPORTED;
+  st = check_ws(ws, ws_bytes, L.total);
   if (st != DION3_OK) return st;
   hipStream_t s = (hipStream_t)stream;
   char* w = (char*)ws;
-  double* sq = (double*)(w + P.o_sq);
-  int* idx = (int*)(w + P.o_idx);
-  double* scale = (double*)(w + P.o_scale);
-  const Bufs bf = carve(P, ws);
+  double* sq = (double*)(w + G.o_sq);
+  int* idx = (int*)(w + G.o_idx);
+  double* scale = (double*)(w + G.o_scale);
+  const XPair xa = pair_a(G, w), xb = pair_b(G, w);
   BatchPtr<const f16> Xb = {(const f16*)X, k * m, nullptr};
   HIP_TRY(launch_row_score_f16(Xb, batch, (int)k, (int)m, m, sq, s));
   HIP_TRY(launch_topk(nullptr, sq, batch, (int)k, (int)k, idx, scale, (double)cfg.eps, s));
-  HIP_TRY(launch_gather_f16(Xb, batch, (int)m, m, (int)k, scale, bf.a.X, bf.a.XT, P.kp * P.mp,
-                            (int)P.kp, (int)P.mp, s));
-  const UpdateSink sink = {{nullptr, 0, nullptr}, 0, idx, 0.0f, (f16*)O, k * m};
-  st = orthogonalize(P, cfg, bf, sink, s);
-  if (st != DION3_OK) return st;
-  return DION3_OK;
+  HIP_TRY(launch_gather_f16(Xb, batch, (int)m, m, (int)k, scale, xa.X, xa.XT, G.P.kp * G.P.mp,
+                            (int)G.P.kp, (int)G.P.mp, s));
+  GroupRun r;
+  r.G = &G;
+  r.x = xa;
+  r.xalt = xb;
+  r.sink = {{nullptr, 0, nullptr}, 0, idx, 0.0f, (f16*)O, k * m};
+  return orthogonalize(L, cfg, w, &r, s);
 }
 
 dion3_status dion3_step(float* W, float* M, int64_t n, int64_t m, int64_t ld, int64_t k, float lr,
                         float mu, const dion3_ns_cfg* cfg, int32_t* idx_out, uint16_t* O_out,
                         void* ws, size_t ws_bytes, void* stream) {
   if (!W || !M) return DION3_ERR_ARG;
-  BatchPtr<float> Wb = {W, 0, nullptr}, Mb = {M, 0, nullptr};
-  BatchPtr<const float> Gb = {nullptr, 0, nullptr};
-  return step_impl(Wb, Mb, Gb, 1, n, m, ld, k, lr, mu, cfg, idx_out, O_out, ws, ws_bytes, stream);
+  const GroupArgs a = {{W, 0, nullptr}, {M, 0, nullptr}, {nullptr, 0, nullptr},
+                       {nullptr, 0, nullptr}, ld, lr, idx_out, O_out};
+  return step_one(a, 1, n, m, k, mu, cfg, nullptr, ws, ws_bytes, stream);
 }
 
 dion3_status dion3_step_accum(float* W, float* M, const float* G, int64_t n, int64_t m, int64_t ld,
@@ -629,9 +805,9 @@ dion3_status dion3_step_accum(float* W, float* M, const float* G, int64_t n, int
                               int32_t* idx_out, uint16_t* O_out, void* ws, size_t ws_bytes,
                               void* stream) {
   if (!W || !M || !G) return DION3_ERR_ARG;
-  BatchPtr<float> Wb = {W, 0, nullptr}, Mb = {M, 0, nullptr};
-  BatchPtr<const float> Gb = {G, 0, nullptr};
-  return step_impl(Wb, Mb, Gb, 1, n, m, ld, k, lr, mu, cfg, idx_out, O_out, ws, ws_bytes, stream);
+  const GroupArgs a = {{W, 0, nullptr}, {M, 0, nullptr}, {G, 0, nullptr},
+                       {nullptr, 0, nullptr}, ld, lr, idx_out, O_out};
+  return step_one(a, 1, n, m, k, mu, cfg, nullptr, ws, ws_bytes, stream);
 }
 
 dion3_status dion3_step_megabatch(float* const* W, float* const* M, int32_t batch, int64_t n,
@@ -639,10 +815,9 @@ dion3_status dion3_step_megabatch(float* const* W, float* const* M, int32_t batc
                                   const dion3_ns_cfg* cfg, int32_t* idx_out, uint16_t* O_out,
                                   void* ws, size_t ws_bytes, void* stream) {
   if (!W || !M) return DION3_ERR_ARG;
-  BatchPtr<float> Wb = {nullptr, 0, W}, Mb = {nullptr, 0, M};
-  BatchPtr<const float> Gb = {nullptr, 0, nullptr};
-  return step_impl(Wb, Mb, Gb, batch, n, m, ld, k, lr, mu, cfg, idx_out, O_out, ws, ws_bytes,
-                   stream);
+  const GroupArgs a = {{nullptr, 0, W}, {nullptr, 0, M}, {nullptr, 0, nullptr},
+                       {nullptr, 0, nullptr}, ld, lr, idx_out, O_out};
+  return step_one(a, batch, n, m, k, mu, cfg, nullptr, ws, ws_bytes, stream);
 }
 
 dion3_status dion3_step_megabatch_accum(float* const* W, float* const* M, const float* const* G,
@@ -651,10 +826,9 @@ dion3_status dion3_step_megabatch_accum(float* const* W, float* const* M, const 
                                         int32_t* idx_out, uint16_t* O_out, void* ws,
                                         size_t ws_bytes, void* stream) {
   if (!W || !M || !G) return DION3_ERR_ARG;
-  BatchPtr<float> Wb = {nullptr, 0, W}, Mb = {nullptr, 0, M};
-  BatchPtr<const float> Gb = {nullptr, 0, G};
-  return step_impl(Wb, Mb, Gb, batch, n, m, ld, k, lr, mu, cfg, idx_out, O_out, ws, ws_bytes,
-                   stream);
+  const GroupArgs a = {{nullptr, 0, W}, {nullptr, 0, M}, {nullptr, 0, G},
+                       {nullptr, 0, nullptr}, ld, lr, idx_out, O_out};
+  return step_one(a, batch, n, m, k, mu, cfg, nullptr, ws, ws_bytes, stream);
 }
 
 dion3_status dion3_step_megabatch_norm(float* const* W, float* const* M, const float* const* G,
@@ -664,10 +838,50 @@ dion3_status dion3_step_megabatch_norm(float* const* W, float* const* M, const f
                                        int32_t* idx_out, uint16_t* O_out, void* ws,
                                        size_t ws_bytes, void* stream) {
   if (!W || !M || !V || !norm) return DION3_ERR_ARG;
-  BatchPtr<float> Wb = {nullptr, 0, W}, Mb = {nullptr, 0, M}, Vb = {nullptr, 0, V};
-  BatchPtr<const float> Gb = {nullptr, 0, G};
-  return step_impl(Wb, Mb, Gb, batch, n, m, ld, k, lr, mu, cfg, idx_out, O_out, ws, ws_bytes,
-                   stream, Vb, norm);
+  const GroupArgs a = {{nullptr, 0, W}, {nullptr, 0, M}, {nullptr, 0, G},
+                       {nullptr, 0, V}, ld, lr, idx_out, O_out};
+  return step_one(a, batch, n, m, k, mu, cfg, norm, ws, ws_bytes, stream);
+}
+
+size_t dion3_group_size(void) { return sizeof(dion3_group); }
+
+dion3_status dion3_workspace_size_groups(const dion3_group* groups, int32_t ngroups,
+                                         const dion3_ns_cfg* cfg_in, size_t* bytes) {
+  if (!bytes) return DION3_ERR_ARG;
+  dion3_ns_cfg cfg;
+  if (cfg_in) cfg = *cfg_in; else dion3_ns_cfg_default(&cfg);
+  dion3_status st = check_cfg(&cfg);
+  if (st != DION3_OK) return st;
+  CallLayout L;
+  st = group_layout(L, groups, ngroups, cfg);
+  if (st != DION3_OK) return st;
+  *bytes = L.total;
+  return DION3_OK;
+}
+
+dion3_status dion3_step_groups(const dion3_group* groups, int32_t ngroups, float mu,
+                               const dion3_ns_cfg* cfg_in, const dion3_norm_cfg* norm, void* ws,
+                               size_t ws_bytes, void* stream) {
+  if (!groups || ngroups < 1 || ngroups > DION3_MAX_GROUPS) return DION3_ERR_ARG;
+  if (!isfinite(mu)) return DION3_ERR_ARG;
+  if (norm && check_norm(norm) != DION3_OK) return DION3_ERR_ARG;
+  GroupArgs A[DION3_MAX_GROUPS];
+  for (int i = 0; i < ngroups; ++i) {
+    const dion3_group& g = groups[i];
+    if (!g.W || !g.M || !isfinite(g.lr) || (norm && !g.V)) return DION3_ERR_ARG;
+    A[i] = {{nullptr, 0, g.W}, {nullptr, 0, g.M}, {nullptr, 0, g.G}, {nullptr, 0, g.V},
+            g.ld, g.lr, g.idx_out, g.O_out};
+  }
+  dion3_ns_cfg cfg;
+  if (cfg_in) cfg = *cfg_in; else dion3_ns_cfg_default(&cfg);
+  dion3_status st = check_cfg(&cfg);
+  if (st != DION3_OK) return st;
+  CallLayout L;
+  st = group_layout(L, groups, ngroups, cfg);
+  if (st != DION3_OK) return st;
+  st = check_ws(ws, ws_bytes, L.total);
+  if (st != DION3_OK) return st;
+  return run_step(L, A, mu, cfg, norm, (char*)ws, (hipStream_t)stream);
 }
 
 dion3_status dion3_syrk_f16(const uint16_t* A, uint16_t* R, int32_t batch, int64_t rows,

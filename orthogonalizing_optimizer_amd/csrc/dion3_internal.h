@@ -38,8 +38,11 @@ constexpr int kKStep = 64;
 //  Otherwise C[m][n] is written when C is set and CT[n][m] when CT is set.
 // M, N must be multiples of 128, K a multiple of 64, ld* multiples of 8.
 // kRoleNsX: the standard-iteration update X' = B X + beta X (rectangular,
-// epilogue reading D = X^T as contiguous runs).
-enum GemmRole { kRoleGram = 0, kRolePoly = 1, kRoleSymm = 2, kRoleRect = 3, kRoleNsX = 4 };
+// epilogue reading D = X^T as contiguous runs).  kRoleBack: the final
+// rectangular product, whose output goes to the fused row-sparse update
+// (sink) instead of memory; kRoleRect: the restart's rectangular product.
+enum GemmRole { kRoleGram = 0, kRolePoly = 1, kRoleSymm = 2, kRoleRect = 3, kRoleNsX = 4,
+                kRoleBack = 5 };
 
 struct GemmDesc {
   int role;
@@ -58,6 +61,7 @@ struct GemmDesc {
   // iterations without a restart and then turns the cross terms into NaN).
   int gdiag;
   double trace_flops;   // algorithmic flops of this launch, for the timing trace
+  double trace_bytes;   // algorithmic HBM bytes of this launch (operands once, outputs once)
   // Fused row-sparse update (rectangular products only): the output in rows
   // layout (the C pass when sink == 1, the CT pass when sink == 2) is not
   // stored; instead, for output row r < kval and column c < mval,

@@ -360,8 +360,9 @@ __device__ __forceinline__ void mma_step(const f16* __restrict__ st, f16* __rest
 }
 
 // ROLE only names the instance (0 Gram, 1 polynomial, 2 symmetric product,
-// 3 rectangular, 4 standard-iteration update) so that profilers report each
-// role as its own kernel.
+// 3 rectangular, 4 standard-iteration update, 5 final rectangular product
+// with the fused update) so that profilers report each role as its own
+// kernel.
 template <class C, int ROLE, bool LOWER, bool EPI>
 __global__ __launch_bounds__(C::NT, (C::BM == 256 ? 1 : 2)) void k_gemm(GemmArgs p) {
   __shared__ __attribute__((aligned(16))) f16 lds[C::LDS];
@@ -674,18 +675,19 @@ bool use_large(const GemmDesc& d) {
 }
 
 const char* trace_name(int role, bool large) {
-  static const char* names[5][2] = {{"gemm_gram_128", "gemm_gram_256"},
+  static const char* names[6][2] = {{"gemm_gram_128", "gemm_gram_256"},
                                     {"gemm_poly_128", "gemm_poly_256"},
                                     {"gemm_symm_128", "gemm_symm_256"},
                                     {"gemm_rect_128", "gemm_rect_256"},
-                                    {"gemm_nsx_128", "gemm_nsx_256"}};
+                                    {"gemm_nsx_128", "gemm_nsx_256"},
+                                    {"gemm_back_128", "gemm_back_256"}};
   return names[role][large ? 1 : 0];
 }
 
 template <int ROLE, bool LOWER, bool EPI>
 hipError_t launch_cfg(const GemmDesc& d, hipStream_t s) {
   const bool large = use_large(d);
-  TraceScope ts(trace_name(ROLE, large), d.trace_flops, 0.0, s);
+  TraceScope ts(trace_name(ROLE, large), d.trace_flops, d.trace_bytes, s);
   return large ? launch<CfgL, ROLE, LOWER, EPI>(d, s) : launch<CfgS, ROLE, LOWER, EPI>(d, s);
 }
 
@@ -707,8 +709,11 @@ hipError_t launch_gemm(const GemmDesc& d, hipStream_t s) {
       if (!d.lower || d.epilogue) break;
       return launch_cfg<kRoleSymm, true, false>(d, s);
     case kRoleRect:
-      if (d.lower || d.epilogue) break;
+      if (d.lower || d.epilogue || d.sink) break;
       return launch_cfg<kRoleRect, false, false>(d, s);
+    case kRoleBack:
+      if (d.lower || d.epilogue || !d.sink) break;
+      return launch_cfg<kRoleBack, false, false>(d, s);
     case kRoleNsX:
       if (d.lower || !d.epilogue || !d.D) break;
       return launch_cfg<kRoleNsX, false, true>(d, s);

@@ -443,7 +443,11 @@ hipError_t launch_gram_ns_small(f16* X, f16* XT, f16* Y, f16* YT, long long sX, 
   p.cfg = cfg;
   p.W = W; p.ldw = ldw; p.idx = idx; p.lr = lr; p.Oout = Oout; p.sO = sO;
   p.kval = kval; p.mval = mval; p.nrows = nrows;
-  TraceScope trace("gram_ns_fused_128", trace_flops, 0.0, s);
+  // algorithmic bytes: X read once, the selected rows of W read and written
+  const double sL = (double)kval * mval;
+  TraceScope trace("gram_ns_fused_128", trace_flops,
+                   (double)batch * sL * (2.0 + (W.ptrs || W.base ? 8.0 : 0.0) + (Oout ? 2.0 : 0.0)),
+                   s);
   hipLaunchKernelGGL(k_gram_ns_small, dim3(batch), dim3(NT), 0, s, p);
   return hipGetLastError();
 }

@@ -1,9 +1,11 @@
 """Shape-grouped Dion3 step over a set of weight matrices.
 
 Transformers hold only a few distinct weight shapes; the matrices of one
-shape are stepped together by one library call ("Dion3: Full-Stack
-Orthogonal Updates", agihunt.info, level-4 paragraph: megabatching; here on
-one GPU, where it turns one launch sequence per matrix into one per shape).
+shape are stepped together ("Dion3: Full-Stack Orthogonal Updates",
+agihunt.info, level-4 paragraph: megabatching; here on one GPU, where it
+turns one launch sequence per matrix into one per shape), and all shape
+groups of a device go to the library in one call, which runs the s x s
+products of groups with equal Gram sides as one launch.
 """
 from __future__ import annotations
 
@@ -49,9 +51,9 @@ class Dion3Step:
         self.ws: Dict[str, _lib.Workspace] = {}     # one per device, shared by its groups
         for key, g in self.groups.items():
             dev = g["M"][0].device
-            g["ws"] = self.ws.setdefault(str(dev), _lib.Workspace())
-            g["ptrs"] = (_lib.pointer_array(g["W"], dev), _lib.pointer_array(g["M"], dev))
+            self.ws.setdefault(str(dev), _lib.Workspace())
             g["k"] = _lib.k_from_fraction(float(self.fraction), key[0][0])
+            g["group"] = _lib.Group(g["W"], g["M"], g["k"], self.lr_eff)
 
     @property
     def lr_eff(self) -> float:
@@ -66,10 +68,16 @@ class Dion3Step:
             if len(grads) != sum(len(g["W"]) for g in self.groups.values()):
                 raise ValueError("need one gradient per weight")
             gmap = {id(w): gr for w, gr in zip(self._order, grads)}
+        by_dev: "OrderedDict[str, List]" = OrderedDict()
         for key, g in self.groups.items():
-            Gs = [gmap[id(w)] for w in g["W"]] if gmap is not None else None
-            _lib.step_megabatch(g["W"], g["M"], g["k"], self.lr_eff, self.mu, self.cfg,
-                                ws=g["ws"], ptrs=g["ptrs"], Gs=Gs)
+            grp = g["group"]
+            if gmap is not None:
+                grp = _lib.Group(g["W"], g["M"], g["k"], self.lr_eff,
+                                 Gs=[gmap[id(w)] for w in g["W"]])
+            by_dev.setdefault(key[2], []).append(grp)
+        for dev, grps in by_dev.items():
+            for i in range(0, len(grps), _lib.MAX_GROUPS):
+                _lib.step_groups(grps[i:i + _lib.MAX_GROUPS], self.mu, self.cfg, ws=self.ws[dev])
 
 
 def _optimizer_base():
@@ -136,14 +144,19 @@ class Dion3(_optimizer_base()):
                         st["second_moment"] = torch.zeros(p.shape[0], dtype=torch.float32,
                                                           device=p.device)
                     buckets.setdefault((tuple(p.shape), p.stride(), str(p.device)), []).append(p)
+                # one library call per device over all of its shape buckets
+                by_dev: "OrderedDict[str, List]" = OrderedDict()
                 for (shape, _, dev), ps in buckets.items():
                     k = _lib.k_from_fraction(f, shape[0])
+                    Vs = ([self.state[p]["second_moment"] for p in ps] if group["normalize"]
+                          else None)
+                    by_dev.setdefault(dev, []).append(
+                        _lib.Group(ps, [self.state[p]["momentum"] for p in ps], k,
+                                   group["lr"] / math.sqrt(f), Gs=[p.grad for p in ps], Vs=Vs))
+                norm = (group["beta2"], group["eps"]) if group["normalize"] else None
+                for dev, grps in by_dev.items():
                     ws = self._ws.setdefault(dev, _lib.Workspace())
-                    norm = None
-                    if group["normalize"]:
-                        norm = ([self.state[p]["second_moment"] for p in ps], group["beta2"],
-                                group["eps"])
-                    _lib.step_megabatch(ps, [self.state[p]["momentum"] for p in ps], k,
-                                        group["lr"] / math.sqrt(f), group["mu"], self.cfg, ws=ws,
-                                        Gs=[p.grad for p in ps], norm=norm)
+                    for i in range(0, len(grps), _lib.MAX_GROUPS):
+                        _lib.step_groups(grps[i:i + _lib.MAX_GROUPS], group["mu"], self.cfg,
+                                         norm=norm, ws=ws)
         return loss

@@ -273,3 +273,83 @@ def test_header_compiles_as_c99_and_host_calls_work_from_c(tmp_path):
     subprocess.run(cmd, check=True)
     out = subprocess.run([exe], check=True, capture_output=True, text=True)
     assert "c abi ok" in out.stdout
+
+
+def _groups(*specs, W=FAKE, M=FAKE, G=None, V=None, ld=None, lr=0.04):
+    """dion3_group array from (batch, n, m, k) tuples; pointers are fake."""
+    arr = (_lib.GroupDesc * len(specs))()
+    for i, (b, n, m, k) in enumerate(specs):
+        arr[i] = _lib.GroupDesc(W, M, G, V, n, m, ld if ld is not None else m, k, b, lr, None, None)
+    return arr
+
+
+def _ws_groups(arr, cfg=None):
+    out = ctypes.c_size_t(0)
+    st = d3.lib().dion3_workspace_size_groups(arr, len(arr), ctypes.byref(cfg) if cfg else None,
+                                              ctypes.byref(out))
+    return st, out.value
+
+
+def test_group_workspace_shares_gram_sides():
+    lib = d3.lib()
+    tiled = _cfg(path=d3.PATH_TILED)
+    # 7B-like shapes at f = 1/4: the attention (k = 1024) and down-projection
+    # (k = 1024) groups share the Gram side 1024, the up-projection (k = 2752)
+    # has its own
+    spec = [(128, 4096, 4096, 1024), (64, 11008, 4096, 2752), (32, 4096, 11008, 1024)]
+    st, grouped = _ws_groups(_groups(*spec), tiled)
+    assert st == 0
+    singles = sum(d3.workspace_size(*s) for s in spec)
+    # one side set per Gram side: the same Gram-side bytes, only alignment differs
+    assert abs(grouped - singles) <= 64 * 1024
+    # a group whose Gram side pads to 128 takes the fused path under AUTO and
+    # needs no Gram-side buffers at all
+    st, fused = _ws_groups(_groups((64, 512, 1024, 128)), _cfg())
+    st2, tiled_one = _ws_groups(_groups((64, 512, 1024, 128)), tiled)
+    assert st == 0 and st2 == 0
+    assert tiled_one - fused >= 5 * 64 * 128 * 128 * 2
+    assert tiled_one == d3.workspace_size(64, 512, 1024, 128)
+
+
+def test_step_groups_rejects_bad_arguments_before_launch():
+    lib = d3.lib()
+    ok = _groups((2, 64, 32, 16), (3, 96, 32, 16))
+    st, need = _ws_groups(ok)
+    assert st == 0 and need > 0
+
+    def call(arr, n=None, mu=0.95, cfg=None, norm=None, ws=FAKE, nbytes=None):
+        return lib.dion3_step_groups(arr, len(arr) if n is None else n, mu,
+                                     ctypes.byref(cfg) if cfg else None,
+                                     ctypes.byref(norm) if norm else None, ws,
+                                     need if nbytes is None else nbytes, None)
+
+    assert lib.dion3_step_groups(None, 1, 0.95, None, None, FAKE, need, None) == ERR_ARG
+    assert call(ok, n=0) == ERR_ARG
+    assert call(ok, n=65) == ERR_ARG
+    assert call(ok, mu=float("nan")) == ERR_ARG
+    assert call(_groups((2, 64, 32, 16), W=None)) == ERR_ARG
+    assert call(_groups((2, 64, 32, 16), M=None)) == ERR_ARG
+    assert call(_groups((2, 64, 32, 16), lr=float("inf"))) == ERR_ARG
+    assert call(_groups((0, 64, 32, 16))) == ERR_ARG
+    assert call(_groups((2, 64, 32, 0), (2, 64, 32, 16))) == ERR_ARG
+    assert call(_groups((2, 64, 32, 16), (2, 64, 32, 65))) == ERR_ARG
+    assert call(_groups((2, 64, 32, 16), ld=31)) == ERR_ARG
+    # an argument error in a later group wins over an unsupported size in an
+    # earlier one
+    assert call(_groups((2, (1 << 20) + 1, 4, 1), (2, 8, 8, 0)), nbytes=1 << 30) == ERR_ARG
+    assert call(_groups((2, (1 << 20) + 1, 4, 1)), nbytes=1 << 30) == ERR_UNSUP
+    assert call(ok, cfg=_cfg(iters=0)) == ERR_ARG
+    assert call(ok, norm=d3.NormCfg(0.9, 1e-8)) == ERR_ARG          # no states V
+    assert call(_groups((2, 64, 32, 16), V=FAKE), norm=d3.NormCfg(1.0, 1e-8)) == ERR_ARG
+    fused = _cfg(path=d3.PATH_FUSED)
+    assert call(_groups((2, 400, 300, 200)), cfg=fused, nbytes=1 << 30) == ERR_UNSUP
+    assert call(ok, ws=None) == ERR_WS
+    assert call(ok, ws=FAKE + 16) == ERR_WS
+    assert call(ok, nbytes=need - 1) == ERR_WS
+    st, _ = _ws_groups(_groups((2, 64, 32, 16), (2, 64, 32, 0)))
+    assert st == ERR_ARG
+    assert lib.dion3_workspace_size_groups(ok, len(ok), None, None) == ERR_ARG
+
+
+def test_group_struct_matches_binding():
+    assert d3.lib().dion3_group_size() == ctypes.sizeof(_lib.GroupDesc)

@@ -1,0 +1,168 @@
+"""GPU checks of the grouped step (dion3_step_groups): several shape groups
+in one call, where groups with equal Gram sides share the launches of their
+s x s products.  Each matrix's arithmetic is the same as in a megabatched
+call of its own group, so the results must equal per-group calls bit for
+bit; one matrix per group is also checked against the fp64 oracle."""
+import sys
+
+import numpy as np
+import pytest
+
+from tests.parity import check_step
+from workloads import host_gaussian
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+import orthogonalizing_optimizer_amd as d3  # noqa: E402
+
+DEV = "cuda:0"
+MU = 0.95
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def make(specs, seed, scale=1.0):
+    """Host fp32 (W, M) lists per group from (batch, n, m) specs."""
+    out = []
+    for gi, (b, n, m) in enumerate(specs):
+        Ws = [host_gaussian((n, m), [seed, gi, j, 1], std=0.02) for j in range(b)]
+        Ms = [host_gaussian((n, m), [seed, gi, j, 2]) * np.float32(scale * (1 + j % 3))
+              for j in range(b)]
+        out.append((Ws, Ms))
+    return out
+
+
+def to_dev(arrs):
+    return [torch.from_numpy(a).to(DEV) for a in arrs]
+
+
+def run_grouped(host, ks, lr, cfg, grads=None, norm=None):
+    groups, tensors = [], []
+    for gi, ((Ws, Ms), k) in enumerate(zip(host, ks)):
+        Wd, Md = to_dev(Ws), to_dev(Ms)
+        Gd = to_dev(grads[gi]) if grads is not None else None
+        Vd = [torch.zeros(Ms[0].shape[0], dtype=torch.float32, device=DEV) for _ in Ms] if norm \
+            else None
+        groups.append(d3.Group(Wd, Md, k, lr, Gs=Gd, Vs=Vd))
+        tensors.append((Wd, Md, Vd))
+    outs = d3.step_groups(groups, MU, cfg, norm=norm, return_idx=True, return_O=True)
+    torch.cuda.synchronize()
+    return tensors, outs
+
+
+def run_per_group(host, ks, lr, cfg, grads=None, norm=None):
+    tensors, outs = [], []
+    for gi, ((Ws, Ms), k) in enumerate(zip(host, ks)):
+        Wd, Md = to_dev(Ws), to_dev(Ms)
+        Gd = to_dev(grads[gi]) if grads is not None else None
+        Vd = [torch.zeros(Ms[0].shape[0], dtype=torch.float32, device=DEV) for _ in Ms] if norm \
+            else None
+        nrm = (Vd, norm[0], norm[1]) if norm else None
+        outs.append(d3.step_megabatch(Wd, Md, k, lr, MU, cfg, return_idx=True, return_O=True,
+                                      Gs=Gd, norm=nrm))
+        tensors.append((Wd, Md, Vd))
+    torch.cuda.synchronize()
+    return tensors, outs
+
+
+def assert_bitwise(ta, oa, tb, ob):
+    for (Wa, Ma, Va), (Wb, Mb, Vb), (ia, Oa), (ib, Ob) in zip(ta, tb, oa, ob):
+        assert torch.equal(ia, ib)
+        assert Oa.cpu().numpy().tobytes() == Ob.cpu().numpy().tobytes()
+        for x, y in zip(Wa + Ma + (Va or []), Wb + Mb + (Vb or [])):
+            assert x.cpu().numpy().tobytes() == y.cpu().numpy().tobytes()
+
+
+# (batch, n, m) per group at f = 1/4: groups 0, 2 and 3 share the Gram side
+# 256 (group 3 has k > m, so its Gram is X^T X with s = m = 256); group 1 has
+# its own (k = 688); group 4's side (k = 32) pads to one 128 tile
+MIXED = [(4, 1024, 1536), (3, 2752, 1024), (2, 1024, 2752), (3, 1200, 256), (5, 128, 512)]
+KS_MIXED = [256, 688, 256, 300, 32]
+
+
+@pytest.mark.parametrize("path", [d3.PATH_AUTO, d3.PATH_TILED])
+def test_groups_equal_per_group_calls_bitwise(path):
+    say("groups vs per-group calls, path", path)
+    host = make(MIXED, 71)
+    cfg = d3.ns_cfg(path=path)
+    ta, oa = run_grouped(host, KS_MIXED, 0.04, cfg)
+    tb, ob = run_per_group(host, KS_MIXED, 0.04, cfg)
+    assert_bitwise(ta, oa, tb, ob)
+
+
+def test_groups_against_oracle():
+    say("groups vs oracle")
+    host = make(MIXED, 72, scale=0.5)
+    cfg = d3.default_cfg()
+    ta, oa = run_grouped(host, KS_MIXED, 0.04, cfg)
+    for gi, ((Ws, Ms), k) in enumerate(zip(host, KS_MIXED)):
+        Wd, Md, _ = ta[gi]
+        idx, O = oa[gi]
+        j = len(Ws) - 1
+        check_step(Ws[j], Ms[j], Wd[j].cpu().numpy(), Md[j].cpu().numpy(), idx[j].cpu().numpy(),
+                   O[j].cpu().numpy(), k, 0.04, MU)
+
+
+def test_groups_standard_method_bitwise():
+    say("groups, standard NS")
+    host = make(MIXED[:3], 73)
+    cfg = d3.ns_cfg(method=d3.NS_STANDARD)
+    ta, oa = run_grouped(host, KS_MIXED[:3], 0.04, cfg)
+    tb, ob = run_per_group(host, KS_MIXED[:3], 0.04, cfg)
+    assert_bitwise(ta, oa, tb, ob)
+
+
+@pytest.mark.parametrize("restarts", [(), (2, 4), (3,)])
+def test_groups_accumulate_and_normalize_bitwise(restarts):
+    say("groups with gradients and normalization, restarts", restarts)
+    host = make(MIXED, 74)
+    grads = [[host_gaussian(Ms[0].shape, [75, gi, j]) * np.float32(0.1) for j in range(len(Ms))]
+             for gi, (_, Ms) in enumerate(host)]
+    cfg = d3.ns_cfg(restart_at=restarts)
+    for norm in (None, (0.9, 1e-8)):
+        ta, oa = run_grouped(host, KS_MIXED, 0.04, cfg, grads=grads, norm=norm)
+        tb, ob = run_per_group(host, KS_MIXED, 0.04, cfg, grads=grads, norm=norm)
+        assert_bitwise(ta, oa, tb, ob)
+
+
+def test_many_groups_one_call():
+    """DION3_MAX_GROUPS groups of seeded random shapes (several sharing each
+    Gram side) in one call, bitwise against per-group calls."""
+    rng = np.random.default_rng(76)
+    specs, ks = [], []
+    for _ in range(d3.MAX_GROUPS):
+        n = int(rng.choice([64, 200, 256, 384, 520]))
+        m = int(rng.choice([96, 256, 300, 640]))
+        specs.append((int(rng.integers(1, 4)), n, m))
+        ks.append(int(rng.choice([n // 4, n // 2, n])) or 1)
+    say("max groups", specs[:4], "...")
+    host = make(specs, 77)
+    cfg = d3.default_cfg()
+    ta, oa = run_grouped(host, ks, 0.02, cfg)
+    tb, ob = run_per_group(host, ks, 0.02, cfg)
+    assert_bitwise(ta, oa, tb, ob)
+
+
+def test_groups_trace_shares_the_side_products():
+    """With groups 0 and 2 sharing the Gram side, the polynomial and symmetric
+    products run once for both: the trace holds the launches of two sides,
+    not three groups."""
+    say("groups trace")
+    host = make(MIXED[:3], 78)
+    cfg = d3.ns_cfg(path=d3.PATH_TILED)
+    run_grouped(host, KS_MIXED[:3], 0.04, cfg)          # warm
+    d3.trace_enable(512)
+    try:
+        run_grouped(host, KS_MIXED[:3], 0.04, cfg)
+        recs = d3.trace_records()
+    finally:
+        d3.trace_disable()
+    names = [r[0] for r in recs]
+    assert sum(n.startswith("gemm_poly") for n in names) == 2 * 5
+    assert sum(n.startswith("gemm_symm") for n in names) == 2 * 9
+    assert sum(n.startswith("gemm_gram") for n in names) == 3 * 2
+    assert sum(n.startswith("gemm_back") for n in names) == 3

@@ -379,11 +379,16 @@ def test_timing_trace_records_every_kernel():
     assert sum(1 for r in gemms if r[0].startswith("gemm_gram")) == 2
     assert sum(1 for r in gemms if r[0].startswith("gemm_poly")) == 5
     assert sum(1 for r in gemms if r[0].startswith("gemm_symm")) == 9
-    assert sum(1 for r in gemms if r[0].startswith("gemm_rect")) == 2
+    # the restart's X <- Q X, then the final multiply-back with the fused update
+    assert sum(1 for r in gemms if r[0].startswith("gemm_rect")) == 1
+    assert sum(1 for r in gemms if r[0].startswith("gemm_back")) == 1
     assert all(r[1] > 0 for r in recs)
     s_, L_ = 75.0, 500.0
     flops = sum(r[2] for r in gemms)
     assert flops == pytest.approx(6 * s_ * s_ * L_ + 14 * s_ ** 3)
+    # algorithmic bytes of the final product: Q and X read, W[S] read and written
+    back = [r for r in gemms if r[0].startswith("gemm_back")][0]
+    assert back[3] == pytest.approx(2 * s_ * s_ + 10 * s_ * L_)
 
 
 def test_dion3step_groups_by_shape():
