@@ -271,6 +271,27 @@ DION3_API dion3_status dion3_step_groups(const dion3_group* groups, int32_t ngro
                                          const dion3_ns_cfg* cfg, const dion3_norm_cfg* norm,
                                          void* ws, size_t ws_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the
+ * megabatched step of dion3_step_megabatch with the same arguments and
+ * results bit for bit, but no workspace argument.  Its scratch is a static
+ * device array of DION3_STATIC_SCRATCH_BYTES in the library, one per GPU
+ * (held until the process ends); the call allocates nothing.  Every call on
+ * one GPU shares that GPU's array, so calls that overlap on one GPU (other
+ * streams, other threads) race; serialize them.  Nothing in the array needs
+ * to start at zero: every region the step reads is written first in the same
+ * call.  The stream must belong to the current device.
+ * DION3_ERR_WORKSPACE: the call needs more than DION3_STATIC_SCRATCH_BYTES
+ * (dion3_workspace_size for the same shapes), checked before any launch.
+ * DION3_ERR_ARG also when the stream belongs to another device; the other
+ * status codes are dion3_step_megabatch's. */
+#define DION3_STATIC_SCRATCH_BYTES (64u << 20)
+DION3_API dion3_status dion3_step_megabatch_noalloc(float* const* W, float* const* M, int32_t batch,
+                                                    int64_t n, int64_t m, int64_t ld, int64_t k,
+                                                    float lr, float mu, const dion3_ns_cfg* cfg,
+                                                    int32_t* idx_out, uint16_t* O_out,
+                                                    void* stream);
+
 /* The symmetric products of the level-2 paragraph, usable on their own.
  *
  * dion3_syrk_f16: R[b] = A[b] A[b]^T for `batch` fp16 matrices A[b]

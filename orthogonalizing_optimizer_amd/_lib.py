@@ -92,6 +92,8 @@ def _declare(lib):
                                                   c.POINTER(sz)]),
         "dion3_step_groups": (c.c_int, [c.POINTER(GroupDesc), i32, f32, c.POINTER(NsCfg),
                                         c.POINTER(NormCfg), vp, sz, vp]),
+        "dion3_step_megabatch_noalloc": (c.c_int, [vp, vp, i32, i64, i64, i64, i64, f32, f32,
+                                                   c.POINTER(NsCfg), vp, vp, vp]),
         "dion3_syrk_f16": (c.c_int, [vp, vp, i32, i64, i64, i64, i64, vp]),
         "dion3_symm_f16": (c.c_int, [vp, vp, vp, vp, i32, i64, i64, f32, f32, f32, vp]),
         "dion3_trace_enable": (c.c_int, [i32]),
@@ -113,7 +115,7 @@ EXPORTED = ("dion3_version", "dion3_ns_cfg_size", "dion3_ns_cfg_default", "dion3
             "dion3_workspace_size", "dion3_row_select", "dion3_gram_ns", "dion3_step",
             "dion3_step_megabatch", "dion3_step_accum", "dion3_step_megabatch_accum",
             "dion3_step_megabatch_norm", "dion3_group_size", "dion3_workspace_size_groups",
-            "dion3_step_groups",
+            "dion3_step_groups", "dion3_step_megabatch_noalloc",
             "dion3_syrk_f16", "dion3_symm_f16", "dion3_trace_enable",
             "dion3_trace_count", "dion3_trace_reset", "dion3_trace_record", "dion3_status_string",
             "dion3_last_hip_error")

@@ -14,7 +14,8 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdion3.so")
 
-SOURCES = ["gemm_f16.hip", "gram_small.hip", "rows.hip", "normalize.hip", "dion3_api.hip", "trace.hip"]
+SOURCES = ["gemm_f16.hip", "gram_small.hip", "rows.hip", "normalize.hip", "dion3_api.hip", "trace.hip",
+           "noalloc.hip"]
 ARCH = "gfx950"
 
 # Packed-fp32 instructions are switched off for all device code.

@@ -675,6 +675,10 @@ void best_rational(unsigned long long mant, int e, unsigned long long qmax,
 
 }  // namespace
 
+namespace dion3 {
+dion3_status note_hip_error(hipError_t e) { return hip_fail(e); }
+}  // namespace dion3
+
 extern "C" {
 
 int dion3_version(void) { return 1; }

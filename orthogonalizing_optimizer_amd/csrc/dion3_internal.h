@@ -77,6 +77,10 @@ struct GemmDesc {
   long long sO;            // elements between the Oout blocks of consecutive matrices
   int kval, mval, nrows;   // nrows: rows of W (row indices outside are skipped)
 };
+// Records e as the calling thread's last HIP error (dion3_last_hip_error)
+// and returns DION3_ERR_HIP.
+dion3_status note_hip_error(hipError_t e);
+
 // Launches the product; records it in the timing trace (when enabled) under
 // "<role>_<tile edge>", e.g. "gemm_symm_256".
 hipError_t launch_gemm(const GemmDesc& d, hipStream_t s);

@@ -353,3 +353,16 @@ def test_step_groups_rejects_bad_arguments_before_launch():
 
 def test_group_struct_matches_binding():
     assert d3.lib().dion3_group_size() == ctypes.sizeof(_lib.GroupDesc)
+
+
+def test_noalloc_refuses_before_any_device_work():
+    lib = d3.lib()
+    assert lib.dion3_step_megabatch_noalloc(None, FAKE, 1, 64, 32, 32, 16, 0.04, 0.95, None, None,
+                                            None, None) == ERR_ARG
+    assert lib.dion3_step_megabatch_noalloc(FAKE, FAKE, 1, 64, 32, 32, 0, 0.04, 0.95, None, None,
+                                            None, None) == ERR_ARG
+    # more than DION3_STATIC_SCRATCH_BYTES of workspace
+    need = d3.workspace_size(16, 2048, 4096, 1024)
+    assert need > (64 << 20)
+    assert lib.dion3_step_megabatch_noalloc(FAKE, FAKE, 16, 2048, 4096, 4096, 1024, 0.04, 0.95,
+                                            None, None, None, None) == ERR_WS
