@@ -286,20 +286,22 @@ void set_sink(GemmDesc& d, const Shape& P, const UpdateSink& sink) {
   d.kval = (int)P.k; d.mval = (int)P.m; d.nrows = (int)P.n;
 }
 
-// Y_math = Q X_math.  The restart needs Y in both layouts.  The final
-// product (sink set) stores nothing: its rows-layout output goes straight
-// into the update of W (and O_out).
-hipError_t rect(const Shape& P, const f16* Q, const XPair& x, const XPair& y, bool both,
-                hipStream_t s, const UpdateSink* sink = nullptr) {
+// Y_math = Q X_math.  X_math (sp x Lp, the layout the Gram reads) is the
+// product's second operand as it is, K x N with N contiguous, read through
+// transposing LDS reads, so no kernel has to keep a transposed copy of X.
+// The restart's Y_math is stored in the same layout for the next Gram.  The
+// final product (sink set) stores nothing: its rows-layout output (the math
+// layout when k <= m, its transpose when k > m) goes straight into the
+// update of W (and O_out).
+hipError_t rect(const Shape& P, const f16* Q, const XPair& x, const XPair& y, hipStream_t s,
+                const UpdateSink* sink = nullptr) {
   const double sv = s_of(P), L = L_of(P);
   GemmDesc d = {};
   d.trace_flops = 2.0 * P.B * sv * sv * L;
   d.role = sink ? kRoleBack : kRoleRect;
   d.A = Q; d.sA = P.sp * P.sp; d.lda = (int)P.sp;
-  d.B = xmathT(P, x); d.sB = P.kp * P.mp; d.ldb = (int)P.sp;
-  const bool want_math = both || !P.tr, want_mathT = both || P.tr;
-  d.C = want_math ? (f16*)xmath(P, y) : nullptr; d.sC = P.kp * P.mp; d.ldc = (int)P.Lp;
-  d.CT = want_mathT ? (f16*)xmathT(P, y) : nullptr; d.sCT = P.kp * P.mp; d.ldct = (int)P.sp;
+  d.B = xmath(P, x); d.sB = P.kp * P.mp; d.ldb = (int)P.Lp; d.b_kn = true;
+  d.C = (f16*)xmath(P, y); d.sC = P.kp * P.mp; d.ldc = (int)P.Lp;
   if (sink) {
     set_sink(d, P, *sink);
     // read Q and X, read and write the selected rows of W (fp32), and write
@@ -395,7 +397,7 @@ dion3_status gram_ns_set(const dion3_ns_cfg& cfg, const SideLayout& S, char* w, 
     if (restart_at(cfg, t)) {      // X <- Q X, R <- X X^T, Q <- I
       if (!q_identity) {
         for (int i = 0; i < nr; ++i)
-          HIP_TRY(rect(r[i].G->P, slice(Q, S, *r[i].G), r[i].x, r[i].xalt, true, s));
+          HIP_TRY(rect(r[i].G->P, slice(Q, S, *r[i].G), r[i].x, r[i].xalt, s));
         swap_pairs(r, nr);
       }
       for (int i = 0; i < nr; ++i) HIP_TRY(gram(r[i].G->P, r[i].x, slice(R, S, *r[i].G), s));
@@ -420,7 +422,7 @@ dion3_status gram_ns_set(const dion3_ns_cfg& cfg, const SideLayout& S, char* w, 
     }
   }
   for (int i = 0; i < nr; ++i)
-    HIP_TRY(rect(r[i].G->P, slice(Q, S, *r[i].G), r[i].x, r[i].xalt, false, s, &r[i].sink));
+    HIP_TRY(rect(r[i].G->P, slice(Q, S, *r[i].G), r[i].x, r[i].xalt, s, &r[i].sink));
   return DION3_OK;
 }
 
@@ -499,6 +501,15 @@ bool free_pair_is_b(const dion3_ns_cfg& cfg) {
 }
 
 XPair pair_a(const GroupLayout& G, char* w) { return {(f16*)(w + G.o_Xa), (f16*)(w + G.o_XaT)}; }
+
+// The layouts of the selected rows that the orthogonalization reads: the
+// tiled Gram iteration reads only X_math (rows when k <= m, their transpose
+// when k > m); the fused small-Gram kernel and the standard iteration read
+// both.  The gather writes only those (a null pointer skips a layout).
+XPair gather_layouts(const Shape& P, const dion3_ns_cfg& cfg, const XPair& x) {
+  if (cfg.method == DION3_NS_STANDARD || use_fused(P, cfg)) return x;
+  return P.tr ? XPair{nullptr, x.XT} : XPair{x.X, nullptr};
+}
 XPair pair_b(const GroupLayout& G, char* w) { return {(f16*)(w + G.o_Xb), (f16*)(w + G.o_XbT)}; }
 
 // One group's arguments in a step call.
@@ -544,8 +555,9 @@ dion3_status run_step(const CallLayout& L, const GroupArgs* A, float mu, const d
     }
     const XPair xa = pair_a(G, w), xb = pair_b(G, w);
     {
+      const XPair out = gather_layouts(P, cfg, xa);
       TraceScope ts("gather", 0.0, Bd * km * 10.0, s);
-      HIP_TRY(launch_gather_f32(a.M, P.B, n, m, a.ld, idx, k, scale, mu, true, xa.X, xa.XT,
+      HIP_TRY(launch_gather_f32(a.M, P.B, n, m, a.ld, idx, k, scale, mu, true, out.X, out.XT,
                                 P.kp * P.mp, (int)P.kp, (int)P.mp, s));
     }
     GroupRun& r = runs[i];
@@ -785,7 +797,8 @@ dion3_status dion3_gram_ns(const uint16_t* X, uint16_t* O, int32_t batch, int64_
   BatchPtr<const f16> Xb = {(const f16*)X, k * m, nullptr};
   HIP_TRY(launch_row_score_f16(Xb, batch, (int)k, (int)m, m, sq, s));
   HIP_TRY(launch_topk(nullptr, sq, batch, (int)k, (int)k, idx, scale, (double)cfg.eps, s));
-  HIP_TRY(launch_gather_f16(Xb, batch, (int)m, m, (int)k, scale, xa.X, xa.XT, G.P.kp * G.P.mp,
+  const XPair out = gather_layouts(G.P, cfg, xa);
+  HIP_TRY(launch_gather_f16(Xb, batch, (int)m, m, (int)k, scale, out.X, out.XT, G.P.kp * G.P.mp,
                             (int)G.P.kp, (int)G.P.mp, s));
   GroupRun r;
   r.G = &G;

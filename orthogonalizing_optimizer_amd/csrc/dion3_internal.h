@@ -48,6 +48,10 @@ struct GemmDesc {
   int role;
   const f16* A; long long sA; int lda;
   const f16* B; long long sB; int ldb;
+  // b_kn (rectangular roles): B is given as its transpose, K x N stored
+  // B[k * ldb + n] (N contiguous), and read through transposing LDS reads;
+  // rows k >= K are never read
+  bool b_kn;
   f16* C; long long sC; int ldc;
   f16* CT; long long sCT; int ldct;
   const f16* D; long long sD; int ldd;
@@ -108,9 +112,9 @@ hipError_t launch_row_score_f16(BatchPtr<const f16> X, int batch, int n, int m, 
 hipError_t launch_topk(const double* l1, const double* sq, int batch, int n, int k, int* idx,
                        double* scale, double eps, hipStream_t s);
 
-// Gather of the selected rows into both layouts: X[b][r][j] and
-// XT[b][j][r] = fp16(M[b][idx[r]][j] * scale[b]) for r < k, j < m, zero in
-// the padding up to kp x mp (X) and mp x kp (XT).  With decay,
+// Gather of the selected rows into X[b][r][j] and/or XT[b][j][r] =
+// fp16(M[b][idx[r]][j] * scale[b]) for r < k, j < m, zero in the padding up
+// to kp x mp (X) and mp x kp (XT); a null X or XT is not written.  With decay,
 // M[b][idx[r]][j] *= mu (one fp32 multiply).  idx == nullptr: identity.
 hipError_t launch_gather_f32(BatchPtr<float> M, int batch, int n, int m, long long ld,
                              const int* idx, int k, const double* scale, float mu, bool decay,

@@ -102,7 +102,12 @@ struct Cfg {
   static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
   static constexpr int FM = WTM / 32, FN = WTN / 32;
   static constexpr int CH = BM * (BK / 8) / NT;          // 16-byte chunks per thread per operand
-  static constexpr int STAGE = (BM + BN) * LDSK;         // halves per LDS stage
+  // B given as [K][N] (N contiguous) takes BK rows of RSB halves in a stage
+  // (the 32-half pad puts the four rows of a transposing read in four
+  // different 64-byte bank windows); [N][K] takes BN rows of LDSK
+  static constexpr int RSB = BN + 32;
+  static constexpr int BPART = (BN * LDSK > BK * RSB) ? BN * LDSK : BK * RSB;
+  static constexpr int STAGE = BM * LDSK + BPART;        // halves per LDS stage
   static constexpr int EP = BN + 8;                      // epilogue staging row stride
   static constexpr int LDS = (2 * STAGE > BM * EP) ? 2 * STAGE : BM * EP;
   static_assert(CH * NT == BM * (BK / 8), "chunk split");
@@ -249,6 +254,50 @@ __device__ __forceinline__ void gload(__amdgpu_buffer_rsrc_t rs, int ld, int r0,
   }
 }
 
+// The B tile of a [K][N] operand: BK rows (K) of BN halves (N), row k0 + r,
+// columns n0 .. n0 + BN - 1; thread chunk e = tid + NT i covers row e / (BN / 8),
+// columns 8 (e % (BN / 8)) ..
+template <class C>
+__device__ __forceinline__ void gload_kn(__amdgpu_buffer_rsrc_t rs, int ld, int n0, int k0, int tid,
+                                         half8 (&reg)[C::CH]) {
+  constexpr int CPR = C::BN / 8;
+#pragma unroll
+  for (int i = 0; i < C::CH; ++i) {
+    const int e = tid + C::NT * i, r = e / CPR, c = e % CPR;
+    const int4v v = __builtin_amdgcn_raw_buffer_load_b128(rs, (r * ld + n0 + c * 8) * 2, k0 * ld * 2, 0);
+    reg[i] = __builtin_bit_cast(half8, v);
+  }
+}
+
+template <class C>
+__device__ __forceinline__ void lstore_kn(f16* __restrict__ s, int tid, const half8 (&reg)[C::CH]) {
+  constexpr int CPR = C::BN / 8;
+#pragma unroll
+  for (int i = 0; i < C::CH; ++i) {
+    const int e = tid + C::NT * i;
+    *(half8*)(s + (e / CPR) * C::RSB + (e % CPR) * 8) = reg[i];
+  }
+}
+
+typedef __fp16 fp16x4_t __attribute__((__vector_size__(4 * sizeof(__fp16))));
+typedef __attribute__((address_space(3))) fp16x4_t lds_fp16x4;
+
+// One MFMA B fragment (8 consecutive K of column n = lane % 32, from
+// K = 8 (lane / 32)) out of a [K][N] LDS tile, as two transposing reads: in
+// each 16-lane group, lane 4e + u points at row e, columns 4u .. 4u + 3 of a
+// 4 x 16 block and receives that block's column (lane % 16), i.e. 4
+// consecutive K of one column.  `p` is this lane's address for the first
+// four K (see boff_kn); the second four are 4 rows further.
+template <class C>
+__device__ __forceinline__ half8 bfrag_kn(const f16* p) {
+  typedef f16 half4v __attribute__((ext_vector_type(4)));
+  const half4v lo = __builtin_bit_cast(
+      half4v, __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4*)p));
+  const half4v hi = __builtin_bit_cast(
+      half4v, __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4*)(p + 4 * C::RSB)));
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
 template <class C>
 __device__ __forceinline__ void lstore(f16* __restrict__ s, int tid, const half8 (&reg)[C::CH]) {
 #pragma unroll
@@ -289,18 +338,27 @@ __device__ __forceinline__ void mfma_slice(const half8 (&af)[C::FM], const half8
 // On the 7B shapes this is 14-25 % faster than the same step left to the
 // compiler's scheduler, with bitwise identical results (the MFMA order per
 // accumulator is unchanged).
-template <class C, bool STORE, bool LOAD, bool NEXT>
+// B fragment j of k-slice kk from a stage: [N][K] rows (boff: this lane's
+// row and K offset) or, with BKN, a [K][N] tile read transposed (boff: this
+// lane's offset for bfrag_kn).
+template <class C, bool BKN>
+__device__ __forceinline__ half8 bfrag(const f16* __restrict__ st, int boff, int j, int kk) {
+  if constexpr (BKN) return bfrag_kn<C>(st + C::BM * LDSK + boff + j * 32 + kk * 16 * C::RSB);
+  return *(const half8*)(st + boff + j * 32 * LDSK + kk * 16);
+}
+
+template <class C, bool STORE, bool LOAD, bool NEXT, bool BKN>
 __device__ __forceinline__ void mma_step(const f16* __restrict__ st, f16* __restrict__ nxt,
                                          __amdgpu_buffer_rsrc_t Ab, __amdgpu_buffer_rsrc_t Bb,
                                          int lda, int ldb, int m0, int n0, int k0_next, int tid,
                                          half8 (&ra)[C::CH], half8 (&rb)[C::CH], int aoff,
                                          int boff, half8 (&fa0)[C::FM], half8 (&fb0)[C::FN],
                                          floatx16 (&acc)[C::FM][C::FN]) {
-  constexpr int NS = BK / 16, NR = C::FM + C::FN, NM = C::FM * C::FN;
+  constexpr int NS = BK / 16, NR = C::FM + (BKN ? 2 : 1) * C::FN, NM = C::FM * C::FN;
   constexpr int WPM = 2 * C::CH / NM;   // LDS writes (and global loads) per MFMA in slice 0
-  static_assert(NM >= NR && WPM * NM == 2 * C::CH, "slice schedules assume these counts");
+  static_assert(WPM * NM == 2 * C::CH, "slice schedules assume these counts");
+  constexpr int NP = NM < NR ? NM : NR;   // read / MFMA pairs of slices 1 and 2
   const f16* a_s = st + aoff;
-  const f16* b_s = st + boff;
   half8 af[2][C::FM], bf[2][C::FN];
 #pragma unroll
   for (int i = 0; i < C::FM; ++i) af[0][i] = fa0[i];
@@ -314,8 +372,7 @@ __device__ __forceinline__ void mma_step(const f16* __restrict__ st, f16* __rest
       for (int i = 0; i < C::FM; ++i)
         af[cb ^ 1][i] = *(const half8*)(a_s + i * 32 * LDSK + (kk + 1) * 16);
 #pragma unroll
-      for (int j = 0; j < C::FN; ++j)
-        bf[cb ^ 1][j] = *(const half8*)(b_s + j * 32 * LDSK + (kk + 1) * 16);
+      for (int j = 0; j < C::FN; ++j) bf[cb ^ 1][j] = bfrag<C, BKN>(st, boff, j, kk + 1);
     }
     if (kk == NS - 1) {
       __syncthreads();
@@ -323,7 +380,7 @@ __device__ __forceinline__ void mma_step(const f16* __restrict__ st, f16* __rest
 #pragma unroll
         for (int i = 0; i < C::FM; ++i) fa0[i] = *(const half8*)(nxt + aoff + i * 32 * LDSK);
 #pragma unroll
-        for (int j = 0; j < C::FN; ++j) fb0[j] = *(const half8*)(nxt + boff + j * 32 * LDSK);
+        for (int j = 0; j < C::FN; ++j) fb0[j] = bfrag<C, BKN>(nxt, boff, j, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
       mfma_slice<C>(af[cb], bf[cb], acc);
@@ -332,11 +389,13 @@ __device__ __forceinline__ void mma_step(const f16* __restrict__ st, f16* __rest
     }
     if (kk == 0 && STORE) {
       lstore<C>(nxt, tid, ra);
-      lstore<C>(nxt + C::BM * LDSK, tid, rb);
+      if constexpr (BKN) lstore_kn<C>(nxt + C::BM * LDSK, tid, rb);
+      else lstore<C>(nxt + C::BM * LDSK, tid, rb);
     }
     if (kk == 0 && LOAD) {
       gload<C>(Ab, lda, m0, k0_next, tid, ra);
-      gload<C>(Bb, ldb, n0, k0_next, tid, rb);
+      if constexpr (BKN) gload_kn<C>(Bb, ldb, n0, k0_next, tid, rb);
+      else gload<C>(Bb, ldb, n0, k0_next, tid, rb);
     }
     mfma_slice<C>(af[cb], bf[cb], acc);
     if (kk == 0) {
@@ -349,11 +408,12 @@ __device__ __forceinline__ void mma_step(const f16* __restrict__ st, f16* __rest
       }
     } else {
 #pragma unroll
-      for (int q = 0; q < NR; ++q) {
+      for (int q = 0; q < NP; ++q) {
         __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
         __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
       }
-      if constexpr (NM > NR) __builtin_amdgcn_sched_group_barrier(kSgMfma, NM - NR, 0);
+      if constexpr (NM > NP) __builtin_amdgcn_sched_group_barrier(kSgMfma, NM - NP, 0);
+      if constexpr (NR > NP) __builtin_amdgcn_sched_group_barrier(kSgDsRead, NR - NP, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -363,7 +423,7 @@ __device__ __forceinline__ void mma_step(const f16* __restrict__ st, f16* __rest
 // 3 rectangular, 4 standard-iteration update, 5 final rectangular product
 // with the fused update) so that profilers report each role as its own
 // kernel.
-template <class C, int ROLE, bool LOWER, bool EPI>
+template <class C, int ROLE, bool LOWER, bool EPI, bool BKN>
 __global__ __launch_bounds__(C::NT, (C::BM == 256 ? 1 : 2)) void k_gemm(GemmArgs p) {
   __shared__ __attribute__((aligned(16))) f16 lds[C::LDS];
 
@@ -392,7 +452,8 @@ __global__ __launch_bounds__(C::NT, (C::BM == 256 ? 1 : 2)) void k_gemm(GemmArgs
   const int m0 = bi * C::BM, n0 = bj * C::BN;
 
   const __amdgpu_buffer_rsrc_t Ab = operand_rsrc(p.A + (long long)b * p.sA, p.M, p.lda);
-  const __amdgpu_buffer_rsrc_t Bb = operand_rsrc(p.B + (long long)b * p.sB, p.N, p.ldb);
+  // B: N rows of K, or with BKN the [K][N] form, K rows of N
+  const __amdgpu_buffer_rsrc_t Bb = operand_rsrc(p.B + (long long)b * p.sB, BKN ? p.K : p.N, p.ldb);
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wm = wid / (C::BN / C::WTN), wn = wid % (C::BN / C::WTN);
@@ -412,37 +473,45 @@ __global__ __launch_bounds__(C::NT, (C::BM == 256 ? 1 : 2)) void k_gemm(GemmArgs
     // that ended step t-1) and tile t+2 is requested into the registers.
     half8 ra[C::CH], rb[C::CH];
     gload<C>(Ab, p.lda, m0, 0, tid, ra);
-    gload<C>(Bb, p.ldb, n0, 0, tid, rb);
+    if constexpr (BKN) gload_kn<C>(Bb, p.ldb, n0, 0, tid, rb);
+    else gload<C>(Bb, p.ldb, n0, 0, tid, rb);
     lstore<C>(lds, tid, ra);
-    lstore<C>(lds + C::BM * LDSK, tid, rb);
+    if constexpr (BKN) lstore_kn<C>(lds + C::BM * LDSK, tid, rb);
+    else lstore<C>(lds + C::BM * LDSK, tid, rb);
     if (nk > 1) {
       gload<C>(Ab, p.lda, m0, BK, tid, ra);
-      gload<C>(Bb, p.ldb, n0, BK, tid, rb);
+      if constexpr (BKN) gload_kn<C>(Bb, p.ldb, n0, BK, tid, rb);
+      else gload<C>(Bb, p.ldb, n0, BK, tid, rb);
     }
     __syncthreads();
     // the first slice's fragments of stage 0; each step then reads those of
     // the stage after it
     const int aoff = (wm * C::WTM + (lane & 31)) * LDSK + (lane >> 5) * 8;
-    const int boff = (C::BM + wn * C::WTN + (lane & 31)) * LDSK + (lane >> 5) * 8;
+    // B, [N][K]: this lane's row and K offset; [K][N]: its transposing-read
+    // address inside the 4 x 16 blocks (row 8 (lane / 32) + (lane % 16) / 4,
+    // column 16 ((lane / 16) % 2) + 4 (lane % 4) of the wave's columns)
+    const int boff = BKN ? ((lane >> 5) * 8 + ((lane & 15) >> 2)) * C::RSB + wn * C::WTN +
+                               ((lane >> 4) & 1) * 16 + (lane & 3) * 4
+                         : (C::BM + wn * C::WTN + (lane & 31)) * LDSK + (lane >> 5) * 8;
     half8 fa0[C::FM], fb0[C::FN];
 #pragma unroll
     for (int i = 0; i < C::FM; ++i) fa0[i] = *(const half8*)(lds + aoff + i * 32 * LDSK);
 #pragma unroll
-    for (int j = 0; j < C::FN; ++j) fb0[j] = *(const half8*)(lds + boff + j * 32 * LDSK);
+    for (int j = 0; j < C::FN; ++j) fb0[j] = bfrag<C, BKN>(lds, boff, j, 0);
     // all steps but the last two store the next tile and load the one after
     int kt = 0;
     for (; kt + 2 < nk; ++kt)
-      mma_step<C, true, true, true>(lds + (kt & 1) * C::STAGE, lds + ((kt + 1) & 1) * C::STAGE, Ab,
+      mma_step<C, true, true, true, BKN>(lds + (kt & 1) * C::STAGE, lds + ((kt + 1) & 1) * C::STAGE, Ab,
                                     Bb, p.lda, p.ldb, m0, n0, (kt + 2) * BK, tid, ra, rb, aoff,
                                     boff, fa0, fb0, acc);
     if (kt + 1 < nk) {   // next to last: store only
-      mma_step<C, true, false, true>(lds + (kt & 1) * C::STAGE, lds + ((kt + 1) & 1) * C::STAGE, Ab,
+      mma_step<C, true, false, true, BKN>(lds + (kt & 1) * C::STAGE, lds + ((kt + 1) & 1) * C::STAGE, Ab,
                                      Bb, p.lda, p.ldb, m0, n0, 0, tid, ra, rb, aoff, boff, fa0,
                                      fb0, acc);
       ++kt;
     }
     // last step: its barrier also frees the LDS for the epilogue
-    mma_step<C, false, false, false>(lds + (kt & 1) * C::STAGE, lds + ((kt + 1) & 1) * C::STAGE, Ab,
+    mma_step<C, false, false, false, BKN>(lds + (kt & 1) * C::STAGE, lds + ((kt + 1) & 1) * C::STAGE, Ab,
                                      Bb, p.lda, p.ldb, m0, n0, 0, tid, ra, rb, aoff, boff, fa0,
                                      fb0, acc);
   }
@@ -644,7 +713,7 @@ __global__ __launch_bounds__(C::NT, (C::BM == 256 ? 1 : 2)) void k_gemm(GemmArgs
   }
 }
 
-template <class C, int ROLE, bool LOWER, bool EPI>
+template <class C, int ROLE, bool LOWER, bool EPI, bool BKN>
 hipError_t launch(const GemmDesc& d, hipStream_t s) {
   GemmArgs p;
   p.A = d.A; p.B = d.B; p.C = d.C; p.CT = d.CT; p.D = d.D;
@@ -662,7 +731,7 @@ hipError_t launch(const GemmDesc& d, hipStream_t s) {
   p.sink = d.sink; p.W = d.W; p.ldw = d.ldw; p.idx = d.idx; p.lr = d.lr; p.Oout = d.Oout;
   p.sO = d.sO;
   p.kval = d.kval; p.mval = d.mval; p.nrows = d.nrows;
-  hipLaunchKernelGGL((k_gemm<C, ROLE, LOWER, EPI>), dim3(p.total), dim3(C::NT), 0, s, p);
+  hipLaunchKernelGGL((k_gemm<C, ROLE, LOWER, EPI, BKN>), dim3(p.total), dim3(C::NT), 0, s, p);
   return hipGetLastError();
 }
 
@@ -684,11 +753,11 @@ const char* trace_name(int role, bool large) {
   return names[role][large ? 1 : 0];
 }
 
-template <int ROLE, bool LOWER, bool EPI>
+template <int ROLE, bool LOWER, bool EPI, bool BKN = false>
 hipError_t launch_cfg(const GemmDesc& d, hipStream_t s) {
   const bool large = use_large(d);
   TraceScope ts(trace_name(ROLE, large), d.trace_flops, d.trace_bytes, s);
-  return large ? launch<CfgL, ROLE, LOWER, EPI>(d, s) : launch<CfgS, ROLE, LOWER, EPI>(d, s);
+  return large ? launch<CfgL, ROLE, LOWER, EPI, BKN>(d, s) : launch<CfgS, ROLE, LOWER, EPI, BKN>(d, s);
 }
 
 }  // namespace
@@ -696,6 +765,7 @@ hipError_t launch_cfg(const GemmDesc& d, hipStream_t s) {
 hipError_t launch_gemm(const GemmDesc& d, hipStream_t s) {
   if (d.M % 128 || d.N % 128 || d.K % BK || d.K <= 0 || d.batch <= 0) return hipErrorInvalidValue;
   if (d.lower && (d.M != d.N || d.CT || !d.C)) return hipErrorInvalidValue;
+  if (d.b_kn && (d.lower || d.epilogue || d.ldb % 8)) return hipErrorInvalidValue;
   if (!d.lower && !d.C && !d.CT && !d.sink) return hipErrorInvalidValue;
   if (d.sink && (d.lower || d.C || d.CT || (d.sink != 1 && d.sink != 2))) return hipErrorInvalidValue;
   switch (d.role) {
@@ -710,10 +780,12 @@ hipError_t launch_gemm(const GemmDesc& d, hipStream_t s) {
       return launch_cfg<kRoleSymm, true, false>(d, s);
     case kRoleRect:
       if (d.lower || d.epilogue || d.sink) break;
-      return launch_cfg<kRoleRect, false, false>(d, s);
+      return d.b_kn ? launch_cfg<kRoleRect, false, false, true>(d, s)
+                    : launch_cfg<kRoleRect, false, false>(d, s);
     case kRoleBack:
       if (d.lower || d.epilogue || !d.sink) break;
-      return launch_cfg<kRoleBack, false, false>(d, s);
+      return d.b_kn ? launch_cfg<kRoleBack, false, false, true>(d, s)
+                    : launch_cfg<kRoleBack, false, false>(d, s);
     case kRoleNsX:
       if (d.lower || !d.epilogue || !d.D) break;
       return launch_cfg<kRoleNsX, false, true>(d, s);

@@ -278,10 +278,11 @@ __global__ __launch_bounds__(TK_THREADS) void k_topk(const double* __restrict__ 
 // ------------------------------------------------------------- gather
 
 // One block per 64 selected rows x 256 columns: reads 1 KB of each selected
-// row of M, writes X in rows layout directly and, through an LDS tile, its
-// transpose XT (eight lanes per 128-byte run of an XT row), so that every
-// product of the Gram iteration reads K-contiguous operands; with DECAY it
-// also writes the rows of M back times mu.  The rows of M are read and
+// row of M, writes X in rows layout directly and/or, through an LDS tile, its
+// transpose XT (eight lanes per 128-byte run of an XT row), whichever of the
+// two is not null: the layout the products of the Gram iteration read, or
+// both for the paths that read both; with DECAY it also writes the rows of M
+// back times mu.  The rows of M are read and
 // written once, and X and XT (read again only by the next products) are far
 // larger than the caches, so the fp32 loads and all stores carry the
 // nontemporal hint (measured on the 7B set: 10-15 % less kernel time than
@@ -327,8 +328,9 @@ __global__ __launch_bounds__(256) void k_gather(BatchPtr<T> M, int n, int m, lon
   const int cl = 4 * (tid & 63);          // 4 columns per thread
   const int rq = tid >> 6;                // rows rq, rq + 4, ..., rq + 60
   const float sc = (float)scale[b];
-  f16* __restrict__ Xb = X + (long long)b * sX;
-  f16* __restrict__ XTb = XT + (long long)b * sX;
+  // (no arithmetic on a null layout pointer: the tests below must stay)
+  f16* __restrict__ Xb = X ? X + (long long)b * sX : nullptr;
+  f16* __restrict__ XTb = XT ? XT + (long long)b * sX : nullptr;
   T* base = M.get(b);
   const int c = c0 + cl;
   if (c < mp) {
@@ -365,10 +367,11 @@ __global__ __launch_bounds__(256) void k_gather(BatchPtr<T> M, int n, int m, lon
         asm("" : "+v"(t));
         h[e] = (f16)t;
       }
-      *(half4*)&tile[rl][cl] = h;
-      __builtin_nontemporal_store(h, (half4*)(Xb + (long long)r * mp + c));
+      if (XTb) *(half4*)&tile[rl][cl] = h;
+      if (Xb) __builtin_nontemporal_store(h, (half4*)(Xb + (long long)r * mp + c));
     }
   }
+  if (!XTb) return;   // uniform: from the kernel argument
   __syncthreads();
   // transposed: XT[c0 + col][r0 .. r0 + 63], 128 bytes per XT row, eight
   // lanes per row, so that each store instruction writes eight whole
