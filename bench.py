@@ -46,7 +46,7 @@ KERNEL_SYMBOLS = {
     "gather": "k_gather<float, true>",
     "gram_ns_fused_128": "k_gram_ns_small",
     "norm_rows": "k_norm_rows",
-    "norm_scale": "k_norm_scale",
+    "norm_stats": "k_norm_stats",
     "norm_update": "k_norm_update",
 }
 

@@ -273,6 +273,10 @@ struct UpdateSink {
   float lr;
   f16* Oout;
   long long sO;   // elements between consecutive matrices' O blocks (>= k * m)
+  // the rows' 128-column block sums of squares of O (per-neuron
+  // normalization), written by the final product when its output rows are
+  // the C pass (k <= m); ignored otherwise
+  float* part;
 };
 
 void set_sink(GemmDesc& d, const Shape& P, const UpdateSink& sink) {
@@ -284,6 +288,10 @@ void set_sink(GemmDesc& d, const Shape& P, const UpdateSink& sink) {
   d.W = sink.W; d.ldw = sink.ldw; d.idx = sink.idx; d.lr = sink.lr; d.Oout = sink.Oout;
   d.sO = sink.sO;
   d.kval = (int)P.k; d.mval = (int)P.m; d.nrows = (int)P.n;
+  if (!P.tr && sink.part) {
+    d.part = sink.part;
+    d.nblk = (int)((P.m + 127) / 128);
+  }
 }
 
 // Y_math = Q X_math.  X_math (sp x Lp, the layout the Gram reads) is the
@@ -565,13 +573,15 @@ dion3_status run_step(const CallLayout& L, const GroupArgs* A, float mu, const d
     r.x = xa;
     r.xalt = xb;
     if (!norm) {
-      r.sink = {a.W, a.ld, idx, a.lr, (f16*)a.O_out, P.k * P.m};
+      r.sink = {a.W, a.ld, idx, a.lr, (f16*)a.O_out, P.k * P.m, nullptr};
     } else {
       // O into the free X buffer, each matrix's rows [k][m] inside that
       // matrix's own padded block (so that in the fused one-launch path no
-      // workgroup writes where another matrix may still be read)
-      f16* Obuf = free_pair_is_b(cfg) ? xb.X : xa.X;
-      r.sink = {{nullptr, 0, nullptr}, 0, idx, a.lr, Obuf, P.kp * P.mp};
+      // workgroup writes where another matrix may still be read), and the
+      // rows' block sums of squares into the free pair's other buffer, which
+      // no product of this call reads
+      const XPair& fp = free_pair_is_b(cfg) ? xb : xa;
+      r.sink = {{nullptr, 0, nullptr}, 0, idx, a.lr, fp.X, P.kp * P.mp, (float*)fp.XT};
     }
   }
   dion3_status st = orthogonalize(L, cfg, w, runs, s);
@@ -586,9 +596,12 @@ dion3_status run_step(const CallLayout& L, const GroupArgs* A, float mu, const d
       // the norm region
       const f16* Obuf = runs[i].sink.Oout;
       const long long sO = runs[i].sink.sO;
+      // the tiled final product wrote the block sums already when its
+      // output rows are O's rows (k <= m); the fused kernel does not
+      const bool part_ready = !P.tr && !use_fused(P, cfg);
       HIP_TRY(launch_normalize(Obuf, sO, P.B, (int)P.k, (int)P.m, idx, a.V, norm->beta2, norm->eps,
-                               a.W, a.ld, a.lr, (float2*)(w + G.o_l1), (double*)(w + G.o_scale),
-                               s));
+                               a.W, a.ld, a.lr, runs[i].sink.part, part_ready,
+                               (float2*)(w + G.o_l1), s));
       if (a.O_out)
         HIP_TRY(hipMemcpy2DAsync(a.O_out, (size_t)P.k * P.m * sizeof(uint16_t), Obuf,
                                  (size_t)sO * sizeof(uint16_t), (size_t)P.k * P.m * sizeof(uint16_t),
@@ -804,7 +817,7 @@ dion3_status dion3_gram_ns(const uint16_t* X, uint16_t* O, int32_t batch, int64_
   r.G = &G;
   r.x = xa;
   r.xalt = xb;
-  r.sink = {{nullptr, 0, nullptr}, 0, idx, 0.0f, (f16*)O, k * m};
+  r.sink = {{nullptr, 0, nullptr}, 0, idx, 0.0f, (f16*)O, k * m, nullptr};
   return orthogonalize(L, cfg, w, &r, s);
 }
 

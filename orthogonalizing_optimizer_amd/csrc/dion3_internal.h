@@ -80,6 +80,11 @@ struct GemmDesc {
   f16* Oout;
   long long sO;            // elements between the Oout blocks of consecutive matrices
   int kval, mval, nrows;   // nrows: rows of W (row indices outside are skipped)
+  // rows layout from the C pass (sink == 1) only: when set, the 128-column
+  // block sums of squares of every output row in the order normalize.hip
+  // fixes, part[(b * kval + r) * nblk + column / 128]
+  float* part;
+  int nblk;
 };
 // Records e as the calling thread's last HIP error (dion3_last_hip_error)
 // and returns DION3_ERR_HIP.
@@ -136,11 +141,16 @@ hipError_t launch_gram_ns_small(f16* X, f16* XT, f16* Y, f16* YT, long long sX, 
                                 double trace_flops, hipStream_t s);
 
 // Per-neuron normalization of O ([k][m] fp16 rows per matrix, matrices sO
-// elements apart) and the
-// update W[idx[i]] -= lr * U_i; V holds one fp32 state per row of each
-// matrix; stats ([batch][k]) and g ([batch]) are scratch.
+// elements apart) and the update W[idx[i]] -= lr * U_i; V holds one fp32
+// state per row of each matrix.  part ([batch][k][ceil(m / 128)] fp32) holds
+// the rows' 128-column block sums of squares in the fixed order of
+// normalize.hip: already written by the product that wrote O when
+// part_ready, else computed here from O; the region must also hold, after
+// those sums (16-byte aligned), 16 bytes per matrix per 256 rows of scratch.
+// stats ([batch][k]) is scratch.
 hipError_t launch_normalize(const f16* O, long long sO, int batch, int k, int m, const int* idx,
                             BatchPtr<float> V, float beta2, float eps, BatchPtr<float> W,
-                            long long ldw, float lr, float2* stats, double* g, hipStream_t s);
+                            long long ldw, float lr, float* part, bool part_ready, float2* stats,
+                            hipStream_t s);
 
 }  // namespace dion3

@@ -50,6 +50,8 @@ struct GemmArgs {
   f16* Oout;
   long long sO;
   int kval, mval, nrows;
+  float* part;
+  int nblk;
 };
 
 // One 8-wide chunk of the output in rows layout (row r, columns c..c+7)
@@ -159,6 +161,12 @@ __device__ __forceinline__ void sink_tile(const GemmArgs& p, int b, int m0, int 
     }
     return v;
   };
+  // SINK 1 with p.part: each chunk's sum of squares (column order, fp32 fma
+  // from +0; zero for chunks outside the output), combined below into the
+  // rows' 128-column block sums in the order normalize.hip fixes
+  float cs[NCH];
+#pragma unroll
+  for (int q = 0; q < NCH; ++q) cs[q] = 0.0f;
   int row[NCH];
   if (SINK == 1) {
 #pragma unroll
@@ -194,6 +202,15 @@ __device__ __forceinline__ void sink_tile(const GemmArgs& p, int b, int m0, int 
       where(q0 + u, gr, gc, sr, sc);
       if (gr >= p.kval || gc >= p.mval) continue;
       const half8 v = staged(sr, sc);
+      if (SINK == 1 && p.part) {
+        float a = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float x = gc + e < p.mval ? (float)v[e] : 0.0f;
+          a = __builtin_fmaf(x, x, a);
+        }
+        cs[q0 + u] = a;
+      }
       const int r = row[q0 + u];
       if (!(vec && r >= 0 && r < p.nrows && gc + 8 <= p.mval)) {
         sink_chunk(p, b, gr, gc, v);
@@ -220,6 +237,21 @@ __device__ __forceinline__ void sink_tile(const GemmArgs& p, int b, int m0, int 
       float4* w = (float4*)(Wb + (long long)r * p.ldw + gc);
       w[0] = a;
       w[1] = c;
+    }
+  }
+  if (SINK == 1 && p.part) {
+    // the 16 lanes tid & ~15 .. hold the 16 chunks of one row's 128-column
+    // block (columns n0 + 8 (tid % CPR) ..; n0 is a multiple of 128): the
+    // butterfly xor 1, 2, 4, 8, with every lane taking part
+#pragma unroll
+    for (int q = 0; q < NCH; ++q) {
+      float v = cs[q];
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) v += __shfl_xor(v, o, 64);
+      int gr, gc, sr, sc;
+      where(q, gr, gc, sr, sc);
+      if ((tid & 15) == 0 && gr < p.kval && gc < p.mval)
+        p.part[((long long)b * p.kval + gr) * p.nblk + gc / 128] = v;
     }
   }
 }
@@ -731,6 +763,7 @@ hipError_t launch(const GemmDesc& d, hipStream_t s) {
   p.sink = d.sink; p.W = d.W; p.ldw = d.ldw; p.idx = d.idx; p.lr = d.lr; p.Oout = d.Oout;
   p.sO = d.sO;
   p.kval = d.kval; p.mval = d.mval; p.nrows = d.nrows;
+  p.part = d.part; p.nblk = d.nblk;
   hipLaunchKernelGGL((k_gemm<C, ROLE, LOWER, EPI, BKN>), dim3(p.total), dim3(C::NT), 0, s, p);
   return hipGetLastError();
 }
@@ -768,6 +801,7 @@ hipError_t launch_gemm(const GemmDesc& d, hipStream_t s) {
   if (d.b_kn && (d.lower || d.epilogue || d.ldb % 8)) return hipErrorInvalidValue;
   if (!d.lower && !d.C && !d.CT && !d.sink) return hipErrorInvalidValue;
   if (d.sink && (d.lower || d.C || d.CT || (d.sink != 1 && d.sink != 2))) return hipErrorInvalidValue;
+  if (d.part && (d.sink != 1 || d.nblk != (d.mval + 127) / 128)) return hipErrorInvalidValue;
   switch (d.role) {
     case kRoleGram:
       if (!d.lower || d.epilogue) break;

@@ -9,11 +9,14 @@
 //   q_i = mean_j O_ij^2,  V[S_i] <- beta2 V[S_i] + (1 - beta2) q_i,
 //   U_i = O_i / (sqrt(V[S_i]) + eps)  (0 for a zero row with zero state),
 //   U  <- U ||O||_F / ||U||_F,  W[S] <- W[S] - lr U.
-// Three passes, each reduction in a fixed order (results do not depend on
-// the launch):
-//   k_norm_rows   one wave per selected row: q, the state, r_i = 1/(sqrt+eps)
-//   k_norm_scale  one workgroup per matrix: g = ||O|| / ||U|| from the rows
-//   k_norm_update W[S_i][j] = fma(-lr g r_i, O_ij, W[S_i][j])
+// Passes, each reduction in a fixed order (results do not depend on the
+// launch or on which kernel summed the squares):
+//   row block sums: the epilogue of the product that writes O, or
+//     k_norm_rows (one wave per selected row) reading O back;
+//   k_norm_stats  one thread per row: s_i, the state, r_i = 1/(sqrt(v_i) + eps),
+//     and per workgroup the sums behind g = ||O|| / ||U||;
+//   k_norm_update g from those sums (in workgroup order), then
+//     W[S_i][j] = fma(-lr g r_i, O_ij, W[S_i][j])
 #include "dion3_internal.h"
 
 namespace dion3 {
@@ -23,61 +26,73 @@ typedef f16 half8 __attribute__((ext_vector_type(8)));
 typedef f16 half4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ float wave_sum(float v) {
-  // fixed butterfly over the 64 lanes: every lane ends with the same sum
+// Per-row sums of squares of O in one fixed order, whatever computes them
+// (this kernel from O in memory, or the epilogue of the product that writes O,
+// gemm_f16.hip): the row is cut into 128-column blocks; in a block, each of
+// the 16 eight-column chunks sums its squares in column order (fp32 fma from
+// +0), and the 16 chunk sums combine by the butterfly xor 1, 2, 4, 8 (a
+// balanced tree in chunk order).  part[b][i][blk] holds block blk's sum; the
+// row's total adds the blocks in increasing order (k_norm_stats).  One wave
+// per row, its four 16-lane quarters on four consecutive blocks.
+__device__ __forceinline__ float chunk_sumsq(const f16* __restrict__ row, int c, int m, bool vec) {
+  float acc = 0.0f;
+  if (vec && c + 8 <= m) {
+    const half8 h = *(const half8*)(row + c);
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+    for (int e = 0; e < 8; ++e) acc = __builtin_fmaf((float)h[e], (float)h[e], acc);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float x = c + e < m ? (float)row[c + e] : 0.0f;
+      acc = __builtin_fmaf(x, x, acc);
+    }
+  }
+  return acc;
 }
 
-// Row stats of O (rows [k][m] per matrix, matrices sO apart): s_i = sum of
-// squares (fp32 lanes, fixed butterfly), the state update and r_i.
 __global__ __launch_bounds__(256) void k_norm_rows(const f16* __restrict__ O, long long sO, int k,
-                                                   int m, const int* __restrict__ idx,
-                                                   BatchPtr<float> V,
-                                                   float beta2, float eps,
-                                                   float2* __restrict__ stats) {
+                                                   int m, int nblk, float* __restrict__ part) {
   const int b = blockIdx.y;
   const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (i >= k) return;                       // whole waves leave together
   const f16* __restrict__ row = O + (long long)b * sO + (long long)i * m;
-  float acc = 0.0f;
   const bool vec = ((uintptr_t)row & 15) == 0;
-  int j = 0;
-  if (vec) {
-    for (; j + 8 * 64 <= m; j += 8 * 64) {
-      const half8 h = *(const half8*)(row + j + 8 * lane);
+  const int quarter = lane >> 4, ch = lane & 15;
+  for (int b0 = 0; b0 < nblk; b0 += 4) {
+    const int blk = b0 + quarter;
+    float v = blk < nblk ? chunk_sumsq(row, blk * 128 + ch * 8, m, vec) : 0.0f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc = __builtin_fmaf((float)h[e], (float)h[e], acc);
-    }
+    for (int o = 1; o < 16; o <<= 1) v += __shfl_xor(v, o, 64);
+    if (ch == 0 && blk < nblk) part[((long long)b * k + i) * nblk + blk] = v;
   }
-  for (int c = j + lane; c < m; c += 64) {
-    const float x = (float)row[c];
-    acc = __builtin_fmaf(x, x, acc);
-  }
-  const float s = wave_sum(acc);
-  if (lane == 0) {
-    const int r = idx[(long long)b * k + i];
-    float* v = V.get(b) + r;
+}
+
+// One thread per selected row (256 rows per workgroup): the row's sum of
+// squares s_i (its block sums in block order), the state update and
+// r_i = 1 / (sqrt(v_i) + eps); each workgroup also leaves the fp64 sums of s_i
+// and s_i r_i^2 over its rows (a fixed tree) for the scale g.
+__global__ __launch_bounds__(256) void k_norm_stats(const float* __restrict__ part, int k, int m,
+                                                    int nblk, const int* __restrict__ idx,
+                                                    BatchPtr<float> V, float beta2, float eps,
+                                                    float2* __restrict__ stats,
+                                                    double2* __restrict__ wsum) {
+  __shared__ double sh0[256], sh1[256];
+  const int b = blockIdx.y, t = threadIdx.x, i = blockIdx.x * 256 + t;
+  double a0 = 0.0, a1 = 0.0;
+  if (i < k) {
+    const float* __restrict__ pr = part + ((long long)b * k + i) * nblk;
+    float s = 0.0f;
+    for (int j = 0; j < nblk; ++j) s += pr[j];
+    float* v = V.get(b) + idx[(long long)b * k + i];
     const float q = s / (float)m;
     const float nv = __builtin_fmaf(beta2, *v, (1.0f - beta2) * q);
     *v = nv;
     const float d = sqrtf(nv) + eps;
-    stats[(long long)b * k + i] = make_float2(s, d > 0.0f ? 1.0f / d : 0.0f);
-  }
-}
-
-// g = sqrt(sum_i s_i / sum_i s_i r_i^2) per matrix (fp64, fixed order).
-__global__ __launch_bounds__(256) void k_norm_scale(const float2* __restrict__ stats, int k,
-                                                    double* __restrict__ g) {
-  __shared__ double sh0[256], sh1[256];
-  const int b = blockIdx.x, t = threadIdx.x;
-  double a0 = 0.0, a1 = 0.0;
-  for (int i = t; i < k; i += 256) {
-    const float2 st = stats[(long long)b * k + i];
-    a0 += (double)st.x;
-    a1 += (double)st.x * (double)st.y * (double)st.y;
+    const float r = d > 0.0f ? 1.0f / d : 0.0f;
+    stats[(long long)b * k + i] = make_float2(s, r);
+    a0 = (double)s;
+    a1 = (double)s * (double)r * (double)r;
   }
   sh0[t] = a0;
   sh1[t] = a1;
@@ -89,21 +104,31 @@ __global__ __launch_bounds__(256) void k_norm_scale(const float2* __restrict__ s
     }
     __syncthreads();
   }
-  if (t == 0) g[b] = sh1[0] > 0.0 ? sqrt(sh0[0] / sh1[0]) : 0.0;
+  if (t == 0) wsum[(long long)b * gridDim.x + blockIdx.x] = make_double2(sh0[0], sh1[0]);
 }
 
 // W[idx[i]][j] = fma(-lr g r_i, O_ij, W[idx[i]][j]): one workgroup per 4 rows
 // of O, 64 lanes along a row, 4 columns per lane per pass.
+// The scale g = sqrt(sum_i s_i / sum_i s_i r_i^2) comes from k_norm_stats'
+// per-workgroup sums, added in workgroup order (every workgroup of a matrix
+// gets the same bits).
 __global__ __launch_bounds__(256) void k_norm_update(const f16* __restrict__ O, long long sO, int k,
                                                      int m, const int* __restrict__ idx,
                                                      BatchPtr<float> W, long long ldw, float lr,
                                                      const float2* __restrict__ stats,
-                                                     const double* __restrict__ g) {
+                                                     const double2* __restrict__ wsum, int nwg) {
   const int b = blockIdx.y;
   const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (i >= k) return;
-  const float c = -lr * (float)g[b] * stats[(long long)b * k + i].y;
+  double a0 = 0.0, a1 = 0.0;
+  for (int j = 0; j < nwg; ++j) {
+    const double2 w2 = wsum[(long long)b * nwg + j];
+    a0 += w2.x;
+    a1 += w2.y;
+  }
+  const double g = a1 > 0.0 ? sqrt(a0 / a1) : 0.0;
+  const float c = -lr * (float)g * stats[(long long)b * k + i].y;
   const f16* __restrict__ src = O + (long long)b * sO + (long long)i * m;
   float* __restrict__ w = W.get(b) + (long long)idx[(long long)b * k + i] * ldw;
   for (int j = 4 * lane; j < m; j += 4 * 64) {
@@ -128,25 +153,30 @@ __global__ __launch_bounds__(256) void k_norm_update(const f16* __restrict__ O, 
 
 hipError_t launch_normalize(const f16* O, long long sO, int batch, int k, int m, const int* idx,
                             BatchPtr<float> V, float beta2, float eps, BatchPtr<float> W,
-                            long long ldw, float lr, float2* stats, double* g, hipStream_t s) {
+                            long long ldw, float lr, float* part, bool part_ready, float2* stats,
+                            hipStream_t s) {
   const dim3 grid((k + 3) / 4, batch);
   const double km = (double)batch * k * m;
-  {
+  const int nblk = (m + 127) / 128;
+  const int nwg = (k + 255) / 256;
+  // the per-workgroup sums sit right after the block sums, 16-byte aligned
+  double2* wsum = (double2*)(part + (((long long)batch * k * nblk + 3) & ~3LL));
+  if (!part_ready) {
     TraceScope ts("norm_rows", 0.0, km * 2.0, s);
-    hipLaunchKernelGGL(k_norm_rows, grid, dim3(256), 0, s, O, sO, k, m, idx, V, beta2, eps,
-                       stats);
+    hipLaunchKernelGGL(k_norm_rows, grid, dim3(256), 0, s, O, sO, k, m, nblk, part);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   {
-    TraceScope ts("norm_scale", 0.0, (double)batch * k * 8.0, s);
-    hipLaunchKernelGGL(k_norm_scale, dim3(batch), dim3(256), 0, s, stats, k, g);
+    TraceScope ts("norm_stats", 0.0, (double)batch * k * (4.0 * nblk + 8.0), s);
+    hipLaunchKernelGGL(k_norm_stats, dim3(nwg, batch), dim3(256), 0, s, part, k, m, nblk, idx, V,
+                       beta2, eps, stats, wsum);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   TraceScope ts("norm_update", 0.0, km * 10.0, s);
   hipLaunchKernelGGL(k_norm_update, grid, dim3(256), 0, s, O, sO, k, m, idx, W, ldw, lr, stats,
-                     g);
+                     wsum, nwg);
   return hipGetLastError();
 }
 

@@ -171,3 +171,28 @@ def test_norm_o_buffer_never_aliases_the_iteration(iters, restarts, method, path
                         norm=(torch.zeros(n, device=DEV), BETA2, EPS))
     torch.cuda.synchronize()
     assert O_norm.cpu().numpy().tobytes() == O_plain.cpu().numpy().tobytes()
+
+
+def test_norm_step_large_tile_block_sums():
+    """16 matrices with k = 1024 take the 256-wide tiles, whose output rows
+    each hold two 128-column blocks of the row sums the final product writes
+    for the normalization; the normalization of the GPU's own O matches the
+    oracle's tightly, on the first and last matrix."""
+    say("norm 256 tile")
+    B, n, m, k = 16, 1100, 2048, 1024
+    Ws = [host_gaussian((n, m), [112, b], std=0.02) for b in range(B)]
+    Ms = [host_gaussian((n, m), [113, b]) for b in range(B)]
+    Vs = [np.random.default_rng([114, b]).uniform(0.0, 0.01, n).astype(np.float32)
+          for b in range(B)]
+    Wd, Md, Vd = [dev(w) for w in Ws], [dev(x) for x in Ms], [dev(v) for v in Vs]
+    idx, O = d3.step_megabatch(Wd, Md, k, LR, MU, norm=(Vd, BETA2, EPS), return_idx=True,
+                               return_O=True)
+    torch.cuda.synchronize()
+    for b in (0, B - 1):
+        S, Ob = idx[b].cpu().numpy(), O[b].cpu().numpy().astype(np.float64)
+        U_ref, V_ref = orc.normalize_neurons(Ob, S, Vs[b], BETA2, EPS)
+        V1, W1 = Vd[b].cpu().numpy(), Wd[b].cpu().numpy()
+        assert np.max(np.abs(V1[S] - V_ref[S]) / V_ref[S]) <= 1e-5
+        assert rel(W1[S] - Ws[b][S], -LR * U_ref) <= 1e-5
+        rest = np.setdiff1d(np.arange(n), S)
+        assert W1[rest].tobytes() == Ws[b][rest].tobytes()
