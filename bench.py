@@ -463,7 +463,7 @@ def main():
             "parallelism": "single GPU, " + (
                 "one megabatched call per shape group" if (args.per_group or args.streams > 1)
                 else "one call for all shape groups (groups with equal Gram sides share their "
-                     "s x s products' launches)") +
+                     "s x s products' launches where that is no slower)") +
                 (f", groups on {args.streams} streams" if args.streams > 1 else ""),
             "gradient_accumulation": bool(args.accumulate),
             "per_neuron_normalization": bool(args.normalize),

@@ -260,8 +260,11 @@ DION3_API dion3_status dion3_workspace_size_groups(const dion3_group* groups, in
  * min(k, m); e.g. the attention and down-projection matrices of a
  * transformer at one fraction) run their s x s products, the polynomial and
  * the symmetric products of the level-2 paragraph, as one launch over the
- * matrices of all of them; each group's products that read its selected
- * rows (the Grams and the multiply-backs) run per group.  norm: NULL, or the
+ * matrices of all of them, where a launch-round cost model says that the
+ * shared launch is no slower than separate ones (it shares on the 1B- and
+ * 14B-shaped sets, not on the 7B-shaped set at f = 1/4); each group's
+ * products that read its selected rows (the Grams and the multiply-backs)
+ * run per group.  norm: NULL, or the
  * per-neuron normalization of dion3_step_megabatch_norm for every group.
  * Results equal calling dion3_step_megabatch (_accum, _norm) once per group
  * with the same arguments, bit for bit.  Matrices written by different

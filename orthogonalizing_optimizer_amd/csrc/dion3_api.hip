@@ -80,9 +80,26 @@ struct CallLayout {
 
 long long side_of(const Shape& P) { return P.tr ? P.m : P.k; }
 
+// Relative time of one s x s product launch over `batch` matrices of padded
+// side sp, in rounds of 256-wide tiles over the 256 CUs: the launch takes the
+// 256 tile from 512 such tiles on, else the 128 tile two per CU, whose round
+// of 512 tiles (half the work of a 256 round) measured about half as long.
+// Merging two groups' launches pays off only when it does not add a round
+// (on the 7B set, attention and down-projection groups at f = 1/4: 1280 +
+// 320 tiles run 6.25 rounds merged against 5 + a small-tile launch apart,
+// measured 0.2 ms per step slower merged; the 1B and 14B sets gain 0.2 ms).
+double side_cost(long long sp, long long batch) {
+  const long long t = (sp + 255) / 256, u = sp / 128;
+  const long long big = t * (t + 1) / 2 * batch;
+  if (big >= 512) return (double)((big + 255) / 256);
+  const long long small = u * (u + 1) / 2 * batch;
+  return 0.5 * (double)((small + 511) / 512);
+}
+
 // Regions in order: every group's rows and X pairs, then the side sets.  A
-// group with no_side[g] set gets no side set; the others join the set of
-// their Gram side.
+// group with no_side[g] set gets no side set; the others join a set of their
+// Gram side when side_cost says the shared launches are no slower, else
+// start a set of their own.
 void make_layout(CallLayout& L, int ng, const Shape* shapes, const bool* no_side) {
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
@@ -105,7 +122,11 @@ void make_layout(CallLayout& L, int ng, const Shape* shapes, const bool* no_side
     G.side_off = 0;
     if (no_side[i]) continue;
     int j = 0;
-    while (j < L.nside && !(L.sd[j].sp == P.sp && L.sd[j].s == side_of(P))) ++j;
+    while (j < L.nside &&
+           !(L.sd[j].sp == P.sp && L.sd[j].s == side_of(P) &&
+             side_cost(P.sp, L.sd[j].batch + P.B) <=
+                 side_cost(P.sp, L.sd[j].batch) + side_cost(P.sp, P.B)))
+      ++j;
     if (j == L.nside) {
       L.sd[j].sp = P.sp;
       L.sd[j].s = side_of(P);
