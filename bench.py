@@ -28,18 +28,18 @@ METRIC = "Dion3 optimizer-step ms per model + Gram-NS TFLOP/s (% fp16 MFMA peak)
 
 # trace name -> the kernel symbol rocprofv3 reports for it
 KERNEL_SYMBOLS = {
-    "gemm_gram_256": "k_gemm<Cfg<256, 2, 4, 1>, 0, true, false>",
-    "gemm_poly_256": "k_gemm<Cfg<256, 2, 4, 1>, 1, true, true>",
-    "gemm_symm_256": "k_gemm<Cfg<256, 2, 4, 1>, 2, true, false>",
-    "gemm_rect_256": "k_gemm<Cfg<256, 2, 4, 1>, 3, false, false>",
-    "gemm_nsx_256": "k_gemm<Cfg<256, 2, 4, 1>, 4, false, true>",
-    "gemm_nsx_128": "k_gemm<Cfg<128, 2, 2, 1>, 4, false, true>",
-    "gemm_gram_128": "k_gemm<Cfg<128, 2, 2, 1>, 0, true, false>",
-    "gemm_poly_128": "k_gemm<Cfg<128, 2, 2, 1>, 1, true, true>",
-    "gemm_symm_128": "k_gemm<Cfg<128, 2, 2, 1>, 2, true, false>",
-    "gemm_rect_128": "k_gemm<Cfg<128, 2, 2, 1>, 3, false, false>",
-    "gemm_back_256": "k_gemm<Cfg<256, 2, 4, 1>, 5, false, false>",
-    "gemm_back_128": "k_gemm<Cfg<128, 2, 2, 1>, 5, false, false>",
+    "gemm_gram_256": "k_gemm<Cfg<256, 2, 4, 1>, 0, true, false, false>",
+    "gemm_poly_256": "k_gemm<Cfg<256, 2, 4, 1>, 1, true, true, false>",
+    "gemm_symm_256": "k_gemm<Cfg<256, 2, 4, 1>, 2, true, false, false>",
+    "gemm_rect_256": "k_gemm<Cfg<256, 2, 4, 1>, 3, false, false, true>",
+    "gemm_nsx_256": "k_gemm<Cfg<256, 2, 4, 1>, 4, false, true, false>",
+    "gemm_back_256": "k_gemm<Cfg<256, 2, 4, 1>, 5, false, false, true>",
+    "gemm_gram_128": "k_gemm<Cfg<128, 2, 2, 1>, 0, true, false, false>",
+    "gemm_poly_128": "k_gemm<Cfg<128, 2, 2, 1>, 1, true, true, false>",
+    "gemm_symm_128": "k_gemm<Cfg<128, 2, 2, 1>, 2, true, false, false>",
+    "gemm_rect_128": "k_gemm<Cfg<128, 2, 2, 1>, 3, false, false, true>",
+    "gemm_nsx_128": "k_gemm<Cfg<128, 2, 2, 1>, 4, false, true, false>",
+    "gemm_back_128": "k_gemm<Cfg<128, 2, 2, 1>, 5, false, false, true>",
     "row_score": "k_row_score_f32",
     "accum_score": "k_accum_score_f32",
     "topk": "k_topk",
