@@ -369,17 +369,18 @@ double gram_ns_flops(const Shape& P, const dion3_ns_cfg& cfg) {
 
 // The fused one-launch path covers Gram sides that pad to one 128 tile.  It
 // runs one workgroup per matrix, so its time grows with the row length L
-// (measured on MI355X, whole Gram iteration: 67 us at L = 512, 153 us at
-// 2048, 265 us at 4096, 490 us at 8192, flat in the batch up to 256
-// matrices) while the tiled launches cost about 210 us at small sizes and
-// spread long rows over many CUs.  Measured crossovers: the fused path wins
-// up to L = 2048 at any batch, up to 4096 from 16 matrices on, and up to
-// 8192 from 64 matrices on.
+// while the tiled launches spread long rows over many CUs.  Measured on
+// MI355X, one dion3_gram_ns call (us, fused / tiled): 72 / 128 at 1 x 32 x
+// 512, 114 / 145 at 1 x 128 x 1024, 172 / 157 at 1 x 128 x 2048, 184 / 186 at
+// 32 x 128 x 2048, 292 / 193 at 1 x 128 x 4096, 302 / 218 at 16 x 128 x 4096,
+// 638 / 533 at 64 x 128 x 8192, 120 / 223 at 256 x 128 x 512, 140 / 459 at
+// 512 x 64 x 256: the fused path wins up to L = 1024 at any batch and ties at
+// L = 2048 from about 32 matrices on.
 bool use_fused(const Shape& P, const dion3_ns_cfg& cfg) {
   if (cfg.method != DION3_NS_GRAM) return false;
   if (cfg.path == DION3_PATH_TILED || P.sp != kTile) return false;
   if (cfg.path == DION3_PATH_FUSED) return true;
-  return P.Lp <= 2048 || (P.Lp <= 4096 && P.B >= 16) || (P.Lp <= 8192 && P.B >= 64);
+  return P.Lp <= 1024 || (P.Lp <= 2048 && P.B >= 32);
 }
 
 // The fused path was asked for explicitly but the Gram side exceeds 128.
