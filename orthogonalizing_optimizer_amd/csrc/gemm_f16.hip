@@ -342,14 +342,52 @@ __device__ __forceinline__ void lstore(f16* __restrict__ s, int tid, const half8
 // Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
 constexpr int kSgMfma = 0x008, kSgVmemRead = 0x020, kSgDsRead = 0x100, kSgDsWrite = 0x200;
 
-template <class C>
+// Which 32 x 32 blocks of its wave tile a wave computes: bit FN i + j of MSK
+// for block (i, j).  Every block but in the diagonal tiles of symmetric
+// outputs, where blocks wholly above the diagonal are never stored (see
+// k_gemm) and are skipped with their fragment reads.
+constexpr int kAllBlocks = 0xFF;
+template <class C, int MSK>
+struct Blocks {
+  static constexpr bool on(int i, int j) { return ((MSK >> (i * C::FN + j)) & 1) != 0; }
+  static constexpr bool arow(int i) {
+    for (int j = 0; j < C::FN; ++j)
+      if (on(i, j)) return true;
+    return false;
+  }
+  static constexpr bool bcol(int j) {
+    for (int i = 0; i < C::FM; ++i)
+      if (on(i, j)) return true;
+    return false;
+  }
+  static constexpr int count() {
+    int n = 0;
+    for (int i = 0; i < C::FM; ++i)
+      for (int j = 0; j < C::FN; ++j) n += on(i, j) ? 1 : 0;
+    return n;
+  }
+  static constexpr int arows() {
+    int n = 0;
+    for (int i = 0; i < C::FM; ++i) n += arow(i) ? 1 : 0;
+    return n;
+  }
+  static constexpr int bcols() {
+    int n = 0;
+    for (int j = 0; j < C::FN; ++j) n += bcol(j) ? 1 : 0;
+    return n;
+  }
+};
+
+template <class C, int MSK>
 __device__ __forceinline__ void mfma_slice(const half8 (&af)[C::FM], const half8 (&bf)[C::FN],
                                            floatx16 (&acc)[C::FM][C::FN]) {
+  typedef Blocks<C, MSK> K;
 #pragma unroll
   for (int i = 0; i < C::FM; ++i)
 #pragma unroll
     for (int j = 0; j < C::FN; ++j)
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+      if (K::on(i, j))
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
 }
 
 // One K step (four 16-wide k-slices) of MFMAs on LDS stage `st`, with the
@@ -379,16 +417,33 @@ __device__ __forceinline__ half8 bfrag(const f16* __restrict__ st, int boff, int
   return *(const half8*)(st + boff + j * 32 * LDSK + kk * 16);
 }
 
-template <class C, bool STORE, bool LOAD, bool NEXT, bool BKN>
+// Slice 0's order: MFMA q, then its share of the NW LDS writes and of the NW
+// global loads, the shares spread as evenly as they go over the NM MFMAs.
+template <int NM, int NW, int Q>
+__device__ __forceinline__ void slice0_order() {
+  if constexpr (Q < NM) {
+    constexpr int w = ((Q + 1) * NW + NM - 1) / NM - (Q * NW + NM - 1) / NM;
+    __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+    if constexpr (w > 0) {
+      __builtin_amdgcn_sched_group_barrier(kSgDsWrite, w, 0);
+      __builtin_amdgcn_sched_group_barrier(kSgVmemRead, w, 0);
+    }
+    slice0_order<NM, NW, Q + 1>();
+  }
+}
+
+template <class C, bool STORE, bool LOAD, bool NEXT, bool BKN, int MSK>
 __device__ __forceinline__ void mma_step(const f16* __restrict__ st, f16* __restrict__ nxt,
                                          __amdgpu_buffer_rsrc_t Ab, __amdgpu_buffer_rsrc_t Bb,
                                          int lda, int ldb, int m0, int n0, int k0_next, int tid,
                                          half8 (&ra)[C::CH], half8 (&rb)[C::CH], int aoff,
                                          int boff, half8 (&fa0)[C::FM], half8 (&fb0)[C::FN],
                                          floatx16 (&acc)[C::FM][C::FN]) {
-  constexpr int NS = BK / 16, NR = C::FM + (BKN ? 2 : 1) * C::FN, NM = C::FM * C::FN;
-  constexpr int WPM = 2 * C::CH / NM;   // LDS writes (and global loads) per MFMA in slice 0
-  static_assert(WPM * NM == 2 * C::CH, "slice schedules assume these counts");
+  typedef Blocks<C, MSK> K;
+  constexpr int NS = BK / 16;
+  constexpr int NR = K::arows() + (BKN ? 2 : 1) * K::bcols(), NM = K::count();
+  constexpr int NW = 2 * C::CH;   // LDS writes (and global loads) of slice 0
+  static_assert(MSK != kAllBlocks || NW % NM == 0, "slice schedules assume these counts");
   constexpr int NP = NM < NR ? NM : NR;   // read / MFMA pairs of slices 1 and 2
   const f16* a_s = st + aoff;
   half8 af[2][C::FM], bf[2][C::FN];
@@ -402,20 +457,23 @@ __device__ __forceinline__ void mma_step(const f16* __restrict__ st, f16* __rest
     if (kk + 1 < NS) {
 #pragma unroll
       for (int i = 0; i < C::FM; ++i)
-        af[cb ^ 1][i] = *(const half8*)(a_s + i * 32 * LDSK + (kk + 1) * 16);
+        if (K::arow(i)) af[cb ^ 1][i] = *(const half8*)(a_s + i * 32 * LDSK + (kk + 1) * 16);
 #pragma unroll
-      for (int j = 0; j < C::FN; ++j) bf[cb ^ 1][j] = bfrag<C, BKN>(st, boff, j, kk + 1);
+      for (int j = 0; j < C::FN; ++j)
+        if (K::bcol(j)) bf[cb ^ 1][j] = bfrag<C, BKN>(st, boff, j, kk + 1);
     }
     if (kk == NS - 1) {
       __syncthreads();
       if (NEXT) {
 #pragma unroll
-        for (int i = 0; i < C::FM; ++i) fa0[i] = *(const half8*)(nxt + aoff + i * 32 * LDSK);
+        for (int i = 0; i < C::FM; ++i)
+          if (K::arow(i)) fa0[i] = *(const half8*)(nxt + aoff + i * 32 * LDSK);
 #pragma unroll
-        for (int j = 0; j < C::FN; ++j) fb0[j] = bfrag<C, BKN>(nxt, boff, j, 0);
+        for (int j = 0; j < C::FN; ++j)
+          if (K::bcol(j)) fb0[j] = bfrag<C, BKN>(nxt, boff, j, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
-      mfma_slice<C>(af[cb], bf[cb], acc);
+      mfma_slice<C, MSK>(af[cb], bf[cb], acc);
       __builtin_amdgcn_sched_barrier(0);
       continue;
     }
@@ -429,14 +487,14 @@ __device__ __forceinline__ void mma_step(const f16* __restrict__ st, f16* __rest
       if constexpr (BKN) gload_kn<C>(Bb, ldb, n0, k0_next, tid, rb);
       else gload<C>(Bb, ldb, n0, k0_next, tid, rb);
     }
-    mfma_slice<C>(af[cb], bf[cb], acc);
+    mfma_slice<C, MSK>(af[cb], bf[cb], acc);
     if (kk == 0) {
       __builtin_amdgcn_sched_group_barrier(kSgDsRead, NR, 0);
-#pragma unroll
-      for (int q = 0; q < NM; ++q) {
-        __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSgDsWrite, WPM, 0);
-        __builtin_amdgcn_sched_group_barrier(kSgVmemRead, WPM, 0);
+      if constexpr (NM == 0) {
+        __builtin_amdgcn_sched_group_barrier(kSgDsWrite, NW, 0);
+        __builtin_amdgcn_sched_group_barrier(kSgVmemRead, NW, 0);
+      } else {
+        slice0_order<NM, NW, 0>();
       }
     } else {
 #pragma unroll
@@ -449,6 +507,66 @@ __device__ __forceinline__ void mma_step(const f16* __restrict__ st, f16* __rest
     }
     __builtin_amdgcn_sched_barrier(0);
   }
+}
+
+// The K loop of one tile, blocks MSK of the wave tile (wm, wn).  One register
+// set: step t multiplies stage t%2; at its start tile t+1 goes from the
+// registers into the other stage (free since the barrier that ended step t-1)
+// and tile t+2 is requested into the registers.  Every instance passes the
+// same barriers, so the waves of one workgroup may run different instances.
+template <class C, bool BKN, int MSK>
+__device__ __forceinline__ void k_loop(f16* lds, __amdgpu_buffer_rsrc_t Ab,
+                                       __amdgpu_buffer_rsrc_t Bb, const GemmArgs& p, int m0,
+                                       int n0, int tid, int wm, int wn,
+                                       floatx16 (&acc)[C::FM][C::FN]) {
+  typedef Blocks<C, MSK> K;
+  const int lane = tid & 63;
+  const int nk = p.K / BK;
+  half8 ra[C::CH], rb[C::CH];
+  gload<C>(Ab, p.lda, m0, 0, tid, ra);
+  if constexpr (BKN) gload_kn<C>(Bb, p.ldb, n0, 0, tid, rb);
+  else gload<C>(Bb, p.ldb, n0, 0, tid, rb);
+  lstore<C>(lds, tid, ra);
+  if constexpr (BKN) lstore_kn<C>(lds + C::BM * LDSK, tid, rb);
+  else lstore<C>(lds + C::BM * LDSK, tid, rb);
+  if (nk > 1) {
+    gload<C>(Ab, p.lda, m0, BK, tid, ra);
+    if constexpr (BKN) gload_kn<C>(Bb, p.ldb, n0, BK, tid, rb);
+    else gload<C>(Bb, p.ldb, n0, BK, tid, rb);
+  }
+  __syncthreads();
+  // the first slice's fragments of stage 0; each step then reads those of
+  // the stage after it
+  const int aoff = (wm * C::WTM + (lane & 31)) * LDSK + (lane >> 5) * 8;
+  // B, [N][K]: this lane's row and K offset; [K][N]: its transposing-read
+  // address inside the 4 x 16 blocks (row 8 (lane / 32) + (lane % 16) / 4,
+  // column 16 ((lane / 16) % 2) + 4 (lane % 4) of the wave's columns)
+  const int boff = BKN ? ((lane >> 5) * 8 + ((lane & 15) >> 2)) * C::RSB + wn * C::WTN +
+                             ((lane >> 4) & 1) * 16 + (lane & 3) * 4
+                       : (C::BM + wn * C::WTN + (lane & 31)) * LDSK + (lane >> 5) * 8;
+  half8 fa0[C::FM], fb0[C::FN];
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+    if (K::arow(i)) fa0[i] = *(const half8*)(lds + aoff + i * 32 * LDSK);
+#pragma unroll
+  for (int j = 0; j < C::FN; ++j)
+    if (K::bcol(j)) fb0[j] = bfrag<C, BKN>(lds, boff, j, 0);
+  // all steps but the last two store the next tile and load the one after
+  int kt = 0;
+  for (; kt + 2 < nk; ++kt)
+    mma_step<C, true, true, true, BKN, MSK>(lds + (kt & 1) * C::STAGE, lds + ((kt + 1) & 1) * C::STAGE,
+                                            Ab, Bb, p.lda, p.ldb, m0, n0, (kt + 2) * BK, tid, ra,
+                                            rb, aoff, boff, fa0, fb0, acc);
+  if (kt + 1 < nk) {   // next to last: store only
+    mma_step<C, true, false, true, BKN, MSK>(lds + (kt & 1) * C::STAGE, lds + ((kt + 1) & 1) * C::STAGE,
+                                             Ab, Bb, p.lda, p.ldb, m0, n0, 0, tid, ra, rb, aoff,
+                                             boff, fa0, fb0, acc);
+    ++kt;
+  }
+  // last step: its barrier also frees the LDS for the epilogue
+  mma_step<C, false, false, false, BKN, MSK>(lds + (kt & 1) * C::STAGE, lds + ((kt + 1) & 1) * C::STAGE,
+                                             Ab, Bb, p.lda, p.ldb, m0, n0, 0, tid, ra, rb, aoff,
+                                             boff, fa0, fb0, acc);
 }
 
 // ROLE only names the instance (0 Gram, 1 polynomial, 2 symmetric product,
@@ -487,8 +605,10 @@ __global__ __launch_bounds__(C::NT, (C::BM == 256 ? 1 : 2)) void k_gemm(GemmArgs
   // B: N rows of K, or with BKN the [K][N] form, K rows of N
   const __amdgpu_buffer_rsrc_t Bb = operand_rsrc(p.B + (long long)b * p.sB, BKN ? p.K : p.N, p.ldb);
 
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int wm = wid / (C::BN / C::WTN), wn = wid % (C::BN / C::WTN);
+  // the wave index, in a scalar register: the wave's branches below are
+  // uniform
+  const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  int wm = wid / (C::BN / C::WTN), wn = wid % (C::BN / C::WTN);
 
   floatx16 acc[C::FM][C::FN];
 #pragma unroll
@@ -498,54 +618,37 @@ __global__ __launch_bounds__(C::NT, (C::BM == 256 ? 1 : 2)) void k_gemm(GemmArgs
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-  const int nk = p.K / BK;
-  {
-    // One register set.  Step t multiplies stage t%2; at its start tile t+1
-    // goes from the registers into the other stage (free since the barrier
-    // that ended step t-1) and tile t+2 is requested into the registers.
-    half8 ra[C::CH], rb[C::CH];
-    gload<C>(Ab, p.lda, m0, 0, tid, ra);
-    if constexpr (BKN) gload_kn<C>(Bb, p.ldb, n0, 0, tid, rb);
-    else gload<C>(Bb, p.ldb, n0, 0, tid, rb);
-    lstore<C>(lds, tid, ra);
-    if constexpr (BKN) lstore_kn<C>(lds + C::BM * LDSK, tid, rb);
-    else lstore<C>(lds + C::BM * LDSK, tid, rb);
-    if (nk > 1) {
-      gload<C>(Ab, p.lda, m0, BK, tid, ra);
-      if constexpr (BKN) gload_kn<C>(Bb, p.ldb, n0, BK, tid, rb);
-      else gload<C>(Bb, p.ldb, n0, BK, tid, rb);
+  if constexpr (LOWER && C::BM == 256 && C::FM == 4 && C::FN == 2) {
+    if (bi == bj) {
+      // A diagonal tile of a symmetric output: its stored values are the
+      // lower triangle (the upper one is their mirror), so 32 x 32 blocks
+      // wholly above the diagonal need no MFMAs.  By wave tile (wm, wn)
+      // that leaves 8 blocks for (1, 0) and (1, 1), 7 for (0, 0) and (1, 2)
+      // (all but block (0, 1)), 3 for (0, 1) and (1, 3) (blocks (2, 0),
+      // (3, 0), (3, 1)) and none for (0, 2) and (0, 3).  Waves w and w + 4
+      // of a workgroup share a SIMD, so the wave tiles are dealt out to pair
+      // 8 with 0 and 7 with 3: at most 10 blocks of MFMAs per SIMD instead
+      // of 15.  Each computed block keeps its MFMA order (same bits).
+      constexpr int kM7 = 0xFD, kM3 = 0xD0;
+      switch (wid) {
+        case 0: wm = 1; wn = 0; break;
+        case 1: wm = 1; wn = 1; break;
+        case 2: wm = 0; wn = 0; break;
+        case 3: wm = 1; wn = 2; break;
+        case 4: wm = 0; wn = 2; break;
+        case 5: wm = 0; wn = 3; break;
+        case 6: wm = 0; wn = 1; break;
+        default: wm = 1; wn = 3; break;
+      }
+      if (wid < 2) k_loop<C, BKN, kAllBlocks>(lds, Ab, Bb, p, m0, n0, tid, wm, wn, acc);
+      else if (wid < 4) k_loop<C, BKN, kM7>(lds, Ab, Bb, p, m0, n0, tid, wm, wn, acc);
+      else if (wid < 6) k_loop<C, BKN, 0>(lds, Ab, Bb, p, m0, n0, tid, wm, wn, acc);
+      else k_loop<C, BKN, kM3>(lds, Ab, Bb, p, m0, n0, tid, wm, wn, acc);
+    } else {
+      k_loop<C, BKN, kAllBlocks>(lds, Ab, Bb, p, m0, n0, tid, wm, wn, acc);
     }
-    __syncthreads();
-    // the first slice's fragments of stage 0; each step then reads those of
-    // the stage after it
-    const int aoff = (wm * C::WTM + (lane & 31)) * LDSK + (lane >> 5) * 8;
-    // B, [N][K]: this lane's row and K offset; [K][N]: its transposing-read
-    // address inside the 4 x 16 blocks (row 8 (lane / 32) + (lane % 16) / 4,
-    // column 16 ((lane / 16) % 2) + 4 (lane % 4) of the wave's columns)
-    const int boff = BKN ? ((lane >> 5) * 8 + ((lane & 15) >> 2)) * C::RSB + wn * C::WTN +
-                               ((lane >> 4) & 1) * 16 + (lane & 3) * 4
-                         : (C::BM + wn * C::WTN + (lane & 31)) * LDSK + (lane >> 5) * 8;
-    half8 fa0[C::FM], fb0[C::FN];
-#pragma unroll
-    for (int i = 0; i < C::FM; ++i) fa0[i] = *(const half8*)(lds + aoff + i * 32 * LDSK);
-#pragma unroll
-    for (int j = 0; j < C::FN; ++j) fb0[j] = bfrag<C, BKN>(lds, boff, j, 0);
-    // all steps but the last two store the next tile and load the one after
-    int kt = 0;
-    for (; kt + 2 < nk; ++kt)
-      mma_step<C, true, true, true, BKN>(lds + (kt & 1) * C::STAGE, lds + ((kt + 1) & 1) * C::STAGE, Ab,
-                                    Bb, p.lda, p.ldb, m0, n0, (kt + 2) * BK, tid, ra, rb, aoff,
-                                    boff, fa0, fb0, acc);
-    if (kt + 1 < nk) {   // next to last: store only
-      mma_step<C, true, false, true, BKN>(lds + (kt & 1) * C::STAGE, lds + ((kt + 1) & 1) * C::STAGE, Ab,
-                                     Bb, p.lda, p.ldb, m0, n0, 0, tid, ra, rb, aoff, boff, fa0,
-                                     fb0, acc);
-      ++kt;
-    }
-    // last step: its barrier also frees the LDS for the epilogue
-    mma_step<C, false, false, false, BKN>(lds + (kt & 1) * C::STAGE, lds + ((kt + 1) & 1) * C::STAGE, Ab,
-                                     Bb, p.lda, p.ldb, m0, n0, 0, tid, ra, rb, aoff, boff, fa0,
-                                     fb0, acc);
+  } else {
+    k_loop<C, BKN, kAllBlocks>(lds, Ab, Bb, p, m0, n0, tid, wm, wn, acc);
   }
 
   // Epilogue: final fp32 value (alpha, D, gamma I) -> fp16, kept in registers.
