@@ -259,6 +259,7 @@ hipError_t gram(const Shape& P, const XPair& x, f16* R, hipStream_t s) {
   d.A = d.B = xmath(P, x); d.sA = d.sB = P.kp * P.mp; d.lda = d.ldb = (int)P.Lp;
   d.C = R; d.sC = P.sp * P.sp; d.ldc = (int)P.sp;
   d.M = d.N = (int)P.sp; d.K = k_loop(L); d.batch = P.B;
+  d.zrows = d.zcols = (int)sv;   // X_math's padding rows
   d.lower = true; d.epilogue = false;
   d.alpha = 1.0f;
   return launch_gemm(d, s);
@@ -282,6 +283,7 @@ hipError_t symm(const SideLayout& S, const f16* A, const f16* B, const f16* D, f
   d.lower = true; d.epilogue = epi;
   d.alpha = alpha; d.beta = beta; d.gamma = gamma;
   d.gdiag = (int)sv;   // the identity of the unpadded Gram side only
+  d.zrows = d.zcols = (int)sv;   // the padding block stays zero
   return launch_gemm(d, s);
 }
 
@@ -341,6 +343,7 @@ hipError_t rect(const Shape& P, const f16* Q, const XPair& x, const XPair& y, hi
     d.trace_bytes = P.B * (2.0 * sv * sv + 4.0 * sv * L);   // read Q and X, write Y
   }
   d.M = (int)P.sp; d.N = (int)P.Lp; d.K = k_loop(sv); d.batch = P.B;
+  d.zrows = (int)sv; d.zcols = (int)L;   // Q's padding rows, X_math's padding columns
   d.lower = false; d.epilogue = false;
   d.alpha = 1.0f;
   return launch_gemm(d, s);

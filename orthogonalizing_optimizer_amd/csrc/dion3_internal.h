@@ -64,6 +64,12 @@ struct GemmDesc {
   // the polynomial's constant term (which overflows fp16 after about nine
   // iterations without a restart and then turns the cross terms into NaN).
   int gdiag;
+  // Operand rows known to be zero: A's rows >= zrows and B's rows (its
+  // columns with b_kn) >= zcols, the zero padding of the Gram-side
+  // matrices and of X.  Output blocks wholly past them accumulate exactly
+  // +0, which the kernel then keeps without running their MFMAs.  0: none
+  // known (M, N).
+  int zrows, zcols;
   double trace_flops;   // algorithmic flops of this launch, for the timing trace
   double trace_bytes;   // algorithmic HBM bytes of this launch (operands once, outputs once)
   // Fused row-sparse update (rectangular products only): the output in rows

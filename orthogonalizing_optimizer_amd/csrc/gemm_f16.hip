@@ -42,6 +42,7 @@ struct GemmArgs {
   int tilesM, tilesN, tilesPerMat, total;
   float alpha, beta, gamma;
   int gdiag;   // gamma only on diagonal elements below this index
+  int zrows, zcols;   // A's rows and B's rows (columns with a [K][N] B) past these are zero
   int sink;
   BatchPtr<float> W;
   long long ldw;
@@ -343,10 +344,8 @@ __device__ __forceinline__ void lstore(f16* __restrict__ s, int tid, const half8
 constexpr int kSgMfma = 0x008, kSgVmemRead = 0x020, kSgDsRead = 0x100, kSgDsWrite = 0x200;
 
 // Which 32 x 32 blocks of its wave tile a wave computes: bit FN i + j of MSK
-// for block (i, j).  Every block but in the diagonal tiles of symmetric
-// outputs, where blocks wholly above the diagonal are never stored (see
-// k_gemm) and are skipped with their fragment reads.
-constexpr int kAllBlocks = 0xFF;
+// for block (i, j).  Blocks whose values are never stored or are known to be
+// +0 (see k_gemm) are skipped with their fragment reads.
 template <class C, int MSK>
 struct Blocks {
   static constexpr bool on(int i, int j) { return ((MSK >> (i * C::FN + j)) & 1) != 0; }
@@ -443,7 +442,7 @@ __device__ __forceinline__ void mma_step(const f16* __restrict__ st, f16* __rest
   constexpr int NS = BK / 16;
   constexpr int NR = K::arows() + (BKN ? 2 : 1) * K::bcols(), NM = K::count();
   constexpr int NW = 2 * C::CH;   // LDS writes (and global loads) of slice 0
-  static_assert(MSK != kAllBlocks || NW % NM == 0, "slice schedules assume these counts");
+  static_assert(MSK != (1 << (C::FM * C::FN)) - 1 || NW % NM == 0, "slice schedules assume these counts");
   constexpr int NP = NM < NR ? NM : NR;   // read / MFMA pairs of slices 1 and 2
   const f16* a_s = st + aoff;
   half8 af[2][C::FM], bf[2][C::FN];
@@ -569,6 +568,24 @@ __device__ __forceinline__ void k_loop(f16* lds, __amdgpu_buffer_rsrc_t Ab,
                                              boff, fa0, fb0, acc);
 }
 
+// The K loop of the first block set in MSKS that covers `need` (the last
+// one must be every block).
+template <class C, bool BKN, int MSK, int... REST>
+__device__ __forceinline__ void k_loop_cover(int need, f16* lds, __amdgpu_buffer_rsrc_t Ab,
+                                             __amdgpu_buffer_rsrc_t Bb, const GemmArgs& p, int m0,
+                                             int n0, int tid, int wm, int wn,
+                                             floatx16 (&acc)[C::FM][C::FN]) {
+  if constexpr (sizeof...(REST) == 0) {
+    static_assert(MSK == (1 << (C::FM * C::FN)) - 1, "the last set holds every block");
+    k_loop<C, BKN, MSK>(lds, Ab, Bb, p, m0, n0, tid, wm, wn, acc);
+  } else {
+    if ((need & ~MSK) == 0)
+      k_loop<C, BKN, MSK>(lds, Ab, Bb, p, m0, n0, tid, wm, wn, acc);
+    else
+      k_loop_cover<C, BKN, REST...>(need, lds, Ab, Bb, p, m0, n0, tid, wm, wn, acc);
+  }
+}
+
 // ROLE only names the instance (0 Gram, 1 polynomial, 2 symmetric product,
 // 3 rectangular, 4 standard-iteration update, 5 final rectangular product
 // with the fused update) so that profilers report each role as its own
@@ -618,37 +635,46 @@ __global__ __launch_bounds__(C::NT, (C::BM == 256 ? 1 : 2)) void k_gemm(GemmArgs
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-  if constexpr (LOWER && C::BM == 256 && C::FM == 4 && C::FN == 2) {
-    if (bi == bj) {
-      // A diagonal tile of a symmetric output: its stored values are the
-      // lower triangle (the upper one is their mirror), so 32 x 32 blocks
-      // wholly above the diagonal need no MFMAs.  By wave tile (wm, wn)
-      // that leaves 8 blocks for (1, 0) and (1, 1), 7 for (0, 0) and (1, 2)
-      // (all but block (0, 1)), 3 for (0, 1) and (1, 3) (blocks (2, 0),
-      // (3, 0), (3, 1)) and none for (0, 2) and (0, 3).  Waves w and w + 4
-      // of a workgroup share a SIMD, so the wave tiles are dealt out to pair
-      // 8 with 0 and 7 with 3: at most 10 blocks of MFMAs per SIMD instead
-      // of 15.  Each computed block keeps its MFMA order (same bits).
-      constexpr int kM7 = 0xFD, kM3 = 0xD0;
-      switch (wid) {
-        case 0: wm = 1; wn = 0; break;
-        case 1: wm = 1; wn = 1; break;
-        case 2: wm = 0; wn = 0; break;
-        case 3: wm = 1; wn = 2; break;
-        case 4: wm = 0; wn = 2; break;
-        case 5: wm = 0; wn = 3; break;
-        case 6: wm = 0; wn = 1; break;
-        default: wm = 1; wn = 3; break;
+  // A diagonal tile of a symmetric output: its stored values are the lower
+  // triangle (the upper one is their mirror), so 32 x 32 blocks wholly above
+  // the diagonal need no MFMAs.  In the large tile that leaves, by wave tile
+  // (wm, wn), 8 blocks for (1, 0) and (1, 1), 7 for (0, 0) and (1, 2) (all
+  // but block (0, 1)), 3 for (0, 1) and (1, 3) (blocks (2, 0), (3, 0),
+  // (3, 1)) and none for (0, 2) and (0, 3).  Waves w and w + 4 of a
+  // workgroup share a SIMD, so there the wave tiles are dealt out to pair 8
+  // with 0 and 7 with 3: at most 10 blocks of MFMAs per SIMD instead of 15.
+  if (LOWER && C::BM == 256 && C::FM == 4 && C::FN == 2 && bi == bj) {
+    // waves 0..7 take (wm, wn) = (1,0) (1,1) (0,0) (1,2) (0,2) (0,3) (0,1) (1,3)
+    constexpr int kWm = 0x8B;      // bit w: wm of wave w
+    constexpr int kWn = 0xDE84;    // bits 2w, 2w + 1: wn of wave w
+    wm = (kWm >> wid) & 1;
+    wn = (kWn >> (2 * wid)) & 3;
+  }
+  // The blocks this wave computes: not wholly above the diagonal of a
+  // diagonal tile, and not wholly in the rows or columns past zrows / zcols,
+  // whose accumulators stay exactly +0 (an MFMA over zero rows adds signed
+  // zeros to +0, which gives +0).  The wave runs the K loop of the smallest
+  // compiled block set that covers them; every computed block keeps its
+  // MFMA order, so the results are the same bits as with every block.
+  // (Large tile only: in the small tile skipping blocks measured 1-3 %
+  // slower.)
+  if constexpr (C::FM == 4 && C::FN == 2) {
+    int need = 0;
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j) {
+        const int r = wm * C::WTM + i * 32, c = wn * C::WTN + j * 32;   // block corner
+        bool on = m0 + r < p.zrows && n0 + c < p.zcols;
+        if (LOWER && bi == bj) on = on && c <= r;
+        need |= on ? 1 << (i * C::FN + j) : 0;
       }
-      if (wid < 2) k_loop<C, BKN, kAllBlocks>(lds, Ab, Bb, p, m0, n0, tid, wm, wn, acc);
-      else if (wid < 4) k_loop<C, BKN, kM7>(lds, Ab, Bb, p, m0, n0, tid, wm, wn, acc);
-      else if (wid < 6) k_loop<C, BKN, 0>(lds, Ab, Bb, p, m0, n0, tid, wm, wn, acc);
-      else k_loop<C, BKN, kM3>(lds, Ab, Bb, p, m0, n0, tid, wm, wn, acc);
-    } else {
-      k_loop<C, BKN, kAllBlocks>(lds, Ab, Bb, p, m0, n0, tid, wm, wn, acc);
-    }
+    // none; row 0; the diagonal tile's 3-block set; rows 0-1; column 0;
+    // rows 0-2; all but block (0, 1); all
+    k_loop_cover<C, BKN, 0x00, 0x03, 0xD0, 0x0F, 0x55, 0x3F, 0xFD, 0xFF>(need, lds, Ab, Bb, p, m0,
+                                                                        n0, tid, wm, wn, acc);
   } else {
-    k_loop<C, BKN, kAllBlocks>(lds, Ab, Bb, p, m0, n0, tid, wm, wn, acc);
+    k_loop<C, BKN, (1 << (C::FM * C::FN)) - 1>(lds, Ab, Bb, p, m0, n0, tid, wm, wn, acc);
   }
 
   // Epilogue: final fp32 value (alpha, D, gamma I) -> fp16, kept in registers.
@@ -863,6 +889,8 @@ hipError_t launch(const GemmDesc& d, hipStream_t s) {
   p.total = (int)total;
   p.alpha = d.alpha; p.beta = d.beta; p.gamma = d.gamma;
   p.gdiag = d.gdiag > 0 ? d.gdiag : d.M;
+  p.zrows = d.zrows > 0 ? d.zrows : d.M;
+  p.zcols = d.zcols > 0 ? d.zcols : d.N;
   p.sink = d.sink; p.W = d.W; p.ldw = d.ldw; p.idx = d.idx; p.lr = d.lr; p.Oout = d.Oout;
   p.sO = d.sO;
   p.kval = d.kval; p.mval = d.mval; p.nrows = d.nrows;

@@ -80,3 +80,34 @@ def test_symm_poly_every_tile_path(B, s):
         A2 = Af @ Af
         assert rel(P[i], A2) <= 2e-3, i
         assert rel(C[i], c * A2 + b_ * Af + a * np.eye(s)) <= 2e-3, i
+
+
+# Gram-NS on the large tile where the Gram side is not a multiple of 256,
+# so the last tile row (and, for the multiply-back of a transposed Gram,
+# the last tile column) lies partly in the zero padding, whose 32 x 32
+# blocks the large tile does not compute.  The same matrices in a launch
+# small enough for the 128 tile (which computes every block) must give the
+# same bits, and both must match the fp64 oracle.
+#   90 x 700 x 1024:  side 700 (6 lower tiles of 256 per matrix, 540 in all)
+#   90 x 1100 x 600:  k > m, side 600, rows of length 1100 (multiply-back
+#                     N = 1152: a last tile column with 76 real columns)
+PAD_CASES = [(90, 700, 1024), (90, 1100, 600)]
+
+
+@pytest.mark.parametrize("B,k,m", PAD_CASES)
+def test_gram_ns_large_tile_padding_blocks(B, k, m):
+    from oracle import dion3_oracle as orc
+    side = min(k, m)
+    assert lower_tiles(side, 256) * B >= 512
+    say("gram-ns padding blocks", B, k, m, "side", side)
+    X = (host_gaussian((B, k, m), [62, B, k, m]) * 0.05).astype(np.float16)
+    tiled = d3.ns_cfg(path=d3.PATH_TILED)
+    O = d3.gram_ns(dev(X), tiled).cpu().numpy()
+    pick = [0, B // 2, B - 1]
+    assert lower_tiles(side, 256) * len(pick) < 512   # the small tile
+    O_small = d3.gram_ns(dev(X[pick]), tiled).cpu().numpy()
+    for j, b in enumerate(pick):
+        assert np.array_equal(O[b].view(np.uint16), O_small[j].view(np.uint16)), b
+    co = orc.default_coeffs()
+    want = orc.ns_gram(X[0].astype(np.float64), co, (3,))
+    assert rel(O[0], want) <= 5e-3
