@@ -83,17 +83,19 @@ long long side_of(const Shape& P) { return P.tr ? P.m : P.k; }
 // Relative time of one s x s product launch over `batch` matrices of padded
 // side sp, in rounds of 256-wide tiles over the 256 CUs: the launch takes the
 // 256 tile from 512 such tiles on, else the 128 tile two per CU, whose round
-// of 512 tiles (half the work of a 256 round) measured about half as long.
-// Merging two groups' launches pays off only when it does not add a round
-// (on the 7B set, attention and down-projection groups at f = 1/4: 1280 +
-// 320 tiles run 6.25 rounds merged against 5 + a small-tile launch apart,
-// measured 0.2 ms per step slower merged; the 1B and 14B sets gain 0.2 ms).
+// of 512 tiles (half the work of a 256 round) measured two thirds as long
+// (symmetric products at side 1024: 29 us per small-tile round, 43.6 us per
+// large-tile round).  Merging two groups' launches pays off only when it
+// adds no more than that: the 1B and 14B sets share (-0.2 ms per step), and
+// so does the 7B set at f = 1/4 (attention and down-projection groups, 1280
+// + 320 tiles: 7 rounds merged against 5 plus a small-tile launch of 3
+// small rounds apart, measured 0.2 ms per step faster merged).
 double side_cost(long long sp, long long batch) {
   const long long t = (sp + 255) / 256, u = sp / 128;
   const long long big = t * (t + 1) / 2 * batch;
   if (big >= 512) return (double)((big + 255) / 256);
   const long long small = u * (u + 1) / 2 * batch;
-  return 0.5 * (double)((small + 511) / 512);
+  return 2.0 * (double)((small + 511) / 512) / 3.0;
 }
 
 // Regions in order: every group's rows and X pairs, then the side sets.  A
@@ -125,7 +127,7 @@ void make_layout(CallLayout& L, int ng, const Shape* shapes, const bool* no_side
     while (j < L.nside &&
            !(L.sd[j].sp == P.sp && L.sd[j].s == side_of(P) &&
              side_cost(P.sp, L.sd[j].batch + P.B) <=
-                 side_cost(P.sp, L.sd[j].batch) + side_cost(P.sp, P.B)))
+                 side_cost(P.sp, L.sd[j].batch) + side_cost(P.sp, P.B) + 1e-9))
       ++j;
     if (j == L.nside) {
       L.sd[j].sp = P.sp;
