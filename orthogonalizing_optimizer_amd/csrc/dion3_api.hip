@@ -564,6 +564,7 @@ struct GroupArgs {
 // been made before this runs.
 dion3_status run_step(const CallLayout& L, const GroupArgs* A, float mu, const dion3_ns_cfg& cfg,
                       const dion3_norm_cfg* norm, char* w, hipStream_t s) {
+  TraceChain chain(s);
   GroupRun runs[DION3_MAX_GROUPS];
   for (int i = 0; i < L.ng; ++i) {
     const GroupLayout& G = L.g[i];
@@ -629,14 +630,18 @@ dion3_status run_step(const CallLayout& L, const GroupArgs* A, float mu, const d
       HIP_TRY(launch_normalize(Obuf, sO, P.B, (int)P.k, (int)P.m, idx, a.V, norm->beta2, norm->eps,
                                a.W, a.ld, a.lr, runs[i].sink.part, part_ready,
                                (float2*)(w + G.o_l1), s));
-      if (a.O_out)
+      if (a.O_out) {
+        trace_break();   // an untimed copy between timed kernels
         HIP_TRY(hipMemcpy2DAsync(a.O_out, (size_t)P.k * P.m * sizeof(uint16_t), Obuf,
                                  (size_t)sO * sizeof(uint16_t), (size_t)P.k * P.m * sizeof(uint16_t),
                                  (size_t)P.B, hipMemcpyDeviceToDevice, s));
+      }
     }
-    if (a.idx_out)
+    if (a.idx_out) {
+      trace_break();
       HIP_TRY(hipMemcpyAsync(a.idx_out, idx, (size_t)P.B * P.k * sizeof(int32_t),
                              hipMemcpyDeviceToDevice, s));
+    }
   }
   return DION3_OK;
 }
@@ -845,6 +850,7 @@ dion3_status dion3_gram_ns(const uint16_t* X, uint16_t* O, int32_t batch, int64_
   r.x = xa;
   r.xalt = xb;
   r.sink = {{nullptr, 0, nullptr}, 0, idx, 0.0f, (f16*)O, k * m, nullptr};
+  TraceChain chain(s);   // (the untimed kernels above are all enqueued)
   return orthogonalize(L, cfg, w, &r, s);
 }
 

@@ -101,13 +101,22 @@ dion3_status note_hip_error(hipError_t e);
 hipError_t launch_gemm(const GemmDesc& d, hipStream_t s);
 
 // Optional kernel timing trace (benchmarks): while enabled, each launch is
-// bracketed by two HIP events on its stream and its algorithmic work noted.
+// timed by HIP events on its stream and its algorithmic work noted.  Inside
+// one library call (a TraceChain on the call's stream) the kernels follow
+// one another with nothing in between, so a kernel's start is the previous
+// kernel's end event and only one event is recorded per kernel; anything
+// else enqueued in between must call trace_break() first.
 struct TraceScope {
   TraceScope(const char* name, double flops, double bytes, hipStream_t s);
   ~TraceScope();
   int slot;
   hipStream_t stream;
 };
+struct TraceChain {
+  explicit TraceChain(hipStream_t s);
+  ~TraceChain();
+};
+void trace_break();
 
 // Per-row l1 (optional) and sum of squares in fp64, one wave per row.
 hipError_t launch_row_score_f32(BatchPtr<const float> M, int batch, int n, int m, long long ld,
