@@ -7,6 +7,8 @@
 #include "../../include/dion3.h"
 #include "dion3_internal.h"
 
+#include <utility>
+
 using namespace dion3;
 
 namespace {
@@ -252,7 +254,7 @@ const f16* xmath(const Shape& P, const XPair& x) { return P.tr ? x.XT : x.X; }
 const f16* xmathT(const Shape& P, const XPair& x) { return P.tr ? x.X : x.XT; }
 
 // R = X_math X_math^T.
-hipError_t gram(const Shape& P, const XPair& x, f16* R, hipStream_t s) {
+GemmDesc gram_desc(const Shape& P, const XPair& x, f16* R) {
   const double sv = s_of(P), L = L_of(P);
   GemmDesc d = {};
   d.trace_flops = P.B * sv * sv * L;
@@ -264,13 +266,35 @@ hipError_t gram(const Shape& P, const XPair& x, f16* R, hipStream_t s) {
   d.zrows = d.zcols = (int)sv;   // X_math's padding rows
   d.lower = true; d.epilogue = false;
   d.alpha = 1.0f;
+  return d;
+}
+
+hipError_t gram(const Shape& P, const XPair& x, f16* R, hipStream_t s) {
+  const GemmDesc d = gram_desc(P, x, R);
   return launch_gemm(d, s);
+}
+
+// Lower-triangle products of one kind for several groups or side sets, as
+// few launches as kGemmMaxSeg allows; each launch takes the products with
+// the longest tiles (largest inner dimension) first.
+hipError_t launch_lower(GemmDesc* d, int n, hipStream_t s) {
+  for (int i = 1; i < n; ++i)   // insertion sort, stable, by K descending
+    for (int j = i; j > 0 && d[j].K > d[j - 1].K; --j) {
+      const GemmDesc t = d[j];
+      d[j] = d[j - 1];
+      d[j - 1] = t;
+    }
+  for (int i = 0; i < n; i += kGemmMaxSeg) {
+    const hipError_t e = launch_gemm_multi(d + i, n - i < kGemmMaxSeg ? n - i : kGemmMaxSeg, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 // C = alpha A B + beta D + gamma I for symmetric commuting s x s matrices,
 // over every matrix of a side set.
-hipError_t symm(const SideLayout& S, const f16* A, const f16* B, const f16* D, f16* C, float alpha,
-                float beta, float gamma, bool epi, hipStream_t s) {
+GemmDesc symm_desc(const SideLayout& S, const f16* A, const f16* B, const f16* D, f16* C,
+                   float alpha, float beta, float gamma, bool epi) {
   const double sv = dbl(S.s);
   GemmDesc d = {};
   d.trace_flops = S.batch * sv * sv * sv;
@@ -286,6 +310,12 @@ hipError_t symm(const SideLayout& S, const f16* A, const f16* B, const f16* D, f
   d.alpha = alpha; d.beta = beta; d.gamma = gamma;
   d.gdiag = (int)sv;   // the identity of the unpadded Gram side only
   d.zrows = d.zcols = (int)sv;   // the padding block stays zero
+  return d;
+}
+
+hipError_t symm(const SideLayout& S, const f16* A, const f16* B, const f16* D, f16* C, float alpha,
+                float beta, float gamma, bool epi, hipStream_t s) {
+  const GemmDesc d = symm_desc(S, A, B, D, C, alpha, beta, gamma, epi);
   return launch_gemm(d, s);
 }
 
@@ -414,50 +444,80 @@ f16* slice(f16* base, const SideLayout& S, const GroupLayout& G) {
   return base + G.side_off * S.sp * S.sp;
 }
 
-// Gram Newton-Schulz on the normalized, padded X of every group of one side
-// set ("Dion3: Full-Stack Orthogonal Updates", agihunt.info, level-1
+// Gram Newton-Schulz on the normalized, padded X of every group of every
+// side set ("Dion3: Full-Stack Orthogonal Updates", agihunt.info, level-1
 // paragraph).  Every matrix here is a polynomial in the first Gram, so all
 // products commute, are symmetric, and only their lower triangles are
-// computed.  The products that read X (the Grams, the restart's X <- Q X
-// and the final multiply-back) run per group; the s x s products run once
-// over the whole set.  The final product hands O to each group's sink.
-dion3_status gram_ns_set(const dion3_ns_cfg& cfg, const SideLayout& S, char* w, GroupRun* r, int nr,
-                         hipStream_t s) {
-  f16 *R = (f16*)(w + S.o_R), *Z = (f16*)(w + S.o_Z), *Tm = (f16*)(w + S.o_T);
-  f16 *Q = (f16*)(w + S.o_Q0), *Qn = (f16*)(w + S.o_Q1);
-  for (int i = 0; i < nr; ++i) HIP_TRY(gram(r[i].G->P, r[i].x, slice(R, S, *r[i].G), s));
+// computed.  The sets run the same schedule in step: each s x s product is
+// one launch over every set, and each Gram one launch over every group (the
+// tails of several small launches become one).  The restart's X <- Q X and
+// the final multiply-back run per group; the final product hands O to each
+// group's sink.
+struct SetRun {
+  const SideLayout* S;
+  GroupRun* r;
+  int nr;
+  f16 *R, *Z, *Tm, *Q, *Qn;
+};
+
+dion3_status gram_ns_sets(const dion3_ns_cfg& cfg, SetRun* set, int ns, hipStream_t s) {
+  GemmDesc d[DION3_MAX_GROUPS];
+  auto grams = [&]() -> hipError_t {
+    int n = 0;
+    for (int j = 0; j < ns; ++j)
+      for (int i = 0; i < set[j].nr; ++i) {
+        const GroupRun& r = set[j].r[i];
+        d[n++] = gram_desc(r.G->P, r.x, slice(set[j].R, *set[j].S, *r.G));
+      }
+    return launch_lower(d, n, s);
+  };
+  // one s x s product per set: C_j = alpha A_j B_j + beta D_j + gamma I
+  auto sides = [&](f16* SetRun::*A, f16* SetRun::*B, f16* SetRun::*D, f16* SetRun::*C, float alpha,
+                   float beta, float gamma, bool epi) -> hipError_t {
+    for (int j = 0; j < ns; ++j)
+      d[j] = symm_desc(*set[j].S, set[j].*A, set[j].*B, D ? set[j].*D : nullptr, set[j].*C, alpha,
+                       beta, gamma, epi);
+    return launch_lower(d, ns, s);
+  };
+  HIP_TRY(grams());
   bool q_identity = true;
   const int T = cfg.iters;
   for (int t = 1; t <= T; ++t) {
     if (restart_at(cfg, t)) {      // X <- Q X, R <- X X^T, Q <- I
-      if (!q_identity) {
-        for (int i = 0; i < nr; ++i)
-          HIP_TRY(rect(r[i].G->P, slice(Q, S, *r[i].G), r[i].x, r[i].xalt, s));
-        swap_pairs(r, nr);
-      }
-      for (int i = 0; i < nr; ++i) HIP_TRY(gram(r[i].G->P, r[i].x, slice(R, S, *r[i].G), s));
+      if (!q_identity)
+        for (int j = 0; j < ns; ++j) {
+          for (int i = 0; i < set[j].nr; ++i) {
+            GroupRun& r = set[j].r[i];
+            HIP_TRY(rect(r.G->P, slice(set[j].Q, *set[j].S, *r.G), r.x, r.xalt, s));
+          }
+          swap_pairs(set[j].r, set[j].nr);
+        }
+      HIP_TRY(grams());
       q_identity = true;
     }
     const float a = cfg.abc[t - 1][0], b = cfg.abc[t - 1][1], c = cfg.abc[t - 1][2];
     // Z = a I + b R + c R^2  (the "A^2 + B" product)
-    HIP_TRY(symm(S, R, R, R, Z, c, b, a, true, s));
-    f16* Zv;
+    HIP_TRY(sides(&SetRun::R, &SetRun::R, &SetRun::R, &SetRun::Z, c, b, a, true));
+    f16* SetRun::*Zv;
     if (q_identity) {           // Q <- Z Q with Q = I: just adopt Z
-      f16* tmp = Q; Q = Z; Z = tmp;
-      Zv = Q;
+      for (int j = 0; j < ns; ++j) std::swap(set[j].Q, set[j].Z);
+      Zv = &SetRun::Q;
       q_identity = false;
     } else {
-      HIP_TRY(symm(S, Z, Q, nullptr, Qn, 1.0f, 0.0f, 0.0f, false, s));
-      f16* tmp = Q; Q = Qn; Qn = tmp;
-      Zv = Z;
+      HIP_TRY(sides(&SetRun::Z, &SetRun::Q, nullptr, &SetRun::Qn, 1.0f, 0.0f, 0.0f, false));
+      for (int j = 0; j < ns; ++j) std::swap(set[j].Q, set[j].Qn);
+      Zv = &SetRun::Z;
     }
     if (t < T && !restart_at(cfg, t + 1)) {   // R <- Z R Z
-      HIP_TRY(symm(S, Zv, R, nullptr, Tm, 1.0f, 0.0f, 0.0f, false, s));
-      HIP_TRY(symm(S, Tm, Zv, nullptr, R, 1.0f, 0.0f, 0.0f, false, s));
+      HIP_TRY(sides(Zv, &SetRun::R, nullptr, &SetRun::Tm, 1.0f, 0.0f, 0.0f, false));
+      HIP_TRY(sides(&SetRun::Tm, Zv, nullptr, &SetRun::R, 1.0f, 0.0f, 0.0f, false));
     }
   }
-  for (int i = 0; i < nr; ++i)
-    HIP_TRY(rect(r[i].G->P, slice(Q, S, *r[i].G), r[i].x, r[i].xalt, s, &r[i].sink));
+  for (int j = 0; j < ns; ++j)
+    for (int i = 0; i < set[j].nr; ++i) {
+      GroupRun& r = set[j].r[i];
+      HIP_TRY(rect(r.G->P, slice(set[j].Q, *set[j].S, *r.G), r.x, r.xalt, s, &r.sink));
+    }
   return DION3_OK;
 }
 
@@ -513,18 +573,25 @@ dion3_status orthogonalize(const CallLayout& L, const dion3_ns_cfg& cfg, char* w
                                  r.sink.sO, (int)P.k, (int)P.m, (int)P.n, gram_ns_flops(P, cfg),
                                  s));
   }
+  GroupRun members[DION3_MAX_GROUPS];
+  SetRun sets[DION3_MAX_GROUPS];
+  int nm = 0, ns = 0;
   for (int j = 0; j < L.nside; ++j) {
-    GroupRun members[DION3_MAX_GROUPS];
-    int nr = 0;
+    GroupRun* first = members + nm;
     for (int i = 0; i < L.ng; ++i)
-      if (L.g[i].side == j && !use_fused(L.g[i].P, cfg)) members[nr++] = runs[i];
+      if (L.g[i].side == j && !use_fused(L.g[i].P, cfg)) members[nm++] = runs[i];
+    const int nr = (int)(members + nm - first);
     if (nr == 0) continue;
-    const dion3_status st = cfg.method == DION3_NS_STANDARD
-                                ? standard_ns_set(cfg, L.sd[j], w, members, nr, s)
-                                : gram_ns_set(cfg, L.sd[j], w, members, nr, s);
-    if (st != DION3_OK) return st;
+    if (cfg.method == DION3_NS_STANDARD) {
+      const dion3_status st = standard_ns_set(cfg, L.sd[j], w, first, nr, s);
+      if (st != DION3_OK) return st;
+      continue;
+    }
+    const SideLayout& S = L.sd[j];
+    sets[ns++] = {&S, first, nr, (f16*)(w + S.o_R), (f16*)(w + S.o_Z), (f16*)(w + S.o_T),
+                  (f16*)(w + S.o_Q0), (f16*)(w + S.o_Q1)};
   }
-  return DION3_OK;
+  return ns ? gram_ns_sets(cfg, sets, ns, s) : DION3_OK;
 }
 
 // The X pair that the orthogonalization no longer reads once it has started

@@ -99,6 +99,13 @@ dion3_status note_hip_error(hipError_t e);
 // Launches the product; records it in the timing trace (when enabled) under
 // "<role>_<tile edge>", e.g. "gemm_symm_256".
 hipError_t launch_gemm(const GemmDesc& d, hipStream_t s);
+// Up to kGemmMaxSeg lower-triangle products of one role and epilogue
+// (alpha, beta, gamma, addend or none) in one launch: each XCD takes a
+// contiguous share of every product's tiles, the products in the given
+// order (longest tiles first keeps the tail short).  The large tile is used
+// when all of them together have 512 large tiles.
+constexpr int kGemmMaxSeg = 4;
+hipError_t launch_gemm_multi(const GemmDesc* d, int n, hipStream_t s);
 
 // Optional kernel timing trace (benchmarks): while enabled, each launch is
 // timed by HIP events on its stream and its algorithmic work noted.  Inside

@@ -34,15 +34,25 @@ constexpr int LDSK = BK + 8;   // halves per LDS operand row
 typedef f16 half8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
-struct GemmArgs {
-  const f16* A; const f16* B; f16* C; f16* CT; const f16* D;
-  long long sA, sB, sC, sCT, sD;
-  int lda, ldb, ldc, ldct, ldd;
+// One product of a launch (a segment): its operands, sizes and tile counts.
+struct Seg {
+  const f16* A; const f16* B; f16* C; const f16* D;
+  long long sA, sB, sC, sD;
+  int lda, ldb, ldc, ldd;
   int M, N, K;
-  int tilesM, tilesN, tilesPerMat, total;
-  float alpha, beta, gamma;
+  int tilesM, tilesN, tilesPerMat, ntiles;
   int gdiag;   // gamma only on diagonal elements below this index
   int zrows, zcols;   // A's rows and B's rows (columns with a [K][N] B) past these are zero
+};
+
+struct GemmArgs {
+  int nseg;
+  Seg seg[kGemmMaxSeg];
+  f16* CT;            // (one-segment launches only)
+  long long sCT;
+  int ldct;
+  int total;
+  float alpha, beta, gamma;
   int sink;
   BatchPtr<float> W;
   long long ldw;
@@ -515,7 +525,7 @@ __device__ __forceinline__ void mma_step(const f16* __restrict__ st, f16* __rest
 // same barriers, so the waves of one workgroup may run different instances.
 template <class C, bool BKN, int MSK>
 __device__ __forceinline__ void k_loop(f16* lds, __amdgpu_buffer_rsrc_t Ab,
-                                       __amdgpu_buffer_rsrc_t Bb, const GemmArgs& p, int m0,
+                                       __amdgpu_buffer_rsrc_t Bb, const Seg& p, int m0,
                                        int n0, int tid, int wm, int wn,
                                        floatx16 (&acc)[C::FM][C::FN]) {
   typedef Blocks<C, MSK> K;
@@ -572,7 +582,7 @@ __device__ __forceinline__ void k_loop(f16* lds, __amdgpu_buffer_rsrc_t Ab,
 // one must be every block).
 template <class C, bool BKN, int MSK, int... REST>
 __device__ __forceinline__ void k_loop_cover(int need, f16* lds, __amdgpu_buffer_rsrc_t Ab,
-                                             __amdgpu_buffer_rsrc_t Bb, const GemmArgs& p, int m0,
+                                             __amdgpu_buffer_rsrc_t Bb, const Seg& p, int m0,
                                              int n0, int tid, int wm, int wn,
                                              floatx16 (&acc)[C::FM][C::FN]) {
   if constexpr (sizeof...(REST) == 0) {
@@ -583,6 +593,31 @@ __device__ __forceinline__ void k_loop_cover(int need, f16* lds, __amdgpu_buffer
       k_loop<C, BKN, MSK>(lds, Ab, Bb, p, m0, n0, tid, wm, wn, acc);
     else
       k_loop_cover<C, BKN, REST...>(need, lds, Ab, Bb, p, m0, n0, tid, wm, wn, acc);
+  }
+}
+
+// Workgroup w's segment and its tile there.  Each XCD (the workgroups with
+// one value of w % 8) takes a contiguous share of every segment's tiles, the
+// segments in order, so each XCD gets the same mix; a segment's ntiles % 8
+// leftover tiles go one each to consecutive XCDs, continuing where the
+// previous segment's left off, so every XCD gets exactly the workgroups the
+// hardware sends it.  With one segment this is XCD x taking tiles
+// x q + min(x, r) ...
+__device__ __forceinline__ void locate(const GemmArgs& p, int w, int& si, int& lid) {
+  const int xcd = w & 7;
+  int slot = w >> 3, off = 0;
+  for (int s = 0;; ++s) {
+    const int n = p.seg[s].ntiles, q = n >> 3, r = n & 7;
+    int before = 0;   // leftover tiles of this segment on XCDs below this one
+    for (int y = 0; y < xcd; ++y) before += ((y - off) & 7) < r ? 1 : 0;
+    const int cnt = q + (((xcd - off) & 7) < r ? 1 : 0);
+    if (slot < cnt || s == p.nseg - 1) {
+      si = s;
+      lid = xcd * q + before + slot;
+      return;
+    }
+    slot -= cnt;
+    off = (off + r) & 7;
   }
 }
 
@@ -597,11 +632,18 @@ __global__ __launch_bounds__(C::NT, (C::BM == 256 ? 1 : 2)) void k_gemm(GemmArgs
   // Workgroups are dispatched round-robin over the 8 XCDs; renumber them so
   // that each XCD works on a contiguous run of tiles (mostly of the same
   // matrices), which keeps their operand panels in that XCD's L2.
-  const int w = blockIdx.x, G = p.total;
-  const int q = G >> 3, rem = G & 7, xcd = w & 7, slot = w >> 3;
-  const int lid = xcd * q + min(xcd, rem) + slot;
-  const int b = lid / p.tilesPerMat;
-  const int t = lid - b * p.tilesPerMat;
+  // (Only lower-triangle products share launches; the others have one
+  // segment and take the plain mapping, which keeps their registers free.)
+  int si = 0, lid;
+  if constexpr (LOWER) {
+    locate(p, blockIdx.x, si, lid);
+  } else {
+    const int w = blockIdx.x, q = p.total >> 3, rem = p.total & 7, xcd = w & 7;
+    lid = xcd * q + min(xcd, rem) + (w >> 3);
+  }
+  const Seg& g = p.seg[si];
+  const int b = lid / g.tilesPerMat;
+  const int t = lid - b * g.tilesPerMat;
   int bi, bj;
   if (LOWER) {
     tri_index(t, bi, bj);
@@ -609,18 +651,18 @@ __global__ __launch_bounds__(C::NT, (C::BM == 256 ? 1 : 2)) void k_gemm(GemmArgs
     // groups of 8 tile rows, column-major inside a group: consecutive tiles
     // share the B panel and cycle through 8 A panels
     const int GR = 8;
-    const int per_group = GR * p.tilesN;
+    const int per_group = GR * g.tilesN;
     const int g0 = (t / per_group) * GR;
-    const int gsz = min(p.tilesM - g0, GR);
+    const int gsz = min(g.tilesM - g0, GR);
     const int r = t - (t / per_group) * per_group;
     bi = g0 + r % gsz;
     bj = r / gsz;
   }
   const int m0 = bi * C::BM, n0 = bj * C::BN;
 
-  const __amdgpu_buffer_rsrc_t Ab = operand_rsrc(p.A + (long long)b * p.sA, p.M, p.lda);
+  const __amdgpu_buffer_rsrc_t Ab = operand_rsrc(g.A + (long long)b * g.sA, g.M, g.lda);
   // B: N rows of K, or with BKN the [K][N] form, K rows of N
-  const __amdgpu_buffer_rsrc_t Bb = operand_rsrc(p.B + (long long)b * p.sB, BKN ? p.K : p.N, p.ldb);
+  const __amdgpu_buffer_rsrc_t Bb = operand_rsrc(g.B + (long long)b * g.sB, BKN ? g.K : g.N, g.ldb);
 
   // the wave index, in a scalar register: the wave's branches below are
   // uniform
@@ -665,16 +707,16 @@ __global__ __launch_bounds__(C::NT, (C::BM == 256 ? 1 : 2)) void k_gemm(GemmArgs
 #pragma unroll
       for (int j = 0; j < C::FN; ++j) {
         const int r = wm * C::WTM + i * 32, c = wn * C::WTN + j * 32;   // block corner
-        bool on = m0 + r < p.zrows && n0 + c < p.zcols;
+        bool on = m0 + r < g.zrows && n0 + c < g.zcols;
         if (LOWER && bi == bj) on = on && c <= r;
         need |= on ? 1 << (i * C::FN + j) : 0;
       }
     // none; row 0; the diagonal tile's 3-block set; rows 0-1; column 0;
     // rows 0-2; all but block (0, 1); all
-    k_loop_cover<C, BKN, 0x00, 0x03, 0xD0, 0x0F, 0x55, 0x3F, 0xFD, 0xFF>(need, lds, Ab, Bb, p, m0,
+    k_loop_cover<C, BKN, 0x00, 0x03, 0xD0, 0x0F, 0x55, 0x3F, 0xFD, 0xFF>(need, lds, Ab, Bb, g, m0,
                                                                         n0, tid, wm, wn, acc);
   } else {
-    k_loop<C, BKN, (1 << (C::FM * C::FN)) - 1>(lds, Ab, Bb, p, m0, n0, tid, wm, wn, acc);
+    k_loop<C, BKN, (1 << (C::FM * C::FN)) - 1>(lds, Ab, Bb, g, m0, n0, tid, wm, wn, acc);
   }
 
   // Epilogue: final fp32 value (alpha, D, gamma I) -> fp16, kept in registers.
@@ -697,14 +739,14 @@ __global__ __launch_bounds__(C::NT, (C::BM == 256 ? 1 : 2)) void k_gemm(GemmArgs
   if (EPI) {
     constexpr int DST = C::BM + 8;
     static_assert(C::BN * DST <= C::LDS, "addend block fits");
-    if (p.D) {
-      const __amdgpu_buffer_rsrc_t Dr = operand_rsrc(p.D + (long long)b * p.sD, p.N, p.ldd);
+    if (g.D) {
+      const __amdgpu_buffer_rsrc_t Dr = operand_rsrc(g.D + (long long)b * g.sD, g.N, g.ldd);
       constexpr int NCHD = C::BN * (C::BM / 8) / C::NT;   // 16-byte chunks per thread
       int4v dchunk[NCHD];
 #pragma unroll
       for (int q = 0; q < NCHD; ++q) {
         const int e = tid + q * C::NT, c = e / (C::BM / 8), r8 = e % (C::BM / 8);
-        const unsigned off = (unsigned)(min(n0 + c, p.N) * p.ldd + m0 + 8 * r8) * 2u;
+        const unsigned off = (unsigned)(min(n0 + c, g.N) * g.ldd + m0 + 8 * r8) * 2u;
         dchunk[q] = __builtin_amdgcn_raw_buffer_load_b128(Dr, off, 0, 0);
       }
 #pragma unroll
@@ -751,7 +793,7 @@ __global__ __launch_bounds__(C::NT, (C::BM == 256 ? 1 : 2)) void k_gemm(GemmArgs
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             val[e] = __builtin_fmaf(val[e], p.alpha, p.beta * (float)dv[e]);
-            if (gr + e == gc && gc < p.gdiag) val[e] += p.gamma;
+            if (gr + e == gc && gc < g.gdiag) val[e] += p.gamma;
             // Keep the fp32 result as written (round to fp32, then to fp16):
             // otherwise the compiler may fuse the fma with the conversion
             // into one mixed-precision fma that rounds once, in some
@@ -767,11 +809,11 @@ __global__ __launch_bounds__(C::NT, (C::BM == 256 ? 1 : 2)) void k_gemm(GemmArgs
   // Outputs: rows (C[m0 + r][n0 + c], or the fused update) and columns (the
   // mirror of an off-diagonal lower tile into C, or the transposed output
   // CT[n0 + c][m0 + r]).
-  f16* __restrict__ Cb = p.C ? p.C + (long long)b * p.sC : nullptr;
+  f16* __restrict__ Cb = g.C ? g.C + (long long)b * g.sC : nullptr;
   f16* __restrict__ Tb = nullptr;
   int ldt = 0;
   if (LOWER) {
-    if (bi != bj) { Tb = Cb; ldt = p.ldc; }
+    if (bi != bj) { Tb = Cb; ldt = g.ldc; }
   } else if (p.CT) {
     Tb = p.CT + (long long)b * p.sCT;
     ldt = p.ldct;
@@ -841,8 +883,8 @@ __global__ __launch_bounds__(C::NT, (C::BM == 256 ? 1 : 2)) void k_gemm(GemmArgs
       for (int e = tid; e < C::BM * (C::BN / 8); e += C::NT) {
         const int r = e / (C::BN / 8), c8 = e - r * (C::BN / 8);
         const int gr = m0 + r, gc = n0 + c8 * 8;
-        if (gr < p.M && gc < p.N)
-          *(half8*)(Cb + (long long)gr * p.ldc + gc) = *(const half8*)(S + r * C::EP + c8 * 8);
+        if (gr < g.M && gc < g.N)
+          *(half8*)(Cb + (long long)gr * g.ldc + gc) = *(const half8*)(S + r * C::EP + c8 * 8);
       }
     }
   }
@@ -868,43 +910,57 @@ __global__ __launch_bounds__(C::NT, (C::BM == 256 ? 1 : 2)) void k_gemm(GemmArgs
     for (int e = tid; e < C::BN * (C::BM / 8); e += C::NT) {
       const int c = e / (C::BM / 8), r8 = e - c * (C::BM / 8);
       const int gr = n0 + c, gc = m0 + r8 * 8;
-      if (gr < p.N && gc < p.M)
+      if (gr < g.N && gc < g.M)
         *(half8*)(Tb + (long long)gr * ldt + gc) = *(const half8*)(St + c * EPT + r8 * 8);
     }
   }
 }
 
 template <class C, int ROLE, bool LOWER, bool EPI, bool BKN>
-hipError_t launch(const GemmDesc& d, hipStream_t s) {
-  GemmArgs p;
-  p.A = d.A; p.B = d.B; p.C = d.C; p.CT = d.CT; p.D = d.D;
-  p.sA = d.sA; p.sB = d.sB; p.sC = d.sC; p.sCT = d.sCT; p.sD = d.sD;
-  p.lda = d.lda; p.ldb = d.ldb; p.ldc = d.ldc; p.ldct = d.ldct; p.ldd = d.ldd;
-  p.M = d.M; p.N = d.N; p.K = d.K;
-  p.tilesM = (d.M + C::BM - 1) / C::BM;
-  p.tilesN = (d.N + C::BN - 1) / C::BN;
-  p.tilesPerMat = LOWER ? p.tilesM * (p.tilesM + 1) / 2 : p.tilesM * p.tilesN;
-  const long long total = (long long)p.tilesPerMat * d.batch;
-  if (total <= 0 || total > 0x7fffffffLL) return hipErrorInvalidValue;
+hipError_t launch(const GemmDesc* d, int n, hipStream_t s) {
+  GemmArgs p = {};
+  p.nseg = n;
+  long long total = 0;
+  for (int i = 0; i < n; ++i) {
+    const GemmDesc& e = d[i];
+    Seg& g = p.seg[i];
+    g.A = e.A; g.B = e.B; g.C = e.C; g.D = e.D;
+    g.sA = e.sA; g.sB = e.sB; g.sC = e.sC; g.sD = e.sD;
+    g.lda = e.lda; g.ldb = e.ldb; g.ldc = e.ldc; g.ldd = e.ldd;
+    g.M = e.M; g.N = e.N; g.K = e.K;
+    g.tilesM = (e.M + C::BM - 1) / C::BM;
+    g.tilesN = (e.N + C::BN - 1) / C::BN;
+    g.tilesPerMat = LOWER ? g.tilesM * (g.tilesM + 1) / 2 : g.tilesM * g.tilesN;
+    const long long tiles = (long long)g.tilesPerMat * e.batch;
+    if (tiles <= 0 || tiles > 0x7fffffffLL) return hipErrorInvalidValue;
+    g.ntiles = (int)tiles;
+    total += tiles;
+    g.gdiag = e.gdiag > 0 ? e.gdiag : e.M;
+    g.zrows = e.zrows > 0 ? e.zrows : e.M;
+    g.zcols = e.zcols > 0 ? e.zcols : e.N;
+  }
+  if (total > 0x7fffffffLL) return hipErrorInvalidValue;
   p.total = (int)total;
-  p.alpha = d.alpha; p.beta = d.beta; p.gamma = d.gamma;
-  p.gdiag = d.gdiag > 0 ? d.gdiag : d.M;
-  p.zrows = d.zrows > 0 ? d.zrows : d.M;
-  p.zcols = d.zcols > 0 ? d.zcols : d.N;
-  p.sink = d.sink; p.W = d.W; p.ldw = d.ldw; p.idx = d.idx; p.lr = d.lr; p.Oout = d.Oout;
-  p.sO = d.sO;
-  p.kval = d.kval; p.mval = d.mval; p.nrows = d.nrows;
-  p.part = d.part; p.nblk = d.nblk;
+  p.CT = d[0].CT; p.sCT = d[0].sCT; p.ldct = d[0].ldct;
+  p.alpha = d[0].alpha; p.beta = d[0].beta; p.gamma = d[0].gamma;
+  p.sink = d[0].sink; p.W = d[0].W; p.ldw = d[0].ldw; p.idx = d[0].idx; p.lr = d[0].lr;
+  p.Oout = d[0].Oout; p.sO = d[0].sO;
+  p.kval = d[0].kval; p.mval = d[0].mval; p.nrows = d[0].nrows;
+  p.part = d[0].part; p.nblk = d[0].nblk;
   hipLaunchKernelGGL((k_gemm<C, ROLE, LOWER, EPI, BKN>), dim3(p.total), dim3(C::NT), 0, s, p);
   return hipGetLastError();
 }
 
 // The large tile needs about two full waves of blocks over the 256 CUs to
-// beat the small one (two blocks per CU).
-bool use_large(const GemmDesc& d) {
-  const long long tm = (d.M + 255) / 256, tn = (d.N + 255) / 256;
-  const long long tiles = d.lower ? tm * (tm + 1) / 2 : tm * tn;
-  return tiles * d.batch >= 512;
+// beat the small one (two blocks per CU); a launch of several products
+// counts all of their tiles.
+bool use_large(const GemmDesc* d, int n) {
+  long long tiles = 0;
+  for (int i = 0; i < n; ++i) {
+    const long long tm = (d[i].M + 255) / 256, tn = (d[i].N + 255) / 256;
+    tiles += (d[i].lower ? tm * (tm + 1) / 2 : tm * tn) * d[i].batch;
+  }
+  return tiles >= 512;
 }
 
 const char* trace_name(int role, bool large) {
@@ -918,44 +974,69 @@ const char* trace_name(int role, bool large) {
 }
 
 template <int ROLE, bool LOWER, bool EPI, bool BKN = false>
-hipError_t launch_cfg(const GemmDesc& d, hipStream_t s) {
-  const bool large = use_large(d);
-  TraceScope ts(trace_name(ROLE, large), d.trace_flops, d.trace_bytes, s);
-  return large ? launch<CfgL, ROLE, LOWER, EPI, BKN>(d, s) : launch<CfgS, ROLE, LOWER, EPI, BKN>(d, s);
+hipError_t launch_cfg(const GemmDesc* d, int n, hipStream_t s) {
+  const bool large = use_large(d, n);
+  double flops = 0.0, bytes = 0.0;
+  for (int i = 0; i < n; ++i) {
+    flops += d[i].trace_flops;
+    bytes += d[i].trace_bytes;
+  }
+  TraceScope ts(trace_name(ROLE, large), flops, bytes, s);
+  return large ? launch<CfgL, ROLE, LOWER, EPI, BKN>(d, n, s)
+               : launch<CfgS, ROLE, LOWER, EPI, BKN>(d, n, s);
+}
+
+bool desc_ok(const GemmDesc& d) {
+  if (d.M % 128 || d.N % 128 || d.K % BK || d.K <= 0 || d.batch <= 0) return false;
+  if (d.lower && (d.M != d.N || d.CT || !d.C)) return false;
+  if (d.b_kn && (d.lower || d.epilogue || d.ldb % 8)) return false;
+  if (!d.lower && !d.C && !d.CT && !d.sink) return false;
+  if (d.sink && (d.lower || d.C || d.CT || (d.sink != 1 && d.sink != 2))) return false;
+  if (d.part && (d.sink != 1 || d.nblk != (d.mval + 127) / 128)) return false;
+  return true;
+}
+
+// Products that may share a launch: the same kernel and epilogue constants;
+// only lower-triangle products, which have no transposed output or sink.
+bool same_launch(const GemmDesc& a, const GemmDesc& b) {
+  return a.lower && b.lower && a.role == b.role && a.epilogue == b.epilogue &&
+         a.alpha == b.alpha && a.beta == b.beta && a.gamma == b.gamma && !a.D == !b.D;
 }
 
 }  // namespace
 
-hipError_t launch_gemm(const GemmDesc& d, hipStream_t s) {
-  if (d.M % 128 || d.N % 128 || d.K % BK || d.K <= 0 || d.batch <= 0) return hipErrorInvalidValue;
-  if (d.lower && (d.M != d.N || d.CT || !d.C)) return hipErrorInvalidValue;
-  if (d.b_kn && (d.lower || d.epilogue || d.ldb % 8)) return hipErrorInvalidValue;
-  if (!d.lower && !d.C && !d.CT && !d.sink) return hipErrorInvalidValue;
-  if (d.sink && (d.lower || d.C || d.CT || (d.sink != 1 && d.sink != 2))) return hipErrorInvalidValue;
-  if (d.part && (d.sink != 1 || d.nblk != (d.mval + 127) / 128)) return hipErrorInvalidValue;
-  switch (d.role) {
+hipError_t launch_gemm_multi(const GemmDesc* d, int n, hipStream_t s) {
+  if (!d || n < 1 || n > kGemmMaxSeg) return hipErrorInvalidValue;
+  for (int i = 0; i < n; ++i) {
+    if (!desc_ok(d[i])) return hipErrorInvalidValue;
+    if (i > 0 && !same_launch(d[0], d[i])) return hipErrorInvalidValue;
+  }
+  const GemmDesc& e = d[0];
+  switch (e.role) {
     case kRoleGram:
-      if (!d.lower || d.epilogue) break;
-      return launch_cfg<kRoleGram, true, false>(d, s);
+      if (!e.lower || e.epilogue) break;
+      return launch_cfg<kRoleGram, true, false>(d, n, s);
     case kRolePoly:
-      if (!d.lower || !d.epilogue) break;
-      return launch_cfg<kRolePoly, true, true>(d, s);
+      if (!e.lower || !e.epilogue) break;
+      return launch_cfg<kRolePoly, true, true>(d, n, s);
     case kRoleSymm:
-      if (!d.lower || d.epilogue) break;
-      return launch_cfg<kRoleSymm, true, false>(d, s);
+      if (!e.lower || e.epilogue) break;
+      return launch_cfg<kRoleSymm, true, false>(d, n, s);
     case kRoleRect:
-      if (d.lower || d.epilogue || d.sink) break;
-      return d.b_kn ? launch_cfg<kRoleRect, false, false, true>(d, s)
-                    : launch_cfg<kRoleRect, false, false>(d, s);
+      if (e.lower || e.epilogue || e.sink) break;
+      return e.b_kn ? launch_cfg<kRoleRect, false, false, true>(d, n, s)
+                    : launch_cfg<kRoleRect, false, false>(d, n, s);
     case kRoleBack:
-      if (d.lower || d.epilogue || !d.sink) break;
-      return d.b_kn ? launch_cfg<kRoleBack, false, false, true>(d, s)
-                    : launch_cfg<kRoleBack, false, false>(d, s);
+      if (e.lower || e.epilogue || !e.sink) break;
+      return e.b_kn ? launch_cfg<kRoleBack, false, false, true>(d, n, s)
+                    : launch_cfg<kRoleBack, false, false>(d, n, s);
     case kRoleNsX:
-      if (d.lower || !d.epilogue || !d.D) break;
-      return launch_cfg<kRoleNsX, false, true>(d, s);
+      if (e.lower || !e.epilogue || !e.D) break;
+      return launch_cfg<kRoleNsX, false, true>(d, n, s);
   }
   return hipErrorInvalidValue;
 }
+
+hipError_t launch_gemm(const GemmDesc& d, hipStream_t s) { return launch_gemm_multi(&d, 1, s); }
 
 }  // namespace dion3

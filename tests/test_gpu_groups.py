@@ -148,9 +148,9 @@ def test_many_groups_one_call():
 
 
 def test_groups_trace_shares_the_side_products():
-    """With groups 0 and 2 sharing the Gram side, the polynomial and symmetric
-    products run once for both: the trace holds the launches of two sides,
-    not three groups."""
+    """Groups 0 and 2 share a Gram side, and the two side sets run their
+    schedule in step: every polynomial and symmetric product is one launch
+    over both sets, and every Gram one launch over the three groups."""
     say("groups trace")
     host = make(MIXED[:3], 78)
     cfg = d3.ns_cfg(path=d3.PATH_TILED)
@@ -162,7 +162,35 @@ def test_groups_trace_shares_the_side_products():
     finally:
         d3.trace_disable()
     names = [r[0] for r in recs]
-    assert sum(n.startswith("gemm_poly") for n in names) == 2 * 5
-    assert sum(n.startswith("gemm_symm") for n in names) == 2 * 9
-    assert sum(n.startswith("gemm_gram") for n in names) == 3 * 2
+    assert sum(n.startswith("gemm_poly") for n in names) == 5
+    assert sum(n.startswith("gemm_symm") for n in names) == 9
+    assert sum(n.startswith("gemm_gram") for n in names) == 2
     assert sum(n.startswith("gemm_back") for n in names) == 3
+
+
+def test_groups_trace_times_every_kernel_within_the_call():
+    """The trace times each kernel from the previous kernel's end inside one
+    call, and restarts after the untimed copies of idx and O (here between
+    the groups' normalization passes): every record is positive, one record
+    per launch, and together they fit in the call's own time."""
+    say("groups trace chain")
+    host = make(MIXED[:3], 79)
+    cfg = d3.ns_cfg(path=d3.PATH_TILED)
+    norm = (0.95, 1e-8)
+    run_grouped(host, KS_MIXED[:3], 0.04, cfg, norm=norm)          # warm
+    d3.trace_enable(512)
+    try:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        run_grouped(host, KS_MIXED[:3], 0.04, cfg, norm=norm)
+        e1.record()
+        torch.cuda.synchronize()
+        recs = d3.trace_records()
+    finally:
+        d3.trace_disable()
+    names = [r[0] for r in recs]
+    # per group: scoring, top-k, gather, the final product, norm stats and update
+    for kind in ("row_score", "topk", "gather", "norm_stats", "norm_update"):
+        assert sum(n == kind for n in names) == 3, kind
+    assert all(r[1] > 0.0 for r in recs)
+    assert sum(r[1] for r in recs) <= e0.elapsed_time(e1) * 1.02
