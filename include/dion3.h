@@ -258,13 +258,16 @@ DION3_API dion3_status dion3_workspace_size_groups(const dion3_group* groups, in
  * Full-Stack Orthogonal Updates", agihunt.info, level-4 paragraph) carried
  * one level further on one GPU: groups whose Gram sides are equal (s =
  * min(k, m); e.g. the attention and down-projection matrices of a
- * transformer at one fraction) run their s x s products, the polynomial and
- * the symmetric products of the level-2 paragraph, as one launch over the
- * matrices of all of them, where a launch-round cost model says that the
- * shared launch is no slower than separate ones (it shares on the 1B- and
- * 14B-shaped sets, not on the 7B-shaped set at f = 1/4); each group's
- * products that read its selected rows (the Grams and the multiply-backs)
- * run per group.  norm: NULL, or the
+ * transformer at one fraction) may share one set of s x s matrices, where a
+ * launch-round cost model says that their products (the polynomial and the
+ * symmetric products of the level-2 paragraph) run no slower as one; the
+ * side sets then run the iteration in step, each s x s product one launch
+ * over every set and each Gram one launch over every group (the
+ * multiply-backs, which write each group's own rows, run per group).  With
+ * the 128-matrix batch of attention-shaped matrices and the 32 of
+ * down-projection shape of a 7B-like model at f = 1/4 that is 9 symmetric,
+ * 5 polynomial and 2 Gram launches per step instead of 18, 10 and 6.
+ * norm: NULL, or the
  * per-neuron normalization of dion3_step_megabatch_norm for every group.
  * Results equal calling dion3_step_megabatch (_accum, _norm) once per group
  * with the same arguments, bit for bit.  Matrices written by different

@@ -4,9 +4,10 @@
 // level-1 and level-2 paragraphs: symmetric products need only the lower
 // triangle, which is then copied to the upper one).
 //
-// C = alpha * A * B^T (+ beta * D + gamma * I), with both operands stored
-// K-contiguous (the step keeps X in both layouts so that every product has
-// this form).  Two tile configurations:
+// C = alpha * A * B^T (+ beta * D + gamma * I).  A is stored K-contiguous;
+// B either K-contiguous too ([N][K]) or N-contiguous ([K][N], the X of the
+// multiply-backs, read through transposing LDS reads).  Two tile
+// configurations:
 //   * 256 x 256 block, 8 waves in 2 x 4, each wave 128 x 64 = 4 x 2
 //     v_mfma_f32_32x32x16_f16 tiles (one block per CU, 147 KB of LDS);
 //   * 128 x 128 block, 4 waves in 2 x 2, each wave 64 x 64 (two blocks per CU),
@@ -17,12 +18,14 @@
 // K step (the large tile's 128 accumulators leave no room for more at two
 // waves per SIMD; a second set in the small tile spilled once the fragments
 // were carried across steps); the next tile's LDS stores and global loads
-// are issued at the start of each step's MFMAs.  The
-// instruction order of each k-slice is fixed by hand (see mma_step) and the
-// next step's first fragments are read under the current step's last MFMAs.
-// The epilogue
-// stages the fp16 tile in LDS and writes it with 16-byte stores as rows, and
-// for the mirrored (symmetric) or transposed outputs as columns.
+// are issued at the start of each step's MFMAs.  The instruction order of
+// each k-slice is fixed by hand (see mma_step) and the next step's first
+// fragments are read under the current step's last MFMAs.  In the large
+// tile each wave runs the K loop for only the 32 x 32 blocks whose values
+// are needed and not known to be zero (see k_gemm).  The epilogue stages
+// the fp16 tile in LDS and writes it with 16-byte stores as rows, and for
+// the mirrored (symmetric) or transposed outputs as columns.  One launch
+// may hold several lower-triangle products (segments; see locate()).
 #include "dion3_internal.h"
 
 namespace dion3 {
