@@ -462,8 +462,8 @@ def main():
             "state_dtype": "fp32 W and M; fp16 X, Gram, polynomials and O with fp32 accumulation",
             "parallelism": "single GPU, " + (
                 "one megabatched call per shape group" if (args.per_group or args.streams > 1)
-                else "one call for all shape groups (groups with equal Gram sides share their "
-                     "s x s products' launches where that is no slower)") +
+                else "one call for all shape groups (each s x s product one launch over all "
+                     "Gram-side sets, each Gram one launch over all groups)") +
                 (f", groups on {args.streams} streams" if args.streams > 1 else ""),
             "gradient_accumulation": bool(args.accumulate),
             "per_neuron_normalization": bool(args.normalize),
