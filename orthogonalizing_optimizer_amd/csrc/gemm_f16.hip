@@ -955,15 +955,20 @@ hipError_t launch(const GemmDesc* d, int n, hipStream_t s) {
 }
 
 // The large tile needs about two full waves of blocks over the 256 CUs to
-// beat the small one (two blocks per CU); a launch of several products
+// beat the small one (two blocks per CU), or half a wave when every K loop
+// is long enough (K >= 2048) for its faster K step to outweigh its larger
+// fixed cost per tile (a 16 x 1024 x 4096 Gram: 588 -> 697 TFLOP/s; at
+// K = 512-1024 the small tile stays ahead).  A launch of several products
 // counts all of their tiles.
 bool use_large(const GemmDesc* d, int n) {
   long long tiles = 0;
+  int kmin = d[0].K;
   for (int i = 0; i < n; ++i) {
     const long long tm = (d[i].M + 255) / 256, tn = (d[i].N + 255) / 256;
     tiles += (d[i].lower ? tm * (tm + 1) / 2 : tm * tn) * d[i].batch;
+    kmin = min(kmin, d[i].K);
   }
-  return tiles >= 512;
+  return tiles >= 512 || (tiles >= 128 && kmin >= 2048);
 }
 
 const char* trace_name(int role, bool large) {

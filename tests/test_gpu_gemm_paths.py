@@ -35,17 +35,25 @@ def lower_tiles(side, tile):
     return t * (t + 1) // 2
 
 
+def large_tile(tiles, k):
+    """The library's tile rule: the 256 tile from 512 tiles of it, or from
+    128 when the inner dimension is at least 2048."""
+    return tiles >= 512 or (tiles >= 128 and k >= 2048)
+
+
 # (batch, rows, cols) and the path each case takes:
 #   52 x 1024 x 2304: 256 tile (520 lower tiles), K >= 2048
 #   35 x 1152 x 1024: 256 tile (525), ragged last tile row, K < 2048
 #   2 x 384 x 2560:   128 tile, ragged for the 256 rule, K >= 2048
 #   3 x 640 x 640:    128 tile, K < 2048
-SYRK_CASES = [(52, 1024, 2304), (35, 1152, 1024), (2, 384, 2560), (3, 640, 640)]
+#   13 x 1024 x 2560: 256 tile by the long-K rule (130 lower tiles, K >= 2048)
+SYRK_CASES = [(52, 1024, 2304), (35, 1152, 1024), (2, 384, 2560), (3, 640, 640),
+              (13, 1024, 2560)]
 
 
 @pytest.mark.parametrize("B,rows,cols", SYRK_CASES)
 def test_syrk_every_tile_path(B, rows, cols):
-    big = lower_tiles(rows, 256) * B >= 512
+    big = large_tile(lower_tiles(rows, 256) * B, cols)
     say("syrk paths", B, rows, cols, "256 tile" if big else "128 tile",
         "K >= 2048" if cols >= 2048 else "K < 2048")
     A = (host_gaussian((B, rows, cols), [60, B, rows, cols]) * 0.03).astype(np.float16)
@@ -58,13 +66,14 @@ def test_syrk_every_tile_path(B, rows, cols):
 
 
 # (batch, side): 15 x 2048 takes the 256 tile (540 lower tiles) with K = 2048;
-# 4 x 2048 the 128 tile with K = 2048; 35 x 1152 the 256 tile, ragged, K < 2048
-SYMM_CASES = [(15, 2048), (4, 2048), (35, 1152)]
+# 3 x 2048 the 128 tile with K = 2048 (108 large tiles); 35 x 1152 the 256
+# tile, ragged, K < 2048
+SYMM_CASES = [(15, 2048), (3, 2048), (35, 1152)]
 
 
 @pytest.mark.parametrize("B,s", SYMM_CASES)
 def test_symm_poly_every_tile_path(B, s):
-    big = lower_tiles(s, 256) * B >= 512
+    big = large_tile(lower_tiles(s, 256) * B, s)
     say("symm poly paths", B, s, "256 tile" if big else "128 tile")
     G = host_gaussian((B, s, s), [61, B, s])
     A = ((G + G.transpose(0, 2, 1)) * (0.5 / np.sqrt(s))).astype(np.float16)   # symmetric
