@@ -71,19 +71,35 @@ __global__ __launch_bounds__(256) void k_norm_rows(const f16* __restrict__ O, lo
 // One thread per selected row (256 rows per workgroup): the row's sum of
 // squares s_i (its block sums in block order), the state update and
 // r_i = 1 / (sqrt(v_i) + eps); each workgroup also leaves the fp64 sums of s_i
-// and s_i r_i^2 over its rows (a fixed tree) for the scale g.
+// and s_i r_i^2 over its rows (a fixed tree) for the scale g.  The
+// workgroup's block sums (contiguous in memory) pass through LDS 32 blocks
+// of every row at a time, read with consecutive threads on consecutive
+// floats.
+constexpr int kStatsCols = 32;
 __global__ __launch_bounds__(256) void k_norm_stats(const float* __restrict__ part, int k, int m,
                                                     int nblk, const int* __restrict__ idx,
                                                     BatchPtr<float> V, float beta2, float eps,
                                                     float2* __restrict__ stats,
                                                     double2* __restrict__ wsum) {
   __shared__ double sh0[256], sh1[256];
-  const int b = blockIdx.y, t = threadIdx.x, i = blockIdx.x * 256 + t;
+  __shared__ float blk[256][kStatsCols + 1];
+  const int b = blockIdx.y, t = threadIdx.x, i0 = blockIdx.x * 256, i = i0 + t;
+  const int rows = min(256, k - i0);
+  const float* __restrict__ pw = part + ((long long)b * k + i0) * nblk;   // this workgroup's rows
+  float s = 0.0f;
+  for (int c0 = 0; c0 < nblk; c0 += kStatsCols) {
+    const int cols = min(kStatsCols, nblk - c0);
+    for (int e = t; e < rows * cols; e += 256) {
+      const int r = e / cols, c = e - r * cols;
+      blk[r][c] = pw[(long long)r * nblk + c0 + c];
+    }
+    __syncthreads();
+    if (i < k)
+      for (int c = 0; c < cols; ++c) s += blk[t][c];
+    __syncthreads();
+  }
   double a0 = 0.0, a1 = 0.0;
   if (i < k) {
-    const float* __restrict__ pr = part + ((long long)b * k + i) * nblk;
-    float s = 0.0f;
-    for (int j = 0; j < nblk; ++j) s += pr[j];
     float* v = V.get(b) + idx[(long long)b * k + i];
     const float q = s / (float)m;
     const float nv = __builtin_fmaf(beta2, *v, (1.0f - beta2) * q);

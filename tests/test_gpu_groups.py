@@ -194,3 +194,28 @@ def test_groups_trace_times_every_kernel_within_the_call():
         assert sum(n == kind for n in names) == 3, kind
     assert all(r[1] > 0.0 for r in recs)
     assert sum(r[1] for r in recs) <= e0.elapsed_time(e1) * 1.02
+
+
+def test_groups_more_side_sets_than_one_launch_holds():
+    """Six Gram sides, more than the four products one launch holds: every
+    s x s product is split over two launches (four sets, then two), and each
+    Gram over two as well; results stay bitwise those of per-group calls."""
+    say("six side sets")
+    specs = [(2, 700, 160), (2, 600, 200), (2, 520, 256), (1, 900, 300), (2, 384, 420), (1, 1000, 520)]
+    ks = [350, 300, 260, 450, 384, 1000]    # Gram sides 160, 200, 256, 300, 384, 520
+    host = make(specs, 80)
+    cfg = d3.ns_cfg(path=d3.PATH_TILED)
+    ta, oa = run_grouped(host, ks, 0.03, cfg)
+    tb, ob = run_per_group(host, ks, 0.03, cfg)
+    assert_bitwise(ta, oa, tb, ob)
+    d3.trace_enable(1024)
+    try:
+        run_grouped(host, ks, 0.03, cfg)
+        recs = d3.trace_records()
+    finally:
+        d3.trace_disable()
+    names = [r[0] for r in recs]
+    assert sum(n.startswith("gemm_poly") for n in names) == 2 * 5
+    assert sum(n.startswith("gemm_symm") for n in names) == 2 * 9
+    assert sum(n.startswith("gemm_gram") for n in names) == 2 * 2
+    assert sum(n.startswith("gemm_back") for n in names) == 6
