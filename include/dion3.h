@@ -320,14 +320,18 @@ DION3_API dion3_status dion3_symm_f16(const uint16_t* A, const uint16_t* B, cons
 
 /* Kernel timing trace, for benchmarks.  dion3_trace_enable(capacity > 0)
  * creates 2 * capacity HIP events (no device memory) and starts recording:
- * each kernel the library then launches is bracketed by an event pair on the
- * caller's stream and noted with its name and the algorithmic work it does
- * on unpadded sizes (flops for the MFMA products, HBM bytes for the row
- * kernels).  Records past the capacity are dropped.  capacity <= 0 stops and
- * frees the trace.  dion3_trace_record(i, ...) waits for record i's second
- * event and returns its kernel name (a static string), elapsed ms, flops and
- * bytes; it returns DION3_ERR_HIP when recording either event of that pair
- * failed.  The trace is process-wide; it is meant for one benchmarking thread. */
+ * each kernel the library then launches is timed by events on the caller's
+ * stream and noted with its name and the algorithmic work it does on
+ * unpadded sizes (flops for the MFMA products, HBM bytes for the row
+ * kernels).  Within one library call a kernel's start is the previous
+ * kernel's end event, so one event is recorded per kernel and a kernel's
+ * time includes its own dispatch; the first kernel of a call, and the first
+ * after an untimed copy, records a start event of its own.  Records past
+ * the capacity are dropped.  capacity <= 0 stops and frees the trace.
+ * dion3_trace_record(i, ...) waits for record i's end event and returns its
+ * kernel name (a static string), elapsed ms, flops and bytes; it returns
+ * DION3_ERR_HIP when recording either event failed.  The trace is
+ * process-wide; it is meant for one benchmarking thread. */
 DION3_API dion3_status dion3_trace_enable(int32_t capacity);
 DION3_API int32_t dion3_trace_count(void);
 DION3_API void dion3_trace_reset(void);

@@ -442,8 +442,9 @@ def workspace_size_groups(groups: Sequence[Group], cfg: Optional[NsCfg] = None) 
 def step_groups(groups: Sequence[Group], mu: float, cfg: Optional[NsCfg] = None, norm=None,
                 return_idx: bool = False, return_O: bool = False,
                 ws: Optional[Workspace] = None):
-    """One Dion3 step over several shape groups in one call (groups with
-    equal Gram sides share their s x s products' launches).  norm: None or
+    """One Dion3 step over several shape groups in one call (each s x s
+    product is one launch over all groups' Gram-side sets, each Gram one
+    launch over all groups).  norm: None or
     (beta2, eps), with every group carrying its states Vs.  Returns one
     (idx, O) pair per group (None unless asked for)."""
     torch = _torch()

@@ -231,7 +231,8 @@ bool restart_at(const dion3_ns_cfg& c, int t) {
 
 // --------------------------------------------------------------- Gram NS
 
-// A selected-row block in both layouts: X [kp][mp] and XT [mp][kp].
+// A selected-row block's two layout slots, X [kp][mp] and XT [mp][kp] (the
+// tiled Gram path fills only the one its products read; null when unused).
 struct XPair {
   f16 *X, *XT;
 };
@@ -736,7 +737,7 @@ dion3_status step_one(const GroupArgs& a, int batch, long long n, long long m, l
 }
 
 // Layout of a grouped call.  Groups that take the fused path get no side set;
-// the others share one per Gram side.
+// the others share one per Gram side where side_cost says so.
 dion3_status group_layout(CallLayout& L, const dion3_group* groups, int32_t ngroups,
                           const dion3_ns_cfg& cfg) {
   if (!groups || ngroups < 1 || ngroups > DION3_MAX_GROUPS) return DION3_ERR_ARG;
