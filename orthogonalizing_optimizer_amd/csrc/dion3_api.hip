@@ -462,7 +462,7 @@ struct SetRun {
 };
 
 dion3_status gram_ns_sets(const dion3_ns_cfg& cfg, SetRun* set, int ns, hipStream_t s) {
-  GemmDesc d[DION3_MAX_GROUPS];
+  GemmDesc d[2 * DION3_MAX_GROUPS];   // up to two products per set in one launch
   auto grams = [&]() -> hipError_t {
     int n = 0;
     for (int j = 0; j < ns; ++j)
@@ -472,13 +472,19 @@ dion3_status gram_ns_sets(const dion3_ns_cfg& cfg, SetRun* set, int ns, hipStrea
       }
     return launch_lower(d, n, s);
   };
-  // one s x s product per set: C_j = alpha A_j B_j + beta D_j + gamma I
+  // one s x s product per set, C_j = alpha A_j B_j + beta D_j + gamma I,
+  // appended to d[n..]
+  auto add = [&](int& n, f16* SetRun::*A, f16* SetRun::*B, f16* SetRun::*D, f16* SetRun::*C,
+                 float alpha, float beta, float gamma, bool epi) {
+    for (int j = 0; j < ns; ++j)
+      d[n++] = symm_desc(*set[j].S, set[j].*A, set[j].*B, D ? set[j].*D : nullptr, set[j].*C,
+                         alpha, beta, gamma, epi);
+  };
   auto sides = [&](f16* SetRun::*A, f16* SetRun::*B, f16* SetRun::*D, f16* SetRun::*C, float alpha,
                    float beta, float gamma, bool epi) -> hipError_t {
-    for (int j = 0; j < ns; ++j)
-      d[j] = symm_desc(*set[j].S, set[j].*A, set[j].*B, D ? set[j].*D : nullptr, set[j].*C, alpha,
-                       beta, gamma, epi);
-    return launch_lower(d, ns, s);
+    int n = 0;
+    add(n, A, B, D, C, alpha, beta, gamma, epi);
+    return launch_lower(d, n, s);
   };
   HIP_TRY(grams());
   bool q_identity = true;
@@ -499,20 +505,24 @@ dion3_status gram_ns_sets(const dion3_ns_cfg& cfg, SetRun* set, int ns, hipStrea
     const float a = cfg.abc[t - 1][0], b = cfg.abc[t - 1][1], c = cfg.abc[t - 1][2];
     // Z = a I + b R + c R^2  (the "A^2 + B" product)
     HIP_TRY(sides(&SetRun::R, &SetRun::R, &SetRun::R, &SetRun::Z, c, b, a, true));
+    const bool next_r = t < T && !restart_at(cfg, t + 1);   // R <- Z R Z follows
     f16* SetRun::*Zv;
     if (q_identity) {           // Q <- Z Q with Q = I: just adopt Z
       for (int j = 0; j < ns; ++j) std::swap(set[j].Q, set[j].Z);
       Zv = &SetRun::Q;
       q_identity = false;
+      if (next_r) HIP_TRY(sides(Zv, &SetRun::R, nullptr, &SetRun::Tm, 1.0f, 0.0f, 0.0f, false));
     } else {
-      HIP_TRY(sides(&SetRun::Z, &SetRun::Q, nullptr, &SetRun::Qn, 1.0f, 0.0f, 0.0f, false));
+      // Q' = Z Q, and T = Z R when R is updated too: independent products
+      // that both read Z, one launch
+      int n = 0;
+      add(n, &SetRun::Z, &SetRun::Q, nullptr, &SetRun::Qn, 1.0f, 0.0f, 0.0f, false);
+      if (next_r) add(n, &SetRun::Z, &SetRun::R, nullptr, &SetRun::Tm, 1.0f, 0.0f, 0.0f, false);
+      HIP_TRY(launch_lower(d, n, s));
       for (int j = 0; j < ns; ++j) std::swap(set[j].Q, set[j].Qn);
       Zv = &SetRun::Z;
     }
-    if (t < T && !restart_at(cfg, t + 1)) {   // R <- Z R Z
-      HIP_TRY(sides(Zv, &SetRun::R, nullptr, &SetRun::Tm, 1.0f, 0.0f, 0.0f, false));
-      HIP_TRY(sides(&SetRun::Tm, Zv, nullptr, &SetRun::R, 1.0f, 0.0f, 0.0f, false));
-    }
+    if (next_r) HIP_TRY(sides(&SetRun::Tm, Zv, nullptr, &SetRun::R, 1.0f, 0.0f, 0.0f, false));
   }
   for (int j = 0; j < ns; ++j)
     for (int i = 0; i < set[j].nr; ++i) {

@@ -163,7 +163,7 @@ def test_groups_trace_shares_the_side_products():
         d3.trace_disable()
     names = [r[0] for r in recs]
     assert sum(n.startswith("gemm_poly") for n in names) == 5
-    assert sum(n.startswith("gemm_symm") for n in names) == 9
+    assert sum(n.startswith("gemm_symm") for n in names) == 8   # iteration 4: Z Q and Z R together
     assert sum(n.startswith("gemm_gram") for n in names) == 2
     assert sum(n.startswith("gemm_back") for n in names) == 3
 
@@ -216,6 +216,8 @@ def test_groups_more_side_sets_than_one_launch_holds():
         d3.trace_disable()
     names = [r[0] for r in recs]
     assert sum(n.startswith("gemm_poly") for n in names) == 2 * 5
-    assert sum(n.startswith("gemm_symm") for n in names) == 2 * 9
+    # two launches per product, but iteration 4's Z Q and Z R together (12
+    # products) take three
+    assert sum(n.startswith("gemm_symm") for n in names) == 2 * 9 - 1
     assert sum(n.startswith("gemm_gram") for n in names) == 2 * 2
     assert sum(n.startswith("gemm_back") for n in names) == 6
