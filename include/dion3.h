@@ -265,8 +265,9 @@ DION3_API dion3_status dion3_workspace_size_groups(const dion3_group* groups, in
  * over every set and each Gram one launch over every group (the
  * multiply-backs, which write each group's own rows, run per group).  With
  * the 128-matrix batch of attention-shaped matrices and the 32 of
- * down-projection shape of a 7B-like model at f = 1/4 that is 9 symmetric,
- * 5 polynomial and 2 Gram launches per step instead of 18, 10 and 6.
+ * down-projection shape of a 7B-like model at f = 1/4 that is 8 symmetric,
+ * 5 polynomial and 2 Gram launches per step instead of 18, 10 and 6 (the
+ * two independent products that read the same polynomial also share one).
  * norm: NULL, or the
  * per-neuron normalization of dion3_step_megabatch_norm for every group.
  * Results equal calling dion3_step_megabatch (_accum, _norm) once per group
