@@ -124,22 +124,25 @@ __global__ __launch_bounds__(256) void k_norm_stats(const float* __restrict__ pa
 }
 
 // W[idx[i]][j] = fma(-lr g r_i, O_ij, W[idx[i]][j]): one workgroup per 4 rows
-// of O, 64 lanes along a row, 4 columns per lane per pass.
+// x 256 columns of O, one wave per row, one 16-byte W run and one 8-byte O
+// run per lane (short workgroups with a single load per thread stream faster
+// than one wave walking a whole row: measured on the 7B shapes).  Grid:
+// x = row groups of 4, y = 256-column blocks, z = matrices.
 // The scale g = sqrt(sum_i s_i / sum_i s_i r_i^2) comes from k_norm_stats'
-// per-workgroup sums, added in workgroup order (every workgroup of a matrix
-// gets the same bits).
+// per-workgroup sums, added in workgroup order (every thread of a matrix gets
+// the same bits).
 __global__ __launch_bounds__(256) void k_norm_update(const f16* __restrict__ O, long long sO, int k,
                                                      int m, const int* __restrict__ idx,
                                                      BatchPtr<float> W, long long ldw, float lr,
                                                      const float2* __restrict__ stats,
                                                      const double2* __restrict__ wsum, int nwg) {
-  const int b = blockIdx.y;
+  const int b = blockIdx.z;
   const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (i >= k) return;
+  const int j = blockIdx.y * 256 + 4 * (threadIdx.x & 63);
+  if (i >= k || j >= m) return;
   double a0 = 0.0, a1 = 0.0;
-  for (int j = 0; j < nwg; ++j) {
-    const double2 w2 = wsum[(long long)b * nwg + j];
+  for (int q = 0; q < nwg; ++q) {
+    const double2 w2 = wsum[(long long)b * nwg + q];
     a0 += w2.x;
     a1 += w2.y;
   }
@@ -147,21 +150,18 @@ __global__ __launch_bounds__(256) void k_norm_update(const f16* __restrict__ O, 
   const float c = -lr * (float)g * stats[(long long)b * k + i].y;
   const f16* __restrict__ src = O + (long long)b * sO + (long long)i * m;
   float* __restrict__ w = W.get(b) + (long long)idx[(long long)b * k + i] * ldw;
-  for (int j = 4 * lane; j < m; j += 4 * 64) {
-    // one 16-byte W run and one 8-byte O run per lane; both are used once,
-    // so they stream with the nontemporal hint (measured 5 % faster)
-    if (j + 3 < m && ((uintptr_t)(w + j) & 15) == 0 && ((uintptr_t)(src + j) & 7) == 0) {
-      f32x4 x = __builtin_nontemporal_load((const f32x4*)(w + j));
-      const half4 o = __builtin_nontemporal_load((const half4*)(src + j));
-      x[0] = __builtin_fmaf(c, (float)o[0], x[0]);
-      x[1] = __builtin_fmaf(c, (float)o[1], x[1]);
-      x[2] = __builtin_fmaf(c, (float)o[2], x[2]);
-      x[3] = __builtin_fmaf(c, (float)o[3], x[3]);
-      __builtin_nontemporal_store(x, (f32x4*)(w + j));
-    } else {
-      for (int e = 0; e < 4 && j + e < m; ++e)
-        w[j + e] = __builtin_fmaf(c, (float)src[j + e], w[j + e]);
-    }
+  // both runs are used once, so they stream with the nontemporal hint
+  if (j + 3 < m && ((uintptr_t)(w + j) & 15) == 0 && ((uintptr_t)(src + j) & 7) == 0) {
+    f32x4 x = __builtin_nontemporal_load((const f32x4*)(w + j));
+    const half4 o = __builtin_nontemporal_load((const half4*)(src + j));
+    x[0] = __builtin_fmaf(c, (float)o[0], x[0]);
+    x[1] = __builtin_fmaf(c, (float)o[1], x[1]);
+    x[2] = __builtin_fmaf(c, (float)o[2], x[2]);
+    x[3] = __builtin_fmaf(c, (float)o[3], x[3]);
+    __builtin_nontemporal_store(x, (f32x4*)(w + j));
+  } else {
+    for (int e = 0; e < 4 && j + e < m; ++e)
+      w[j + e] = __builtin_fmaf(c, (float)src[j + e], w[j + e]);
   }
 }
 
@@ -191,8 +191,8 @@ hipError_t launch_normalize(const f16* O, long long sO, int batch, int k, int m,
     if (e != hipSuccess) return e;
   }
   TraceScope ts("norm_update", 0.0, km * 10.0, s);
-  hipLaunchKernelGGL(k_norm_update, grid, dim3(256), 0, s, O, sO, k, m, idx, W, ldw, lr, stats,
-                     wsum, nwg);
+  hipLaunchKernelGGL(k_norm_update, dim3((k + 3) / 4, (m + 255) / 256, batch), dim3(256), 0, s, O,
+                     sO, k, m, idx, W, ldw, lr, stats, wsum, nwg);
   return hipGetLastError();
 }
 
