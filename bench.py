@@ -44,6 +44,7 @@ KERNEL_SYMBOLS = {
     "accum_score": "k_accum_score_f32",
     "topk": "k_topk",
     "gather": "k_gather<float, true>",
+    "gather_rows": "k_gather_rows<float, true>",
     "gram_ns_fused_128": "k_gram_ns_small",
     "norm_rows": "k_norm_rows",
     "norm_stats": "k_norm_stats",

@@ -670,7 +670,8 @@ dion3_status run_step(const CallLayout& L, const GroupArgs* A, float mu, const d
     const XPair xa = pair_a(G, w), xb = pair_b(G, w);
     {
       const XPair out = gather_layouts(P, cfg, xa);
-      TraceScope ts("gather", 0.0, Bd * km * 10.0, s);
+      // the rows-only gather is a kernel of its own (k_gather_rows)
+      TraceScope ts(out.XT ? "gather" : "gather_rows", 0.0, Bd * km * 10.0, s);
       HIP_TRY(launch_gather_f32(a.M, P.B, n, m, a.ld, idx, k, scale, mu, true, out.X, out.XT,
                                 P.kp * P.mp, (int)P.kp, (int)P.mp, s));
     }

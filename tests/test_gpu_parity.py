@@ -371,7 +371,7 @@ def test_timing_trace_records_every_kernel():
     finally:
         d3.trace_disable()
     names = [r[0] for r in recs]
-    assert names[:3] == ["row_score", "topk", "gather"]
+    assert names[:3] == ["row_score", "topk", "gather_rows"]   # k <= m: rows layout only
     gemms = [r for r in recs if r[0].startswith("gemm_")]
     # 5 iterations with a restart at 3: 2 Grams, 5 polynomials, 2 multiply-backs
     # and 9 symmetric products (iterations 1-2: R <- Z R Z, Q <- Z Q; iterations
