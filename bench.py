@@ -46,6 +46,8 @@ KERNEL_SYMBOLS = {
     "gather": "k_gather<float, true>",
     "gather_rows": "k_gather_rows<float, true>",
     "gram_ns_fused_128": "k_gram_ns_small",
+    "gram_ns_fused_64": "k_gram_ns_tiny<2>",
+    "gram_ns_fused_32": "k_gram_ns_tiny<1>",
     "norm_rows": "k_norm_rows",
     "norm_stats": "k_norm_stats",
     "norm_update": "k_norm_update",

@@ -104,10 +104,10 @@ typedef struct {
  * DION3_PATH_TILED: one tiled MFMA product per step of the iteration (about
  *   20 launches per call, every grid spread over the whole GPU).
  * DION3_PATH_FUSED: one launch, one workgroup per matrix running the whole
- *   iteration with R, Z, Q in LDS; only when the Gram side min(k, m) is at
- *   most 128, else DION3_ERR_UNSUPPORTED.  Its result is bitwise identical
- *   to the tiled path (same products, same accumulation order, same
- *   roundings).
+ *   iteration with R, Z, Q in LDS (for Gram sides up to 64 one wave runs
+ *   every s x s product); only when the Gram side min(k, m) is at most 128,
+ *   else DION3_ERR_UNSUPPORTED.  Its result is bitwise identical to the
+ *   tiled path (same products, same accumulation order, same roundings).
  * DION3_PATH_AUTO: the fused path where it is allowed and expected to be
  *   faster (Gram side <= 128 and enough matrices or short enough rows for
  *   one workgroup each), the tiled path otherwise.

@@ -405,17 +405,22 @@ double gram_ns_flops(const Shape& P, const dion3_ns_cfg& cfg) {
 
 // The fused one-launch path covers Gram sides that pad to one 128 tile.  It
 // runs one workgroup per matrix, so its time grows with the row length L
-// while the tiled launches spread long rows over many CUs.  Measured on
-// MI355X, one dion3_gram_ns call (us, fused / tiled): 72 / 128 at 1 x 32 x
-// 512, 114 / 145 at 1 x 128 x 1024, 172 / 157 at 1 x 128 x 2048, 184 / 186 at
-// 32 x 128 x 2048, 292 / 193 at 1 x 128 x 4096, 302 / 218 at 16 x 128 x 4096,
-// 638 / 533 at 64 x 128 x 8192, 120 / 223 at 256 x 128 x 512, 140 / 459 at
-// 512 x 64 x 256: the fused path wins up to L = 1024 at any batch and ties at
-// L = 2048 from about 32 matrices on.
+// while the tiled launches spread long rows over many CUs.  Sides up to 64
+// take the one-wave kernel, which gains most.  Measured on MI355X, one
+// dion3_gram_ns call (us, fused / tiled): side 32: 37 / 137 at 1 x 32 x 512,
+// 110 / 195 at 1 x 32 x 4096, 230 / 298 at 16 x 32 x 8192, 292 / 434 at 64 x
+// 32 x 8192; side 64: 122 / 162 at 1 x 64 x 2048, 201 / 195 at 1 x 64 x 4096,
+// 252 / 279 at 64 x 64 x 4096, 394 / 302 at 16 x 64 x 8192, 84 / 480 at 512 x
+// 64 x 256; side 128: 114 / 153 at 1 x 128 x 1024, 172 / 169 at 1 x 128 x
+// 2048, 186 / 193 at 32 x 128 x 2048, 302 / 224 at 16 x 128 x 4096, 120 / 248
+// at 256 x 128 x 512.
 bool use_fused(const Shape& P, const dion3_ns_cfg& cfg) {
   if (cfg.method != DION3_NS_GRAM) return false;
   if (cfg.path == DION3_PATH_TILED || P.sp != kTile) return false;
   if (cfg.path == DION3_PATH_FUSED) return true;
+  const long long side = P.tr ? P.m : P.k;
+  if (side <= 32) return P.Lp <= 8192;
+  if (side <= 64) return P.Lp <= 2048 || (P.Lp <= 4096 && P.B >= 32);
   return P.Lp <= 1024 || (P.Lp <= 2048 && P.B >= 32);
 }
 

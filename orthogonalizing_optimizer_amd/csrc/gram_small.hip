@@ -1,6 +1,8 @@
 // Whole Gram Newton-Schulz in one workgroup per matrix, for Gram sides of at
 // most 128 ("Dion3: Full-Stack Orthogonal Updates", agihunt.info, level-1
-// paragraph).  Small matrices would otherwise pay one launch per product
+// paragraph): k_gram_ns_small (described here) pads the side to 128;
+// k_gram_ns_tiny (further down) takes sides up to 64 with one wave running
+// the s x s products.  Small matrices would otherwise pay one launch per product
 // (about 20 per step, each a few microseconds of fixed cost); here R, Z, Q
 // and T stay in LDS (4 x 34 KB), 64-wide K slices of X stream through an
 // 18 KB staging buffer with a register prefetch of several slices, and the final
@@ -430,6 +432,268 @@ __global__ __launch_bounds__(NT, 1) void k_gram_ns_small(SmallArgs p) {
   rect_small(Q, xs, R, T, XT, p.Lp, Y, YT, p, b, true, w, kn);
 }
 
+
+// ---------------------------------------------------------------------------
+// Gram sides of at most 64: the s x s matrices are one or two 32 x 32 blocks
+// per side (NB), so each symmetric product of the iteration is a handful of
+// MFMAs.  One wave runs all of them back to back, with R, Z, Q and T in LDS
+// and no workgroup barrier between products (a wave's LDS accesses execute
+// in order); the Gram and the multiply-backs, which stream X, spread their
+// 32 x 32 output blocks over the four waves.  Every element is computed as
+// in the tiled kernels: its k-groups of 16 in increasing order into one fp32
+// accumulator that starts at +0, the same epilogue, and symmetric results
+// taken from the lower triangle (so the bits equal the tiled path's).
+constexpr int TS = 64;           // padded side
+constexpr int TL = TS + 8;       // LDS row stride of R, Z, Q, T (halves)
+constexpr int TB = 32 + 8;       // row stride of a wave's 32 x 32 output staging
+
+// Orders this wave's LDS accesses around the call (writes before, reads
+// after) without a workgroup barrier.
+__device__ __forceinline__ void wave_lds_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+}
+
+// Accumulator (v) of lane l in a 32 x 32 MFMA block: row 8 (v / 4) + 4 (l / 32)
+// + v % 4, column l % 32.
+__device__ __forceinline__ int acc_row(int v4, int lane) { return 8 * v4 + 4 * (lane >> 5); }
+
+// Stores the fp16 value h (4 consecutive rows p..p+3 of column q) of a
+// symmetric result: the lower elements (row >= column) at both (row, col)
+// and (col, row); the upper ones come from their mirror.
+__device__ __forceinline__ void store_sym4(f16* out, int p, int q, bool diag, const half4& h) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    if (!diag || p + e >= q) {
+      out[(p + e) * TL + q] = h[e];
+      out[q * TL + p + e] = h[e];
+    }
+}
+
+// out = alpha A B + beta D + gamma I (POLY) or A B for symmetric NB x NB-block
+// matrices in LDS, by one wave.  out may be A or B: every operand read comes
+// before the first store.
+template <int NB, bool POLY>
+__device__ __forceinline__ void tiny_symm(f16* out, const f16* A, const f16* B, const f16* D,
+                                          float alpha, float beta, float gamma, int lane, int gd) {
+  constexpr int NL = NB * (NB + 1) / 2;
+  floatx16 acc[NL];
+#pragma unroll
+  for (int l = 0; l < NL; ++l)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[l][v] = 0.0f;
+  const int fr = (lane & 31) * TL + 8 * (lane >> 5);
+#pragma unroll
+  for (int s = 0; s < 2 * NB; ++s) {
+    half8 af[NB], bf[NB];
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      af[i] = *(const half8*)(A + i * 32 * TL + fr + 16 * s);
+      bf[i] = *(const half8*)(B + i * 32 * TL + fr + 16 * s);
+    }
+    int l = 0;
+#pragma unroll
+    for (int i = 0; i < NB; ++i)
+#pragma unroll
+      for (int j = 0; j <= i; ++j, ++l)
+        acc[l] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[l], 0, 0, 0);
+  }
+  int l = 0;
+#pragma unroll
+  for (int i = 0; i < NB; ++i)
+#pragma unroll
+    for (int j = 0; j <= i; ++j, ++l)
+#pragma unroll
+      for (int v4 = 0; v4 < 4; ++v4) {
+        const int p = i * 32 + acc_row(v4, lane), q = j * 32 + (lane & 31);
+        float val[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) val[e] = acc[l][4 * v4 + e];
+        if (POLY) {
+          const half4 d = *(const half4*)(D + q * TL + p);   // D[p + e][q] (D symmetric)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            val[e] = __builtin_fmaf(val[e], alpha, beta * (float)d[e]);
+            if (p + e == q && q < gd) val[e] += gamma;
+            asm("" : "+v"(val[e]));   // fp32 rounding, then fp16, as in the tiled kernels
+          }
+        }
+        half4 h;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) h[e] = (f16)val[e];
+        store_sym4(out, p, q, i == j, h);
+      }
+  wave_lds_fence();
+}
+
+// R = X X^T (K = Lp, X rows in global memory, row stride Lp): lower block
+// (bi, bj) on wave bi (bi + 1) / 2 + bj, the K loop in increasing order, its
+// loads two batches of 4 k-groups ahead.  The caller's barrier follows.
+template <int NB>
+__device__ __forceinline__ void tiny_gram(f16* R, const f16* X, int Lp, int wave, int lane) {
+  constexpr int NL = NB * (NB + 1) / 2, G = 4;
+  if (wave >= NL) return;
+  const int bi = (NB == 2 && wave >= 1) ? 1 : 0, bj = (NB == 2 && wave == 2) ? 1 : 0;
+  const bool dg = bi == bj;
+  const f16* xa = X + (long long)(bi * 32 + (lane & 31)) * Lp + 8 * (lane >> 5);
+  const f16* xb = X + (long long)(bj * 32 + (lane & 31)) * Lp + 8 * (lane >> 5);
+  floatx16 acc;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
+  const int ng = Lp / 16;   // a multiple of 2 G (Lp is a multiple of 128)
+  half8 fa[2][G], fb[2][G];
+  auto load = [&](int h, int g0) {
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+      fa[h][u] = *(const half8*)(xa + 16 * (g0 + u));
+      if (!dg) fb[h][u] = *(const half8*)(xb + 16 * (g0 + u));
+    }
+  };
+  auto run = [&](int h) {
+#pragma unroll
+    for (int u = 0; u < G; ++u)
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[h][u], dg ? fa[h][u] : fb[h][u], acc, 0, 0, 0);
+  };
+  load(0, 0);
+  for (int g0 = 0; g0 < ng; g0 += 2 * G) {
+    if (g0 + G < ng) load(1, g0 + G);
+    run(0);
+    if (g0 + G >= ng) break;
+    if (g0 + 2 * G < ng) load(0, g0 + 2 * G);
+    run(1);
+  }
+#pragma unroll
+  for (int v4 = 0; v4 < 4; ++v4) {
+    const int p = bi * 32 + acc_row(v4, lane), q = bj * 32 + (lane & 31);
+    half4 h;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) h[e] = (f16)acc[4 * v4 + e];
+    store_sym4(R, p, q, dg, h);
+  }
+}
+
+// Y = Q X_math over the L side in 32 x 32 output blocks (NB row blocks x
+// Lp / 32 column blocks, dealt to the waves in turn); X_math^T is read from
+// global memory (XT, Lp x 128), Q from LDS.  Each block goes through this
+// wave's staging (St, column-major: St[c][r]) and leaves in 16-byte runs: to
+// Y and YT (restart) or, in rows layout, into the update (final).
+template <int NB>
+__device__ __forceinline__ void tiny_rect(const f16* Q, const f16* XT, int Lp, f16* Y, f16* YT,
+                                          f16* St, const SmallArgs& p, int b, bool final_pass,
+                                          int wave, int lane) {
+  const int ncb = Lp / 32, nblk = NB * ncb;
+  const int fr = (lane & 31) * TL + 8 * (lane >> 5);
+  // X_math^T fragments of the wave's next block are loaded one block ahead
+  auto load = [&](int blk, half8 (&f)[2 * NB]) {
+    const int j0 = (blk % ncb) * 32;
+    const f16* xt = XT + (long long)(j0 + (lane & 31)) * S + 8 * (lane >> 5);
+#pragma unroll
+    for (int s = 0; s < 2 * NB; ++s) f[s] = *(const half8*)(xt + 16 * s);
+  };
+  half8 xn[2 * NB];
+  if (wave < nblk) load(wave, xn);
+  for (int blk = wave; blk < nblk; blk += 4) {
+    const int bi = blk / ncb, j0 = (blk - bi * ncb) * 32;
+    half8 xf[2 * NB];
+#pragma unroll
+    for (int s = 0; s < 2 * NB; ++s) xf[s] = xn[s];
+    if (blk + 4 < nblk) load(blk + 4, xn);
+    floatx16 acc;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
+#pragma unroll
+    for (int s = 0; s < 2 * NB; ++s) {
+      const half8 qf = *(const half8*)(Q + bi * 32 * TL + fr + 16 * s);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(qf, xf[s], acc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int v4 = 0; v4 < 4; ++v4) {
+      const int r = acc_row(v4, lane), c = lane & 31;
+      half4 h;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) h[e] = (f16)acc[4 * v4 + e];
+      *(half4*)(St + c * TB + r) = h;
+    }
+    wave_lds_fence();
+    // 32 x 32 block = 128 runs of 8 per layout, two per lane
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int e = lane + 64 * u, a = e >> 2, c8 = (e & 3) * 8;
+      // column-major run: column a (of the block), rows c8..c8+7
+      const half8 colrun = *(const half8*)(St + a * TB + c8);
+      const int row0 = bi * 32;
+      if (!final_pass) {
+        // YT[j0 + a][row0 + c8 ..]
+        *(half8*)(YT + (long long)(j0 + a) * S + row0 + c8) = colrun;
+      } else if (p.tr) {      // rows layout = transposed: O[j0 + a][row0 + c8 ..]
+        sink8(p, b, j0 + a, row0 + c8, colrun);
+      }
+      if (!final_pass || !p.tr) {
+        // row-major run: row a, columns c8..c8+7, gathered from St's columns
+        half8 rowrun;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) rowrun[q] = St[(c8 + q) * TB + a];
+        if (!final_pass)
+          *(half8*)(Y + (long long)(row0 + a) * Lp + j0 + c8) = rowrun;
+        else
+          sink8(p, b, row0 + a, j0 + c8, rowrun);
+      }
+    }
+    wave_lds_fence();   // the next block's staging overwrites St
+  }
+}
+
+template <int NB>
+__global__ __launch_bounds__(NT) void k_gram_ns_tiny(SmallArgs p) {
+  __shared__ __attribute__((aligned(16))) f16 mats[4 * TS * TL];
+  __shared__ __attribute__((aligned(16))) f16 stage[4 * 32 * TB];
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  f16* X = p.X + (long long)b * p.sX;
+  f16* XT = p.XT + (long long)b * p.sX;
+  f16* Y = p.Y + (long long)b * p.sX;
+  f16* YT = p.YT + (long long)b * p.sX;
+  f16 *R = mats, *Z = mats + TS * TL, *Q = mats + 2 * TS * TL, *T = mats + 3 * TS * TL;
+  f16* St = stage + wave * 32 * TB;
+  const int sreal = p.tr ? p.mval : p.kval;
+  tiny_gram<NB>(R, X, p.Lp, wave, lane);
+  __syncthreads();
+  bool q_identity = true;
+  const int iters = p.cfg.iters;
+  for (int t = 1; t <= iters; ++t) {
+    if (is_restart(p.cfg, t)) {      // X <- Q X, R <- X X^T, Q <- I
+      if (!q_identity) {
+        __syncthreads();             // Q complete
+        tiny_rect<NB>(Q, XT, p.Lp, Y, YT, St, p, b, false, wave, lane);
+        f16* tx = X; X = Y; Y = tx;
+        f16* tt = XT; XT = YT; YT = tt;
+        __syncthreads();             // the new X in memory, Q read
+      }
+      tiny_gram<NB>(R, X, p.Lp, wave, lane);
+      __syncthreads();
+      q_identity = true;
+    }
+    const float a = p.cfg.abc[t - 1][0], bb = p.cfg.abc[t - 1][1], c = p.cfg.abc[t - 1][2];
+    const bool next_r = t < iters && !is_restart(p.cfg, t + 1);
+    // the products of this iteration, all on wave 0 (uniform pointer swaps on every wave)
+    f16* Zv;
+    if (wave == 0) tiny_symm<NB, true>(Z, R, R, R, c, bb, a, lane, sreal);   // Z = a I + b R + c R^2
+    if (q_identity) {
+      f16* tmp = Q; Q = Z; Z = tmp;
+      Zv = Q;
+      q_identity = false;
+    } else {
+      if (wave == 0) tiny_symm<NB, false>(Q, Z, Q, nullptr, 1.0f, 0.0f, 0.0f, lane, sreal);
+      Zv = Z;
+    }
+    if (next_r && wave == 0) {       // R <- Z R Z
+      tiny_symm<NB, false>(T, Zv, R, nullptr, 1.0f, 0.0f, 0.0f, lane, sreal);
+      tiny_symm<NB, false>(R, T, Zv, nullptr, 1.0f, 0.0f, 0.0f, lane, sreal);
+    }
+  }
+  __syncthreads();                   // Q complete
+  tiny_rect<NB>(Q, XT, p.Lp, Y, YT, St, p, b, true, wave, lane);
+}
 }  // namespace
 
 hipError_t launch_gram_ns_small(f16* X, f16* XT, f16* Y, f16* YT, long long sX, int batch, int Lp,
@@ -445,9 +709,21 @@ hipError_t launch_gram_ns_small(f16* X, f16* XT, f16* Y, f16* YT, long long sX, 
   p.kval = kval; p.mval = mval; p.nrows = nrows;
   // algorithmic bytes: X read once, the selected rows of W read and written
   const double sL = (double)kval * mval;
-  TraceScope trace("gram_ns_fused_128", trace_flops,
-                   (double)batch * sL * (2.0 + (W.ptrs || W.base ? 8.0 : 0.0) + (Oout ? 2.0 : 0.0)),
-                   s);
+  const double bytes =
+      (double)batch * sL * (2.0 + (W.ptrs || W.base ? 8.0 : 0.0) + (Oout ? 2.0 : 0.0));
+  // Gram sides up to 64: the one-wave s x s path
+  const int sreal = tr ? mval : kval;
+  if (sreal <= 32) {
+    TraceScope trace("gram_ns_fused_32", trace_flops, bytes, s);
+    hipLaunchKernelGGL(k_gram_ns_tiny<1>, dim3(batch), dim3(NT), 0, s, p);
+    return hipGetLastError();
+  }
+  if (sreal <= TS) {
+    TraceScope trace("gram_ns_fused_64", trace_flops, bytes, s);
+    hipLaunchKernelGGL(k_gram_ns_tiny<2>, dim3(batch), dim3(NT), 0, s, p);
+    return hipGetLastError();
+  }
+  TraceScope trace("gram_ns_fused_128", trace_flops, bytes, s);
   hipLaunchKernelGGL(k_gram_ns_small, dim3(batch), dim3(NT), 0, s, p);
   return hipGetLastError();
 }

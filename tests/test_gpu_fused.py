@@ -40,8 +40,11 @@ def same(a, b):
 
 # (n, m, k): k <= m with the Gram on X X^T, k > m with X^T X (m <= 128),
 # ragged sides, one row, one column, long rows (L = 4096)
+# (sides up to 32 and up to 64 take the one-wave kernel, larger sides the
+# 128-padded one)
 FUSED_STEP_CASES = [(128, 512, 32), (300, 200, 75), (512, 512, 128), (1024, 96, 512),
-                    (200, 128, 200), (64, 4096, 16), (130, 1, 5), (1, 16, 1), (129, 129, 128)]
+                    (200, 128, 200), (64, 4096, 16), (130, 1, 5), (1, 16, 1), (129, 129, 128),
+                    (300, 200, 40), (300, 200, 64), (120, 40, 100), (100, 30, 90), (65, 700, 33)]
 
 
 @pytest.mark.parametrize("n,m,k", FUSED_STEP_CASES)
@@ -57,11 +60,12 @@ def test_fused_step_equals_tiled_bitwise(n, m, k):
     print(f"{n}x{m} k={k}: fused O rel err {err:.3e}", flush=True)
 
 
+@pytest.mark.parametrize("k,m", [(96, 333), (40, 333), (24, 256)])
 @pytest.mark.parametrize("iters,restarts", [(5, ()), (5, (2, 4)), (3, (2,)), (7, (3, 6)), (1, ()),
                                             (16, (4, 8, 12, 16))])
-def test_fused_schedules(iters, restarts):
-    say("fused schedule", iters, restarts)
-    X = dev(host_gaussian((3, 96, 333), [42, iters]).astype(np.float16))
+def test_fused_schedules(iters, restarts, k, m):
+    say("fused schedule", iters, restarts, k, m)
+    X = dev(host_gaussian((3, k, m), [42, iters]).astype(np.float16))
     co = [orc.MUON_COEFFS] * iters
     fused = d3.gram_ns(X, d3.ns_cfg(iters=iters, restart_at=restarts, coeffs=co,
                                     path=d3.PATH_FUSED)).cpu().numpy()
@@ -105,10 +109,11 @@ def test_long_schedule_without_restart_stays_finite(k, m):
         assert rel(_polar(O[b]), _polar(X[b])) <= O_TOL
 
 
-def test_fused_transposed_gram_ns():
+@pytest.mark.parametrize("m", [100, 50, 20])
+def test_fused_transposed_gram_ns(m):
     """k > m: the Gram is X^T X and the multiply-back runs along k."""
-    say("fused gram_ns k>m")
-    X = dev(host_gaussian((2, 700, 100), 43).astype(np.float16))
+    say("fused gram_ns k>m", m)
+    X = dev(host_gaussian((2, 700, m), 43).astype(np.float16))
     fused = d3.gram_ns(X, d3.ns_cfg(path=d3.PATH_FUSED)).cpu().numpy()
     tiled = d3.gram_ns(X, d3.ns_cfg(path=d3.PATH_TILED)).cpu().numpy()
     assert same(fused, tiled)
@@ -117,16 +122,17 @@ def test_fused_transposed_gram_ns():
         assert rel(fused[b], orc.ns_gram(Xh[b].astype(np.float64), orc.default_coeffs(), (3,))) <= O_TOL
 
 
-def test_fused_restart_on_lowrank():
-    """Ill-conditioned input: the restart lives inside the fused kernel too."""
-    say("fused lowrank")
-    M = host_lowrank(100, 2048, 44)
+@pytest.mark.parametrize("k", [100, 60])
+def test_fused_restart_on_lowrank(k):
+    """Ill-conditioned input: the restart lives inside the fused kernels too."""
+    say("fused lowrank", k)
+    M = host_lowrank(k, 2048, 44)
     Xn = (M.astype(np.float64) / np.linalg.norm(M.astype(np.float64))).astype(np.float16)
     ref = orc.ns_gram(Xn.astype(np.float64), orc.default_coeffs(), (3,))
     fused = d3.gram_ns(dev(Xn), d3.ns_cfg(path=d3.PATH_FUSED)).cpu().numpy()
     tiled = d3.gram_ns(dev(Xn), d3.ns_cfg(path=d3.PATH_TILED)).cpu().numpy()
     assert same(fused, tiled)
-    print(f"lowrank 100x2048 fused rel err {rel(fused, ref):.3e}", flush=True)
+    print(f"lowrank {k}x2048 fused rel err {rel(fused, ref):.3e}", flush=True)
     assert rel(fused, ref) <= O_TOL
 
 
@@ -152,20 +158,22 @@ def test_fused_megabatch_equals_tiled_bitwise():
         check_step(Ws[b], Ms[b], Wf[b], Mf[b], If[b], Of[b], k, 0.04, 0.95)
 
 
-def test_fused_trace_records_one_launch():
-    say("fused trace")
+@pytest.mark.parametrize("k,name", [(75, "gram_ns_fused_128"), (64, "gram_ns_fused_64"),
+                                    (32, "gram_ns_fused_32")])
+def test_fused_trace_records_one_launch(k, name):
+    say("fused trace", k)
     W = dev(host_gaussian((300, 500), 47, std=0.02))
     M = dev(host_gaussian((300, 500), 48))
     cfg = d3.ns_cfg(path=d3.PATH_FUSED)
-    d3.step(W, M, 75, 0.04, 0.95, cfg)
+    d3.step(W, M, k, 0.04, 0.95, cfg)
     torch.cuda.synchronize()
     d3.trace_enable(64)
     try:
-        d3.step(W, M, 75, 0.04, 0.95, cfg)
+        d3.step(W, M, k, 0.04, 0.95, cfg)
         recs = d3.trace_records()
     finally:
         d3.trace_disable()
-    assert [r[0] for r in recs] == ["row_score", "topk", "gather", "gram_ns_fused_128"]
-    s_, L_ = 75.0, 500.0
+    assert [r[0] for r in recs] == ["row_score", "topk", "gather", name]
+    s_, L_ = float(k), 500.0
     assert recs[3][2] == pytest.approx(6 * s_ * s_ * L_ + 14 * s_ ** 3)
     assert recs[3][1] > 0
