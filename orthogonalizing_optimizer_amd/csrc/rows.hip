@@ -275,6 +275,52 @@ __global__ __launch_bounds__(TK_THREADS) void k_topk(const double* __restrict__ 
   if (tid == 0) scale[b] = 1.0 / (sqrt(red_sh[0]) + eps);
 }
 
+// Top-k for matrices of at most 256 rows, one thread per row: a row's rank
+// is the number of rows ahead of it (a larger score, or an equal one at a
+// lower index, scores compared as the same fp64 bit patterns as k_topk), the
+// rows of rank < k are taken and written in index order through wave
+// ballots, and ||X||_F^2 goes through k_topk's fixed tree (whose levels above
+// 256 only add zeros when n <= 256), so idx and scale are k_topk's bit for
+// bit with a handful of barriers instead of about seventy.
+constexpr int TKS_THREADS = 256;
+
+__global__ __launch_bounds__(TKS_THREADS) void k_topk_small(const double* __restrict__ l1,
+                                                          const double* __restrict__ sq, int n,
+                                                          int k, int* __restrict__ idx,
+                                                          double* __restrict__ scale, double eps) {
+  __shared__ unsigned long long key_sh[TKS_THREADS];
+  __shared__ int wcnt_sh[TKS_THREADS / 64];
+  __shared__ double red_sh[TKS_THREADS];
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const bool all = k >= n, valid = tid < n;
+  unsigned long long key = 0;
+  if (!all && valid) key = (unsigned long long)__double_as_longlong(l1[(long long)b * n + tid]);
+  key_sh[tid] = key;
+  __syncthreads();
+  bool take = valid;
+  if (!all && valid) {
+    int ahead = 0;
+    for (int j = 0; j < n; ++j) {
+      const unsigned long long kj = key_sh[j];
+      ahead += (kj > key) || (kj == key && j < tid);
+    }
+    take = ahead < k;
+  }
+  const unsigned long long bal = __ballot(take);
+  if (lane == 0) wcnt_sh[w] = __popcll(bal);
+  __syncthreads();
+  int pos = __popcll(bal & ((1ull << lane) - 1ull));
+  for (int v = 0; v < w; ++v) pos += wcnt_sh[v];
+  if (take) idx[(long long)b * k + pos] = tid;
+  red_sh[tid] = take ? sq[(long long)b * n + tid] : 0.0;
+  __syncthreads();
+  for (int off = TKS_THREADS / 2; off >= 1; off >>= 1) {
+    if (tid < off) red_sh[tid] += red_sh[tid + off];
+    __syncthreads();
+  }
+  if (tid == 0) scale[b] = 1.0 / (sqrt(red_sh[0]) + eps);
+}
+
 // ------------------------------------------------------------- gather
 
 // One block per 64 selected rows x 256 columns: reads 1 KB of each selected
@@ -453,7 +499,11 @@ hipError_t launch_row_score_f16(BatchPtr<const f16> X, int batch, int n, int m, 
 
 hipError_t launch_topk(const double* l1, const double* sq, int batch, int n, int k, int* idx,
                        double* scale, double eps, hipStream_t s) {
-  hipLaunchKernelGGL(k_topk, dim3(batch), dim3(TK_THREADS), 0, s, l1, sq, n, k, idx, scale, eps);
+  if (n <= TKS_THREADS)
+    hipLaunchKernelGGL(k_topk_small, dim3(batch), dim3(TKS_THREADS), 0, s, l1, sq, n, k, idx,
+                       scale, eps);
+  else
+    hipLaunchKernelGGL(k_topk, dim3(batch), dim3(TK_THREADS), 0, s, l1, sq, n, k, idx, scale, eps);
   return hipGetLastError();
 }
 

@@ -177,3 +177,18 @@ def test_fused_trace_records_one_launch(k, name):
     s_, L_ = float(k), 500.0
     assert recs[3][2] == pytest.approx(6 * s_ * s_ * L_ + 14 * s_ ** 3)
     assert recs[3][1] > 0
+
+
+@pytest.mark.parametrize("B,k,m", [(512, 32, 256), (256, 64, 512), (2, 32, 8192), (33, 64, 4096)])
+def test_auto_path_small_sides_equal_tiled_bitwise(B, k, m):
+    """Shapes the automatic rule now sends to the one-wave kernel (many small
+    matrices; Gram side 32 with rows up to 8192): bitwise the tiled result."""
+    say("auto small sides", B, k, m)
+    X = dev(host_gaussian((B, k, m), [49, B, k, m]).astype(np.float16))
+    auto = d3.gram_ns(X, d3.ns_cfg()).cpu().numpy()
+    tiled = d3.gram_ns(X, d3.ns_cfg(path=d3.PATH_TILED)).cpu().numpy()
+    assert same(auto, tiled)
+    Xh = X.cpu().numpy()
+    for b in (0, B - 1):
+        ref = orc.ns_gram(Xh[b].astype(np.float64), orc.default_coeffs(), (3,))
+        assert rel(auto[b], ref) <= O_TOL

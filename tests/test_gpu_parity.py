@@ -40,7 +40,8 @@ def run_step(W, M, k, lr, mu, cfg=None):
 SELECT_CASES = [
     ("gauss", 128, 512, 32), ("gauss", 1000, 77, 250), ("gauss", 1, 5, 1), ("gauss", 300, 300, 300),
     ("gauss", 13824, 8, 1728), ("tied", 37, 11, 5), ("tied", 4096, 64, 1024), ("tied", 999, 3, 998),
-    ("gauss", 2049, 130, 2048),
+    ("gauss", 2049, 130, 2048), ("tied", 256, 9, 100), ("tied", 200, 5, 199), ("gauss", 255, 33, 64),
+    ("tied", 257, 9, 100),
 ]
 
 
@@ -66,6 +67,26 @@ def test_row_select_batched():
     for b in range(3):
         l1, _ = orc.row_scores(M[b])
         assert np.array_equal(idx[b], orc.select_rows(l1, 123))
+
+
+@pytest.mark.parametrize("n,m,k", [(200, 96, 50), (256, 130, 256), (37, 300, 5), (129, 64, 128)])
+def test_small_topk_matches_radix_topk_bitwise(n, m, k):
+    """Matrices of at most 256 rows take the one-thread-per-row top-k.  With
+    zero momentum rows appended (300 rows in all: the radix top-k; zero rows
+    score 0 and are never taken) the step must give the same selection, the
+    same Frobenius scale and so the same outputs, bit for bit."""
+    say("small top-k", n, m, k)
+    W = host_gaussian((n, m), [60, n, m], std=0.02)
+    M = host_gaussian((n, m), [61, n, m])
+    pad = 300 - n
+    Wp = np.vstack([W, host_gaussian((pad, m), [62, n, m], std=0.02)])
+    Mp = np.vstack([M, np.zeros((pad, m), np.float32)])
+    W1, M1, S1, O1 = run_step(W, M, k, 0.04, 0.95)
+    W2, M2, S2, O2 = run_step(Wp, Mp, k, 0.04, 0.95)
+    assert np.array_equal(S1, S2)
+    assert O1.tobytes() == O2.tobytes()
+    assert W1.tobytes() == W2[:n].tobytes() and M1.tobytes() == M2[:n].tobytes()
+    assert W2[n:].tobytes() == Wp[n:].tobytes() and M2[n:].tobytes() == Mp[n:].tobytes()
 
 
 # ------------------------------------------------------------ symmetric kernels
