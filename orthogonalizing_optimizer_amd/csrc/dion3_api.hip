@@ -407,20 +407,20 @@ double gram_ns_flops(const Shape& P, const dion3_ns_cfg& cfg) {
 // runs one workgroup per matrix, so its time grows with the row length L
 // while the tiled launches spread long rows over many CUs.  Sides up to 64
 // take the one-wave kernel, which gains most.  Measured on MI355X, one
-// dion3_gram_ns call (us, fused / tiled): side 32: 37 / 137 at 1 x 32 x 512,
-// 110 / 195 at 1 x 32 x 4096, 230 / 298 at 16 x 32 x 8192, 292 / 434 at 64 x
-// 32 x 8192; side 64: 122 / 162 at 1 x 64 x 2048, 201 / 195 at 1 x 64 x 4096,
-// 252 / 279 at 64 x 64 x 4096, 394 / 302 at 16 x 64 x 8192, 84 / 480 at 512 x
-// 64 x 256; side 128: 114 / 153 at 1 x 128 x 1024, 172 / 169 at 1 x 128 x
-// 2048, 186 / 193 at 32 x 128 x 2048, 302 / 224 at 16 x 128 x 4096, 120 / 248
-// at 256 x 128 x 512.
+// dion3_gram_ns call (us, fused / tiled): side 32: 32 / 136 at 1 x 32 x 512,
+// 100 / 194 at 1 x 32 x 4096, 194 / 297 at 16 x 32 x 8192, 226 / 438 at 64 x
+// 32 x 8192; side 64: 191 / 195 at 1 x 64 x 4096, 200 / 212 at 16 x 64 x
+// 4096, 364 / 301 at 16 x 64 x 8192, 404 / 460 at 64 x 64 x 8192, 69 / 477 at
+// 512 x 64 x 256; side 128: 113 / 152 at 1 x 128 x 1024, 171 / 168 at 1 x 128
+// x 2048, 184 / 191 at 32 x 128 x 2048, 300 / 224 at 16 x 128 x 4096, 117 /
+// 247 at 256 x 128 x 512.
 bool use_fused(const Shape& P, const dion3_ns_cfg& cfg) {
   if (cfg.method != DION3_NS_GRAM) return false;
   if (cfg.path == DION3_PATH_TILED || P.sp != kTile) return false;
   if (cfg.path == DION3_PATH_FUSED) return true;
   const long long side = P.tr ? P.m : P.k;
   if (side <= 32) return P.Lp <= 8192;
-  if (side <= 64) return P.Lp <= 2048 || (P.Lp <= 4096 && P.B >= 32);
+  if (side <= 64) return P.Lp <= 4096 || (P.Lp <= 8192 && P.B >= 64);
   return P.Lp <= 1024 || (P.Lp <= 2048 && P.B >= 32);
 }
 
@@ -621,11 +621,13 @@ bool free_pair_is_b(const dion3_ns_cfg& cfg) {
 XPair pair_a(const GroupLayout& G, char* w) { return {(f16*)(w + G.o_Xa), (f16*)(w + G.o_XaT)}; }
 
 // The layouts of the selected rows that the orthogonalization reads: the
-// tiled Gram iteration reads only X_math (rows when k <= m, their transpose
-// when k > m); the fused small-Gram kernel and the standard iteration read
-// both.  The gather writes only those (a null pointer skips a layout).
+// tiled Gram iteration and the one-wave fused kernel (Gram sides up to 64)
+// read only X_math (rows when k <= m, their transpose when k > m); the
+// 128-padded fused kernel and the standard iteration read both.  The gather
+// writes only those (a null pointer skips a layout).
 XPair gather_layouts(const Shape& P, const dion3_ns_cfg& cfg, const XPair& x) {
-  if (cfg.method == DION3_NS_STANDARD || use_fused(P, cfg)) return x;
+  const long long side = P.tr ? P.m : P.k;
+  if (cfg.method == DION3_NS_STANDARD || (use_fused(P, cfg) && side > 64)) return x;
   return P.tr ? XPair{nullptr, x.XT} : XPair{x.X, nullptr};
 }
 XPair pair_b(const GroupLayout& G, char* w) { return {(f16*)(w + G.o_Xb), (f16*)(w + G.o_XbT)}; }

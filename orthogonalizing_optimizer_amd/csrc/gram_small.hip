@@ -572,31 +572,58 @@ __device__ __forceinline__ void tiny_gram(f16* R, const f16* X, int Lp, int wave
 }
 
 // Y = Q X_math over the L side in 32 x 32 output blocks (NB row blocks x
-// Lp / 32 column blocks, dealt to the waves in turn); X_math^T is read from
-// global memory (XT, Lp x 128), Q from LDS.  Each block goes through this
-// wave's staging (St, column-major: St[c][r]) and leaves in 16-byte runs: to
-// Y and YT (restart) or, in rows layout, into the update (final).
+// Lp / 32 column blocks, dealt to the waves in turn).  The block's operand,
+// X_math rows 0 .. 32 NB - 1 by 32 columns, is loaded one block ahead with
+// 16-byte runs, staged in this wave's LDS block (row stride TX) and read as
+// MFMA fragments (8 consecutive K of one column) with two transposing reads
+// each, so only the rows layout of X is ever read.  The output block goes
+// through the same LDS block (column-major: St[c][r]) and leaves in 16-byte
+// runs: to Y (restart) or, in rows layout, into the update (final).
+constexpr int TX = 32 + 8;       // row stride of the staged X_math block (halves)
+typedef __fp16 fp16x4_t __attribute__((__vector_size__(4 * sizeof(__fp16))));
+typedef __attribute__((address_space(3))) fp16x4_t lds_fp16x4;
+
 template <int NB>
-__device__ __forceinline__ void tiny_rect(const f16* Q, const f16* XT, int Lp, f16* Y, f16* YT,
-                                          f16* St, const SmallArgs& p, int b, bool final_pass,
-                                          int wave, int lane) {
+__device__ __forceinline__ void tiny_rect(const f16* Q, const f16* Xm, int Lp, f16* Y, f16* St,
+                                          const SmallArgs& p, int b, bool final_pass, int wave,
+                                          int lane) {
+  typedef f16 half4v __attribute__((ext_vector_type(4)));
   const int ncb = Lp / 32, nblk = NB * ncb;
   const int fr = (lane & 31) * TL + 8 * (lane >> 5);
-  // X_math^T fragments of the wave's next block are loaded one block ahead
+  // this lane's two 16-byte runs of the X block: run c = lane + 64 u is row
+  // c / 4, columns 8 (c % 4) ..
   auto load = [&](int blk, half8 (&f)[2 * NB]) {
     const int j0 = (blk % ncb) * 32;
-    const f16* xt = XT + (long long)(j0 + (lane & 31)) * S + 8 * (lane >> 5);
 #pragma unroll
-    for (int s = 0; s < 2 * NB; ++s) f[s] = *(const half8*)(xt + 16 * s);
+    for (int u = 0; u < 2 * NB; ++u) {
+      const int c = lane + 64 * u;
+      f[u] = *(const half8*)(Xm + (long long)(c >> 2) * Lp + j0 + (c & 3) * 8);
+    }
   };
+  // transposing-read address: row 8 (lane / 32) + (lane % 16) / 4, column
+  // 16 ((lane / 16) % 2) + 4 (lane % 4) of the staged block
+  const int toff = (8 * (lane >> 5) + ((lane & 15) >> 2)) * TX + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
   half8 xn[2 * NB];
   if (wave < nblk) load(wave, xn);
   for (int blk = wave; blk < nblk; blk += 4) {
     const int bi = blk / ncb, j0 = (blk - bi * ncb) * 32;
+#pragma unroll
+    for (int u = 0; u < 2 * NB; ++u) {
+      const int c = lane + 64 * u;
+      *(half8*)(St + (c >> 2) * TX + (c & 3) * 8) = xn[u];
+    }
+    wave_lds_fence();
+    if (blk + 4 < nblk) load(blk + 4, xn);
     half8 xf[2 * NB];
 #pragma unroll
-    for (int s = 0; s < 2 * NB; ++s) xf[s] = xn[s];
-    if (blk + 4 < nblk) load(blk + 4, xn);
+    for (int s = 0; s < 2 * NB; ++s) {
+      const f16* q = St + toff + 16 * s * TX;
+      const half4v lo =
+          __builtin_bit_cast(half4v, __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4*)q));
+      const half4v hi = __builtin_bit_cast(
+          half4v, __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4*)(q + 4 * TX)));
+      xf[s] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
     floatx16 acc;
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
@@ -605,6 +632,7 @@ __device__ __forceinline__ void tiny_rect(const f16* Q, const f16* XT, int Lp, f
       const half8 qf = *(const half8*)(Q + bi * 32 * TL + fr + 16 * s);
       acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(qf, xf[s], acc, 0, 0, 0);
     }
+    // the fragments are in registers: the block's LDS now stages the output
 #pragma unroll
     for (int v4 = 0; v4 < 4; ++v4) {
       const int r = acc_row(v4, lane), c = lane & 31;
@@ -614,21 +642,16 @@ __device__ __forceinline__ void tiny_rect(const f16* Q, const f16* XT, int Lp, f
       *(half4*)(St + c * TB + r) = h;
     }
     wave_lds_fence();
-    // 32 x 32 block = 128 runs of 8 per layout, two per lane
+    // 32 x 32 block = 128 runs of 8, two per lane
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int e = lane + 64 * u, a = e >> 2, c8 = (e & 3) * 8;
-      // column-major run: column a (of the block), rows c8..c8+7
-      const half8 colrun = *(const half8*)(St + a * TB + c8);
       const int row0 = bi * 32;
-      if (!final_pass) {
-        // YT[j0 + a][row0 + c8 ..]
-        *(half8*)(YT + (long long)(j0 + a) * S + row0 + c8) = colrun;
-      } else if (p.tr) {      // rows layout = transposed: O[j0 + a][row0 + c8 ..]
-        sink8(p, b, j0 + a, row0 + c8, colrun);
-      }
-      if (!final_pass || !p.tr) {
-        // row-major run: row a, columns c8..c8+7, gathered from St's columns
+      if (final_pass && p.tr) {
+        // rows layout = transposed: O[j0 + a][row0 + c8 ..], a column run
+        sink8(p, b, j0 + a, row0 + c8, *(const half8*)(St + a * TB + c8));
+      } else {
+        // row a, columns c8..c8+7, gathered from St's columns
         half8 rowrun;
 #pragma unroll
         for (int q = 0; q < 8; ++q) rowrun[q] = St[(c8 + q) * TB + a];
@@ -645,16 +668,18 @@ __device__ __forceinline__ void tiny_rect(const f16* Q, const f16* XT, int Lp, f
 template <int NB>
 __global__ __launch_bounds__(NT) void k_gram_ns_tiny(SmallArgs p) {
   __shared__ __attribute__((aligned(16))) f16 mats[4 * TS * TL];
-  __shared__ __attribute__((aligned(16))) f16 stage[4 * 32 * TB];
+  // per wave: the staged X_math block (32 NB x TX) and then the output block
+  // (32 x TB) in the same place
+  constexpr int SW = 32 * NB * TX > 32 * TB ? 32 * NB * TX : 32 * TB;
+  __shared__ __attribute__((aligned(16))) f16 stage[4 * SW];
   const int b = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // only the rows layout of X_math (and of the restart's output) is used
   f16* X = p.X + (long long)b * p.sX;
-  f16* XT = p.XT + (long long)b * p.sX;
   f16* Y = p.Y + (long long)b * p.sX;
-  f16* YT = p.YT + (long long)b * p.sX;
   f16 *R = mats, *Z = mats + TS * TL, *Q = mats + 2 * TS * TL, *T = mats + 3 * TS * TL;
-  f16* St = stage + wave * 32 * TB;
+  f16* St = stage + wave * SW;
   const int sreal = p.tr ? p.mval : p.kval;
   tiny_gram<NB>(R, X, p.Lp, wave, lane);
   __syncthreads();
@@ -664,9 +689,8 @@ __global__ __launch_bounds__(NT) void k_gram_ns_tiny(SmallArgs p) {
     if (is_restart(p.cfg, t)) {      // X <- Q X, R <- X X^T, Q <- I
       if (!q_identity) {
         __syncthreads();             // Q complete
-        tiny_rect<NB>(Q, XT, p.Lp, Y, YT, St, p, b, false, wave, lane);
+        tiny_rect<NB>(Q, X, p.Lp, Y, St, p, b, false, wave, lane);
         f16* tx = X; X = Y; Y = tx;
-        f16* tt = XT; XT = YT; YT = tt;
         __syncthreads();             // the new X in memory, Q read
       }
       tiny_gram<NB>(R, X, p.Lp, wave, lane);
@@ -692,7 +716,7 @@ __global__ __launch_bounds__(NT) void k_gram_ns_tiny(SmallArgs p) {
     }
   }
   __syncthreads();                   // Q complete
-  tiny_rect<NB>(Q, XT, p.Lp, Y, YT, St, p, b, true, wave, lane);
+  tiny_rect<NB>(Q, X, p.Lp, Y, St, p, b, true, wave, lane);
 }
 }  // namespace
 

@@ -158,9 +158,12 @@ def test_fused_megabatch_equals_tiled_bitwise():
         check_step(Ws[b], Ms[b], Wf[b], Mf[b], If[b], Of[b], k, 0.04, 0.95)
 
 
-@pytest.mark.parametrize("k,name", [(75, "gram_ns_fused_128"), (64, "gram_ns_fused_64"),
-                                    (32, "gram_ns_fused_32")])
-def test_fused_trace_records_one_launch(k, name):
+# the 128-padded kernel reads both layouts of X (gather), the one-wave
+# kernel only the rows layout (gather_rows)
+@pytest.mark.parametrize("k,gather,name", [(75, "gather", "gram_ns_fused_128"),
+                                           (64, "gather_rows", "gram_ns_fused_64"),
+                                           (32, "gather_rows", "gram_ns_fused_32")])
+def test_fused_trace_records_one_launch(k, gather, name):
     say("fused trace", k)
     W = dev(host_gaussian((300, 500), 47, std=0.02))
     M = dev(host_gaussian((300, 500), 48))
@@ -173,7 +176,7 @@ def test_fused_trace_records_one_launch(k, name):
         recs = d3.trace_records()
     finally:
         d3.trace_disable()
-    assert [r[0] for r in recs] == ["row_score", "topk", "gather", name]
+    assert [r[0] for r in recs] == ["row_score", "topk", gather, name]
     s_, L_ = float(k), 500.0
     assert recs[3][2] == pytest.approx(6 * s_ * s_ * L_ + 14 * s_ ** 3)
     assert recs[3][1] > 0
