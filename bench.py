@@ -370,29 +370,43 @@ def main():
             graph.replay()
             torch.cuda.synchronize()
         launches_per_step = len(groups) * (3 + 2 * (1 + cfg.n_restart) + 5 * cfg.iters + 8)
-        if not no_trace:
-            d3.trace_enable(launches_per_step * args.steps + 64)
         stream = torch.cuda.current_stream()
-        # one event before the first step and one after each step: the mean
-        # over the whole timed region is the reported value; the per-step
-        # times give its spread
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-        torch.cuda.synchronize()
-        evs[0].record(stream)
-        for i in range(args.steps):
-            if graph is not None:
-                graph.replay()
-            else:
-                one_step()
-            evs[i + 1].record(stream)
-        torch.cuda.synchronize()
-        ms_per_step = evs[0].elapsed_time(evs[-1]) / args.steps
-        step_ms = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
+
+        def timed(trace):
+            # one event before the first step and one after each step: the
+            # mean over the whole timed region, and the per-step times for
+            # its spread; with `trace`, the library's per-kernel events too
+            if trace:
+                d3.trace_enable(launches_per_step * args.steps + 64)
+            evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+            torch.cuda.synchronize()
+            evs[0].record(stream)
+            for i in range(args.steps):
+                if graph is not None:
+                    graph.replay()
+                else:
+                    one_step()
+                evs[i + 1].record(stream)
+            torch.cuda.synchronize()
+            recs = None
+            if trace:
+                recs = d3.trace_records()
+                d3.trace_disable()
+            return (evs[0].elapsed_time(evs[-1]) / args.steps,
+                    sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)), recs)
+
+        # the reported step time comes from steps with the trace off (on small
+        # steps its events cost a few microseconds per kernel); the same
+        # number of steps then runs again with it on, for the per-kernel
+        # figures and the roofline
+        ms_per_step, step_ms, _ = timed(False)
         kernels, by_shape = {}, {}
+        ms_traced = None
         if not no_trace:
-            kernels, by_shape = kernel_stats(d3.trace_records(), args.steps)
-            d3.trace_disable()
-        log(f"-- {wl.name} at f = {fraction}: {ms_per_step:.3f} ms per step")
+            ms_traced, _, recs = timed(True)
+            kernels, by_shape = kernel_stats(recs, args.steps)
+        log(f"-- {wl.name} at f = {fraction}: {ms_per_step:.3f} ms per step"
+            + (f" ({ms_traced:.3f} with the kernel trace on)" if ms_traced is not None else ""))
         for (name, fl, by), st in sorted(by_shape.items()):
             rate = (f"{st['tflops']:7.1f} TFLOP/s" if fl > 0 else "") + \
                    (f"  {st['gbs']:7.1f} GB/s" if by > 0 else "")
@@ -417,6 +431,7 @@ def main():
                if samples else None)
         return {
             "ms_per_step": round(ms_per_step, 3),
+            "ms_per_step_traced": round(ms_traced, 3) if ms_traced is not None else None,
             "k": [gr.k for gr in groups], "lr": round(lr, 6),
             "matrices_per_s": round(wl.n_matrices / (ms_per_step * 1e-3), 1),
             "step_ms": {"median": round(float(np.median(step_ms)), 4),
