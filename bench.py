@@ -463,6 +463,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": head["ms_per_step"],
+        "ms_per_step_traced": head["ms_per_step_traced"],
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
