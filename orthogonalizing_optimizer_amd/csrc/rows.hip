@@ -440,16 +440,20 @@ __global__ __launch_bounds__(256) void k_gather(BatchPtr<T> M, int n, int m, lon
 // store, fp16 store), with no LDS tile.  The same arithmetic as k_gather,
 // element by element.  Short blocks with a single load per thread stream
 // faster than k_gather's 16 loads per thread (measured on the 7B shapes:
-// 5.6-6.2 against 5.3-5.6 TB/s in isolation).  Grid: x = kp / 4 row blocks,
-// y = column blocks, z = matrices.
+// 5.6-6.2 against 5.3-5.6 TB/s in isolation).  Grid: x = (kp / 4 row
+// blocks) x (column blocks), y = matrices.
 template <typename T, bool DECAY>
 __global__ __launch_bounds__(256) void k_gather_rows(BatchPtr<T> M, int n, int m, long long ld,
                                                      const int* __restrict__ idx, int k,
                                                      const double* __restrict__ scale, float mu,
                                                      f16* __restrict__ X, long long sX, int mp) {
-  const int b = blockIdx.z;
-  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int c = blockIdx.y * GC + 4 * (threadIdx.x & 63);
+  // workgroup x: column block fastest, so consecutive workgroups take
+  // consecutive 1 KB pieces of the same four rows
+  const int b = blockIdx.y;
+  const int ncb = (mp + GC - 1) / GC;
+  const int rg = blockIdx.x / ncb, cb = blockIdx.x - rg * ncb;
+  const int r = rg * 4 + (threadIdx.x >> 6);
+  const int c = cb * GC + 4 * (threadIdx.x & 63);
   if (c >= mp) return;
   int row = -1;
   if (r < k) {
@@ -511,7 +515,7 @@ hipError_t launch_gather_f32(BatchPtr<float> M, int batch, int n, int m, long lo
                              const int* idx, int k, const double* scale, float mu, bool decay,
                              f16* X, f16* XT, long long sX, int kp, int mp, hipStream_t s) {
   if (X && !XT) {
-    const dim3 grid(kp / 4, (mp + GC - 1) / GC, batch);
+    const dim3 grid((kp / 4) * ((mp + GC - 1) / GC), batch);
     if (decay)
       hipLaunchKernelGGL((k_gather_rows<float, true>), grid, dim3(256), 0, s, M, n, m, ld, idx, k,
                          scale, mu, X, sX, mp);
@@ -534,7 +538,7 @@ hipError_t launch_gather_f16(BatchPtr<const f16> Xin, int batch, int m, long lon
                              const double* scale, f16* X, f16* XT, long long sX, int kp, int mp,
                              hipStream_t s) {
   if (X && !XT) {
-    const dim3 grid(kp / 4, (mp + GC - 1) / GC, batch);
+    const dim3 grid((kp / 4) * ((mp + GC - 1) / GC), batch);
     hipLaunchKernelGGL((k_gather_rows<const f16, false>), grid, dim3(256), 0, s, Xin, k, m, ld,
                        nullptr, k, scale, 1.0f, X, sX, mp);
     return hipGetLastError();
