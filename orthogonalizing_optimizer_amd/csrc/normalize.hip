@@ -127,7 +127,7 @@ __global__ __launch_bounds__(256) void k_norm_stats(const float* __restrict__ pa
 // x 256 columns of O, one wave per row, one 16-byte W run and one 8-byte O
 // run per lane (short workgroups with a single load per thread stream faster
 // than one wave walking a whole row: measured on the 7B shapes).  Grid:
-// x = row groups of 4, y = 256-column blocks, z = matrices.
+// x = (row groups of 4) x (256-column blocks), y = matrices.
 // The scale g = sqrt(sum_i s_i / sum_i s_i r_i^2) comes from k_norm_stats'
 // per-workgroup sums, added in workgroup order (every thread of a matrix gets
 // the same bits).
@@ -136,9 +136,13 @@ __global__ __launch_bounds__(256) void k_norm_update(const f16* __restrict__ O, 
                                                      BatchPtr<float> W, long long ldw, float lr,
                                                      const float2* __restrict__ stats,
                                                      const double2* __restrict__ wsum, int nwg) {
-  const int b = blockIdx.z;
-  const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int j = blockIdx.y * 256 + 4 * (threadIdx.x & 63);
+  // workgroup x: column block fastest, so consecutive workgroups take
+  // consecutive pieces of the same four rows
+  const int b = blockIdx.y;
+  const int ncb = (m + 255) / 256;
+  const int rg = blockIdx.x / ncb, cb = blockIdx.x - rg * ncb;
+  const int i = rg * 4 + (threadIdx.x >> 6);
+  const int j = cb * 256 + 4 * (threadIdx.x & 63);
   if (i >= k || j >= m) return;
   double a0 = 0.0, a1 = 0.0;
   for (int q = 0; q < nwg; ++q) {
@@ -191,8 +195,8 @@ hipError_t launch_normalize(const f16* O, long long sO, int batch, int k, int m,
     if (e != hipSuccess) return e;
   }
   TraceScope ts("norm_update", 0.0, km * 10.0, s);
-  hipLaunchKernelGGL(k_norm_update, dim3((k + 3) / 4, (m + 255) / 256, batch), dim3(256), 0, s, O,
-                     sO, k, m, idx, W, ldw, lr, stats, wsum, nwg);
+  hipLaunchKernelGGL(k_norm_update, dim3(((k + 3) / 4) * ((m + 255) / 256), batch), dim3(256), 0,
+                     s, O, sO, k, m, idx, W, ldw, lr, stats, wsum, nwg);
   return hipGetLastError();
 }
 
