@@ -100,6 +100,10 @@ def parse():
     p.add_argument("--also-fraction", default="1/2",
                    help="for the 7B set (c4), also step the same resident matrices at this "
                         "fraction and report it in a sub-object (\"none\" to skip)")
+    p.add_argument("--paths", action="store_true",
+                   help="only time one dion3_gram_ns call on the fused and the tiled path for "
+                        "Gram sides up to 128 (the measurements behind the automatic path "
+                        "rule) and print the table")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 2 GiB device-to-device copy (a known-size kernel for "
                         "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE) and print its GB/s")
@@ -126,6 +130,52 @@ def copy_calibration():
     ms = e0.elapsed_time(e1) / reps
     print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n,
                       "ms": round(ms, 4), "gbs": round(8 * n / (ms * 1e-3) / 1e9, 1)}), flush=True)
+
+
+# (matrices, k, m) of the fused / tiled comparison: Gram sides 32, 64 and 128
+# at short and long rows, few and many matrices
+PATH_SHAPES = [(1, 32, 512), (1, 64, 512), (1, 32, 4096), (16, 32, 8192), (64, 32, 8192),
+               (1, 64, 2048), (1, 64, 4096), (16, 64, 4096), (64, 64, 4096), (16, 64, 8192),
+               (64, 64, 8192), (512, 32, 256), (512, 64, 256), (2048, 32, 512), (1, 128, 1024),
+               (1, 128, 2048), (32, 128, 2048), (16, 128, 4096), (256, 128, 512)]
+
+
+def path_crossover(reps: int = 20):
+    """One dion3_gram_ns call on the fused and on the tiled path (HIP events
+    around `reps` eager calls, after one warm-up call), and which path the
+    automatic rule takes (from the names of the kernels it launches)."""
+    import torch
+    import orthogonalizing_optimizer_amd as d3
+
+    def timed(X, path):
+        cfg = d3.ns_cfg(path=path)
+        d3.gram_ns(X, cfg)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            d3.gram_ns(X, cfg)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e3
+
+    rows = []
+    for B, k, m in PATH_SHAPES:
+        g = torch.Generator(device="cuda:0")
+        g.manual_seed(B * 7919 + k * 31 + m)
+        X = (torch.randn((B, k, m), generator=g, device="cuda:0") * 0.05).to(torch.float16)
+        fused, tiled = timed(X, d3.PATH_FUSED), timed(X, d3.PATH_TILED)
+        d3.trace_enable(4096)
+        d3.trace_reset()
+        d3.gram_ns(X, d3.ns_cfg())
+        auto = "fused" if any(r[0].startswith("gram_ns_fused") for r in d3.trace_records()) else "tiled"
+        d3.trace_disable()
+        rows.append({"matrices": B, "k": k, "m": m, "fused_us": round(fused, 1),
+                     "tiled_us": round(tiled, 1), "auto": auto})
+        log(f"{B:5d} x {k:4d} x {m:5d}: fused {fused:8.1f} us  tiled {tiled:8.1f} us  "
+            f"auto takes {auto}")
+        del X
+    print(json.dumps({"paths": rows, "reps": reps}), flush=True)
 
 
 def kernel_source_hash(kernel: str) -> str:
@@ -267,6 +317,9 @@ def main():
     args = parse()
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.paths:
+        path_crossover()
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: every matrix of a Dion3 step is independent, and this "
