@@ -578,7 +578,8 @@ __device__ __forceinline__ void tiny_gram(f16* R, const f16* X, int Lp, int wave
 // MFMA fragments (8 consecutive K of one column) with two transposing reads
 // each, so only the rows layout of X is ever read.  The output block goes
 // through the same LDS block (column-major: St[c][r]) and leaves in 16-byte
-// runs: to Y (restart) or, in rows layout, into the update (final).
+// runs: to Y (restart) or into the update (final; a W update in rows layout
+// takes tiny_final below instead).
 constexpr int TX = 32 + 8;       // row stride of the staged X_math block (halves)
 typedef __fp16 fp16x4_t __attribute__((__vector_size__(4 * sizeof(__fp16))));
 typedef __attribute__((address_space(3))) fp16x4_t lds_fp16x4;
@@ -665,6 +666,150 @@ __device__ __forceinline__ void tiny_rect(const f16* Q, const f16* Xm, int Lp, f
   }
 }
 
+// The final pass when the output rows are the selected rows of W (rows
+// layout, O = Q X_math) and W is updated: as tiny_rect's final pass, but the
+// selected-row indices of this lane's two output runs per row block are read
+// once up front, and each block's W runs are requested one block ahead
+// together with its X block, so they are in flight during the previous
+// block's products instead of starting after the block's own (megabatches
+// of 128 x 4096 matrices at f = 1/4: 191 -> 163 us per step; the same
+// arithmetic, so the same bits).
+template <int NB>
+__device__ __forceinline__ void tiny_final(const f16* Q, const f16* Xm, int Lp, f16* St,
+                                           const SmallArgs& p, int b, int wave, int lane) {
+  typedef f16 half4v __attribute__((ext_vector_type(4)));
+  const int ncb = Lp / 32, nblk = NB * ncb;
+  const int fr = (lane & 31) * TL + 8 * (lane >> 5);
+  float* Wb = (p.W.ptrs || p.W.base) ? p.W.get(b) : nullptr;
+  const bool vec = Wb && ((uintptr_t)Wb & 15) == 0 && (p.ldw & 3) == 0;
+  // selected W row of run u (output row 32 bi + (lane + 64 u) / 4), or -1
+  int rows0[2], rows1[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int a = (lane + 64 * u) >> 2;
+    int r0 = -1, r1 = -1;
+    if (Wb && a < p.kval) r0 = p.idx[(long long)b * p.kval + a];
+    if (NB == 2 && Wb && 32 + a < p.kval) r1 = p.idx[(long long)b * p.kval + 32 + a];
+    rows0[u] = (r0 >= 0 && r0 < p.nrows) ? r0 : -1;
+    rows1[u] = (r1 >= 0 && r1 < p.nrows) ? r1 : -1;
+  }
+  auto load = [&](int blk, half8 (&f)[2 * NB]) {
+    const int j0 = (blk % ncb) * 32;
+#pragma unroll
+    for (int u = 0; u < 2 * NB; ++u) {
+      const int c = lane + 64 * u;
+      f[u] = *(const half8*)(Xm + (long long)(c >> 2) * Lp + j0 + (c & 3) * 8);
+    }
+  };
+  auto wload = [&](int blk, float4 (&w)[2][2]) {
+    const int bi = blk / ncb, j0 = (blk - bi * ncb) * 32;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int row = (NB == 2 && bi) ? rows1[u] : rows0[u];
+      const int c = j0 + ((lane + 64 * u) & 3) * 8;
+      if (vec && row >= 0 && c + 8 <= p.mval) {
+        const float4* q = (const float4*)(Wb + (long long)row * p.ldw + c);
+        w[u][0] = q[0];
+        w[u][1] = q[1];
+      }
+    }
+  };
+  const int toff = (8 * (lane >> 5) + ((lane & 15) >> 2)) * TX + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  half8 xn[2 * NB];
+  float4 wn[2][2];
+  if (wave < nblk) {
+    load(wave, xn);
+    wload(wave, wn);
+  }
+  for (int blk = wave; blk < nblk; blk += 4) {
+    const int bi = blk / ncb, j0 = (blk - bi * ncb) * 32;
+#pragma unroll
+    for (int u = 0; u < 2 * NB; ++u) {
+      const int c = lane + 64 * u;
+      *(half8*)(St + (c >> 2) * TX + (c & 3) * 8) = xn[u];
+    }
+    float4 wc[2][2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      wc[u][0] = wn[u][0];
+      wc[u][1] = wn[u][1];
+    }
+    wave_lds_fence();
+    if (blk + 4 < nblk) {
+      load(blk + 4, xn);
+      wload(blk + 4, wn);
+    }
+    half8 xf[2 * NB];
+#pragma unroll
+    for (int s = 0; s < 2 * NB; ++s) {
+      const f16* q = St + toff + 16 * s * TX;
+      const half4v lo =
+          __builtin_bit_cast(half4v, __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4*)q));
+      const half4v hi = __builtin_bit_cast(
+          half4v, __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4*)(q + 4 * TX)));
+      xf[s] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+    floatx16 acc;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
+#pragma unroll
+    for (int s = 0; s < 2 * NB; ++s) {
+      const half8 qf = *(const half8*)(Q + bi * 32 * TL + fr + 16 * s);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(qf, xf[s], acc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int v4 = 0; v4 < 4; ++v4) {
+      const int r = acc_row(v4, lane), c = lane & 31;
+      half4 h;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) h[e] = (f16)acc[4 * v4 + e];
+      *(half4*)(St + c * TB + r) = h;
+    }
+    wave_lds_fence();
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int e = lane + 64 * u, a = e >> 2, c8 = (e & 3) * 8;
+      half8 v;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[q] = St[(c8 + q) * TB + a];
+      const int orow = bi * 32 + a, ocol = j0 + c8;
+      if (orow >= p.kval || ocol >= p.mval) continue;
+      const bool full = ocol + 8 <= p.mval;
+      if (p.Oout) {
+        f16* o = p.Oout + (long long)b * p.sO + (long long)orow * p.mval + ocol;
+        if (full && ((uintptr_t)o & 15) == 0) {
+          *(half8*)o = v;
+        } else {
+#pragma unroll
+          for (int q = 0; q < 8; ++q)
+            if (ocol + q < p.mval) o[q] = v[q];
+        }
+      }
+      const int row = (NB == 2 && bi) ? rows1[u] : rows0[u];
+      if (row < 0) continue;
+      float* wp = Wb + (long long)row * p.ldw + ocol;
+      if (vec && full) {
+        float4 w0 = wc[u][0], w1 = wc[u][1];
+        w0.x = __builtin_fmaf(-p.lr, (float)v[0], w0.x);
+        w0.y = __builtin_fmaf(-p.lr, (float)v[1], w0.y);
+        w0.z = __builtin_fmaf(-p.lr, (float)v[2], w0.z);
+        w0.w = __builtin_fmaf(-p.lr, (float)v[3], w0.w);
+        w1.x = __builtin_fmaf(-p.lr, (float)v[4], w1.x);
+        w1.y = __builtin_fmaf(-p.lr, (float)v[5], w1.y);
+        w1.z = __builtin_fmaf(-p.lr, (float)v[6], w1.z);
+        w1.w = __builtin_fmaf(-p.lr, (float)v[7], w1.w);
+        ((float4*)wp)[0] = w0;
+        ((float4*)wp)[1] = w1;
+      } else {
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          if (ocol + q < p.mval) wp[q] = __builtin_fmaf(-p.lr, (float)v[q], wp[q]);
+      }
+    }
+    wave_lds_fence();   // the next block's staging overwrites St
+  }
+}
+
 template <int NB>
 __global__ __launch_bounds__(NT) void k_gram_ns_tiny(SmallArgs p) {
   __shared__ __attribute__((aligned(16))) f16 mats[4 * TS * TL];
@@ -716,7 +861,8 @@ __global__ __launch_bounds__(NT) void k_gram_ns_tiny(SmallArgs p) {
     }
   }
   __syncthreads();                   // Q complete
-  tiny_rect<NB>(Q, X, p.Lp, Y, St, p, b, true, wave, lane);
+  if (p.tr || !(p.W.ptrs || p.W.base)) tiny_rect<NB>(Q, X, p.Lp, Y, St, p, b, true, wave, lane);
+  else tiny_final<NB>(Q, X, p.Lp, St, p, b, wave, lane);
 }
 }  // namespace
 
