@@ -459,14 +459,22 @@ __device__ __forceinline__ int acc_row(int v4, int lane) { return 8 * v4 + 4 * (
 
 // Stores the fp16 value h (4 consecutive rows p..p+3 of column q) of a
 // symmetric result: the lower elements (row >= column) at both (row, col)
-// and (col, row); the upper ones come from their mirror.
+// and (col, row); the upper ones come from their mirror.  An upper element of
+// a diagonal block is written to the row's padding columns TS .. TS + 7,
+// which nothing reads, instead of being skipped: the stores need no branch
+// (a branch per element took about 40 % of a 32 x 32 product's time).
+// OPAQUE hides p and q from the optimizer, which otherwise keeps every
+// store address of every product in registers (two waves per SIMD instead
+// of three for the 64-side kernel).
+template <bool OPAQUE>
 __device__ __forceinline__ void store_sym4(f16* out, int p, int q, bool diag, const half4& h) {
+  if (OPAQUE) asm volatile("" : "+v"(p), "+v"(q));
 #pragma unroll
-  for (int e = 0; e < 4; ++e)
-    if (!diag || p + e >= q) {
-      out[(p + e) * TL + q] = h[e];
-      out[q * TL + p + e] = h[e];
-    }
+  for (int e = 0; e < 4; ++e) {
+    const bool keep = !diag || p + e >= q;
+    out[(p + e) * TL + (keep ? q : TS + e)] = h[e];
+    out[q * TL + (keep ? p + e : TS + 4 + e)] = h[e];
+  }
 }
 
 // out = alpha A B + beta D + gamma I (POLY) or A B for symmetric NB x NB-block
@@ -520,54 +528,69 @@ __device__ __forceinline__ void tiny_symm(f16* out, const f16* A, const f16* B, 
         half4 h;
 #pragma unroll
         for (int e = 0; e < 4; ++e) h[e] = (f16)val[e];
-        store_sym4(out, p, q, i == j, h);
+        store_sym4<(NB > 1)>(out, p, q, i == j, h);
       }
   wave_lds_fence();
 }
 
-// R = X X^T (K = Lp, X rows in global memory, row stride Lp): lower block
-// (bi, bj) on wave bi (bi + 1) / 2 + bj, the K loop in increasing order, its
-// loads two batches of 4 k-groups ahead.  The caller's barrier follows.
-template <int NB>
-__device__ __forceinline__ void tiny_gram(f16* R, const f16* X, int Lp, int wave, int lane) {
-  constexpr int NL = NB * (NB + 1) / 2, G = 4;
-  if (wave >= NL) return;
-  const int bi = (NB == 2 && wave >= 1) ? 1 : 0, bj = (NB == 2 && wave == 2) ? 1 : 0;
-  const bool dg = bi == bj;
-  const f16* xa = X + (long long)(bi * 32 + (lane & 31)) * Lp + 8 * (lane >> 5);
-  const f16* xb = X + (long long)(bj * 32 + (lane & 31)) * Lp + 8 * (lane >> 5);
+// One Gram block's accumulator over K = 16 ng (ng a multiple of 8): the
+// k-groups in increasing order, in batches of 4 with two batches in flight
+// (each pass multiplies the older batch and requests the one after the
+// newer).  The loop is peeled so that its loads are unconditional and each
+// wait counts only the loads it needs (with a conditional load the compiler
+// waited for every load before each batch).
+template <bool DG>
+__device__ __forceinline__ floatx16 tiny_gram_acc(const f16* xa, const f16* xb, int ng) {
+  constexpr int G = 4;
   floatx16 acc;
 #pragma unroll
   for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
-  const int ng = Lp / 16;   // a multiple of 2 G (Lp is a multiple of 128)
   half8 fa[2][G], fb[2][G];
   auto load = [&](int h, int g0) {
 #pragma unroll
     for (int u = 0; u < G; ++u) {
       fa[h][u] = *(const half8*)(xa + 16 * (g0 + u));
-      if (!dg) fb[h][u] = *(const half8*)(xb + 16 * (g0 + u));
+      if (!DG) fb[h][u] = *(const half8*)(xb + 16 * (g0 + u));
     }
   };
   auto run = [&](int h) {
 #pragma unroll
     for (int u = 0; u < G; ++u)
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[h][u], dg ? fa[h][u] : fb[h][u], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[h][u], DG ? fa[h][u] : fb[h][u], acc, 0, 0, 0);
   };
   load(0, 0);
-  for (int g0 = 0; g0 < ng; g0 += 2 * G) {
-    if (g0 + G < ng) load(1, g0 + G);
+  load(1, G);
+  for (int g0 = 0; g0 + 2 * G < ng; g0 += 2 * G) {
     run(0);
-    if (g0 + G >= ng) break;
-    if (g0 + 2 * G < ng) load(0, g0 + 2 * G);
+    load(0, g0 + 2 * G);
     run(1);
+    load(1, g0 + 3 * G);
   }
+  run(0);
+  run(1);
+  return acc;
+}
+
+// R = X X^T (K = Lp, X rows in global memory, row stride Lp): lower block
+// (bi, bj) on wave bi (bi + 1) / 2 + bj (tiny_gram_acc).  The caller's
+// barrier follows.
+template <int NB>
+__device__ __forceinline__ void tiny_gram(f16* R, const f16* X, int Lp, int wave, int lane) {
+  constexpr int NL = NB * (NB + 1) / 2;
+  if (wave >= NL) return;
+  const int bi = (NB == 2 && wave >= 1) ? 1 : 0, bj = (NB == 2 && wave == 2) ? 1 : 0;
+  const bool dg = bi == bj;
+  const f16* xa = X + (long long)(bi * 32 + (lane & 31)) * Lp + 8 * (lane >> 5);
+  const f16* xb = X + (long long)(bj * 32 + (lane & 31)) * Lp + 8 * (lane >> 5);
+  const int ng = Lp / 16;   // a multiple of 8 (Lp is a multiple of 128)
+  const floatx16 acc = dg ? tiny_gram_acc<true>(xa, xa, ng) : tiny_gram_acc<false>(xa, xb, ng);
 #pragma unroll
   for (int v4 = 0; v4 < 4; ++v4) {
     const int p = bi * 32 + acc_row(v4, lane), q = bj * 32 + (lane & 31);
     half4 h;
 #pragma unroll
     for (int e = 0; e < 4; ++e) h[e] = (f16)acc[4 * v4 + e];
-    store_sym4(R, p, q, dg, h);
+    store_sym4<(NB > 1)>(R, p, q, dg, h);
   }
 }
 
@@ -673,7 +696,9 @@ __device__ __forceinline__ void tiny_rect(const f16* Q, const f16* Xm, int Lp, f
 // together with its X block, so they are in flight during the previous
 // block's products instead of starting after the block's own (megabatches
 // of 128 x 4096 matrices at f = 1/4: 191 -> 163 us per step; the same
-// arithmetic, so the same bits).
+// arithmetic, so the same bits).  Every pass issues the same loads (see
+// wload and the next-block index), so the waits before a block's staging
+// and update count only the loads that block needs.
 template <int NB>
 __device__ __forceinline__ void tiny_final(const f16* Q, const f16* Xm, int Lp, f16* St,
                                            const SmallArgs& p, int b, int wave, int lane) {
@@ -701,17 +726,19 @@ __device__ __forceinline__ void tiny_final(const f16* Q, const f16* Xm, int Lp, 
       f[u] = *(const half8*)(Xm + (long long)(c >> 2) * Lp + j0 + (c & 3) * 8);
     }
   };
+  // W runs of a block, read by every lane (a lane whose run does not take
+  // this path reads W's first 8 elements instead)
+  const bool pre = vec && p.mval >= 8;
   auto wload = [&](int blk, float4 (&w)[2][2]) {
     const int bi = blk / ncb, j0 = (blk - bi * ncb) * 32;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int row = (NB == 2 && bi) ? rows1[u] : rows0[u];
       const int c = j0 + ((lane + 64 * u) & 3) * 8;
-      if (vec && row >= 0 && c + 8 <= p.mval) {
-        const float4* q = (const float4*)(Wb + (long long)row * p.ldw + c);
-        w[u][0] = q[0];
-        w[u][1] = q[1];
-      }
+      const bool real = row >= 0 && c + 8 <= p.mval;
+      const float4* q = (const float4*)(real ? Wb + (long long)row * p.ldw + c : Wb);
+      w[u][0] = q[0];
+      w[u][1] = q[1];
     }
   };
   const int toff = (8 * (lane >> 5) + ((lane & 15) >> 2)) * TX + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
@@ -719,7 +746,7 @@ __device__ __forceinline__ void tiny_final(const f16* Q, const f16* Xm, int Lp, 
   float4 wn[2][2];
   if (wave < nblk) {
     load(wave, xn);
-    wload(wave, wn);
+    if (pre) wload(wave, wn);
   }
   for (int blk = wave; blk < nblk; blk += 4) {
     const int bi = blk / ncb, j0 = (blk - bi * ncb) * 32;
@@ -735,10 +762,10 @@ __device__ __forceinline__ void tiny_final(const f16* Q, const f16* Xm, int Lp, 
       wc[u][1] = wn[u][1];
     }
     wave_lds_fence();
-    if (blk + 4 < nblk) {
-      load(blk + 4, xn);
-      wload(blk + 4, wn);
-    }
+    // the next block's operands (the last block requests its own again)
+    const int nx = blk + 4 < nblk ? blk + 4 : blk;
+    load(nx, xn);
+    if (pre) wload(nx, wn);
     half8 xf[2 * NB];
 #pragma unroll
     for (int s = 0; s < 2 * NB; ++s) {
@@ -788,7 +815,7 @@ __device__ __forceinline__ void tiny_final(const f16* Q, const f16* Xm, int Lp, 
       const int row = (NB == 2 && bi) ? rows1[u] : rows0[u];
       if (row < 0) continue;
       float* wp = Wb + (long long)row * p.ldw + ocol;
-      if (vec && full) {
+      if (pre && full) {
         float4 w0 = wc[u][0], w1 = wc[u][1];
         w0.x = __builtin_fmaf(-p.lr, (float)v[0], w0.x);
         w0.y = __builtin_fmaf(-p.lr, (float)v[1], w0.y);
