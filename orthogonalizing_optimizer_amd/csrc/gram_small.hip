@@ -438,8 +438,9 @@ __global__ __launch_bounds__(NT, 1) void k_gram_ns_small(SmallArgs p) {
 // per side (NB), so each symmetric product of the iteration is a handful of
 // MFMAs.  One wave runs all of them back to back, with R, Z, Q and T in LDS
 // and no workgroup barrier between products (a wave's LDS accesses execute
-// in order); the Gram and the multiply-backs, which stream X, spread their
-// 32 x 32 output blocks over the four waves.  Every element is computed as
+// in order); the Gram (X staged through LDS by all four waves, one lower
+// 32 x 32 block per wave) and the multiply-backs (32 x 32 output blocks
+// dealt to the four waves) stream X.  Every element is computed as
 // in the tiled kernels: its k-groups of 16 in increasing order into one fp32
 // accumulator that starts at +0, the same epilogue, and symmetric results
 // taken from the lower triangle (so the bits equal the tiled path's).
@@ -533,64 +534,72 @@ __device__ __forceinline__ void tiny_symm(f16* out, const f16* A, const f16* B, 
   wave_lds_fence();
 }
 
-// One Gram block's accumulator over K = 16 ng (ng a multiple of 8): the
-// k-groups in increasing order, in batches of 4 with two batches in flight
-// (each pass multiplies the older batch and requests the one after the
-// newer).  The loop is peeled so that its loads are unconditional and each
-// wait counts only the loads it needs (with a conditional load the compiler
-// waited for every load before each batch).
-template <bool DG>
-__device__ __forceinline__ floatx16 tiny_gram_acc(const f16* xa, const f16* xb, int ng) {
-  constexpr int G = 4;
+// R = X X^T with X streamed through LDS by all four waves: chunks of CW
+// columns (32 NB rows x CW, 32 KB) are staged in `buf` (the s x s matrices'
+// space, all dead during a Gram) while the next chunk is already on its way
+// into registers; the lower 32 x 32 blocks accumulate on waves 0 .. NL - 1,
+// each from +0 over its k-groups in increasing order (the tiled Gram's order).
+// One wave reading X from global memory itself waited for every batch of
+// loads; here each chunk's loads have a whole chunk of MFMAs to arrive.
+template <int NB>
+__device__ __forceinline__ void tiny_gram_lds(f16* R, f16* buf, const f16* X, int Lp, int tid,
+                                              int wave, int lane) {
+  constexpr int NL = NB * (NB + 1) / 2, ROWS = 32 * NB, CW = 512 / NB, LS = CW + 8;
+  constexpr int CPR = CW / 8, NCH = ROWS * CPR / NT;   // 16-byte runs per row, per thread
+  static_assert(NCH * NT == ROWS * CPR && ROWS * LS <= 4 * TS * TL, "chunk fits");
+  const int nc = (Lp + CW - 1) / CW;
+  half8 pre[NCH];
+  auto gl = [&](int c0) {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int e = tid + NT * i, r = e / CPR, cc = (e % CPR) * 8;
+      if (c0 + cc < Lp) pre[i] = *(const half8*)(X + (long long)r * Lp + c0 + cc);
+    }
+  };
+  auto st = [&](int c0) {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int e = tid + NT * i, r = e / CPR, cc = (e % CPR) * 8;
+      if (c0 + cc < Lp) *(half8*)(buf + r * LS + cc) = pre[i];
+    }
+  };
+  const int bi = (NB == 2 && wave >= 1) ? 1 : 0, bj = (NB == 2 && wave == 2) ? 1 : 0;
+  const bool dg = bi == bj;
+  const f16* ra = buf + (bi * 32 + (lane & 31)) * LS + 8 * (lane >> 5);
+  const f16* rb = buf + (bj * 32 + (lane & 31)) * LS + 8 * (lane >> 5);
   floatx16 acc;
 #pragma unroll
   for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
-  half8 fa[2][G], fb[2][G];
-  auto load = [&](int h, int g0) {
+  gl(0);
+  for (int c = 0; c < nc; ++c) {
+    const int c0 = c * CW;
+    st(c0);
+    __syncthreads();
+    if (c + 1 < nc) gl(c0 + CW);
+    if (wave < NL) {
+      const int nkg = min(CW, Lp - c0) / 16;   // a multiple of 8
+      for (int kg = 0; kg < nkg; kg += 8) {
+        half8 a[8], b[8];
 #pragma unroll
-    for (int u = 0; u < G; ++u) {
-      fa[h][u] = *(const half8*)(xa + 16 * (g0 + u));
-      if (!DG) fb[h][u] = *(const half8*)(xb + 16 * (g0 + u));
+        for (int u = 0; u < 8; ++u) {
+          a[u] = *(const half8*)(ra + 16 * (kg + u));
+          b[u] = dg ? a[u] : *(const half8*)(rb + 16 * (kg + u));
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[u], b[u], acc, 0, 0, 0);
+      }
     }
-  };
-  auto run = [&](int h) {
-#pragma unroll
-    for (int u = 0; u < G; ++u)
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[h][u], DG ? fa[h][u] : fb[h][u], acc, 0, 0, 0);
-  };
-  load(0, 0);
-  load(1, G);
-  for (int g0 = 0; g0 + 2 * G < ng; g0 += 2 * G) {
-    run(0);
-    load(0, g0 + 2 * G);
-    run(1);
-    load(1, g0 + 3 * G);
+    __syncthreads();   // the chunk's reads end before the next chunk (or R) overwrites buf
   }
-  run(0);
-  run(1);
-  return acc;
-}
-
-// R = X X^T (K = Lp, X rows in global memory, row stride Lp): lower block
-// (bi, bj) on wave bi (bi + 1) / 2 + bj (tiny_gram_acc).  The caller's
-// barrier follows.
-template <int NB>
-__device__ __forceinline__ void tiny_gram(f16* R, const f16* X, int Lp, int wave, int lane) {
-  constexpr int NL = NB * (NB + 1) / 2;
-  if (wave >= NL) return;
-  const int bi = (NB == 2 && wave >= 1) ? 1 : 0, bj = (NB == 2 && wave == 2) ? 1 : 0;
-  const bool dg = bi == bj;
-  const f16* xa = X + (long long)(bi * 32 + (lane & 31)) * Lp + 8 * (lane >> 5);
-  const f16* xb = X + (long long)(bj * 32 + (lane & 31)) * Lp + 8 * (lane >> 5);
-  const int ng = Lp / 16;   // a multiple of 8 (Lp is a multiple of 128)
-  const floatx16 acc = dg ? tiny_gram_acc<true>(xa, xa, ng) : tiny_gram_acc<false>(xa, xb, ng);
+  if (wave < NL) {
 #pragma unroll
-  for (int v4 = 0; v4 < 4; ++v4) {
-    const int p = bi * 32 + acc_row(v4, lane), q = bj * 32 + (lane & 31);
-    half4 h;
+    for (int v4 = 0; v4 < 4; ++v4) {
+      const int p = bi * 32 + acc_row(v4, lane), q = bj * 32 + (lane & 31);
+      half4 h;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) h[e] = (f16)acc[4 * v4 + e];
-    store_sym4<(NB > 1)>(R, p, q, dg, h);
+      for (int e = 0; e < 4; ++e) h[e] = (f16)acc[4 * v4 + e];
+      store_sym4<(NB > 1)>(R, p, q, dg, h);
+    }
   }
 }
 
@@ -853,7 +862,7 @@ __global__ __launch_bounds__(NT) void k_gram_ns_tiny(SmallArgs p) {
   f16 *R = mats, *Z = mats + TS * TL, *Q = mats + 2 * TS * TL, *T = mats + 3 * TS * TL;
   f16* St = stage + wave * SW;
   const int sreal = p.tr ? p.mval : p.kval;
-  tiny_gram<NB>(R, X, p.Lp, wave, lane);
+  tiny_gram_lds<NB>(R, mats, X, p.Lp, tid, wave, lane);
   __syncthreads();
   bool q_identity = true;
   const int iters = p.cfg.iters;
@@ -865,7 +874,7 @@ __global__ __launch_bounds__(NT) void k_gram_ns_tiny(SmallArgs p) {
         f16* tx = X; X = Y; Y = tx;
         __syncthreads();             // the new X in memory, Q read
       }
-      tiny_gram<NB>(R, X, p.Lp, wave, lane);
+      tiny_gram_lds<NB>(R, mats, X, p.Lp, tid, wave, lane);
       __syncthreads();
       q_identity = true;
     }
