@@ -44,7 +44,8 @@ def same(a, b):
 # 128-padded one)
 FUSED_STEP_CASES = [(128, 512, 32), (300, 200, 75), (512, 512, 128), (1024, 96, 512),
                     (200, 128, 200), (64, 4096, 16), (130, 1, 5), (1, 16, 1), (129, 129, 128),
-                    (300, 200, 40), (300, 200, 64), (120, 40, 100), (100, 30, 90), (65, 700, 33)]
+                    (300, 200, 40), (300, 200, 64), (120, 40, 100), (100, 30, 90), (65, 700, 33),
+                    (20, 6, 3), (64, 13, 8)]
 
 
 @pytest.mark.parametrize("n,m,k", FUSED_STEP_CASES)
@@ -58,6 +59,32 @@ def test_fused_step_equals_tiled_bitwise(n, m, k):
         assert same(a, b), what
     err = check_step(W, M, *ft, k, 0.04, 0.95)
     print(f"{n}x{m} k={k}: fused O rel err {err:.3e}", flush=True)
+
+
+# W and M as column slices of wider buffers: row stride ld, first column off
+# (off > 0 or an odd ld leaves the rows without 16-byte alignment, so the
+# update takes its element path)
+@pytest.mark.parametrize("n,m,k,ld,off", [(96, 40, 24, 64, 0), (96, 40, 24, 65, 1),
+                                          (80, 200, 40, 203, 3), (300, 520, 60, 528, 4)])
+def test_fused_step_strided_equals_tiled_bitwise(n, m, k, ld, off):
+    say("fused step strided", n, m, k, ld, off)
+    W = host_gaussian((n, ld), [47, n, ld], std=0.02)
+    M = host_gaussian((n, ld), [48, n, ld])
+    outs = []
+    for path in (d3.PATH_FUSED, d3.PATH_TILED):
+        Wb, Mb = dev(W), dev(M)
+        idx, O = d3.step(Wb[:, off:off + m], Mb[:, off:off + m], k, 0.04, 0.95,
+                         d3.ns_cfg(path=path), return_idx=True, return_O=True)
+        torch.cuda.synchronize()
+        outs.append((Wb.cpu().numpy(), Mb.cpu().numpy(), idx.cpu().numpy(), O.cpu().numpy()))
+    for a, b, what in zip(outs[0], outs[1], ("W", "M", "idx", "O")):
+        assert same(a, b), what
+    W1, M1, S, O = outs[0]
+    for X0, X1 in ((W, W1), (M, M1)):   # columns outside the slice untouched
+        assert same(X0[:, :off], X1[:, :off]) and same(X0[:, off + m:], X1[:, off + m:])
+    sl = slice(off, off + m)
+    check_step(np.ascontiguousarray(W[:, sl]), np.ascontiguousarray(M[:, sl]),
+               np.ascontiguousarray(W1[:, sl]), np.ascontiguousarray(M1[:, sl]), S, O, k, 0.04, 0.95)
 
 
 @pytest.mark.parametrize("k,m", [(96, 333), (40, 333), (24, 256)])
