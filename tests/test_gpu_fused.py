@@ -45,7 +45,10 @@ def same(a, b):
 FUSED_STEP_CASES = [(128, 512, 32), (300, 200, 75), (512, 512, 128), (1024, 96, 512),
                     (200, 128, 200), (64, 4096, 16), (130, 1, 5), (1, 16, 1), (129, 129, 128),
                     (300, 200, 40), (300, 200, 64), (120, 40, 100), (100, 30, 90), (65, 700, 33),
-                    (20, 6, 3), (64, 13, 8)]
+                    (20, 6, 3), (64, 13, 8),
+                    # rows that end in a partial chunk of the Gram's LDS staging
+                    # (512 columns at sides up to 32, 256 up to 64), both orientations
+                    (100, 600, 20), (100, 300, 50), (2000, 20, 600), (1000, 50, 300)]
 
 
 @pytest.mark.parametrize("n,m,k", FUSED_STEP_CASES)
