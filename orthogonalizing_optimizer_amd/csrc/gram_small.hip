@@ -465,8 +465,8 @@ __device__ __forceinline__ int acc_row(int v4, int lane) { return 8 * v4 + 4 * (
 // which nothing reads, instead of being skipped: the stores need no branch
 // (a branch per element took about 40 % of a 32 x 32 product's time).
 // OPAQUE hides p and q from the optimizer, which otherwise keeps every
-// store address of every product in registers (two waves per SIMD instead
-// of three for the 64-side kernel).
+// store address of every product in registers (256 VGPRs and one wave per
+// SIMD for the 64-side kernel).
 template <bool OPAQUE>
 __device__ __forceinline__ void store_sym4(f16* out, int p, int q, bool diag, const half4& h) {
   if (OPAQUE) asm volatile("" : "+v"(p), "+v"(q));
