@@ -151,6 +151,38 @@ def test_gram_ns_schedules(iters, restarts):
         assert rel(O[b], ref) <= O_TOL
 
 
+# A coefficient table that changes from iteration to iteration (Muon's
+# quintic, the convergent (15/8, -10/8, 3/8) one, a third), on inputs and a
+# schedule for which the result depends strongly on which set each iteration
+# uses: the table reversed gives an oracle result far outside the tolerance,
+# so reading a set at the wrong iteration would fail.
+VARIED = [orc.MUON_COEFFS, (15 / 8, -10 / 8, 3 / 8), (3.0, -3.2, 1.2)]
+
+
+@pytest.mark.parametrize("method,path", [(d3.NS_GRAM, d3.PATH_TILED), (d3.NS_GRAM, d3.PATH_FUSED),
+                                         (d3.NS_STANDARD, d3.PATH_AUTO)])
+@pytest.mark.parametrize("k,m", [(96, 333), (24, 256), (300, 100)])
+def test_per_iteration_coefficients(method, path, k, m):
+    say("per-iteration coefficients", method, path, k, m)
+    # ill-conditioned rows (singular values spread as i^-1.5), far from the
+    # quintic's fixed point after three iterations
+    X = np.stack([host_lowrank(k, m, 53 + b) for b in range(2)]).astype(np.float16)
+    restarts = (2,) if method == d3.NS_GRAM else ()
+    cfg = d3.ns_cfg(iters=3, restart_at=restarts, coeffs=VARIED, method=method, path=path)
+    O = d3.gram_ns(dev(X), cfg).cpu().numpy()
+    for b in range(2):
+        Xb = X[b].astype(np.float64)
+        if method == d3.NS_GRAM:
+            ref, rev = orc.ns_gram(Xb, VARIED, restarts), orc.ns_gram(Xb, VARIED[::-1], restarts)
+        else:
+            ref, rev = orc.ns_standard(Xb, VARIED), orc.ns_standard(Xb, VARIED[::-1])
+        assert rel(rev, ref) > 5 * O_TOL      # the test can tell the tables apart
+        err = rel(O[b], ref)
+        print(f"{k}x{m} matrix {b}: O rel err {err:.3e} (reversed table {rel(rev, ref):.3e})",
+              flush=True)
+        assert err <= O_TOL, (b, err)
+
+
 @pytest.mark.parametrize("B,k,m", [(2, 100, 300), (1, 300, 100), (1, 257, 1000), (3, 64, 64)])
 def test_standard_ns(B, k, m):
     """The standard iteration on X (the Muon baseline) on the same kernels."""
