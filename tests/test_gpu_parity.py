@@ -375,11 +375,15 @@ def test_megabatch_accum_equals_add_then_step_bitwise():
         assert Ma[b].cpu().numpy().tobytes() == Mb[b].cpu().numpy().tobytes()
 
 
-def test_graph_capture_replays_match_eager():
+# the fused one-launch iteration (automatic path at this Gram side) and the
+# tiled products
+@pytest.mark.parametrize("path", [d3.PATH_AUTO, d3.PATH_TILED])
+def test_graph_capture_replays_match_eager(path):
     """The step's launch sequence (no allocation, no memset) captured in a HIP
     graph: every replay, with eager work and synchronizations in between,
     equals the same number of eager steps bit for bit."""
-    say("graph capture")
+    say("graph capture", path)
+    cfg = d3.ns_cfg(path=path)
     B, n, m, k = 3, 160, 288, 40
     Ws = [host_gaussian((n, m), [25, b], std=0.02) for b in range(B)]
     Ms = [host_gaussian((n, m), [26, b]) for b in range(B)]
@@ -392,16 +396,16 @@ def test_graph_capture_replays_match_eager():
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):          # warm the path outside the capture
-        d3.step_megabatch(Wg, Mg, k, 0.04, 0.95, ws=ws_g, ptrs=pg)
+        d3.step_megabatch(Wg, Mg, k, 0.04, 0.95, cfg, ws=ws_g, ptrs=pg)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
-    d3.step_megabatch(We, Me, k, 0.04, 0.95, ws=ws_e)
+    d3.step_megabatch(We, Me, k, 0.04, 0.95, cfg, ws=ws_e)
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
-        d3.step_megabatch(Wg, Mg, k, 0.04, 0.95, ws=ws_g, ptrs=pg)
+        d3.step_megabatch(Wg, Mg, k, 0.04, 0.95, cfg, ws=ws_g, ptrs=pg)
     for rep in range(3):
         graph.replay()
-        d3.step_megabatch(We, Me, k, 0.04, 0.95, ws=ws_e)
+        d3.step_megabatch(We, Me, k, 0.04, 0.95, cfg, ws=ws_e)
         junk = torch.randn(1000, device=DEV).sum()        # eager work between replays
         torch.cuda.synchronize()
         assert float(junk) == float(junk)
