@@ -224,13 +224,14 @@ def test_groups_more_side_sets_than_one_launch_holds():
     assert sum(n.startswith("gemm_back") for n in names) == 6
 
 
-@pytest.mark.parametrize("path", [d3.PATH_AUTO, d3.PATH_TILED])
-def test_grouped_step_graph_capture(path):
+@pytest.mark.parametrize("path,norm", [(d3.PATH_AUTO, None), (d3.PATH_TILED, None),
+                                       (d3.PATH_AUTO, (0.95, 1e-8))])
+def test_grouped_step_graph_capture(path, norm):
     """The grouped call (shared side-set launches, several products per
     launch, the fused small group on the automatic path) captured in a HIP
     graph: every replay equals an eager grouped step bit for bit, with eager
     work and synchronizations between replays."""
-    say("grouped step graph capture, path", path)
+    say("grouped step graph capture, path", path, "norm", norm)
     host = make(MIXED, 73)
     cfg = d3.ns_cfg(path=path)
 
@@ -238,8 +239,10 @@ def test_grouped_step_graph_capture(path):
         groups, tensors = [], []
         for (Ws, Ms), k in zip(host, KS_MIXED):
             Wd, Md = to_dev(Ws), to_dev(Ms)
-            groups.append(d3.Group(Wd, Md, k, 0.04))
-            tensors += Wd + Md
+            Vd = [torch.zeros(Ms[0].shape[0], dtype=torch.float32, device=DEV) for _ in Ms] \
+                if norm else None
+            groups.append(d3.Group(Wd, Md, k, 0.04, Vs=Vd))
+            tensors += Wd + Md + (Vd or [])
         return groups, tensors
 
     (ge, te), (gg, tg) = build(), build()
@@ -247,16 +250,16 @@ def test_grouped_step_graph_capture(path):
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):           # sizes the workspace outside the capture
-        d3.step_groups(gg, MU, cfg, ws=ws_g)
+        d3.step_groups(gg, MU, cfg, norm=norm, ws=ws_g)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
-    d3.step_groups(ge, MU, cfg, ws=ws_e)    # the eager copy takes the same first step
+    d3.step_groups(ge, MU, cfg, norm=norm, ws=ws_e)    # the eager copy takes the same first step
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
-        d3.step_groups(gg, MU, cfg, ws=ws_g)
+        d3.step_groups(gg, MU, cfg, norm=norm, ws=ws_g)
     for rep in range(3):
         graph.replay()
-        d3.step_groups(ge, MU, cfg, ws=ws_e)
+        d3.step_groups(ge, MU, cfg, norm=norm, ws=ws_e)
         junk = torch.randn(1000, device=DEV).sum()      # eager work between replays
         torch.cuda.synchronize()
         assert float(junk) == float(junk)
