@@ -224,14 +224,15 @@ def test_groups_more_side_sets_than_one_launch_holds():
     assert sum(n.startswith("gemm_back") for n in names) == 6
 
 
-@pytest.mark.parametrize("path,norm", [(d3.PATH_AUTO, None), (d3.PATH_TILED, None),
-                                       (d3.PATH_AUTO, (0.95, 1e-8))])
-def test_grouped_step_graph_capture(path, norm):
+@pytest.mark.parametrize("path,norm,acc", [(d3.PATH_AUTO, None, False), (d3.PATH_TILED, None, False),
+                                           (d3.PATH_AUTO, (0.95, 1e-8), False),
+                                           (d3.PATH_AUTO, None, True)])
+def test_grouped_step_graph_capture(path, norm, acc):
     """The grouped call (shared side-set launches, several products per
     launch, the fused small group on the automatic path) captured in a HIP
     graph: every replay equals an eager grouped step bit for bit, with eager
     work and synchronizations between replays."""
-    say("grouped step graph capture, path", path, "norm", norm)
+    say("grouped step graph capture, path", path, "norm", norm, "accumulate", acc)
     host = make(MIXED, 73)
     cfg = d3.ns_cfg(path=path)
 
@@ -241,7 +242,8 @@ def test_grouped_step_graph_capture(path, norm):
             Wd, Md = to_dev(Ws), to_dev(Ms)
             Vd = [torch.zeros(Ms[0].shape[0], dtype=torch.float32, device=DEV) for _ in Ms] \
                 if norm else None
-            groups.append(d3.Group(Wd, Md, k, 0.04, Vs=Vd))
+            Gd = [g * 0.1 for g in to_dev(Ms)] if acc else None    # fixed gradients
+            groups.append(d3.Group(Wd, Md, k, 0.04, Gs=Gd, Vs=Vd))
             tensors += Wd + Md + (Vd or [])
         return groups, tensors
 
